@@ -1,0 +1,20 @@
+"""CPU oracle of the MoE feed-forward block — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP path.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
+against brute force, closed forms, library routines and the parameter counts
+printed on the pages; see the docstring of each test.
+"""
+from .block import (NEAR_TIE_GAP, align, gelu_tanh, geglu, geglu_hidden, moe_ffn,
+                      moe_ffn_layer_residual, route, router_logits,
+                      routed_mixture_dense_mask, select_topk, softmax, widen_bf16)
+from .nvfp4 import E2M1_TABLE, E4M3_TABLE, dequant_matrix, e2m1_value, e4m3fn_value
+
+__all__ = [
+    "NEAR_TIE_GAP", "align", "gelu_tanh", "geglu", "geglu_hidden", "moe_ffn",
+    "moe_ffn_layer_residual", "route", "router_logits", "routed_mixture_dense_mask",
+    "select_topk", "softmax", "widen_bf16", "E2M1_TABLE", "E4M3_TABLE",
+    "dequant_matrix", "e2m1_value", "e4m3fn_value",
+]

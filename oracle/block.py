@@ -1,0 +1,299 @@
+"""CPU oracle of the Gemma 4 26B-A4B MoE feed-forward block (fp64, numpy).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+links this module; only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+kernels and imports nothing from the product package or from the input
+generators.
+
+What the block computes, with the passage each step follows:
+
+* Router logits z = x . W_r (one bias-free [H, E] matrix; the NVFP4
+  checkpoint config lists it as ``router.proj`` and keeps it unquantised) —
+  plus an optional per-expert logit bias, which only the skewed-load workload
+  uses to shape expert loads.
+* Gating: softmax over all expert logits (archdb page "Gemma-4-26B-A4B",
+  field "Gating function over expert logits": softmax).
+* Selection: the top_k_experts = 8 of num_experts = 128 (gemma-llm API page
+  ``gm.nn.Gemma4_26B_A4B``, ``TransformerConfig``; archdb fields "Routed
+  experts per MoE layer", "Routed experts selected per token").  Equal logits
+  go to the lower expert id.
+* Renormalisation: the selected softmax weights are divided by their sum
+  (archdb field "Selected expert weights are renormalized to sum to 1": Yes).
+* Each routed expert is a bias-free GeGLU MLP H -> I -> H with the
+  tanh-approximate GELU on the gate projection (archdb fields "FFN
+  activation": GeGLU (tanh-approximate GELU), "FFN projections have bias
+  terms": No, "Intermediate width of one routed expert": 704; NVFP4 config
+  ``hidden_activation: gelu_pytorch_tanh``).
+* The always-on dense branch is the same GeGLU form H -> D -> H with
+  D = 2112 (API page: "A dense shared MLP branch (intermediate_dim=2112)";
+  archdb fields "Always-on experts per MoE layer": 1, "Total intermediate
+  width of the shared expert(s)": 2,112).
+* The block output is the plain sum of the routed mixture and the dense
+  branch (the API page lists both branches in every layer; no weighting of
+  the dense branch is stated, so its weight is 1).
+
+Precision.  Inputs are bf16 and are widened exactly; all arithmetic is fp64.
+One decision is not arithmetic: which experts win.  The HIP path ranks fp32
+logits, so the oracle ranks its logits rounded to fp32 too (a decision taken
+in the kernel's precision); tokens whose k-th/(k+1)-th logit gap is at most
+1e-3 are reported as near-ties because either side may legitimately pick a
+different set there.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+SQRT_2_OVER_PI = math.sqrt(2.0 / math.pi)
+GELU_CUBIC = 0.044715
+NEAR_TIE_GAP = 1e-3
+
+
+# ---------------------------------------------------------------------------
+# element formats
+# ---------------------------------------------------------------------------
+
+
+def widen_bf16(bits) -> np.ndarray:
+    """bf16 raw bits (uint16) -> fp64.  A bf16 value is the top half of an fp32."""
+    b = np.asarray(bits)
+    if b.dtype != np.uint16:
+        return np.asarray(b, dtype=np.float64)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def gelu_tanh(v: np.ndarray) -> np.ndarray:
+    """tanh approximation of GELU (Hendrycks & Gimpel 2016, eq. for GELU(x)
+    ~ 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))))."""
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * v * (1.0 + np.tanh(SQRT_2_OVER_PI * (v + GELU_CUBIC * v * v * v)))
+
+
+# ---------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------
+
+
+def router_logits(x: np.ndarray, router_w: np.ndarray, bias=None) -> np.ndarray:
+    """z[t, e] = sum_h x[t, h] W_r[h, e] (+ b[e]), fp64."""
+    z = widen_bf16(x) @ widen_bf16(router_w)
+    if bias is not None:
+        z = z + np.asarray(bias, dtype=np.float64)[None, :]
+    return z
+
+
+def softmax(z: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis (shifted by the row maximum)."""
+    m = np.max(z, axis=-1, keepdims=True)
+    ez = np.exp(z - m)
+    return ez / np.sum(ez, axis=-1, keepdims=True)
+
+
+def select_topk(z: np.ndarray, k: int) -> tuple:
+    """Top-k expert ids per row, ranked on fp32 logits, lower id wins ties.
+
+    Returns (ids sorted by descending logit, the full ranking).
+    """
+    zd = np.asarray(z, dtype=np.float64).astype(np.float32)
+    T, E = zd.shape
+    ids = np.broadcast_to(np.arange(E), (T, E))
+    # np.lexsort sorts by the last key first: descending logit, then ascending id
+    order = np.lexsort((ids, -zd), axis=-1)
+    return order[:, :k], order
+
+
+def route(x, router_w, k: int, bias=None, force_routing=None) -> dict:
+    """Router of the block: logits, top-k selection, softmax, renormalise.
+
+    topk_idx[t] lists the selected experts in ascending id order and topk_w[t]
+    their renormalised weights in the same order.  ``force_routing`` replaces
+    the selected sets (used for near-tie tokens, where both sets are valid).
+    """
+    z = router_logits(x, router_w, bias)
+    T, E = z.shape
+    if force_routing is None:
+        sel, order = select_topk(z, k)
+    else:
+        sel = np.asarray(force_routing, dtype=np.int64).reshape(T, k)
+        _, order = select_topk(z, k)
+    idx = np.sort(sel, axis=1)
+    if k < E:
+        rows = np.arange(T)
+        gap = z[rows, order[:, k - 1]] - z[rows, order[:, k]]
+    else:
+        gap = np.full(T, np.inf)
+    p = softmax(z)
+    ps = np.take_along_axis(p, idx, axis=1)
+    w = ps / np.sum(ps, axis=1, keepdims=True)
+    return {"z": z, "p": p, "topk_idx": idx.astype(np.int32), "topk_w": w,
+            "gap": gap, "near_tie": gap <= NEAR_TIE_GAP}
+
+
+def align(topk_idx: np.ndarray, num_experts: int) -> dict:
+    """Group the (token, slot) pairs by expert: a stable counting sort.
+
+    counts[e]  = number of tokens that selected e
+    offsets    = exclusive prefix sum of counts, offsets[E] = T*k
+    perm[r]    = token id of row r; rows of expert e are
+                 offsets[e] .. offsets[e+1]-1, tokens ascending
+    pos[t, j]  = row of slot (t, j), i.e. where token t sits among the rows
+                 of expert topk_idx[t, j]
+    """
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, k = idx.shape
+    counts = np.zeros(num_experts, dtype=np.int64)
+    for e in idx.ravel():
+        counts[e] += 1
+    offsets = np.zeros(num_experts + 1, dtype=np.int64)
+    for e in range(num_experts):
+        offsets[e + 1] = offsets[e] + counts[e]
+    cursor = offsets[:-1].copy()
+    perm = np.empty(T * k, dtype=np.int64)
+    pos = np.empty((T, k), dtype=np.int64)
+    for t in range(T):              # token-major order keeps each expert's
+        for j in range(k):          # rows in ascending token order
+            e = idx[t, j]
+            r = cursor[e]
+            perm[r] = t
+            pos[t, j] = r
+            cursor[e] = r + 1
+    return {"counts": counts.astype(np.int32), "offsets": offsets.astype(np.int32),
+            "perm": perm.astype(np.int32), "pos": pos.astype(np.int32)}
+
+
+# ---------------------------------------------------------------------------
+# GeGLU MLPs
+# ---------------------------------------------------------------------------
+
+
+def geglu_hidden(X: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray) -> np.ndarray:
+    """h = gelu_tanh(X W_gate) * (X W_up); weights are [K, N] matrices."""
+    return gelu_tanh(X @ w_gate) * (X @ w_up)
+
+
+def geglu(X: np.ndarray, w_gate, w_up, w_down) -> tuple:
+    """One bias-free GeGLU MLP: returns (hidden, output)."""
+    h = geglu_hidden(X, w_gate, w_up)
+    return h, h @ w_down
+
+
+def _matrix(w, g: int) -> np.ndarray:
+    """fp64 [K, N] matrix g of a weight stack (bf16 bits, floats or NVFP4)."""
+    if isinstance(w, dict):
+        from .nvfp4 import dequant_matrix
+        return dequant_matrix(w["q"][g], w["scale"][g], w["tensor_scale"][g])
+    return widen_bf16(w[g])
+
+
+def _dense_matrix(w) -> np.ndarray:
+    if isinstance(w, dict):
+        return _matrix(w, 0)
+    return widen_bf16(w)
+
+
+# ---------------------------------------------------------------------------
+# the block
+# ---------------------------------------------------------------------------
+
+
+def moe_ffn(x, router_w, w_gate, w_up, w_down, d_gate=None, d_up=None, d_down=None,
+            top_k: int = 8, bias=None, force_routing=None, tokens=None,
+            intermediates: bool = True) -> dict:
+    """Forward of the MoE feed-forward block.
+
+    x [T, H] (bf16 bits or floats); router_w [H, E]; w_gate, w_up [E, H, I];
+    w_down [E, I, H]; d_gate, d_up [H, D]; d_down [D, H] (None: no dense
+    branch).  Expert and dense matrices may be NVFP4 packs (dicts with q,
+    scale, tensor_scale), which are dequantised first.
+
+    out[t] = sum_j w[t, j] * Expert_{e_j}(x_t) + Dense(x_t), the j-sum in
+    ascending j, then the dense term.  With ``tokens`` only those output rows
+    are computed (routing is still evaluated for every token).
+    """
+    X = widen_bf16(x)
+    T, H = X.shape
+    E = np.asarray(router_w).shape[1]
+    r = route(x, router_w, top_k, bias, force_routing)
+    a = align(r["topk_idx"], E)
+    res = dict(r)
+    res.update(a)
+    have_dense = d_gate is not None
+
+    if tokens is not None:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        out = np.zeros((len(tokens), H))
+        for i, t in enumerate(tokens):
+            acc = np.zeros(H)
+            for j in range(top_k):
+                e = int(r["topk_idx"][t, j])
+                _, ye = geglu(X[t:t + 1], _matrix(w_gate, e), _matrix(w_up, e),
+                              _matrix(w_down, e))
+                acc += r["topk_w"][t, j] * ye[0]
+            if have_dense:
+                _, yd = geglu(X[t:t + 1], _dense_matrix(d_gate), _dense_matrix(d_up),
+                              _dense_matrix(d_down))
+                acc += yd[0]
+            out[i] = acc
+        res["out"] = out
+        res["tokens"] = tokens
+        return res
+
+    I = (w_down["q"].shape[2] * 2) if isinstance(w_down, dict) else np.asarray(w_down).shape[1]
+    rows = T * top_k
+    h = np.zeros((rows, I)) if intermediates else None
+    y = np.zeros((rows, H))
+    offsets, perm = a["offsets"], a["perm"]
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        Xe = X[perm[lo:hi]]
+        he, ye = geglu(Xe, _matrix(w_gate, e), _matrix(w_up, e), _matrix(w_down, e))
+        if intermediates:
+            h[lo:hi] = he
+        y[lo:hi] = ye
+    if have_dense:
+        h_d, y_d = geglu(X, _dense_matrix(d_gate), _dense_matrix(d_up), _dense_matrix(d_down))
+    else:
+        h_d, y_d = None, np.zeros((T, H))
+    out = np.zeros((T, H))
+    pos, w = a["pos"], r["topk_w"]
+    for j in range(top_k):
+        out += w[:, j:j + 1] * y[pos[:, j]]
+    out += y_d
+    res.update({"out": out, "h": h, "y": y, "h_d": h_d, "y_d": y_d})
+    return res
+
+
+def moe_ffn_layer_residual(x, weights: dict, top_k: int, bias=None) -> tuple:
+    """One layer of a residual stack without attention: (x + FFN(x), details).
+
+    ``weights`` holds router, gate, up, down, dgate, dup, ddown.  Normalisation
+    layers around the block are not part of this stack.
+    """
+    r = moe_ffn(x, weights["router"], weights["gate"], weights["up"], weights["down"],
+                weights.get("dgate"), weights.get("dup"), weights.get("ddown"),
+                top_k=top_k, bias=bias, intermediates=False)
+    return widen_bf16(x) + r["out"], r
+
+
+def routed_mixture_dense_mask(x, router_w, w_gate, w_up, w_down, top_k: int,
+                              bias=None) -> np.ndarray:
+    """Routed branch by brute force: every expert on every token, weighted by a
+    dense [T, E] weight matrix that is zero outside the selected set.
+
+    Independent of ``align`` (no grouping or permutation); used to pin it.
+    """
+    X = widen_bf16(x)
+    T, H = X.shape
+    E = np.asarray(router_w).shape[1]
+    r = route(x, router_w, top_k, bias)
+    W = np.zeros((T, E))
+    np.put_along_axis(W, r["topk_idx"].astype(np.int64), r["topk_w"], axis=1)
+    acc = np.zeros((T, H))
+    for e in range(E):
+        _, ye = geglu(X, _matrix(w_gate, e), _matrix(w_up, e), _matrix(w_down, e))
+        acc += W[:, e:e + 1] * ye
+    return acc

@@ -1,0 +1,196 @@
+"""Planted mistakes in the CPU oracle must be caught by its pins.
+
+Each case swaps one oracle function for a plausibly wrong version (a sign
+flip, a dropped term, a swapped operand or index, a wrong tie-break, a wrong
+bit field) on the CPU, runs the pins that should notice, and expects at least
+one of them to fail.  Nothing here touches the GPU path.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.block as om
+import oracle.nvfp4 as on
+from tests import test_oracle_pins as pins
+
+
+def _patch(monkeypatch, name, fn, module=om):
+    monkeypatch.setattr(module, name, fn)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, fn)
+
+
+def _expect_caught(tests):
+    failures = 0
+    for t in tests:
+        try:
+            t()
+        except (AssertionError, ValueError, IndexError):
+            failures += 1
+    assert failures > 0, "planted mistake went unnoticed"
+
+
+ROUTING_PINS = [pins.test_routing_sets_match_brute_force_tiny,
+                pins.test_routing_tie_break_lowest_index,
+                pins.test_routing_weights_closed_form,
+                pins.test_routing_k1_and_kE]
+BLOCK_PINS = [pins.test_routed_branch_equals_dense_mask_brute_force,
+              pins.test_dense_branch_is_torch_geglu_mlp,
+              pins.test_single_expert_is_torch_geglu_mlp,
+              pins.test_identical_experts_give_one_expert,
+              pins.test_k_equals_E_is_full_softmax_mixture,
+              pins.test_zero_input_gives_zero_output]
+
+
+def test_gelu_cubic_sign(monkeypatch):
+    _patch(monkeypatch, "gelu_tanh", lambda v: 0.5 * np.asarray(v) * (
+        1 + np.tanh(om.SQRT_2_OVER_PI * (np.asarray(v) - om.GELU_CUBIC * np.asarray(v) ** 3))))
+    _expect_caught([pins.test_gelu_matches_torch_tanh_gelu] + BLOCK_PINS)
+
+
+def test_gelu_on_up_instead_of_gate(monkeypatch):
+    _patch(monkeypatch, "geglu_hidden", lambda X, g, u: (X @ g) * om.gelu_tanh(X @ u))
+    _expect_caught(BLOCK_PINS)
+
+
+def test_missing_renormalisation(monkeypatch):
+    real = om.route
+
+    def bad(*a, **k):
+        r = real(*a, **k)
+        r["topk_w"] = np.take_along_axis(r["p"], r["topk_idx"].astype(np.int64), axis=1)
+        return r
+
+    _patch(monkeypatch, "route", bad)
+    _expect_caught(ROUTING_PINS + BLOCK_PINS)
+
+
+def test_bottom_k_selection(monkeypatch):
+    def bad(z, k):
+        zd = np.asarray(z).astype(np.float32)
+        order = np.lexsort((np.broadcast_to(np.arange(zd.shape[1]), zd.shape), zd), axis=-1)
+        return order[:, :k], order
+
+    _patch(monkeypatch, "select_topk", bad)
+    _expect_caught(ROUTING_PINS)
+
+
+def test_highest_index_tie_break(monkeypatch):
+    def bad(z, k):
+        zd = np.asarray(z).astype(np.float32)
+        order = np.lexsort((-np.broadcast_to(np.arange(zd.shape[1]), zd.shape), -zd), axis=-1)
+        return order[:, :k], order
+
+    _patch(monkeypatch, "select_topk", bad)
+    _expect_caught(ROUTING_PINS)
+
+
+def test_align_descending_tokens(monkeypatch):
+    real = om.align
+
+    def bad(idx, E):
+        a = real(idx, E)
+        perm = a["perm"].copy()
+        for e in range(E):
+            lo, hi = a["offsets"][e], a["offsets"][e + 1]
+            perm[lo:hi] = perm[lo:hi][::-1]
+        a["perm"] = perm
+        return a
+
+    _patch(monkeypatch, "align", bad)
+    _expect_caught([lambda: pins.test_align_matches_stable_argsort(32, 8, 2)])
+
+
+def test_combine_uses_perm_not_pos(monkeypatch):
+    real_align = om.align
+
+    def bad(idx, E):
+        a = real_align(idx, E)
+        T, k = np.asarray(idx).shape
+        a["pos"] = np.arange(T * k).reshape(T, k).astype(np.int32)
+        return a
+
+    _patch(monkeypatch, "align", bad)
+    _expect_caught(BLOCK_PINS)
+
+
+def test_dropped_dense_term(monkeypatch):
+    real = om.geglu
+    calls = {"n": 0}
+
+    def bad(X, g, u, d):
+        h, y = real(X, g, u, d)
+        # the dense branch is the call with the whole token batch and a
+        # dense-width hidden layer; drop its output
+        if np.asarray(g).shape[1] == 128:
+            calls["n"] += 1
+            return h, np.zeros_like(y)
+        return h, y
+
+    _patch(monkeypatch, "geglu", bad)
+    _expect_caught([pins.test_dense_branch_is_torch_geglu_mlp])
+    assert calls["n"] > 0
+
+
+def test_transposed_down_operand(monkeypatch):
+    real = om._matrix
+
+    def bad(w, g):
+        m = real(w, g)
+        if m.shape[0] == m.shape[1]:
+            return m.T
+        return m
+
+    # on a square-shaped variant the slip is silent to numpy; use the tiny
+    # block with I == H to make it plausible and check the pins catch it
+    monkeypatch.setattr(om, "_matrix", bad)
+    import synth
+    shape = synth.FFNShape("sq", 16, 64, 4, 2, 64, 64)
+    x = synth.make_x(shape)
+    w = synth.make_weights(shape)
+    r = om.moe_ffn(x, w["router"], w["gate"], w["up"], w["down"], top_k=2)
+    monkeypatch.undo()
+    bf = om.routed_mixture_dense_mask(x, w["router"], w["gate"], w["up"], w["down"], 2)
+    assert np.max(np.abs(r["out"] - bf)) > 1e-6
+
+
+def test_e4m3_wrong_bias(monkeypatch):
+    def bad(b):
+        b = int(b) & 0xFF
+        e, m = (b >> 3) & 0xF, b & 7
+        s = -1.0 if b >> 7 else 1.0
+        if e == 15 and m == 7:
+            return float("nan")
+        return s * ((m / 8) * 2.0 ** -7 if e == 0 else (1 + m / 8) * 2.0 ** (e - 8))
+
+    table = np.array([bad(b) for b in range(256)])
+    monkeypatch.setattr(on, "E4M3_TABLE", table)
+    monkeypatch.setattr(oracle, "E4M3_TABLE", table)
+    _expect_caught([pins.test_e4m3_decoder_matches_torch_all_codes,
+                    pins.test_nvfp4_dequant_layout_and_roundtrip])
+
+
+def test_nibble_order_swapped(monkeypatch):
+    def bad(q):
+        q = np.asarray(q, dtype=np.uint8)
+        N, KH = q.shape
+        c = np.empty((N, 2 * KH), dtype=np.uint8)
+        c[:, 0::2] = q >> 4
+        c[:, 1::2] = q & 0xF
+        return c
+
+    monkeypatch.setattr(on, "unpack_codes", bad)
+    _expect_caught([pins.test_nvfp4_dequant_layout_and_roundtrip])
+
+
+@pytest.mark.parametrize("exp_bias", [0, 2])
+def test_e2m1_wrong_exponent_bias(monkeypatch, exp_bias):
+    def bad(code):
+        code = int(code) & 0xF
+        s = -1.0 if code >> 3 else 1.0
+        e, m = (code >> 1) & 3, code & 1
+        return s * ((m / 2) * 2.0 ** (1 - exp_bias) if e == 0 else (1 + m / 2) * 2.0 ** (e - exp_bias))
+
+    monkeypatch.setattr(on, "e2m1_value", bad)
+    monkeypatch.setattr(oracle, "e2m1_value", bad)
+    _expect_caught([pins.test_e2m1_decoder_matches_ocp_table])
