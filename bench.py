@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE feed-forward block on one MI355X.
+
+One step = one forward of the whole block (router, grouping, gate/up with
+GeGLU, down, combine) over one batch of synthetic tokens at the Gemma 4
+26B-A4B layer shape.  The headline line is the decode workload (T = 8); the
+prefill workload (T = 4096) is reported in the same JSON line.
+
+Inputs are generated on the host from fixed seeds and uploaded before timing;
+the weights are replicated into several bit-identical device copies that the
+steps rotate through, so each step streams its weights from HBM rather than
+from the 256 MB last-level cache.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "MoE-FFN tokens/s per layer (26B-A4B shape, bf16) at T=8 and 4096; % roofline"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--prefill-steps", type=int, default=40)
+    p.add_argument("--copies", type=int, default=4, help="weight copies rotated at decode")
+    p.add_argument("--graph", action="store_true", help="replay each step from a HIP graph")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def to_dev_bf16(torch, a):
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    return t.to("cuda")
+
+
+def gateup_bytes(shape, n_act):
+    """Algorithmic HBM bytes of one gate/up launch (routed experts + dense)."""
+    H, I, D, T, k = shape.hidden, shape.expert_dim, shape.dense_dim, shape.tokens, shape.top_k
+    weights = n_act * 2 * H * I * 2 + 2 * H * D * 2
+    acts = T * H * 2 + (T * k * I + T * D) * 2
+    return weights + acts
+
+
+def step_bytes(shape, n_act):
+    """Algorithmic HBM bytes of one whole forward (weights once, activations once)."""
+    H, I, D, E, T = shape.hidden, shape.expert_dim, shape.dense_dim, shape.experts, shape.tokens
+    return n_act * 3 * H * I * 2 + 3 * H * D * 2 + H * E * 2 + 2 * T * H * 2
+
+
+def gateup_flops(shape):
+    H, I, D, T, k = shape.hidden, shape.expert_dim, shape.dense_dim, shape.tokens, shape.top_k
+    return 2 * T * k * H * 2 * I + 2 * T * H * 2 * D
+
+
+def step_flops(shape):
+    H, I, D, E, T, k = (shape.hidden, shape.expert_dim, shape.dense_dim, shape.experts,
+                        shape.tokens, shape.top_k)
+    return T * (2 * H * E + k * 2 * 3 * H * I + 2 * 3 * H * D)
+
+
+def run_workload(torch, shape, steps, warmup, copies, graph):
+    """Time `steps` forwards; returns a dict of measurements."""
+    import synth
+    from sparse_moe_transformer_amd import MoeFFN, binding
+
+    x = synth.make_x(shape)
+    w = synth.make_weights(shape)
+    bias = synth.zipf_bias(shape.experts) if shape.skew else None
+    xd = to_dev_bf16(torch, x)
+    base = {k: to_dev_bf16(torch, v) for k, v in w.items() if v is not None}
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+    bd = torch.from_numpy(bias).cuda() if bias is not None else None
+    out = torch.empty_like(xd)
+    ffn = MoeFFN.for_shape(shape)
+    torch.cuda.synchronize()
+
+    def fwd(i):
+        ffn.forward(xd, sets[i % copies], out, bd)
+
+    graphs = None
+    if graph:
+        for i in range(copies):  # warm the kernels before capture
+            fwd(i)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fwd(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step(i):
+        if graphs is not None:
+            graphs[i % copies].replay()
+        else:
+            fwd(i)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    counts = ffn.routing(shape.tokens)["counts"].cpu().numpy()
+    n_act = int((counts > 0).sum())
+
+    # timed region
+    t0 = time.perf_counter()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / steps
+
+    # per-stage durations: HIP events recorded by the library on the
+    # forward's stream around each kernel group, over `steps` eager forwards
+    stage_mask = (1 << binding.MOE_FFN_NUM_STAGES) - 1
+    binding.check(binding.moe_ffn_profile_begin(ffn.h, stage_mask, steps))
+    for i in range(steps):
+        fwd(i)
+    rc, stage_ms, stage_n = binding.moe_ffn_profile_end(ffn.h)
+    binding.check(rc)
+    stage_avg_us = [1000.0 * m / n if n else 0.0 for m, n in zip(stage_ms, stage_n)]
+    ffn.close()
+    return {"ms_per_step": ms_step, "wall_s": wall, "n_act": n_act, "counts": counts,
+            "stage_avg_us": stage_avg_us, "x": x, "w": w, "bias": bias}
+
+
+def cpu_baseline(shape, x, w, bias, seconds):
+    """The oracle (as it stands) on the host cores over a bounded sample."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+                or [1])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.moe_ffn(x, w["router"], w["gate"], w["up"], w["down"], w["dgate"], w["dup"],
+                       w["ddown"], top_k=shape.top_k, bias=bias, intermediates=False)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 50:
+            break
+    return {"value": n * shape.tokens / el, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n} full fp64 oracle forwards of the T={shape.tokens} workload "
+                      f"({el:.1f} s, numpy/OpenBLAS)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the block shards by tokens with replicated weights; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import synth
+
+    dec = synth.DECODE
+    r = run_workload(torch, dec, args.steps, args.warmup, args.copies, args.graph)
+    gu_bytes = gateup_bytes(dec, r["n_act"])
+    gu_us = r["stage_avg_us"][2]
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": dec.tokens / (r["ms_per_step"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded x ~ N(0,1), weights ~ N(0,1/fan_in), rounded to bf16",
+        "config": {"workload": "Gemma 4 26B-A4B MoE FFN layer, decode T=8 (H=2816, E=128, "
+                               "top-8, expert 704, dense 2112)",
+                   "tokens": dec.tokens, "hidden": dec.hidden, "experts": dec.experts,
+                   "top_k": dec.top_k, "expert_dim": dec.expert_dim, "dense_dim": dec.dense_dim,
+                   "weight_copies": args.copies, "graph": bool(args.graph),
+                   "active_experts": r["n_act"]},
+        "roofline": {"bound": "hbm", "kernel": "gate/up (stream_gateup: routed + dense)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": gu_bytes, "avg_us": gu_us},
+        "step_hbm": {"algorithmic_bytes": step_bytes(dec, r["n_act"]),
+                     "GBps": step_bytes(dec, r["n_act"]) / (r["ms_per_step"] * 1e-3) / 1e9,
+                     "frac": step_bytes(dec, r["n_act"]) / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "stage_avg_us": dict(zip(["route", "align", "gateup", "down", "combine"],
+                                 [round(v, 2) for v in r["stage_avg_us"]])),
+    }
+    if not args.no_prefill:
+        pre = synth.PREFILL
+        rp = run_workload(torch, pre, args.prefill_steps, max(3, args.warmup // 4), 2, args.graph)
+        gu_us = rp["stage_avg_us"][2]
+        tf = gateup_flops(pre) / (gu_us * 1e-6) / 1e12
+        step_tf = step_flops(pre) / (rp["ms_per_step"] * 1e-3) / 1e12
+        line["prefill"] = {
+            "workload": "same layer, prefill T=4096", "tokens": pre.tokens,
+            "value": pre.tokens / (rp["ms_per_step"] * 1e-3), "unit": "tokens/s",
+            "ms_per_step": rp["ms_per_step"], "steps": args.prefill_steps,
+            "step_tflops": step_tf, "step_mfma_frac": step_tf / BF16_PEAK_TFLOPS,
+            "roofline": {"bound": "mfma", "kernel": "gate/up (gemm MFMA: routed + dense)",
+                         "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
+                         "algorithmic_flops": gateup_flops(pre), "avg_us": gu_us},
+            "stage_avg_us": dict(zip(["route", "align", "gateup", "down", "combine"],
+                                     [round(v, 2) for v in rp["stage_avg_us"]])),
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(dec, r["x"], r["w"], r["bias"], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,600 @@
+// C ABI of the MoE FFN block: validation, workspace ownership, variant choice
+// and the launch sequence on the caller's stream.  Declared in moe_ffn.h.
+#include "moe_ffn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <exception>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+// event pairs of one profiled stage
+struct StageProfile {
+  std::vector<hipEvent_t> start, stop;
+  int used = 0;
+};
+}  // namespace
+
+struct moe_ffn_handle {
+  moe_ffn_config cfg;
+  int device;
+  void* ws_base;
+  size_t ws_bytes;
+  moe::Workspace ws;
+  int variant;
+  int max_mtiles;
+  int last_T;
+  bool sync_mode;
+  uint32_t prof_mask;
+  int prof_max;
+  int prof_fwd;  // forwards timed so far
+  StageProfile prof[MOE_FFN_NUM_STAGES];
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_FFN_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxTokensLimit = 1 << 20;
+
+int validate_config(const moe_ffn_config* c) {
+  if (!c) return fail(MOE_FFN_ERR_INVALID_ARG, "config is NULL");
+  if (c->max_tokens < 1 || c->max_tokens > kMaxTokensLimit)
+    return fail(MOE_FFN_ERR_INVALID_ARG, "max_tokens must be in [1, 2^20]");
+  if (c->hidden <= 0 || c->hidden % 256)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "hidden must be a positive multiple of 256");
+  if (c->num_experts < 1 || c->num_experts > 256)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "num_experts must be in [1, 256]");
+  if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->num_experts)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "top_k must be in [1, min(num_experts, 16)]");
+  if (c->expert_dim <= 0 || c->expert_dim % 64)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "expert_dim must be a positive multiple of 64");
+  if (c->dense_dim < 0 || c->dense_dim % 64)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "dense_dim must be 0 or a positive multiple of 64");
+  if (c->weight_format != MOE_FFN_W_BF16 && c->weight_format != MOE_FFN_W_NVFP4)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "unknown weight_format");
+  if (c->flags & ~uint32_t(MOE_FFN_ACCUMULATE)) return fail(MOE_FFN_ERR_UNSUPPORTED, "unknown flag bits");
+  return MOE_FFN_OK;
+}
+
+// Workspace layout: every buffer 256-byte aligned.
+struct Layout {
+  size_t off[17];
+  size_t total;
+  int max_mtiles;
+};
+
+Layout layout(const moe_ffn_config& c) {
+  const size_t T = size_t(c.max_tokens), E = size_t(c.num_experts), k = size_t(c.top_k);
+  const size_t H = size_t(c.hidden), I = size_t(c.expert_dim), D = size_t(c.dense_dim);
+  const size_t nb = (T + 63) / 64;
+  Layout L{};
+  L.max_mtiles = int((T * k + moe::kGemmBM - 1) / moe::kGemmBM + E);
+  const size_t sizes[17] = {
+      T * E * 4,                                  // logits
+      size_t(moe::kRouteSplits) * 64 * E * 4,     // route_part
+      T * k * 4,                                  // topk_idx
+      T * k * 4,                                  // topk_w
+      E * 4,                                      // counts
+      (E + 1) * 4,                                // offsets
+      nb * E * 8,                                 // blk_mask
+      nb * E * 4,                                 // blk_base
+      T * k * 4,                                  // perm
+      T * k * 4,                                  // pos
+      size_t(L.max_mtiles) * 16,                  // mtiles
+      E * 16,                                     // active
+      16 * 4,                                     // meta
+      T * k * I * 2,                              // h
+      T * (D ? D : 1) * 2,                        // h_d
+      T * k * H * 2,                              // y
+      T * H * 2,                                  // y_d
+  };
+  size_t o = 0;
+  for (int i = 0; i < 17; ++i) {
+    L.off[i] = o;
+    o += (sizes[i] + 255) & ~size_t(255);
+  }
+  L.total = o;
+  return L;
+}
+
+moe::Workspace bind(void* base, const Layout& L) {
+  char* b = static_cast<char*>(base);
+  moe::Workspace w;
+  w.logits = reinterpret_cast<float*>(b + L.off[0]);
+  w.route_part = reinterpret_cast<float*>(b + L.off[1]);
+  w.topk_idx = reinterpret_cast<int32_t*>(b + L.off[2]);
+  w.topk_w = reinterpret_cast<float*>(b + L.off[3]);
+  w.counts = reinterpret_cast<int32_t*>(b + L.off[4]);
+  w.offsets = reinterpret_cast<int32_t*>(b + L.off[5]);
+  w.blk_mask = reinterpret_cast<uint64_t*>(b + L.off[6]);
+  w.blk_base = reinterpret_cast<int32_t*>(b + L.off[7]);
+  w.perm = reinterpret_cast<int32_t*>(b + L.off[8]);
+  w.pos = reinterpret_cast<int32_t*>(b + L.off[9]);
+  w.mtiles = reinterpret_cast<int32_t*>(b + L.off[10]);
+  w.active = reinterpret_cast<int32_t*>(b + L.off[11]);
+  w.meta = reinterpret_cast<int32_t*>(b + L.off[12]);
+  w.h = reinterpret_cast<moe::bf16_t*>(b + L.off[13]);
+  w.h_d = reinterpret_cast<moe::bf16_t*>(b + L.off[14]);
+  w.y = reinterpret_cast<moe::bf16_t*>(b + L.off[15]);
+  w.y_d = reinterpret_cast<moe::bf16_t*>(b + L.off[16]);
+  return w;
+}
+
+// Makes the handle's device current for the scope of a call.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+int check_handle(moe_ffn_handle* h) {
+  if (!h) return fail(MOE_FFN_ERR_INVALID_ARG, "handle is NULL");
+  return MOE_FFN_OK;
+}
+
+int finish(moe_ffn_handle* h, hipStream_t s, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (h->sync_mode) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  g_err.clear();
+  return MOE_FFN_OK;
+}
+
+moe::Shape shape_of(const moe_ffn_handle* h, int T) {
+  const moe_ffn_config& c = h->cfg;
+  return moe::Shape{T, c.hidden, c.num_experts, c.top_k, c.expert_dim, c.dense_dim};
+}
+
+// stream weights when every expert sees few rows; MFMA tiles otherwise
+constexpr int kStreamMaxTokens = 32;
+
+// Records the stage's start event (when profiled) on construction and its
+// stop event on stop().
+struct StageTimer {
+  moe_ffn_handle* h;
+  int stage;
+  hipStream_t s;
+  bool on;
+  StageTimer(moe_ffn_handle* h_, int stage_, hipStream_t s_, bool timing) : h(h_), stage(stage_), s(s_) {
+    StageProfile& p = h->prof[stage];
+    on = timing && (h->prof_mask & (1u << stage)) && p.used < int(p.start.size());
+    if (on) (void)hipEventRecord(p.start[p.used], s);
+  }
+  void stop() {
+    if (!on) return;
+    StageProfile& p = h->prof[stage];
+    (void)hipEventRecord(p.stop[p.used], s);
+    ++p.used;
+    on = false;
+  }
+};
+
+int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, const float* bias,
+                const moe::StreamArgs& args, void* out, hipStream_t s) {
+  const moe::Shape sh = args.sh;
+  const moe::Workspace& ws = h->ws;
+  const bool timing = h->prof_mask != 0 && h->prof_fwd < h->prof_max;
+  hipError_t e;
+  const auto* xb = static_cast<const moe::bf16_t*>(x);
+  const auto* wr = static_cast<const moe::bf16_t*>(router_w);
+  {
+    StageTimer tm(h, MOE_FFN_STAGE_ROUTE, s, timing);
+    e = (T <= moe::kRouteSmallT) ? moe::launch_route_small(sh, xb, wr, bias, ws, s)
+                                 : moe::launch_route_large(sh, xb, wr, bias, ws, s);
+    tm.stop();
+    if (e != hipSuccess) return hip_fail(e, "route");
+  }
+  if (T > moe::kRouteSmallT) {
+    StageTimer tm(h, MOE_FFN_STAGE_ALIGN, s, timing);
+    e = moe::launch_align(sh, ws, s);
+    tm.stop();
+    if (e != hipSuccess) return hip_fail(e, "align");
+  }
+  bool stream = (h->variant == MOE_FFN_VARIANT_STREAM) ||
+                (h->variant == MOE_FFN_VARIANT_AUTO && T <= kStreamMaxTokens);
+  if (args.nvfp4) stream = false;  // the streaming kernels read bf16 [K, N] weights only
+  const int mt = int((size_t(T) * sh.k + moe::kGemmBM - 1) / moe::kGemmBM + sh.E);
+  {
+    StageTimer tm(h, MOE_FFN_STAGE_GATEUP, s, timing);
+    e = stream ? moe::launch_stream_gateup(args, ws, s) : moe::launch_gemm_gateup(args, ws, mt, s);
+    tm.stop();
+    if (e != hipSuccess) return hip_fail(e, "gate/up");
+  }
+  {
+    StageTimer tm(h, MOE_FFN_STAGE_DOWN, s, timing);
+    e = stream ? moe::launch_stream_down(args, ws, s) : moe::launch_gemm_down(args, ws, mt, s);
+    tm.stop();
+    if (e != hipSuccess) return hip_fail(e, "down");
+  }
+  {
+    StageTimer tm(h, MOE_FFN_STAGE_COMBINE, s, timing);
+    e = moe::launch_combine(sh, ws, static_cast<moe::bf16_t*>(out), (h->cfg.flags & MOE_FFN_ACCUMULATE) != 0, s);
+    tm.stop();
+    if (e != hipSuccess) return hip_fail(e, "combine");
+  }
+  if (timing) ++h->prof_fwd;
+  h->last_T = T;
+  return finish(h, s, "forward");
+}
+
+void profile_release(moe_ffn_handle* h) {
+  for (auto& p : h->prof) {
+    for (auto ev : p.start) (void)hipEventDestroy(ev);
+    for (auto ev : p.stop) (void)hipEventDestroy(ev);
+    p.start.clear();
+    p.stop.clear();
+    p.used = 0;
+  }
+  h->prof_mask = 0;
+  h->prof_max = 0;
+  h->prof_fwd = 0;
+}
+
+int common_forward_checks(moe_ffn_handle* h, int T, const void* x, const void* router_w,
+                          const float* bias, const void* out, int fmt) {
+  if (int r = check_handle(h)) return r;
+  if (h->cfg.weight_format != fmt)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "weight format of the handle does not match this entry point");
+  if (T < 0 || T > h->cfg.max_tokens) return fail(MOE_FFN_ERR_INVALID_ARG, "T must be in [0, max_tokens]");
+  if (!x || !router_w || !out) return fail(MOE_FFN_ERR_INVALID_ARG, "x, router_w and out must not be NULL");
+  if (!aligned16(x) || !aligned16(router_w) || !aligned16(out))
+    return fail(MOE_FFN_ERR_INVALID_ARG, "x, router_w and out must be 16-byte aligned");
+  if (bias && (reinterpret_cast<uintptr_t>(bias) & 3u))
+    return fail(MOE_FFN_ERR_INVALID_ARG, "router_bias must be 4-byte aligned");
+  if (!(h->cfg.flags & MOE_FFN_ACCUMULATE) && x == out)
+    return fail(MOE_FFN_ERR_INVALID_ARG, "out may alias x only with MOE_FFN_ACCUMULATE");
+  return MOE_FFN_OK;
+}
+
+int check_fp4(const moe_ffn_nvfp4_t* m, bool required, const char* name) {
+  if (!required) {
+    if (m && (m->q || m->scale || m->tensor_scale))
+      return fail(MOE_FFN_ERR_INVALID_ARG, std::string(name) + " must be empty when dense_dim == 0");
+    return MOE_FFN_OK;
+  }
+  if (!m || !m->q || !m->scale || !m->tensor_scale)
+    return fail(MOE_FFN_ERR_INVALID_ARG, std::string(name) + ": q, scale and tensor_scale must not be NULL");
+  if (!aligned16(m->q) || (reinterpret_cast<uintptr_t>(m->scale) & 1u) ||
+      (reinterpret_cast<uintptr_t>(m->tensor_scale) & 3u))
+    return fail(MOE_FFN_ERR_INVALID_ARG, std::string(name) + ": misaligned pointer");
+  return MOE_FFN_OK;
+}
+
+moe::Fp4Mat to_mat(const moe_ffn_nvfp4_t* m) {
+  if (!m) return moe::Fp4Mat{nullptr, nullptr, nullptr};
+  return moe::Fp4Mat{m->q, m->scale, m->tensor_scale};
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ffn_workspace_bytes(const moe_ffn_config* cfg, size_t* bytes) {
+  try {
+    if (!bytes) return fail(MOE_FFN_ERR_INVALID_ARG, "bytes is NULL");
+    if (int r = validate_config(cfg)) return r;
+    *bytes = layout(*cfg).total;
+    return MOE_FFN_OK;
+  } catch (const std::exception& ex) {
+    return fail(MOE_FFN_ERR_INVALID_ARG, ex.what());
+  } catch (...) {
+    return fail(MOE_FFN_ERR_INVALID_ARG, "unknown exception");
+  }
+}
+
+int moe_ffn_create(const moe_ffn_config* cfg, moe_ffn_handle** out_handle) {
+  try {
+    if (!out_handle) return fail(MOE_FFN_ERR_INVALID_ARG, "out_handle is NULL");
+    *out_handle = nullptr;
+    if (int r = validate_config(cfg)) return r;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    Layout L = layout(*cfg);
+    void* base = nullptr;
+    e = hipMalloc(&base, L.total);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MOE_FFN_ERR_OOM, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
+    }
+    // tickets and tables start at zero; this is the only memset (create is
+    // never part of a captured graph)
+    e = hipMemset(base, 0, L.total);
+    if (e != hipSuccess) {
+      (void)hipFree(base);
+      return hip_fail(e, "workspace hipMemset");
+    }
+    auto* h = new moe_ffn_handle{};
+    h->cfg = *cfg;
+    h->device = dev;
+    h->ws_base = base;
+    h->ws_bytes = L.total;
+    h->ws = bind(base, L);
+    h->variant = MOE_FFN_VARIANT_AUTO;
+    h->max_mtiles = L.max_mtiles;
+    h->last_T = 0;
+    const char* sm = std::getenv("MOE_FFN_SYNC");
+    h->sync_mode = sm && std::strcmp(sm, "1") == 0;
+    *out_handle = h;
+    g_err.clear();
+    return MOE_FFN_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(MOE_FFN_ERR_OOM, "host allocation failed");
+  } catch (const std::exception& ex) {
+    return fail(MOE_FFN_ERR_HIP, ex.what());
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_destroy(moe_ffn_handle* h) {
+  try {
+    if (!h) return MOE_FFN_OK;
+    DeviceGuard g(h->device);
+    hipError_t e = hipDeviceSynchronize();
+    profile_release(h);
+    hipError_t f = hipFree(h->ws_base);
+    delete h;
+    if (e != hipSuccess) return hip_fail(e, "destroy: device sync");
+    if (f != hipSuccess) return hip_fail(f, "destroy: hipFree");
+    return MOE_FFN_OK;
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_set_variant(moe_ffn_handle* h, int32_t variant) {
+  if (int r = check_handle(h)) return r;
+  if (variant < MOE_FFN_VARIANT_AUTO || variant > MOE_FFN_VARIANT_MFMA)
+    return fail(MOE_FFN_ERR_INVALID_ARG, "unknown variant");
+  h->variant = variant;
+  return MOE_FFN_OK;
+}
+
+int moe_ffn_forward(moe_ffn_handle* h, int32_t T, const void* x, const void* router_w,
+                    const float* router_bias, const void* w_gate, const void* w_up, const void* w_down,
+                    const void* d_gate, const void* d_up, const void* d_down, void* out, void* stream) {
+  try {
+    if (int r = common_forward_checks(h, T, x, router_w, router_bias, out, MOE_FFN_W_BF16)) return r;
+    if (!w_gate || !w_up || !w_down) return fail(MOE_FFN_ERR_INVALID_ARG, "expert weights must not be NULL");
+    if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down))
+      return fail(MOE_FFN_ERR_INVALID_ARG, "expert weights must be 16-byte aligned");
+    const bool dense = h->cfg.dense_dim > 0;
+    if (dense) {
+      if (!d_gate || !d_up || !d_down) return fail(MOE_FFN_ERR_INVALID_ARG, "dense weights must not be NULL");
+      if (!aligned16(d_gate) || !aligned16(d_up) || !aligned16(d_down))
+        return fail(MOE_FFN_ERR_INVALID_ARG, "dense weights must be 16-byte aligned");
+    } else if (d_gate || d_up || d_down) {
+      return fail(MOE_FFN_ERR_INVALID_ARG, "dense weights must be NULL when dense_dim == 0");
+    }
+    if (T == 0) {
+      g_err.clear();
+      return MOE_FFN_OK;
+    }
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(MOE_FFN_ERR_HIP, "cannot make the handle's device current");
+    moe::StreamArgs a{};
+    a.sh = shape_of(h, T);
+    a.x = static_cast<const moe::bf16_t*>(x);
+    a.wg = static_cast<const moe::bf16_t*>(w_gate);
+    a.wu = static_cast<const moe::bf16_t*>(w_up);
+    a.wd = static_cast<const moe::bf16_t*>(w_down);
+    a.dg = static_cast<const moe::bf16_t*>(d_gate);
+    a.du = static_cast<const moe::bf16_t*>(d_up);
+    a.dd = static_cast<const moe::bf16_t*>(d_down);
+    a.nvfp4 = false;
+    return run_forward(h, T, x, router_w, router_bias, a, out, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return fail(MOE_FFN_ERR_HIP, ex.what());
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_forward_nvfp4(moe_ffn_handle* h, int32_t T, const void* x, const void* router_w,
+                          const float* router_bias, const moe_ffn_nvfp4_t* w_gate, const moe_ffn_nvfp4_t* w_up,
+                          const moe_ffn_nvfp4_t* w_down, const moe_ffn_nvfp4_t* d_gate,
+                          const moe_ffn_nvfp4_t* d_up, const moe_ffn_nvfp4_t* d_down, void* out,
+                          void* stream) {
+  try {
+    if (int r = common_forward_checks(h, T, x, router_w, router_bias, out, MOE_FFN_W_NVFP4)) return r;
+    if (int r = check_fp4(w_gate, true, "w_gate")) return r;
+    if (int r = check_fp4(w_up, true, "w_up")) return r;
+    if (int r = check_fp4(w_down, true, "w_down")) return r;
+    const bool dense = h->cfg.dense_dim > 0;
+    if (int r = check_fp4(d_gate, dense, "d_gate")) return r;
+    if (int r = check_fp4(d_up, dense, "d_up")) return r;
+    if (int r = check_fp4(d_down, dense, "d_down")) return r;
+    if (T == 0) {
+      g_err.clear();
+      return MOE_FFN_OK;
+    }
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(MOE_FFN_ERR_HIP, "cannot make the handle's device current");
+    moe::StreamArgs a{};
+    a.sh = shape_of(h, T);
+    a.x = static_cast<const moe::bf16_t*>(x);
+    a.fg = to_mat(w_gate);
+    a.fu = to_mat(w_up);
+    a.fd = to_mat(w_down);
+    a.fdg = to_mat(dense ? d_gate : nullptr);
+    a.fdu = to_mat(dense ? d_up : nullptr);
+    a.fdd = to_mat(dense ? d_down : nullptr);
+    a.nvfp4 = true;
+    return run_forward(h, T, x, router_w, router_bias, a, out, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return fail(MOE_FFN_ERR_HIP, ex.what());
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_get_routing(moe_ffn_handle* h, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* pos, void* stream) {
+  try {
+    if (int r = check_handle(h)) return r;
+    DeviceGuard g(h->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t Tk = size_t(h->last_T) * h->cfg.top_k;
+    const size_t E = size_t(h->cfg.num_experts);
+    struct C {
+      void* dst;
+      const void* src;
+      size_t n;
+    } cps[6] = {{topk_idx, h->ws.topk_idx, Tk * 4}, {topk_w, h->ws.topk_w, Tk * 4},
+                {counts, h->ws.counts, E * 4},      {offsets, h->ws.offsets, (E + 1) * 4},
+                {perm, h->ws.perm, Tk * 4},         {pos, h->ws.pos, Tk * 4}};
+    for (auto& c : cps) {
+      if (!c.dst || c.n == 0) continue;
+      hipError_t e = hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "get_routing copy");
+    }
+    return finish(h, s, "get_routing");
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_get_intermediates(moe_ffn_handle* h, void* h_rows, void* y_rows, void* h_dense, void* y_dense,
+                              void* stream) {
+  try {
+    if (int r = check_handle(h)) return r;
+    DeviceGuard g(h->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t T = size_t(h->last_T), k = size_t(h->cfg.top_k);
+    const size_t H = size_t(h->cfg.hidden), I = size_t(h->cfg.expert_dim), D = size_t(h->cfg.dense_dim);
+    struct C {
+      void* dst;
+      const void* src;
+      size_t n;
+    } cps[4] = {{h_rows, h->ws.h, T * k * I * 2},
+                {y_rows, h->ws.y, T * k * H * 2},
+                {h_dense, h->ws.h_d, T * D * 2},
+                {y_dense, h->ws.y_d, T * H * 2}};
+    for (auto& c : cps) {
+      if (!c.dst || c.n == 0) continue;
+      hipError_t e = hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "get_intermediates copy");
+    }
+    return finish(h, s, "get_intermediates");
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_align_only(moe_ffn_handle* h, int32_t T, const int32_t* topk_idx, void* stream) {
+  try {
+    if (int r = check_handle(h)) return r;
+    if (T < 0 || T > h->cfg.max_tokens) return fail(MOE_FFN_ERR_INVALID_ARG, "T must be in [0, max_tokens]");
+    if (!topk_idx) return fail(MOE_FFN_ERR_INVALID_ARG, "topk_idx must not be NULL");
+    if (reinterpret_cast<uintptr_t>(topk_idx) & 3u)
+      return fail(MOE_FFN_ERR_INVALID_ARG, "topk_idx must be 4-byte aligned");
+    if (T == 0) {
+      h->last_T = 0;
+      g_err.clear();
+      return MOE_FFN_OK;
+    }
+    DeviceGuard g(h->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(h->ws.topk_idx, topk_idx, size_t(T) * h->cfg.top_k * 4,
+                                  hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "align_only copy");
+    e = moe::launch_align(shape_of(h, T), h->ws, s);
+    if (e != hipSuccess) return hip_fail(e, "align");
+    h->last_T = T;
+    return finish(h, s, "align_only");
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_profile_begin(moe_ffn_handle* h, uint32_t stage_mask, int32_t max_samples) {
+  try {
+    if (int r = check_handle(h)) return r;
+    if (max_samples < 1 || max_samples > (1 << 16))
+      return fail(MOE_FFN_ERR_INVALID_ARG, "max_samples must be in [1, 65536]");
+    if (stage_mask & ~((1u << MOE_FFN_NUM_STAGES) - 1u)) return fail(MOE_FFN_ERR_INVALID_ARG, "bad stage_mask");
+    DeviceGuard g(h->device);
+    profile_release(h);
+    for (int st = 0; st < MOE_FFN_NUM_STAGES; ++st) {
+      if (!(stage_mask & (1u << st))) continue;
+      StageProfile& p = h->prof[st];
+      p.start.resize(max_samples);
+      p.stop.resize(max_samples);
+      for (int i = 0; i < max_samples; ++i) {
+        hipError_t e1 = hipEventCreate(&p.start[i]);
+        hipError_t e2 = hipEventCreate(&p.stop[i]);
+        if (e1 != hipSuccess || e2 != hipSuccess) {
+          p.start.resize(e1 == hipSuccess ? i + 1 : i);
+          p.stop.resize(e2 == hipSuccess ? i + 1 : i);
+          profile_release(h);
+          return hip_fail(e1 != hipSuccess ? e1 : e2, "hipEventCreate");
+        }
+      }
+    }
+    h->prof_mask = stage_mask;
+    h->prof_max = max_samples;
+    h->prof_fwd = 0;
+    g_err.clear();
+    return MOE_FFN_OK;
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_profile_end(moe_ffn_handle* h, float* total_ms, int32_t* samples) {
+  try {
+    if (int r = check_handle(h)) return r;
+    DeviceGuard g(h->device);
+    int rc = MOE_FFN_OK;
+    for (int st = 0; st < MOE_FFN_NUM_STAGES; ++st) {
+      StageProfile& p = h->prof[st];
+      float sum = 0.f;
+      for (int i = 0; i < p.used; ++i) {
+        hipError_t e = hipEventSynchronize(p.stop[i]);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.start[i], p.stop[i]);
+        if (e != hipSuccess && rc == MOE_FFN_OK) rc = hip_fail(e, "profile events");
+        sum += ms;
+      }
+      if (total_ms) total_ms[st] = sum;
+      if (samples) samples[st] = p.used;
+    }
+    profile_release(h);
+    if (rc == MOE_FFN_OK) g_err.clear();
+    return rc;
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+const char* moe_ffn_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

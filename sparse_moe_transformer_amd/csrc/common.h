@@ -1,0 +1,111 @@
+// Shared device helpers and kernel launch declarations of the MoE FFN block.
+// gfx950 (CDNA4) only: 64-wide wavefronts, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bf16 storage
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;  // MFMA A/B operand
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;  // 32x32 MFMA accumulator
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;  // 16-byte load/store
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+constexpr int kWave = 64;
+
+// bf16 <-> fp32 ---------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// round to nearest even; NaN stays a quiet NaN
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// GELU, tanh form: 0.5 v (1 + tanh(u)), u = sqrt(2/pi) (v + 0.044715 v^3).
+// With 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)) it is v / (1 + exp(-2u)); the
+// exponential is the hardware 2^x on -2u*log2(e).  Large |u| saturates
+// cleanly: exp -> inf gives -0, exp -> 0 gives v.
+__device__ __forceinline__ float gelu_tanh(float v) {
+  const float k2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  float u = v * (1.0f + 0.044715f * v * v);
+  return v / (1.0f + exp2f(k2 * u));
+}
+
+// Workspace of one handle (device pointers), laid out once at create.
+struct Workspace {
+  float* logits;        // [Tmax, E] fp32 router logits (large-T path)
+  float* route_part;    // [kRouteSplits, 64, E] split-K partial logits (small-T path)
+  int32_t* topk_idx;    // [Tmax, k]
+  float* topk_w;        // [Tmax, k]
+  int32_t* counts;      // [E]
+  int32_t* offsets;     // [E+1]
+  uint64_t* blk_mask;   // [NB, E] bit t%64 set if token t of block picked e
+  int32_t* blk_base;    // [NB, E] counts, then first row of (block, expert)
+  int32_t* perm;        // [Tmax*k]
+  int32_t* pos;         // [Tmax*k]
+  int32_t* mtiles;      // [max_mtiles, 4] (expert, row0, rows, 0) for MFMA tiles
+  int32_t* active;      // [E, 4] (expert, row0, rows, 0) per expert with rows
+  int32_t* meta;        // [16]: 0 = #mtiles, 1 = #active, 8.. = tickets
+  bf16_t* h;            // [Tmax*k, I]
+  bf16_t* h_d;          // [Tmax, D]
+  bf16_t* y;            // [Tmax*k, H]
+  bf16_t* y_d;          // [Tmax, H]
+};
+
+constexpr int kRouteSplits = 64;   // K-slices of the small-T router
+constexpr int kRouteSmallT = 64;   // largest T of the fused single-block router
+constexpr int kGemmBM = 128;       // MFMA tile rows (tokens)
+
+struct Shape {
+  int T, H, E, k, I, D;
+};
+
+// NVFP4 matrix stack
+struct Fp4Mat {
+  const uint8_t* q;
+  const uint8_t* scale;
+  const float* tscale;
+};
+
+// ---- launches (each queues on `s` and returns the launch status) ----------
+
+hipError_t launch_route_small(const Shape& sh, const bf16_t* x, const bf16_t* wr, const float* bias,
+                              const Workspace& ws, hipStream_t s);
+hipError_t launch_route_large(const Shape& sh, const bf16_t* x, const bf16_t* wr, const float* bias,
+                              const Workspace& ws, hipStream_t s);
+hipError_t launch_align(const Shape& sh, const Workspace& ws, hipStream_t s);
+
+// weight streaming (small T)
+struct StreamArgs {
+  Shape sh;
+  const bf16_t* x;
+  // bf16 weights (nvfp4 == false)
+  const bf16_t *wg, *wu, *wd, *dg, *du, *dd;
+  // NVFP4 weights (nvfp4 == true)
+  Fp4Mat fg, fu, fd, fdg, fdu, fdd;
+  bool nvfp4;
+};
+hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, hipStream_t s);
+hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStream_t s);
+
+// MFMA tiles (large T)
+hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s);
+hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s);
+
+hipError_t launch_combine(const Shape& sh, const Workspace& ws, bf16_t* out, bool accumulate,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,435 @@
+// Grouped GEMMs of the MoE block on bf16 MFMA (gfx950 v_mfma_f32_32x32x16_bf16).
+//
+//   gate/up (GeGLU, fused):  h = gelu_tanh(A . Wg) * (A . Wu)     -> bf16
+//   down:                    y = A . Wd                          -> bf16
+//   router logits:           z = x . W_r                         -> fp32
+//
+// One launch serves two segments: a host-sized one (the dense branch, or
+// the router) and an expert-grouped one whose M-tiles (expert, first row,
+// rows) come from the device-side tile list written by the grouping
+// kernels; blocks past the list's end exit at once, so no host sync is
+// needed to size the grid.  Routed A rows of the gate/up GEMM are gathered
+// from x through perm and never copied out.
+//
+// Tile: 128 rows x 128 B-columns x 64 K, 256 threads = 4 waves in 2 x 2,
+// each wave owning 64 x 64 outputs as 2 x 2 MFMA 32x32 blocks (fp32
+// accumulators).  For gate/up the 128 B-columns are 64 gate + 64 up
+// columns at the same output positions, so the GeGLU epilogue pairs them in
+// registers.
+//
+// Weights are [K, N] with N contiguous, while the MFMA B operand wants 8
+// consecutive k of one column per lane.  Each thread loads a 4(k) x 8(n)
+// block with four 16-byte loads, transposes it in registers and stores
+// 4-k runs to an LDS tile laid out [n][k] (k contiguous); MFMA operands are
+// then single 16-byte LDS reads.  Rows are padded to 72 elements (144 B) so
+// that 8 lanes of a 16-byte read hit 8 distinct 4-bank groups.  NVFP4
+// weights are already k-contiguous ([N, K/2]): each thread decodes 32
+// codes of one column to bf16 (an e2m1 x e4m3 product is exact in bf16)
+// and the fp32 tensor scale is applied in the epilogue.
+//
+// Block ids are remapped so consecutive logical tiles (the N-tiles of one
+// M-tile, then the next M-tile of the same expert) run on one XCD and share
+// its L2.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int BM = kGemmBM;  // 128
+constexpr int BN = 128;      // B columns per tile
+constexpr int BK = 64;
+constexpr int LDSK = BK + 8;  // padded row (elements)
+constexpr int kThreads = 256;
+constexpr int kXcd = 8;
+
+enum { MODE_PLAIN_BF16 = 0, MODE_PLAIN_F32 = 1, MODE_GATEUP = 2 };
+enum { W_BF16 = 0, W_FP4 = 1 };
+
+struct Seg {
+  const bf16_t* A;
+  int lda;
+  const int32_t* gather;  // routed gate/up: tile row r reads A row gather[row0 + r]
+  const bf16_t* B0;       // bf16 [G][K][ldb] (gate or the only matrix)
+  const bf16_t* B1;       // up (gate/up mode)
+  long long b_gstride;    // elements between groups
+  int ldb;
+  Fp4Mat F0, F1;          // NVFP4 [G][N][K/2], [G][N][K/16], [G]
+  int K;
+  int N;                  // output columns
+  void* C;
+  int ldc;
+  int n_ntiles;           // output column tiles
+  int host_rows;          // host-sized segment: number of rows (tiles at BM)
+  const int32_t* mtiles;  // expert-grouped segment: device tile list (else null)
+  const int32_t* n_mtiles;
+  int max_mtiles;
+};
+
+__device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
+  // (a.lo16, b.lo16) -> a.lo | b.lo << 16
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// e2m1 code (4 bits) -> fp32 bits
+__device__ __forceinline__ uint32_t e2m1_f32_bits(uint32_t c) {
+  uint32_t s = (c & 8u) << 28;
+  uint32_t e = (c >> 1) & 3u;
+  uint32_t m = c & 1u;
+  uint32_t mag = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
+  return s | mag;
+}
+// float8_e4m3fn byte -> fp32 (finite codes): bit 7 sign, bits 6..3 exponent
+// (bias 7), bits 2..0 mantissa; exponent 0 is subnormal, m * 2^-9
+__device__ __forceinline__ float e4m3_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u;
+  const uint32_t m = b & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0.001953125f;
+  return (b & 0x80u) ? -mag : mag;
+}
+
+template <int MODE, int WF>
+__global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0, int units_total) {
+  // ---- logical tile of this block (XCD-aware remap) ----
+  const int per = (units_total + kXcd - 1) / kXcd;
+  const int u = (blockIdx.x % kXcd) * per + blockIdx.x / kXcd;
+  if (u >= units_total) return;
+  const bool second = u >= units0;
+  const Seg& S = second ? s1 : s0;
+  const int uu = second ? u - units0 : u;
+  const int mt = uu / S.n_ntiles;
+  const int nt = uu % S.n_ntiles;
+  int grp = 0, row0, rows;
+  if (S.mtiles) {
+    if (mt >= *S.n_mtiles) return;
+    grp = S.mtiles[4 * mt];
+    row0 = S.mtiles[4 * mt + 1];
+    rows = S.mtiles[4 * mt + 2];
+  } else {
+    row0 = mt * BM;
+    rows = min(BM, S.host_rows - row0);
+  }
+  const int K = S.K;
+  // output columns of this tile
+  constexpr int OUTN = (MODE == MODE_GATEUP) ? BN / 2 : BN;
+  const int n0 = nt * OUTN;
+
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDSK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDSK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- A rows this thread loads: chunks c = tid + 256 i, row c/8, k-chunk c%8
+  const bf16_t* arow[4];
+  int akc[4];
+  bool aval[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int c = tid + kThreads * i;
+    int r = c >> 3;
+    akc[i] = (c & 7) * 8;
+    aval[i] = r < rows;
+    long long gr = aval[i] ? (S.gather ? S.gather[row0 + r] : row0 + r) : 0;
+    arow[i] = S.A + gr * S.lda;
+  }
+
+  // ---- B source of this thread
+  const bf16_t* bsrc = nullptr;  // bf16: 4 rows x 8 cols at (kb*4, col)
+  int bkb = 0, bcol = 0;
+  const uint8_t* fq = nullptr;   // fp4: 32 codes (16 bytes) of one column
+  const uint8_t* fs = nullptr;
+  int fn = 0, fkh = 0;
+  if (WF == W_BF16) {
+    const int nb = tid >> 4;  // 16 groups of 8 columns
+    bkb = tid & 15;           // 16 groups of 4 k
+    bcol = nb * 8;
+    const bf16_t* Bm = S.B0;
+    int ncol = n0 + nb * 8;
+    if (MODE == MODE_GATEUP && nb >= 8) {
+      Bm = S.B1;
+      ncol = n0 + (nb - 8) * 8;
+    }
+    bsrc = Bm + grp * S.b_gstride + ncol;
+  } else {
+    fn = tid >> 1;   // LDS column 0..127
+    fkh = tid & 1;   // which 32-k half of the 64-k step
+    const Fp4Mat* F = &S.F0;
+    int ncol = n0 + fn;
+    if (MODE == MODE_GATEUP && fn >= 64) {
+      F = &S.F1;
+      ncol = n0 + fn - 64;
+    }
+    const long long NN = S.N;
+    fq = F->q + (grp * NN + ncol) * (long long)(K / 2) + fkh * 16;
+    fs = F->scale + (grp * NN + ncol) * (long long)(K / 16) + fkh * 2;
+  }
+
+  u32x4_t ra[4];
+  u32x4_t rb[4];
+
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (aval[i])
+        ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + k0 + akc[i]);
+      else
+        ra[i] = u32x4_t{0, 0, 0, 0};
+    }
+    if (WF == W_BF16) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        rb[r] = *reinterpret_cast<const u32x4_t*>(bsrc + (long long)(k0 + bkb * 4 + r) * S.ldb);
+    } else {
+      rb[0] = *reinterpret_cast<const u32x4_t*>(fq + k0 / 2);
+      uint32_t sc = *reinterpret_cast<const uint16_t*>(fs + k0 / 16);
+      rb[1] = u32x4_t{sc, 0, 0, 0};
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    bf16_t* as = As[buf];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + kThreads * i;
+      *reinterpret_cast<u32x4_t*>(as + (c >> 3) * LDSK + (c & 7) * 8) = ra[i];
+    }
+    bf16_t* bs = Bs[buf];
+    if (WF == W_BF16) {
+      // rb[r] holds k = 4kb + r, columns bcol..bcol+7 (2 per dword)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t r0 = rb[0][d], r1 = rb[1][d], r2 = rb[2][d], r3 = rb[3][d];
+        // column 2d: lo halves; column 2d+1: hi halves
+        u32x2_t c0 = {perm_lo16(r0, r1), perm_lo16(r2, r3)};
+        u32x2_t c1 = {perm_hi16(r0, r1), perm_hi16(r2, r3)};
+        *reinterpret_cast<u32x2_t*>(bs + (bcol + 2 * d) * LDSK + bkb * 4) = c0;
+        *reinterpret_cast<u32x2_t*>(bs + (bcol + 2 * d + 1) * LDSK + bkb * 4) = c1;
+      }
+    } else {
+      const uint32_t sc = rb[1][0];
+      const float s0v = e4m3_f32(sc & 0xFFu);
+      const float s1v = e4m3_f32((sc >> 8) & 0xFFu);
+      uint32_t outw[16];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t q = rb[0][d];  // 8 codes, k = 8d .. 8d+7 (low nibble first)
+        float sv = d < 2 ? s0v : s1v;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          uint32_t clo = (q >> (8 * p)) & 0xFu;
+          uint32_t chi = (q >> (8 * p + 4)) & 0xFu;
+          float vlo = __uint_as_float(e2m1_f32_bits(clo)) * sv;
+          float vhi = __uint_as_float(e2m1_f32_bits(chi)) * sv;
+          // exact in bf16: keep the top 16 bits
+          outw[d * 4 + p] = (__float_as_uint(vlo) >> 16) | (__float_as_uint(vhi) & 0xFFFF0000u);
+        }
+      }
+      bf16_t* dst = bs + fn * LDSK + fkh * 32;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        *reinterpret_cast<u32x4_t*>(dst + v * 8) =
+            u32x4_t{outw[4 * v], outw[4 * v + 1], outw[4 * v + 2], outw[4 * v + 3]};
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // LDS rows of this lane's operands
+  const int kofs = (lane >> 5) * 8;
+  int arow_l[2], brow_l[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) arow_l[i] = (wm * 64 + i * 32 + (lane & 31)) * LDSK + kofs;
+  if (MODE == MODE_GATEUP) {
+    brow_l[0] = (wn * 32 + (lane & 31)) * LDSK + kofs;
+    brow_l[1] = (64 + wn * 32 + (lane & 31)) * LDSK + kofs;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) brow_l[j] = (wn * 64 + j * 32 + (lane & 31)) * LDSK + kofs;
+  }
+
+  const int nk = K / BK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tile((kt + 1) * BK);
+    const bf16_t* as = As[cur];
+    const bf16_t* bs = Bs[cur];
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(as + arow_l[i] + kk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8_t*>(bs + brow_l[j] + kk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds column (lane & 31); rows 8(r/4) + 4(lane/32) + r%4
+  float ts0 = 1.f, ts1 = 1.f;
+  if (WF == W_FP4) {
+    ts0 = S.F0.tscale[grp];
+    if (MODE == MODE_GATEUP) ts1 = S.F1.tscale[grp];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row >= rows) continue;
+      const long long orow = (long long)(row0 + row) * S.ldc;
+      if (MODE == MODE_GATEUP) {
+        const int col = n0 + wn * 32 + (lane & 31);
+        float g = acc[i][0][r] * ts0;
+        float up = acc[i][1][r] * ts1;
+        reinterpret_cast<bf16_t*>(S.C)[orow + col] = (bf16_t)f32_to_bf16_bits(gelu_tanh(g) * up);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+          float v = acc[i][j][r] * ts0;
+          if (MODE == MODE_PLAIN_F32)
+            reinterpret_cast<float*>(S.C)[orow + col] = v;
+          else
+            reinterpret_cast<bf16_t*>(S.C)[orow + col] = (bf16_t)f32_to_bf16_bits(v);
+        }
+      }
+    }
+  }
+}
+
+Seg empty_seg() {
+  Seg s{};
+  s.n_ntiles = 1;
+  return s;
+}
+
+template <int MODE, int WF>
+hipError_t launch(const Seg& a, const Seg& b, int units_a, int units_b, hipStream_t st) {
+  const int total = units_a + units_b;
+  if (total <= 0) return hipSuccess;
+  const int per = (total + kXcd - 1) / kXcd;
+  hipLaunchKernelGGL((k_gemm<MODE, WF>), dim3(per * kXcd), dim3(kThreads), 0, st, a, b, units_a, total);
+  return hipGetLastError();
+}
+
+int host_units(const Seg& s) { return ((s.host_rows + BM - 1) / BM) * s.n_ntiles; }
+int grouped_units(const Seg& s) { return s.max_mtiles * s.n_ntiles; }
+
+}  // namespace
+
+hipError_t launch_gemm_router(const Shape& sh, const bf16_t* x, const bf16_t* wr, float* logits,
+                              hipStream_t s) {
+  Seg r = empty_seg();
+  r.A = x;
+  r.lda = sh.H;
+  r.B0 = wr;
+  r.ldb = sh.E;
+  r.K = sh.H;
+  r.N = sh.E;
+  r.C = logits;
+  r.ldc = sh.E;
+  r.n_ntiles = sh.E / BN;
+  r.host_rows = sh.T;
+  Seg none = empty_seg();
+  return launch<MODE_PLAIN_F32, W_BF16>(r, none, host_units(r), 0, s);
+}
+
+hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s) {
+  const Shape& sh = a.sh;
+  Seg d = empty_seg(), e = empty_seg();
+  // dense branch: all T tokens
+  if (sh.D > 0) {
+    d.A = a.x;
+    d.lda = sh.H;
+    d.B0 = a.dg;
+    d.B1 = a.du;
+    d.ldb = sh.D;
+    d.F0 = a.fdg;
+    d.F1 = a.fdu;
+    d.K = sh.H;
+    d.N = sh.D;
+    d.C = ws.h_d;
+    d.ldc = sh.D;
+    d.n_ntiles = sh.D / (BN / 2);
+    d.host_rows = sh.T;
+  }
+  // routed experts: rows gathered through perm
+  e.A = a.x;
+  e.lda = sh.H;
+  e.gather = ws.perm;
+  e.B0 = a.wg;
+  e.B1 = a.wu;
+  e.b_gstride = (long long)sh.H * sh.I;
+  e.ldb = sh.I;
+  e.F0 = a.fg;
+  e.F1 = a.fu;
+  e.K = sh.H;
+  e.N = sh.I;
+  e.C = ws.h;
+  e.ldc = sh.I;
+  e.n_ntiles = sh.I / (BN / 2);
+  e.mtiles = ws.mtiles;
+  e.n_mtiles = ws.meta;
+  e.max_mtiles = max_mtiles;
+  const int ud = sh.D > 0 ? host_units(d) : 0;
+  if (a.nvfp4) return launch<MODE_GATEUP, W_FP4>(d, e, ud, grouped_units(e), s);
+  return launch<MODE_GATEUP, W_BF16>(d, e, ud, grouped_units(e), s);
+}
+
+hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s) {
+  const Shape& sh = a.sh;
+  Seg d = empty_seg(), e = empty_seg();
+  if (sh.D > 0) {
+    d.A = ws.h_d;
+    d.lda = sh.D;
+    d.B0 = a.dd;
+    d.ldb = sh.H;
+    d.F0 = a.fdd;
+    d.K = sh.D;
+    d.N = sh.H;
+    d.C = ws.y_d;
+    d.ldc = sh.H;
+    d.n_ntiles = sh.H / BN;
+    d.host_rows = sh.T;
+  }
+  e.A = ws.h;
+  e.lda = sh.I;
+  e.B0 = a.wd;
+  e.b_gstride = (long long)sh.I * sh.H;
+  e.ldb = sh.H;
+  e.F0 = a.fd;
+  e.K = sh.I;
+  e.N = sh.H;
+  e.C = ws.y;
+  e.ldc = sh.H;
+  e.n_ntiles = sh.H / BN;
+  e.mtiles = ws.mtiles;
+  e.n_mtiles = ws.meta;
+  e.max_mtiles = max_mtiles;
+  const int ud = sh.D > 0 ? host_units(d) : 0;
+  if (a.nvfp4) return launch<MODE_PLAIN_BF16, W_FP4>(d, e, ud, grouped_units(e), s);
+  return launch<MODE_PLAIN_BF16, W_BF16>(d, e, ud, grouped_units(e), s);
+}
+
+}  // namespace moe

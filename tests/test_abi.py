@@ -1,0 +1,92 @@
+"""The C ABI library: it loads, exports every declared symbol, and rejects bad
+arguments before touching the GPU (these run on a machine without one)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_moe_transformer_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_ffn_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libmoe_ffn.so is not built (run python -m sparse_moe_transformer_amd.build)")
+    return binding.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(binding.EXPORTS) == set(names), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_ffn_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def cfg(**kw):
+    base = dict(hidden=2816, num_experts=128, top_k=8, expert_dim=704, dense_dim=2112, max_tokens=16)
+    base.update(kw)
+    return binding.make_config(**base)
+
+
+def test_workspace_bytes_valid_config(lib):
+    rc, n = binding.moe_ffn_workspace_bytes(cfg())
+    assert rc == binding.MOE_FFN_OK
+    # at least y = T*k*H bf16 and h = T*k*I bf16
+    assert n >= 16 * 8 * (2816 + 704) * 2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=2800), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(num_experts=0), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(num_experts=300), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(top_k=0), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(top_k=17), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(num_experts=4, top_k=5), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(expert_dim=700), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(dense_dim=-64), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(dense_dim=100), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(max_tokens=0), binding.MOE_FFN_ERR_INVALID_ARG),
+    (dict(weight_format=7), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(flags=2), binding.MOE_FFN_ERR_UNSUPPORTED),
+])
+def test_bad_configs_rejected(lib, kw, code):
+    rc, _ = binding.moe_ffn_workspace_bytes(cfg(**kw))
+    assert rc == code
+    assert binding.moe_ffn_last_error() != ""
+    rc, h = binding.moe_ffn_create(cfg(**kw))
+    assert rc == code and not h
+
+
+def test_null_arguments(lib):
+    assert lib.moe_ffn_workspace_bytes(None, None) == binding.MOE_FFN_ERR_INVALID_ARG
+    assert lib.moe_ffn_create(None, None) == binding.MOE_FFN_ERR_INVALID_ARG
+    assert binding.moe_ffn_forward(None, 8, *([None] * 11)) == binding.MOE_FFN_ERR_INVALID_ARG
+    assert binding.moe_ffn_forward_nvfp4(None, 8, *([None] * 11)) == binding.MOE_FFN_ERR_INVALID_ARG
+    assert binding.moe_ffn_get_routing(None, *([None] * 7)) == binding.MOE_FFN_ERR_INVALID_ARG
+    assert binding.moe_ffn_get_intermediates(None, *([None] * 5)) == binding.MOE_FFN_ERR_INVALID_ARG
+    assert binding.moe_ffn_align_only(None, 4, None, None) == binding.MOE_FFN_ERR_INVALID_ARG
+    assert binding.moe_ffn_set_variant(None, 0) == binding.MOE_FFN_ERR_INVALID_ARG
+    assert binding.moe_ffn_destroy(None) == binding.MOE_FFN_OK
+    assert "NULL" in binding.moe_ffn_last_error()
+
+
+def test_last_error_never_null(lib):
+    assert isinstance(lib.moe_ffn_last_error(), bytes)

@@ -1,0 +1,327 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Rules (bf16 block output): routing sets bit-exact on every token whose
+k-th/(k+1)-th logit gap exceeds 1e-3 (near-ties are counted and compared
+against the oracle re-run with the GPU's sets); counts, offsets, perm and pos
+bit-exact against the oracle's grouping of the GPU's routing; outputs within
+2e-2 * (|oracle| + rms(oracle)) element by element.  Full-size workloads
+check every routing/grouping entry and a sample of output rows (the oracle
+computes those rows one by one).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+STREAM = 1
+MFMA = 2
+AUTO = 0
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    assert _t.cuda.is_available()
+    return _t
+
+
+def ffn_for(shape, variant=AUTO, max_tokens=None, accumulate=False):
+    from sparse_moe_transformer_amd import MoeFFN
+    return MoeFFN.for_shape(shape, max_tokens=max_tokens or max(shape.tokens, 1), variant=variant,
+                            accumulate=accumulate)
+
+
+def run_gpu(torch, shape, x, w, bias, variant, nvfp4=False, ffn=None):
+    T = x.shape[0]
+    ffn = ffn or ffn_for(shape, variant, max_tokens=T)
+    xd = G.up_bf16(x)
+    bd = G.up(bias) if bias is not None else None
+    out = torch.empty_like(xd)
+    if nvfp4:
+        ffn.forward_nvfp4(xd, G.up_nvfp4_weights(w), out, bd)
+    else:
+        ffn.forward(xd, G.up_weights(w), out, bd)
+    torch.cuda.synchronize()
+    r = {k: G.to_np(v) for k, v in ffn.routing(T).items()}
+    inter = ffn.intermediates(T)
+    torch.cuda.synchronize()
+    return G.to_f64(out), r, inter, ffn
+
+
+def full_check(shape, x, w, bias, out, r, inter=None, nvfp4_w=None, k=None):
+    """Routing, grouping and every output element against the full oracle."""
+    k = k or shape.top_k
+    wts = nvfp4_w or w
+    ref = oracle.moe_ffn(x, w["router"], wts["gate"], wts["up"], wts["down"], wts.get("dgate"),
+                         wts.get("dup"), wts.get("ddown"), top_k=k, bias=bias)
+    near = G.check_routing(r["topk_idx"], r["topk_w"], ref)
+    G.check_align(r, r["topk_idx"], shape.experts)
+    if near.any() and not np.array_equal(r["topk_idx"], ref["topk_idx"]):
+        ref = oracle.moe_ffn(x, w["router"], wts["gate"], wts["up"], wts["down"], wts.get("dgate"),
+                             wts.get("dup"), wts.get("ddown"), top_k=k, bias=bias,
+                             force_routing=r["topk_idx"])
+    G.assert_block_close(out, ref["out"])
+    if inter is not None:
+        G.assert_block_close(G.to_f64(inter["h"]), ref["h"], what="h")
+        G.assert_block_close(G.to_f64(inter["y"]), ref["y"], what="y")
+        if shape.dense_dim:
+            G.assert_block_close(G.to_f64(inter["y_d"]), ref["y_d"], what="y_d")
+    return ref, int(near.sum())
+
+
+def sampled_check(shape, x, w, bias, out, r, tokens, nvfp4_w=None):
+    """Every routing/grouping entry; output rows `tokens` one by one."""
+    wts = nvfp4_w or w
+    rt = oracle.route(x, w["router"], shape.top_k, bias)
+    near = G.check_routing(r["topk_idx"], r["topk_w"], rt)
+    G.check_align(r, r["topk_idx"], shape.experts)
+    ref = oracle.moe_ffn(x, w["router"], wts["gate"], wts["up"], wts["down"], wts.get("dgate"),
+                         wts.get("dup"), wts.get("ddown"), top_k=shape.top_k, bias=bias,
+                         force_routing=r["topk_idx"], tokens=tokens)
+    G.assert_block_close(out[tokens], ref["out"])
+    return int(near.sum())
+
+
+# ---------------------------------------------------------------------------
+# tiny workload and ragged shapes
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("variant", [AUTO, MFMA, STREAM])
+def test_tiny_block(torch, variant):
+    s = synth.TINY
+    x, w, bias = G.make_inputs(s)
+    out, r, inter, _ = run_gpu(torch, s, x, w, bias, variant)
+    ref, near = full_check(s, x, w, bias, out, r, inter)
+    assert near == 0
+    # with no near-ties the grouping equals the oracle's own
+    assert np.array_equal(r["perm"], ref["perm"])
+
+
+MID = synth.FFNShape("mid", 0, 512, 32, 4, 128, 192)
+MID128 = synth.FFNShape("mid128", 0, 512, 128, 8, 128, 128)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 63, 64, 65, 200, 333])
+@pytest.mark.parametrize("variant", [STREAM, MFMA])
+def test_ragged_tokens(torch, T, variant):
+    s = MID.with_tokens(T)
+    x, w, bias = G.make_inputs(s, seed=T)
+    out, r, inter, _ = run_gpu(torch, s, x, w, bias, variant)
+    full_check(s, x, w, bias, out, r, inter)
+
+
+@pytest.mark.parametrize("T", [40, 300])
+def test_mfma_router_and_bias(torch, T):
+    """E = 128 takes the MFMA router tiles at T > 64; a logit bias shifts loads."""
+    s = MID128.with_tokens(T)
+    x, w, _ = G.make_inputs(s, seed=11)
+    bias = synth.zipf_bias(s.experts, lam=0.5)
+    for variant in (AUTO, MFMA):
+        out, r, inter, _ = run_gpu(torch, s, x, w, bias, variant)
+        full_check(s, x, w, bias, out, r, inter)
+
+
+def test_no_dense_branch(torch):
+    s = synth.FFNShape("nodense", 70, 256, 8, 2, 64, 0)
+    x, w, _ = G.make_inputs(s)
+    for variant in (STREAM, MFMA):
+        out, r, inter, _ = run_gpu(torch, s, x, w, None, variant)
+        full_check(s, x, w, None, out, r, inter)
+
+
+def test_zero_input(torch):
+    """x = 0: every logit is 0, the set is {0..k-1} with weights 1/k, out = 0."""
+    s = MID.with_tokens(100)
+    _, w, _ = G.make_inputs(s)
+    x = np.zeros((100, s.hidden), dtype=np.uint16)
+    for variant in (STREAM, MFMA):
+        out, r, _, _ = run_gpu(torch, s, x, w, None, variant)
+        assert np.all(out == 0.0)
+        assert np.all(r["topk_idx"] == np.arange(s.top_k))
+        assert np.allclose(r["topk_w"], 1.0 / s.top_k, atol=1e-7)
+
+
+def test_duplicate_router_columns_tie_break(torch):
+    """Bit-identical logits for experts 2 and 5 (same column, same large
+    bias): the lower id must win when only one fits."""
+    s = MID.with_tokens(40)
+    x, w, _ = G.make_inputs(s)
+    w["router"] = w["router"].copy()
+    w["router"][:, 5] = w["router"][:, 2]
+    bias = np.zeros(s.experts, dtype=np.float32)
+    bias[[2, 5]] = 100.0
+    bias[7] = 200.0
+    # k = 4: 7 first, then 2 and 5 (tied), then the best other; with k=2 only 2 fits
+    from sparse_moe_transformer_amd import MoeFFN
+    ffn = MoeFFN(s.hidden, s.experts, 2, s.expert_dim, s.dense_dim, 40)
+    out, r, _, _ = run_gpu(torch, s, x, w, bias, AUTO, ffn=ffn)
+    assert np.all(r["topk_idx"] == np.array([2, 7]))
+    ref = oracle.moe_ffn(x, w["router"], w["gate"], w["up"], w["down"], w["dgate"], w["dup"],
+                         w["ddown"], top_k=2, bias=bias)
+    G.assert_block_close(out, ref["out"])
+
+
+def test_determinism(torch):
+    s = MID.with_tokens(333)
+    x, w, bias = G.make_inputs(s)
+    for variant in (STREAM, MFMA):
+        ffn = ffn_for(s, variant)
+        a, ra, _, _ = run_gpu(torch, s, x, w, bias, variant, ffn=ffn)
+        b, rb, _, _ = run_gpu(torch, s, x, w, bias, variant, ffn=ffn)
+        assert np.array_equal(a, b)
+        for n in ra:
+            assert np.array_equal(ra[n], rb[n]), n
+
+
+def test_accumulate_in_place(torch):
+    """MOE_FFN_ACCUMULATE with out == x: x <- x + block(x)."""
+    s = MID.with_tokens(65)
+    x, w, _ = G.make_inputs(s)
+    for variant in (STREAM, MFMA):
+        ffn = ffn_for(s, variant, accumulate=True)
+        xd = G.up_bf16(x)
+        ffn.forward(xd, G.up_weights(w), xd)
+        torch.cuda.synchronize()
+        got = G.to_f64(xd)
+        ref = oracle.widen_bf16(x) + oracle.moe_ffn(x, w["router"], w["gate"], w["up"], w["down"],
+                                                    w["dgate"], w["dup"], w["ddown"], top_k=s.top_k)["out"]
+        G.assert_block_close(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# grouping with injected routing
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("case", ["hot", "uniform", "sparse", "single"])
+def test_align_only(torch, case):
+    E, k = 32, 4
+    rng = np.random.default_rng(5)
+    T = {"hot": 300, "uniform": 1000, "sparse": 129, "single": 1}[case]
+    if case == "hot":      # every token picks experts 0..3: one expert gets all T rows
+        idx = np.broadcast_to(np.arange(k), (T, k)).copy()
+    elif case == "sparse":  # only 5 experts used, many empty
+        idx = np.sort(np.stack([rng.choice(5, k, replace=False) for _ in range(T)]), 1)
+    else:
+        idx = np.sort(np.stack([rng.choice(E, k, replace=False) for _ in range(T)]), 1)
+    from sparse_moe_transformer_amd import MoeFFN
+    ffn = MoeFFN(512, E, k, 128, 192, T)
+    ffn.align_only(G.up(idx.astype(np.int32)))
+    torch.cuda.synchronize()
+    r = {n: G.to_np(v) for n, v in ffn.routing(T).items()}
+    assert np.array_equal(r["topk_idx"], idx)
+    G.check_align(r, idx, E)
+
+
+# ---------------------------------------------------------------------------
+# the 26B-A4B layer shape
+# ---------------------------------------------------------------------------
+
+
+@pytest.fixture(scope="module")
+def w26():
+    return synth.make_weights(synth.DECODE)
+
+
+@pytest.mark.parametrize("variant", [AUTO, MFMA])
+def test_decode_26b(torch, w26, variant):
+    s = synth.DECODE
+    x = synth.make_x(s)
+    out, r, inter, _ = run_gpu(torch, s, x, w26, None, variant)
+    _, near = full_check(s, x, w26, None, out, r, inter)
+    print(f"decode near-ties: {near}, active experts: {int((r['counts'] > 0).sum())}")
+
+
+def sample_tokens(T, n=24, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, T // 2, T - 2, T - 1], rng.choice(T, n, replace=False)]))
+
+
+def test_prefill_26b(torch, w26):
+    s = synth.PREFILL
+    x = synth.make_x(s)
+    out, r, _, _ = run_gpu(torch, s, x, w26, None, AUTO)
+    near = sampled_check(s, x, w26, None, out, r, sample_tokens(s.tokens))
+    print(f"prefill near-ties: {near}")
+
+
+def test_skew_26b(torch, w26):
+    s = synth.SKEW
+    x = synth.make_x(s)
+    bias = synth.zipf_bias(s.experts)
+    out, r, _, _ = run_gpu(torch, s, x, w26, bias, AUTO)
+    near = sampled_check(s, x, w26, bias, out, r, sample_tokens(s.tokens))
+    loads = r["counts"]
+    print(f"skew near-ties: {near}; max/mean load {loads.max() / loads.mean():.2f}")
+    assert loads.max() / loads.mean() > 5
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 weight-only
+# ---------------------------------------------------------------------------
+
+
+def nvfp4_inputs(shape, seed=0):
+    x = synth.make_x(shape, seed)
+    w = synth.make_weights(shape, seed)
+    pk = {"router": w["router"]}
+    for n in ("gate", "up", "down"):
+        pk[n] = synth.nvfp4_pack_stack(w[n])
+    for n in ("dgate", "dup", "ddown"):
+        pk[n] = synth.nvfp4_pack_stack(w[n][None]) if w[n] is not None else None
+    return x, w, pk
+
+
+@pytest.mark.parametrize("T", [32, 65, 200])
+def test_nvfp4_block(torch, T):
+    s = synth.FFNShape("mid_fp4", T, 512, 32, 4, 128, 192, nvfp4=True)
+    x, w, pk = nvfp4_inputs(s, seed=T)
+    out, r, inter, _ = run_gpu(torch, s, x, pk, None, AUTO, nvfp4=True)
+    full_check(s, x, w, None, out, r, inter, nvfp4_w=pk)
+
+
+def test_nvfp4_26b_sampled(torch):
+    s = synth.NVFP4_STACK
+    x = synth.make_x(s)
+    pk = synth.make_nvfp4_weights(s)
+    out, r, _, _ = run_gpu(torch, s, x, pk, None, AUTO, nvfp4=True)
+    sampled_check(s, x, pk, None, out, r, sample_tokens(s.tokens, 12), nvfp4_w=pk)
+
+
+# ---------------------------------------------------------------------------
+# argument validation with a live handle
+# ---------------------------------------------------------------------------
+
+
+def test_validation_with_handle(torch):
+    from sparse_moe_transformer_amd import binding as B
+    from sparse_moe_transformer_amd import MoeFFN
+    s = MID.with_tokens(16)
+    ffn = MoeFFN.for_shape(s)
+    x, w, _ = G.make_inputs(s)
+    xd, wd = G.up_bf16(x), G.up_weights(w)
+    out = torch.empty_like(xd)
+    p = {k: v.data_ptr() for k, v in wd.items()}
+    args = [p["router"], None, p["gate"], p["up"], p["down"], p["dgate"], p["dup"], p["ddown"]]
+    st = torch.cuda.current_stream().cuda_stream
+    assert B.moe_ffn_forward(ffn.h, 0, xd.data_ptr(), *args, out.data_ptr(), st) == B.MOE_FFN_OK
+    assert B.moe_ffn_forward(ffn.h, 17, xd.data_ptr(), *args, out.data_ptr(), st) == B.MOE_FFN_ERR_INVALID_ARG
+    assert B.moe_ffn_forward(ffn.h, -1, xd.data_ptr(), *args, out.data_ptr(), st) == B.MOE_FFN_ERR_INVALID_ARG
+    assert B.moe_ffn_forward(ffn.h, 16, xd.data_ptr() + 2, *args, out.data_ptr(), st) == B.MOE_FFN_ERR_INVALID_ARG
+    assert B.moe_ffn_forward(ffn.h, 16, None, *args, out.data_ptr(), st) == B.MOE_FFN_ERR_INVALID_ARG
+    bad = list(args)
+    bad[5] = None
+    assert B.moe_ffn_forward(ffn.h, 16, xd.data_ptr(), *bad, out.data_ptr(), st) == B.MOE_FFN_ERR_INVALID_ARG
+    assert B.moe_ffn_forward(ffn.h, 16, xd.data_ptr(), *args, xd.data_ptr(), st) == B.MOE_FFN_ERR_INVALID_ARG
+    assert B.moe_ffn_forward_nvfp4(ffn.h, 16, xd.data_ptr(), p["router"], None, None, None, None,
+                                   None, None, None, out.data_ptr(), st) == B.MOE_FFN_ERR_UNSUPPORTED
+    assert B.moe_ffn_set_variant(ffn.h, 9) == B.MOE_FFN_ERR_INVALID_ARG
+    assert B.moe_ffn_forward(ffn.h, 16, xd.data_ptr(), *args, out.data_ptr(), st) == B.MOE_FFN_OK
+    torch.cuda.synchronize()
