@@ -85,16 +85,16 @@ enum { MOE_FFN_ACCUMULATE = 1u << 0 }; /* out += block(x) (residual stack); out 
 /* execution variants (moe_ffn_set_variant) */
 enum {
   MOE_FFN_VARIANT_AUTO = 0,   /* weight streaming for small T, MFMA tiles for large T */
-  MOE_FFN_VARIANT_STREAM = 1, /* force weight streaming (any T) */
+  MOE_FFN_VARIANT_STREAM = 1, /* force weight streaming (bf16 weights, T <= 64; else MFMA) */
   MOE_FFN_VARIANT_MFMA = 2    /* force MFMA tiles (any T) */
 };
 
 typedef struct {
-  int32_t hidden;        /* H: 2816 (multiple of 256) */
-  int32_t num_experts;   /* E: 128 (1..256) */
+  int32_t hidden;        /* H: 2816 (multiple of 256, at most 4096) */
+  int32_t num_experts;   /* E: 128 (multiple of 4, 4..256) */
   int32_t top_k;         /* k: 8 (1..min(E,16)) */
-  int32_t expert_dim;    /* I: 704 (multiple of 64) */
-  int32_t dense_dim;     /* D: 2112 (multiple of 64), or 0 for no dense branch */
+  int32_t expert_dim;    /* I: 704 (multiple of 64, at most 4096) */
+  int32_t dense_dim;     /* D: 2112 (multiple of 64, at most 4096), or 0: no dense branch */
   int32_t max_tokens;    /* largest T a forward on this handle may use (>= 1) */
   int32_t weight_format; /* MOE_FFN_W_BF16 or MOE_FFN_W_NVFP4 */
   uint32_t flags;        /* MOE_FFN_ACCUMULATE or 0 */

@@ -34,6 +34,10 @@ struct moe_ffn_handle {
   int prof_max;
   int prof_fwd;  // forwards timed so far
   StageProfile prof[MOE_FFN_NUM_STAGES];
+  // the dense branch of the streaming path runs on this stream, forked from
+  // and joined back to the caller's stream with the two events
+  hipStream_t side;
+  hipEvent_t ev_fork, ev_join;
 };
 
 namespace {
@@ -57,16 +61,16 @@ int validate_config(const moe_ffn_config* c) {
   if (!c) return fail(MOE_FFN_ERR_INVALID_ARG, "config is NULL");
   if (c->max_tokens < 1 || c->max_tokens > kMaxTokensLimit)
     return fail(MOE_FFN_ERR_INVALID_ARG, "max_tokens must be in [1, 2^20]");
-  if (c->hidden <= 0 || c->hidden % 256)
-    return fail(MOE_FFN_ERR_UNSUPPORTED, "hidden must be a positive multiple of 256");
-  if (c->num_experts < 1 || c->num_experts > 256)
-    return fail(MOE_FFN_ERR_UNSUPPORTED, "num_experts must be in [1, 256]");
+  if (c->hidden <= 0 || c->hidden % 256 || c->hidden > 4096)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "hidden must be a multiple of 256 in [256, 4096]");
+  if (c->num_experts < 4 || c->num_experts > 256 || c->num_experts % 4)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "num_experts must be a multiple of 4 in [4, 256]");
   if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->num_experts)
     return fail(MOE_FFN_ERR_UNSUPPORTED, "top_k must be in [1, min(num_experts, 16)]");
-  if (c->expert_dim <= 0 || c->expert_dim % 64)
-    return fail(MOE_FFN_ERR_UNSUPPORTED, "expert_dim must be a positive multiple of 64");
-  if (c->dense_dim < 0 || c->dense_dim % 64)
-    return fail(MOE_FFN_ERR_UNSUPPORTED, "dense_dim must be 0 or a positive multiple of 64");
+  if (c->expert_dim <= 0 || c->expert_dim % 64 || c->expert_dim > 4096)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "expert_dim must be a multiple of 64 in [64, 4096]");
+  if (c->dense_dim < 0 || c->dense_dim % 64 || c->dense_dim > 4096)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "dense_dim must be 0 or a multiple of 64 in [64, 4096]");
   if (c->weight_format != MOE_FFN_W_BF16 && c->weight_format != MOE_FFN_W_NVFP4)
     return fail(MOE_FFN_ERR_UNSUPPORTED, "unknown weight_format");
   if (c->flags & ~uint32_t(MOE_FFN_ACCUMULATE)) return fail(MOE_FFN_ERR_UNSUPPORTED, "unknown flag bits");
@@ -75,7 +79,7 @@ int validate_config(const moe_ffn_config* c) {
 
 // Workspace layout: every buffer 256-byte aligned.
 struct Layout {
-  size_t off[17];
+  size_t off[19];
   size_t total;
   int max_mtiles;
 };
@@ -86,9 +90,9 @@ Layout layout(const moe_ffn_config& c) {
   const size_t nb = (T + 63) / 64;
   Layout L{};
   L.max_mtiles = int((T * k + moe::kGemmBM - 1) / moe::kGemmBM + E);
-  const size_t sizes[17] = {
-      T * E * 4,                                  // logits
-      size_t(moe::kRouteSplits) * 64 * E * 4,     // route_part
+  const size_t sizes[19] = {
+      size_t(moe::kRouterSlices) * T * E * 4,     // logits (K-slices)
+      size_t(moe::kRouteSplits) * 256 * 64 * 4,   // route_part (slices x phases x 64 x E)
       T * k * 4,                                  // topk_idx
       T * k * 4,                                  // topk_w
       E * 4,                                      // counts
@@ -99,14 +103,17 @@ Layout layout(const moe_ffn_config& c) {
       T * k * 4,                                  // pos
       size_t(L.max_mtiles) * 16,                  // mtiles
       E * 16,                                     // active
-      16 * 4,                                     // meta
+      512 * 4,                                    // meta: counters and tickets
       T * k * I * 2,                              // h
       T * (D ? D : 1) * 2,                        // h_d
       T * k * H * 2,                              // y
       T * H * 2,                                  // y_d
+      size_t(moe::kStreamKS) * 2 *                // streaming gate/up partials
+          (size_t(moe::kStreamRows) * I + size_t(moe::kRouteSmallT) * (D ? D : 1)) * 4,
+      size_t(moe::kDenseDownKS) * moe::kRouteSmallT * H * 4,  // streaming dense down partials
   };
   size_t o = 0;
-  for (int i = 0; i < 17; ++i) {
+  for (int i = 0; i < 19; ++i) {
     L.off[i] = o;
     o += (sizes[i] + 255) & ~size_t(255);
   }
@@ -134,6 +141,8 @@ moe::Workspace bind(void* base, const Layout& L) {
   w.h_d = reinterpret_cast<moe::bf16_t*>(b + L.off[14]);
   w.y = reinterpret_cast<moe::bf16_t*>(b + L.off[15]);
   w.y_d = reinterpret_cast<moe::bf16_t*>(b + L.off[16]);
+  w.part = reinterpret_cast<float*>(b + L.off[17]);
+  w.ydp = reinterpret_cast<float*>(b + L.off[18]);
   return w;
 }
 
@@ -204,6 +213,22 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   hipError_t e;
   const auto* xb = static_cast<const moe::bf16_t*>(x);
   const auto* wr = static_cast<const moe::bf16_t*>(router_w);
+  bool stream = (h->variant == MOE_FFN_VARIANT_STREAM) ||
+                (h->variant == MOE_FFN_VARIANT_AUTO && T <= kStreamMaxTokens);
+  if (args.nvfp4) stream = false;             // the streaming kernels read bf16 [K, N] weights only
+  if (T > moe::kRouteSmallT) stream = false;  // their scratch holds at most 64 tokens' rows
+  const int mt = int((size_t(T) * sh.k + moe::kGemmBM - 1) / moe::kGemmBM + sh.E);
+  const bool fork = stream && sh.D > 0;
+  if (fork) {
+    // the always-on dense branch does not depend on the routing: run it on
+    // the side stream while the router runs here
+    e = hipEventRecord(h->ev_fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_fork, 0);
+    if (e == hipSuccess) e = moe::launch_stream_gateup(args, ws, moe::StreamPart::Dense, h->side);
+    if (e == hipSuccess) e = moe::launch_stream_down(args, ws, moe::StreamPart::Dense, h->side);
+    if (e == hipSuccess) e = hipEventRecord(h->ev_join, h->side);
+    if (e != hipSuccess) return hip_fail(e, "dense branch");
+  }
   {
     StageTimer tm(h, MOE_FFN_STAGE_ROUTE, s, timing);
     e = (T <= moe::kRouteSmallT) ? moe::launch_route_small(sh, xb, wr, bias, ws, s)
@@ -217,25 +242,27 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "align");
   }
-  bool stream = (h->variant == MOE_FFN_VARIANT_STREAM) ||
-                (h->variant == MOE_FFN_VARIANT_AUTO && T <= kStreamMaxTokens);
-  if (args.nvfp4) stream = false;  // the streaming kernels read bf16 [K, N] weights only
-  const int mt = int((size_t(T) * sh.k + moe::kGemmBM - 1) / moe::kGemmBM + sh.E);
   {
     StageTimer tm(h, MOE_FFN_STAGE_GATEUP, s, timing);
-    e = stream ? moe::launch_stream_gateup(args, ws, s) : moe::launch_gemm_gateup(args, ws, mt, s);
+    e = stream ? moe::launch_stream_gateup(args, ws, moe::StreamPart::Routed, s)
+               : moe::launch_gemm_gateup(args, ws, mt, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "gate/up");
   }
   {
     StageTimer tm(h, MOE_FFN_STAGE_DOWN, s, timing);
-    e = stream ? moe::launch_stream_down(args, ws, s) : moe::launch_gemm_down(args, ws, mt, s);
+    e = stream ? moe::launch_stream_down(args, ws, moe::StreamPart::Routed, s) : moe::launch_gemm_down(args, ws, mt, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "down");
   }
+  if (fork) {
+    e = hipStreamWaitEvent(s, h->ev_join, 0);
+    if (e != hipSuccess) return hip_fail(e, "join dense branch");
+  }
   {
     StageTimer tm(h, MOE_FFN_STAGE_COMBINE, s, timing);
-    e = moe::launch_combine(sh, ws, static_cast<moe::bf16_t*>(out), (h->cfg.flags & MOE_FFN_ACCUMULATE) != 0, s);
+    e = moe::launch_combine(sh, ws, static_cast<moe::bf16_t*>(out), (h->cfg.flags & MOE_FFN_ACCUMULATE) != 0,
+                            stream ? moe::kDenseDownKS : 0, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "combine");
   }
@@ -342,6 +369,14 @@ int moe_ffn_create(const moe_ffn_config* cfg, moe_ffn_handle** out_handle) {
     h->last_T = 0;
     const char* sm = std::getenv("MOE_FFN_SYNC");
     h->sync_mode = sm && std::strcmp(sm, "1") == 0;
+    e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipFree(base);
+      delete h;
+      return hip_fail(e, "side stream/events");
+    }
     *out_handle = h;
     g_err.clear();
     return MOE_FFN_OK;
@@ -360,6 +395,9 @@ int moe_ffn_destroy(moe_ffn_handle* h) {
     DeviceGuard g(h->device);
     hipError_t e = hipDeviceSynchronize();
     profile_release(h);
+    (void)hipEventDestroy(h->ev_fork);
+    (void)hipEventDestroy(h->ev_join);
+    (void)hipStreamDestroy(h->side);
     hipError_t f = hipFree(h->ws_base);
     delete h;
     if (e != hipSuccess) return hip_fail(e, "destroy: device sync");

@@ -4,19 +4,22 @@
 // branch; the sum carries no extra weight on the dense term).
 //
 //   out[t] = sum_{j < k} w[t, j] * y[pos[t, j]] + y_d[t]     (fp32, j ascending)
+//   (y_d is bf16, or the sum of fp32 K-slices of the dense down projection)
 //   with the accumulate flag: out[t] = out_old[t] + (the above)
 //
-// One block per token; each thread handles 8 columns with 16-byte loads.
+// Each thread handles 8 columns with 16-byte loads, issuing the k expert
+// rows' loads together.
 #include "common.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;
 
+// grid (T, ceil(H / (8 * kThreads))): one token per blockIdx.x, 8 columns per thread
 __global__ __launch_bounds__(kThreads) void k_combine(Shape sh, Workspace ws, bf16_t* __restrict__ out,
-                                                      int accumulate) {
+                                                      int accumulate, int yd_slices) {
   const int t = blockIdx.x;
   const int H = sh.H, k = sh.k;
   __shared__ int prow[16];
@@ -26,47 +29,76 @@ __global__ __launch_bounds__(kThreads) void k_combine(Shape sh, Workspace ws, bf
     pw[threadIdx.x] = ws.topk_w[(long long)t * k + threadIdx.x];
   }
   __syncthreads();
-  for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
-    float acc[8];
+  const int c = (blockIdx.y * kThreads + threadIdx.x) * 8;
+  if (c >= H) return;
+  // issue every row's load before summing them in slot order
+  u32x4_t v[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      u32x4_t v = *reinterpret_cast<const u32x4_t*>(ws.y + (long long)prow[j] * H + c);
+  for (int j = 0; j < 16; ++j)
+    if (j < k) v[j] = *reinterpret_cast<const u32x4_t*>(ws.y + (long long)prow[j] * H + c);
+  float yd[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) yd[i] = 0.f;
+  if (sh.D > 0 && yd_slices == 0) {
+    const u32x4_t vd = *reinterpret_cast<const u32x4_t*>(ws.y_d + (long long)t * H + c);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      yd[2 * d] = bf16_lo(vd[d]);
+      yd[2 * d + 1] = bf16_hi(vd[d]);
+    }
+  } else if (sh.D > 0) {
+    for (int sl = 0; sl < yd_slices; ++sl) {
+      const float4* p = reinterpret_cast<const float4*>(ws.ydp + ((long long)sl * kRouteSmallT + t) * H + c);
+      const float4 a = p[0], b = p[1];
+      yd[0] += a.x; yd[1] += a.y; yd[2] += a.z; yd[3] += a.w;
+      yd[4] += b.x; yd[5] += b.y; yd[6] += b.z; yd[7] += b.w;
+    }
+    // the dense branch's output, rounded to bf16, kept for inspection; the
+    // sum below uses the same rounded values as the bf16 path
+#pragma unroll
+    for (int i = 0; i < 8; ++i) yd[i] = __uint_as_float(f32_to_bf16_bits(yd[i]) << 16);
+    *reinterpret_cast<u32x4_t*>(ws.y_d + (long long)t * H + c) =
+        u32x4_t{pack_bf16x2(yd[0], yd[1]), pack_bf16x2(yd[2], yd[3]), pack_bf16x2(yd[4], yd[5]),
+                pack_bf16x2(yd[6], yd[7])};
+  }
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (long long)t * H + c);
+  u32x4_t o = {0, 0, 0, 0};
+  if (accumulate) o = *dst;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < k) {
       const float w = pw[j];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        acc[2 * d] += w * bf16_lo(v[d]);
-        acc[2 * d + 1] += w * bf16_hi(v[d]);
+        acc[2 * d] += w * bf16_lo(v[j][d]);
+        acc[2 * d + 1] += w * bf16_hi(v[j][d]);
       }
     }
-    if (sh.D > 0) {
-      u32x4_t v = *reinterpret_cast<const u32x4_t*>(ws.y_d + (long long)t * H + c);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        acc[2 * d] += bf16_lo(v[d]);
-        acc[2 * d + 1] += bf16_hi(v[d]);
-      }
-    }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (long long)t * H + c);
-    if (accumulate) {
-      u32x4_t o = *dst;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        acc[2 * d] = bf16_lo(o[d]) + acc[2 * d];
-        acc[2 * d + 1] = bf16_hi(o[d]) + acc[2 * d + 1];
-      }
-    }
-    u32x4_t r;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) r[d] = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
-    *dst = r;
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] += yd[i];
+  if (accumulate) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      acc[2 * d] = bf16_lo(o[d]) + acc[2 * d];
+      acc[2 * d + 1] = bf16_hi(o[d]) + acc[2 * d + 1];
+    }
+  }
+  u32x4_t r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) r[d] = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
+  *dst = r;
 }
 
 }  // namespace
 
-hipError_t launch_combine(const Shape& sh, const Workspace& ws, bf16_t* out, bool accumulate, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3(sh.T), dim3(kThreads), 0, s, sh, ws, out, accumulate ? 1 : 0);
+hipError_t launch_combine(const Shape& sh, const Workspace& ws, bf16_t* out, bool accumulate, int yd_slices,
+                          hipStream_t s) {
+  const int cols = (sh.H + 8 * kThreads - 1) / (8 * kThreads);
+  hipLaunchKernelGGL(k_combine, dim3(sh.T, cols), dim3(kThreads), 0, s, sh, ws, out, accumulate ? 1 : 0, yd_slices);
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@ namespace moe {
 typedef uint16_t bf16_t;  // raw bf16 storage
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;  // MFMA A/B operand
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;  // dot2 operand
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;  // 32x32 MFMA accumulator
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;  // 16-byte load/store
@@ -46,8 +47,8 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 
 // Workspace of one handle (device pointers), laid out once at create.
 struct Workspace {
-  float* logits;        // [Tmax, E] fp32 router logits (large-T path)
-  float* route_part;    // [kRouteSplits, 64, E] split-K partial logits (small-T path)
+  float* logits;        // [kRouterSlices, Tmax, E] fp32 partial router logits (large-T path)
+  float* route_part;    // [kRouteSplits * 256 / E, 64, E] partial logits (small-T path)
   int32_t* topk_idx;    // [Tmax, k]
   float* topk_w;        // [Tmax, k]
   int32_t* counts;      // [E]
@@ -58,16 +59,23 @@ struct Workspace {
   int32_t* pos;         // [Tmax*k]
   int32_t* mtiles;      // [max_mtiles, 4] (expert, row0, rows, 0) for MFMA tiles
   int32_t* active;      // [E, 4] (expert, row0, rows, 0) per expert with rows
-  int32_t* meta;        // [16]: 0 = #mtiles, 1 = #active, 8.. = tickets
+  int32_t* meta;        // [512]: 0 = #mtiles, 1 = #active; tickets: 8 router, 9 dense
+                        // gate/up, 16 + e expert e's gate/up
   bf16_t* h;            // [Tmax*k, I]
   bf16_t* h_d;          // [Tmax, D]
   bf16_t* y;            // [Tmax*k, H]
   bf16_t* y_d;          // [Tmax, H]
+  float* part;          // [kStreamKS][kStreamRows][2][I] + [kStreamKS][64][2][D] gate/up partials
+  float* ydp;           // [kDenseDownKS][64][H] dense down partials (streaming path)
 };
 
-constexpr int kRouteSplits = 64;   // K-slices of the small-T router
+constexpr int kRouteSplits = 16;   // K-slices (blocks) of the small-T router
+constexpr int kRouterSlices = 16;  // most K-slices of the large-T router logits
 constexpr int kRouteSmallT = 64;   // largest T of the fused single-block router
 constexpr int kGemmBM = 128;       // MFMA tile rows (tokens)
+constexpr int kStreamKS = 2;       // K-slices of the streaming gate/up units
+constexpr int kDenseDownKS = 4;    // K-slices of the streaming dense down units
+constexpr int kStreamRows = kRouteSmallT * 16;  // routed rows of the streaming path (T <= 64, k <= 16)
 
 struct Shape {
   int T, H, E, k, I, D;
@@ -98,14 +106,17 @@ struct StreamArgs {
   Fp4Mat fg, fu, fd, fdg, fdu, fdd;
   bool nvfp4;
 };
-hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, hipStream_t s);
-hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStream_t s);
+enum class StreamPart { Routed, Dense };
+hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s);
+hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s);
 
 // MFMA tiles (large T)
 hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s);
 hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s);
 
-hipError_t launch_combine(const Shape& sh, const Workspace& ws, bf16_t* out, bool accumulate,
+// yd_slices: 0 = dense output in ws.y_d (bf16); n > 0 = n fp32 slices in
+// ws.ydp, summed in order (and stored to ws.y_d as bf16)
+hipError_t launch_combine(const Shape& sh, const Workspace& ws, bf16_t* out, bool accumulate, int yd_slices,
                           hipStream_t s);
 
 }  // namespace moe

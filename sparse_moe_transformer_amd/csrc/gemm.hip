@@ -64,6 +64,8 @@ struct Seg {
   const int32_t* mtiles;  // expert-grouped segment: device tile list (else null)
   const int32_t* n_mtiles;
   int max_mtiles;
+  int ksplit;             // K-slices (host-sized segment only); slice s writes C + s * c_slice
+  long long c_slice;
 };
 
 __device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
@@ -99,7 +101,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0
   if (u >= units_total) return;
   const bool second = u >= units0;
   const Seg& S = second ? s1 : s0;
-  const int uu = second ? u - units0 : u;
+  int uu = second ? u - units0 : u;
+  const int ks = uu % S.ksplit;
+  uu /= S.ksplit;
   const int mt = uu / S.n_ntiles;
   const int nt = uu % S.n_ntiles;
   int grp = 0, row0, rows;
@@ -259,13 +263,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0
     for (int j = 0; j < 2; ++j) brow_l[j] = (wn * 64 + j * 32 + (lane & 31)) * LDSK + kofs;
   }
 
-  const int nk = K / BK;
-  load_tile(0);
+  // K-steps of this tile's slice
+  const int nk_all = K / BK;
+  const int kt0 = ks * nk_all / S.ksplit;
+  const int nk = (ks + 1) * nk_all / S.ksplit - kt0;
+  load_tile(kt0 * BK);
   store_tile(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_tile((kt + 1) * BK);
+    if (kt + 1 < nk) load_tile((kt0 + kt + 1) * BK);
     const bf16_t* as = As[cur];
     const bf16_t* bs = Bs[cur];
 #pragma unroll
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0
     for (int r = 0; r < 16; ++r) {
       const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (row >= rows) continue;
-      const long long orow = (long long)(row0 + row) * S.ldc;
+      const long long orow = (long long)(row0 + row) * S.ldc + ks * S.c_slice;
       if (MODE == MODE_GATEUP) {
         const int col = n0 + wn * 32 + (lane & 31);
         float g = acc[i][0][r] * ts0;
@@ -321,6 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0
 Seg empty_seg() {
   Seg s{};
   s.n_ntiles = 1;
+  s.ksplit = 1;
   return s;
 }
 
@@ -333,12 +341,13 @@ hipError_t launch(const Seg& a, const Seg& b, int units_a, int units_b, hipStrea
   return hipGetLastError();
 }
 
-int host_units(const Seg& s) { return ((s.host_rows + BM - 1) / BM) * s.n_ntiles; }
+int host_units(const Seg& s) { return ((s.host_rows + BM - 1) / BM) * s.n_ntiles * s.ksplit; }
 int grouped_units(const Seg& s) { return s.max_mtiles * s.n_ntiles; }
 
 }  // namespace
 
-hipError_t launch_gemm_router(const Shape& sh, const bf16_t* x, const bf16_t* wr, float* logits,
+// Router logits as ksplit K-slices of partial sums: slice s -> logits + s*T*E.
+hipError_t launch_gemm_router(const Shape& sh, const bf16_t* x, const bf16_t* wr, float* logits, int ksplit,
                               hipStream_t s) {
   Seg r = empty_seg();
   r.A = x;
@@ -351,6 +360,8 @@ hipError_t launch_gemm_router(const Shape& sh, const bf16_t* x, const bf16_t* wr
   r.ldc = sh.E;
   r.n_ntiles = sh.E / BN;
   r.host_rows = sh.T;
+  r.ksplit = ksplit;
+  r.c_slice = (long long)sh.T * sh.E;
   Seg none = empty_seg();
   return launch<MODE_PLAIN_F32, W_BF16>(r, none, host_units(r), 0, s);
 }

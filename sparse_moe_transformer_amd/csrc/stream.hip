@@ -1,21 +1,34 @@
-// Weight-streaming GEMMs of the MoE block for few tokens per expert (decode).
+// Weight-streaming GEMMs of the MoE block for few tokens (T <= 64, decode).
 //
-// At T = 8 every selected expert sees 1..8 tokens, so its matrices are read
-// once and each weight feeds only a handful of FMAs: the work is bound by
-// HBM bandwidth.  A work unit is (expert or dense branch, a block of output
-// columns); its weights are read with 16-byte coalesced loads, each thread
-// owning 8 adjacent columns and a strided subset of the K rows, and the few
-// token rows live in LDS transposed ([k][token], 8 tokens = 16 bytes) so one
-// LDS read feeds 8 x NT FMAs.  Partial sums over K are reduced across lanes
-// (shuffles) and waves (LDS).  The grid is sized by the upper bound on active
-// experts; units past the device-side active list exit at once.
+// At T = 8 each selected expert sees 1..8 tokens, so its matrices are read
+// once and each weight feeds a handful of FMAs: the work is bound by HBM
+// bandwidth.  Both kernels are built from one unit routine:
 //
-//   gate/up unit: 64 columns of both Wg and Wu over all K = H rows, then
-//                 h = gelu_tanh(g) * u (GeGLU) for each token row.
-//   down unit:    256 columns of Wd over all K = I (or D) rows.
-// Token rows are processed in chunks of 8; a unit with more rows re-reads
-// its weights (from L2) per chunk.
+//   unit = (weight matrix, NCOLS output columns, K rows [kbeg, kend)),
+//   applied to <= 8 activation rows (bf16, in global memory).
+//   Thread = (column group of 8 columns = one 16-byte load per weight row,
+//   row group owning a contiguous run of R rows).  16 (1-2 rows) or 8 (more
+//   rows) weight rows' loads are in flight per thread.  For 1-2 activation rows each thread loads its own
+//   activation values alongside the weights (no LDS staging, no barrier);
+//   for more rows they are staged in LDS transposed ([k][row], one 16-byte
+//   read feeds 8 rows) while the first weight batch is already in flight.
+//   Row-group partial sums are folded with shuffles, then across waves.
+//
+//   gate/up (k_stream_gateup): units are (expert or dense branch, gate or up
+//     matrix, 64 columns, one of kStreamKS K-slices) over the group's token
+//     rows (x gathered through perm).  Each unit writes fp32 partial
+//     pre-activations; a small kernel then sums the slices in fixed order
+//     and writes h = gelu_tanh(G) * U (the GeGLU) in bf16.  (No in-kernel
+//     hand-off between blocks: on this multi-XCD part a device-scope
+//     release writes back the L2, which is far dearer than a launch.)
+//   down (k_stream_down): units are (expert, 128 columns) over the expert's
+//     h rows, output rows y in bf16; the dense branch's longer K is cut into
+//     kDenseDownKS slices whose fp32 partial outputs the combine sums.
+//
+// Grids are sized by the upper bound on active experts; units past the
+// device-side active list exit at once.  Dense-branch units come first.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -25,170 +38,264 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsChunk = 8;
+constexpr int kU = 16;  // weight rows in flight per thread
 
-// 8 consecutive bf16 (one 16-byte load) -> 8 floats
-__device__ __forceinline__ void unpack8(const u32x4_t& v, float* f) {
+__device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);  // a.lo | b.lo << 16
+}
+__device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);  // a.hi | b.hi << 16
+}
+
+// partial pre-activations: [KS][rows][2][N] fp32; routed rows first, then
+// the dense rows (max 64) in their own region
+__device__ __forceinline__ float* part_ptr(const Workspace& ws, const Shape& sh, bool dense, int ks, int row,
+                                           int mat) {
+  if (!dense) return ws.part + ((size_t(ks) * kStreamRows + row) * 2 + mat) * sh.I;
+  float* base = ws.part + size_t(kStreamKS) * kStreamRows * 2 * sh.I;
+  return base + ((size_t(ks) * kRouteSmallT + row) * 2 + mat) * sh.D;
+}
+
+// Fold acc over the row groups of the block; returns [NT][NCOLS] sums in LDS.
+template <int NT, int NCOLS, int CPT>
+__device__ const float* fold_rows(float (&acc)[NT][CPT], float* red) {
+  constexpr int CG = NCOLS / CPT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    f[2 * d] = bf16_lo(v[d]);
-    f[2 * d + 1] = bf16_hi(v[d]);
+  for (int r = 0; r < NT; ++r)
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int off = CG; off < kWave; off <<= 1) acc[r][c] += __shfl_xor(acc[r][c], off, kWave);
+  __syncthreads();  // red may alias staged rows
+  if (lane < CG) {
+#pragma unroll
+    for (int r = 0; r < NT; ++r)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) red[(wave * NT + r) * NCOLS + lane * CPT + c] = acc[r][c];
+  }
+  __syncthreads();
+  float* sums = red + 4 * NT * NCOLS;
+  for (int o = tid; o < NT * NCOLS; o += kThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) s += red[wv * NT * NCOLS + o];
+    sums[o] = s;
+  }
+  __syncthreads();
+  return sums;
+}
+
+// acc[c] += x.lo * w[k][c] + x.hi * w[k+1][c] for the CPT columns of a row
+// pair: the rows' packed bf16 pairs are re-paired along k with a byte
+// permute and fed to the bf16 dot2 instruction (fp32 accumulate).
+template <int CPT, class V>
+__device__ __forceinline__ void dot_rows2(float (&acc)[CPT], const V& w0, const V& w1, uint32_t xpair) {
+  const bf16x2_t xp = __builtin_bit_cast(bf16x2_t, xpair);
+#pragma unroll
+  for (int d = 0; d < CPT / 2; ++d) {
+    const bf16x2_t lo = __builtin_bit_cast(bf16x2_t, perm_lo16(w0[d], w1[d]));  // column 2d
+    const bf16x2_t hi = __builtin_bit_cast(bf16x2_t, perm_hi16(w0[d], w1[d]));  // column 2d+1
+    acc[2 * d] = __builtin_amdgcn_fdot2_f32_bf16(lo, xp, acc[2 * d], false);
+    acc[2 * d + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, xp, acc[2 * d + 1], false);
   }
 }
 
-struct UnitRows {
-  int grp;     // expert id, or -1 for the dense branch
-  int row0;    // first row (expert-grouped order) or first token (dense)
-  int rows;
-};
+// NT <= 2 rows: activations loaded per batch into registers.
+// act[r] = the activation row r (bf16, length >= kend), or null for zero.
+template <int NT, int NCOLS>
+__device__ const float* unit_direct(const bf16_t* __restrict__ w, int ldw, int kbeg, int kend,
+                                    const bf16_t* const* act, float* red) {
+  constexpr int CG = NCOLS / 8, RG = kThreads / CG;
+  const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
+  const int R = (kend - kbeg) / RG;  // rows per thread (multiple of 4)
+  const int k0 = kbeg + rg * R;
+  float acc[NT][8];
+#pragma unroll
+  for (int r = 0; r < NT; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
+  const bf16_t* pw = w + (long long)k0 * ldw + cg * 8;
+  for (int b = 0; b < R; b += kU) {
+    u32x4_t vw[kU];
+    u32x2_t va[NT][kU / 4];
+#pragma unroll
+    for (int i = 0; i < kU; ++i)
+      vw[i] = (b + i < R) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pw + (long long)(b + i) * ldw))
+                          : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < NT; ++r)
+#pragma unroll
+      for (int q = 0; q < kU / 4; ++q)
+        va[r][q] = (act[r] && b + 4 * q < R) ? *reinterpret_cast<const u32x2_t*>(act[r] + k0 + b + 4 * q)
+                                              : u32x2_t{0, 0};
+    // rows past R hold zero weights: no branch, so the loop fully unrolls
+#pragma unroll
+    for (int i = 0; i < kU; i += 2)
+#pragma unroll
+      for (int r = 0; r < NT; ++r) dot_rows2<8>(acc[r], vw[i], vw[i + 1], va[r][i / 4][(i / 2) & 1]);
+  }
+  return fold_rows<NT, NCOLS, 8>(acc, red);
+}
+
+// NT in (2, 8] rows: activations staged in LDS as xs[k - kbeg][8]; the first
+// weight batch is issued before the staging.
+template <int NT, int NCOLS, int CPT, int U>
+__device__ const float* unit_staged(const bf16_t* __restrict__ w, int ldw, int kbeg, int kend,
+                                    const bf16_t* const* act, bf16_t* xs, float* red) {
+  constexpr int CG = NCOLS / CPT, RG = kThreads / CG;
+  typedef typename std::conditional<CPT == 8, u32x4_t, u32x2_t>::type vec_t;
+  const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
+  const int R = (kend - kbeg) / RG;  // even
+  const int k0 = kbeg + rg * R;
+  float acc[NT][CPT];
+#pragma unroll
+  for (int r = 0; r < NT; ++r)
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[r][c] = 0.f;
+  const bf16_t* pw = w + (long long)k0 * ldw + cg * CPT;
+  vec_t vw[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i)
+    vw[i] = (i < R) ? __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(pw + (long long)i * ldw)) : vec_t{};
+  // stage: a thread loads one 8-k piece of every row (two halves of 4 rows)
+  // and transposes it in registers into 16-bit runs of xs[k][0..8)
+  const int nch = (kend - kbeg) / 8;
+#pragma unroll 1
+  for (int c = threadIdx.x; c < nch; c += kThreads) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bf16_t* src = act[4 * hf + r];
+        v[r] = src ? *reinterpret_cast<const u32x4_t*>(src + kbeg + c * 8) : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const u32x2_t lo = {perm_lo16(v[0][d], v[1][d]), perm_lo16(v[2][d], v[3][d])};
+        const u32x2_t hi = {perm_hi16(v[0][d], v[1][d]), perm_hi16(v[2][d], v[3][d])};
+        *reinterpret_cast<u32x2_t*>(xs + (c * 8 + 2 * d) * kRowsChunk + 4 * hf) = lo;
+        *reinterpret_cast<u32x2_t*>(xs + (c * 8 + 2 * d + 1) * kRowsChunk + 4 * hf) = hi;
+      }
+    }
+  }
+  __syncthreads();
+  for (int b = 0;;) {
+#pragma unroll
+    for (int i = 0; i < U; i += 2) {
+      // rows past R hold zero weights; their LDS row index is clamped
+      const int kr = min(b + i, R - 2);
+      const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(xs + (k0 - kbeg + kr) * kRowsChunk);
+      const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(xs + (k0 - kbeg + kr + 1) * kRowsChunk);
+#pragma unroll
+      for (int r = 0; r < NT; ++r) {
+        // (x[r][k], x[r][k+1]) from the two staged rows
+        const uint32_t xp = (r & 1) ? perm_hi16(v0[r / 2], v1[r / 2]) : perm_lo16(v0[r / 2], v1[r / 2]);
+        dot_rows2<CPT>(acc[r], vw[i], vw[i + 1], xp);
+      }
+    }
+    b += U;
+    if (b >= R) break;
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+      vw[i] = (b + i < R) ? __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(pw + (long long)(b + i) * ldw))
+                          : vec_t{};
+  }
+  return fold_rows<NT, NCOLS, CPT>(acc, red);
+}
+
+// one chunk of nr <= 8 rows: sums [nr][NCOLS] in LDS
+template <int NCOLS>
+__device__ const float* stream_unit(int nr, const bf16_t* w, int ldw, int kbeg, int kend, const bf16_t* const* act,
+                                    bf16_t* xs, float* red) {
+  if (nr <= 1) return unit_direct<1, NCOLS>(w, ldw, kbeg, kend, act, red);
+  if (nr <= 2) return unit_direct<2, NCOLS>(w, ldw, kbeg, kend, act, red);
+  if (nr <= 4) return unit_staged<4, NCOLS, 8, 8>(w, ldw, kbeg, kend, act, xs, red);
+  return unit_staged<8, NCOLS, 8, 4>(w, ldw, kbeg, kend, act, xs, red);
+}
 
 // ---------------------------------------------------------------------------
 // gate/up
 // ---------------------------------------------------------------------------
 
-template <int NT>
-__device__ void gateup_chunk(const StreamArgs& a, const bf16_t* wg, const bf16_t* wu, int ldw, int K,
-                             const bf16_t* xs, float* red, int n0, int nrows, bf16_t* out, int ldo) {
-  const int tid = threadIdx.x;
-  const int cg = tid & 7;    // 8 column groups of 8
-  const int rg = tid >> 3;   // 32 row groups
-  float ag[NT][8], au[NT][8];
-#pragma unroll
-  for (int r = 0; r < NT; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) ag[r][c] = au[r][c] = 0.f;
-
-  const bf16_t* pg = wg + n0 + cg * 8;
-  const bf16_t* pu = wu + n0 + cg * 8;
-  constexpr int U = 4;
-  int k = rg;
-  for (; k + 32 * (U - 1) < K; k += 32 * U) {
-    u32x4_t vg[U], vu[U], vx[U];
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      vg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg + (long long)(k + 32 * i) * ldw));
-      vu[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pu + (long long)(k + 32 * i) * ldw));
-    }
-#pragma unroll
-    for (int i = 0; i < U; ++i) vx[i] = *reinterpret_cast<const u32x4_t*>(xs + (k + 32 * i) * kRowsChunk);
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      float fg[8], fu[8], fx[8];
-      unpack8(vg[i], fg);
-      unpack8(vu[i], fu);
-      unpack8(vx[i], fx);
-#pragma unroll
-      for (int r = 0; r < NT; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          ag[r][c] += fx[r] * fg[c];
-          au[r][c] += fx[r] * fu[c];
-        }
-    }
-  }
-  for (; k < K; k += 32) {
-    u32x4_t vg = *reinterpret_cast<const u32x4_t*>(pg + (long long)k * ldw);
-    u32x4_t vu = *reinterpret_cast<const u32x4_t*>(pu + (long long)k * ldw);
-    u32x4_t vx = *reinterpret_cast<const u32x4_t*>(xs + k * kRowsChunk);
-    float fg[8], fu[8], fx[8];
-    unpack8(vg, fg);
-    unpack8(vu, fu);
-    unpack8(vx, fx);
-#pragma unroll
-    for (int r = 0; r < NT; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        ag[r][c] += fx[r] * fg[c];
-        au[r][c] += fx[r] * fu[c];
-      }
-  }
-  // reduce the 8 row groups of a wave (lane bits 3..5)
-#pragma unroll
-  for (int r = 0; r < NT; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int off = 8; off < 64; off <<= 1) {
-        ag[r][c] += __shfl_xor(ag[r][c], off, kWave);
-        au[r][c] += __shfl_xor(au[r][c], off, kWave);
-      }
-  const int lane = tid & 63, wave = tid >> 6;
-  __syncthreads();  // red aliases the staged rows
-  // red layout: [wave][r][g/u][64 columns]
-  if (lane < 8) {
-#pragma unroll
-    for (int r = 0; r < NT; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        red[((wave * NT + r) * 2 + 0) * 64 + lane * 8 + c] = ag[r][c];
-        red[((wave * NT + r) * 2 + 1) * 64 + lane * 8 + c] = au[r][c];
-      }
-  }
-  __syncthreads();
-  for (int o = tid; o < nrows * 64; o += kThreads) {
-    const int r = o >> 6, col = o & 63;
-    float g = 0.f, u = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      g += red[((w * NT + r) * 2 + 0) * 64 + col];
-      u += red[((w * NT + r) * 2 + 1) * 64 + col];
-    }
-    out[(long long)r * ldo + n0 + col] = (bf16_t)f32_to_bf16_bits(gelu_tanh(g) * u);
-  }
-  __syncthreads();
-}
-
+// blocks [0, units_dense) are dense-branch units, the rest routed units
 __global__ __launch_bounds__(kThreads) void k_stream_gateup(StreamArgs a, Workspace ws, int units_dense) {
   const Shape& sh = a.sh;
   const int H = sh.H;
   int u = blockIdx.x;
-  UnitRows ur;
-  int n0, N;
-  const bf16_t *wg, *wu;
-  bf16_t* out;
+  bool dense;
+  int grp = -1, row0 = 0, rows, N;
   if (u < units_dense) {
+    dense = true;
+    rows = sh.T;
     N = sh.D;
-    n0 = u * 64;
-    ur = {-1, 0, sh.T};
-    wg = a.dg;
-    wu = a.du;
-    out = ws.h_d;
   } else {
     u -= units_dense;
-    const int nblk = sh.I / 64;
-    const int ai = u / nblk;
+    const int per = (sh.I / 64) * 2 * kStreamKS;
+    const int ai = u / per;
     if (ai >= ws.meta[1]) return;
+    u %= per;
+    dense = false;
+    grp = ws.active[4 * ai];
+    row0 = ws.active[4 * ai + 1];
+    rows = ws.active[4 * ai + 2];
     N = sh.I;
-    n0 = (u % nblk) * 64;
-    ur = {ws.active[4 * ai], ws.active[4 * ai + 1], ws.active[4 * ai + 2]};
-    wg = a.wg + (long long)ur.grp * H * sh.I;
-    wu = a.wu + (long long)ur.grp * H * sh.I;
-    out = ws.h;
   }
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  bf16_t* xs = reinterpret_cast<bf16_t*>(smem_raw);  // [H][8] staged rows
-  float* red = reinterpret_cast<float*>(smem_raw);   // [4][8][2][64], after the K loop
+  // u -> (n-block, matrix, K-slice), K-slice fastest
+  const int ks = u % kStreamKS;
+  const int mat = (u / kStreamKS) & 1;
+  const int n0 = (u / (2 * kStreamKS)) * 64;
+  const int kbeg = ks * H / kStreamKS, kend = (ks + 1) * H / kStreamKS;
+  const bf16_t* w = dense ? (mat ? a.du : a.dg) + n0 : (mat ? a.wu : a.wg) + (long long)grp * H * sh.I + n0;
 
-  for (int c0 = 0; c0 < ur.rows; c0 += kRowsChunk) {
-    const int nr = min(kRowsChunk, ur.rows - c0);
-    // stage the chunk's token rows transposed: xs[k][r]
-    for (int r = 0; r < kRowsChunk; ++r) {
-      const bf16_t* src = nullptr;
-      if (r < nr) {
-        int tok = (ur.grp >= 0) ? ws.perm[ur.row0 + c0 + r] : c0 + r;
-        src = a.x + (long long)tok * H;
-      }
-      for (int k = threadIdx.x; k < H; k += kThreads) xs[k * kRowsChunk + r] = src ? src[k] : (bf16_t)0;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16_t* xs = reinterpret_cast<bf16_t*>(smem_raw);  // [kend-kbeg][8] staged rows
+  float* red = reinterpret_cast<float*>(smem_raw);   // [5][8][64]
+  __shared__ const bf16_t* act[kRowsChunk];
+
+  for (int c0 = 0; c0 < rows; c0 += kRowsChunk) {
+    const int nr = min(kRowsChunk, rows - c0);
+    if (threadIdx.x < kRowsChunk) {
+      const int r = threadIdx.x;
+      act[r] = r < nr ? a.x + (long long)(dense ? c0 + r : ws.perm[row0 + c0 + r]) * H : nullptr;
     }
     __syncthreads();
-    bf16_t* o = out + (long long)(ur.row0 + c0) * N;
-    if (nr <= 1)
-      gateup_chunk<1>(a, wg, wu, N, H, xs, red, n0, nr, o, N);
-    else if (nr <= 2)
-      gateup_chunk<2>(a, wg, wu, N, H, xs, red, n0, nr, o, N);
-    else if (nr <= 4)
-      gateup_chunk<4>(a, wg, wu, N, H, xs, red, n0, nr, o, N);
-    else
-      gateup_chunk<8>(a, wg, wu, N, H, xs, red, n0, nr, o, N);
+    const bf16_t* rowp[kRowsChunk];
+#pragma unroll
+    for (int r = 0; r < kRowsChunk; ++r) rowp[r] = act[r];
+    const float* sums = stream_unit<64>(nr, w, N, kbeg, kend, rowp, xs, red);
+    float* out = part_ptr(ws, sh, dense, ks, (dense ? 0 : row0) + c0, mat) + n0;
+    for (int o = threadIdx.x; o < nr * 64; o += kThreads) out[(long long)(o >> 6) * 2 * N + (o & 63)] = sums[o];
+    __syncthreads();
+  }
+
+}
+
+// GeGLU of the streamed rows: h = gelu_tanh(sum G) * (sum U), K-slices in
+// fixed order, bf16.  Rows: the T*k routed rows (expert-grouped order) and/or
+// the T dense rows; 4 columns per thread.
+__global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace ws, int routed, int dense_rows) {
+  const int rrows = routed ? sh.T * sh.k : 0;
+  const long long nr4 = (long long)rrows * (sh.I / 4);
+  const long long nd4 = dense_rows ? (long long)sh.T * (sh.D / 4) : 0;
+  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < nr4 + nd4;
+       i += (long long)gridDim.x * kThreads) {
+    const bool dense = i >= nr4;
+    const long long j = dense ? i - nr4 : i;
+    const int N = dense ? sh.D : sh.I;
+    const int row = int(j / (N / 4)), n4 = int(j % (N / 4)) * 4;
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f), up = g;
+#pragma unroll
+    for (int s = 0; s < kStreamKS; ++s) {
+      const float4 pg = *reinterpret_cast<const float4*>(part_ptr(ws, sh, dense, s, row, 0) + n4);
+      const float4 pu = *reinterpret_cast<const float4*>(part_ptr(ws, sh, dense, s, row, 1) + n4);
+      g.x += pg.x; g.y += pg.y; g.z += pg.z; g.w += pg.w;
+      up.x += pu.x; up.y += pu.y; up.z += pu.z; up.w += pu.w;
+    }
+    bf16_t* hout = (dense ? ws.h_d : ws.h) + (long long)row * N + n4;
+    *reinterpret_cast<u32x2_t*>(hout) = u32x2_t{pack_bf16x2(gelu_tanh(g.x) * up.x, gelu_tanh(g.y) * up.y),
+                                                pack_bf16x2(gelu_tanh(g.z) * up.z, gelu_tanh(g.w) * up.w)};
   }
 }
 
@@ -196,142 +303,92 @@ __global__ __launch_bounds__(kThreads) void k_stream_gateup(StreamArgs a, Worksp
 // down
 // ---------------------------------------------------------------------------
 
-template <int NT>
-__device__ void down_chunk(const bf16_t* wd, int ldw, int K, const bf16_t* hs, float* red, int n0,
-                           int nrows, bf16_t* out, int ldo) {
-  const int tid = threadIdx.x;
-  const int cg = tid & 31;   // 32 column groups of 8 -> 256 columns
-  const int rg = tid >> 5;   // 8 row groups
-  float acc[NT][8];
-#pragma unroll
-  for (int r = 0; r < NT; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
-  const bf16_t* pw = wd + n0 + cg * 8;
-  constexpr int U = 4;
-  int k = rg;
-  for (; k + 8 * (U - 1) < K; k += 8 * U) {
-    u32x4_t vw[U], vh[U];
-#pragma unroll
-    for (int i = 0; i < U; ++i)
-      vw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pw + (long long)(k + 8 * i) * ldw));
-#pragma unroll
-    for (int i = 0; i < U; ++i) vh[i] = *reinterpret_cast<const u32x4_t*>(hs + (k + 8 * i) * kRowsChunk);
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      float fw[8], fh[8];
-      unpack8(vw[i], fw);
-      unpack8(vh[i], fh);
-#pragma unroll
-      for (int r = 0; r < NT; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[r][c] += fh[r] * fw[c];
-    }
-  }
-  for (; k < K; k += 8) {
-    u32x4_t vw = *reinterpret_cast<const u32x4_t*>(pw + (long long)k * ldw);
-    u32x4_t vh = *reinterpret_cast<const u32x4_t*>(hs + k * kRowsChunk);
-    float fw[8], fh[8];
-    unpack8(vw, fw);
-    unpack8(vh, fh);
-#pragma unroll
-    for (int r = 0; r < NT; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[r][c] += fh[r] * fw[c];
-  }
-#pragma unroll
-  for (int r = 0; r < NT; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[r][c] += __shfl_xor(acc[r][c], 32, kWave);
-  const int lane = tid & 63, wave = tid >> 6;
-  __syncthreads();  // red aliases the staged rows
-  if (lane < 32) {
-#pragma unroll
-    for (int r = 0; r < NT; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) red[(wave * NT + r) * 256 + lane * 8 + c] = acc[r][c];
-  }
-  __syncthreads();
-  for (int o = tid; o < nrows * 256; o += kThreads) {
-    const int r = o >> 8, col = o & 255;
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) s += red[(w * NT + r) * 256 + col];
-    out[(long long)r * ldo + n0 + col] = (bf16_t)f32_to_bf16_bits(s);
-  }
-  __syncthreads();
-}
-
+// blocks [0, units_dense) are dense-branch units, the rest routed units
 __global__ __launch_bounds__(kThreads) void k_stream_down(StreamArgs a, Workspace ws, int units_dense) {
   const Shape& sh = a.sh;
   const int H = sh.H;
-  const int nblk = H / 256;
+  const int nblk = H / 128;
   int u = blockIdx.x;
-  UnitRows ur;
-  int K, n0;
-  const bf16_t* wd;
-  const bf16_t* hin;
-  bf16_t* out;
+  bool dense;
+  int grp = -1, row0 = 0, rows, K, kbeg = 0, kend;
   if (u < units_dense) {
+    // dense branch: (column block, K-slice of whole 64-row groups), fp32 partials
+    dense = true;
+    rows = sh.T;
     K = sh.D;
-    n0 = u * 256;
-    ur = {-1, 0, sh.T};
-    wd = a.dd;
-    hin = ws.h_d;
-    out = ws.y_d;
+    const int ks = u % kDenseDownKS, g64 = sh.D / 64;
+    u /= kDenseDownKS;
+    kbeg = (ks * g64 / kDenseDownKS) * 64;
+    kend = ((ks + 1) * g64 / kDenseDownKS) * 64;
+    (void)ks;
   } else {
     u -= units_dense;
     const int ai = u / nblk;
     if (ai >= ws.meta[1]) return;
+    u %= nblk;
+    dense = false;
+    grp = ws.active[4 * ai];
+    row0 = ws.active[4 * ai + 1];
+    rows = ws.active[4 * ai + 2];
     K = sh.I;
-    n0 = (u % nblk) * 256;
-    ur = {ws.active[4 * ai], ws.active[4 * ai + 1], ws.active[4 * ai + 2]};
-    wd = a.wd + (long long)ur.grp * sh.I * H;
-    hin = ws.h;
-    out = ws.y;
+    kend = K;
   }
+  const int n0 = u * 128;
+  const bf16_t* wd = (dense ? a.dd : a.wd + (long long)grp * sh.I * H) + n0;
+  const bf16_t* hin = dense ? ws.h_d : ws.h + (long long)row0 * sh.I;
+  const int ksd = dense ? (blockIdx.x % kDenseDownKS) : 0;
+
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16_t* hs = reinterpret_cast<bf16_t*>(smem_raw);  // [K][8] staged rows
-  float* red = reinterpret_cast<float*>(smem_raw);   // [4][8][256], after the K loop
-  for (int c0 = 0; c0 < ur.rows; c0 += kRowsChunk) {
-    const int nr = min(kRowsChunk, ur.rows - c0);
-    for (int r = 0; r < kRowsChunk; ++r) {
-      const bf16_t* src = (r < nr) ? hin + (long long)(ur.row0 + c0 + r) * K : nullptr;
-      for (int k = threadIdx.x; k < K; k += kThreads) hs[k * kRowsChunk + r] = src ? src[k] : (bf16_t)0;
+  float* red = reinterpret_cast<float*>(smem_raw);   // [5][8][128]
+  for (int c0 = 0; c0 < rows; c0 += kRowsChunk) {
+    const int nr = min(kRowsChunk, rows - c0);
+    const bf16_t* rowp[kRowsChunk];
+#pragma unroll
+    for (int r = 0; r < kRowsChunk; ++r) rowp[r] = r < nr ? hin + (long long)(c0 + r) * K : nullptr;
+    const float* sums = stream_unit<128>(nr, wd, H, kbeg, kend, rowp, hs, red);
+    if (dense) {
+      float* o = ws.ydp + ((long long)ksd * kRouteSmallT + c0) * H + n0;
+      for (int i = threadIdx.x; i < nr * 128; i += kThreads) o[(long long)(i >> 7) * H + (i & 127)] = sums[i];
+    } else {
+      bf16_t* o = ws.y + (long long)(row0 + c0) * H + n0;
+      for (int i = threadIdx.x; i < nr * 128; i += kThreads)
+        o[(long long)(i >> 7) * H + (i & 127)] = (bf16_t)f32_to_bf16_bits(sums[i]);
     }
     __syncthreads();
-    bf16_t* o = out + (long long)(ur.row0 + c0) * H;
-    if (nr <= 1)
-      down_chunk<1>(wd, H, K, hs, red, n0, nr, o, H);
-    else if (nr <= 2)
-      down_chunk<2>(wd, H, K, hs, red, n0, nr, o, H);
-    else if (nr <= 4)
-      down_chunk<4>(wd, H, K, hs, red, n0, nr, o, H);
-    else
-      down_chunk<8>(wd, H, K, hs, red, n0, nr, o, H);
   }
 }
 
 }  // namespace
 
-hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
+// part: which branch to queue (the dense branch does not depend on the
+// routing, so the caller may run it on another stream)
+hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s) {
   const Shape& sh = a.sh;
-  const int ud = sh.D > 0 ? sh.D / 64 : 0;
-  const int max_active = std::min(sh.E, sh.T * sh.k);
-  const int units = ud + max_active * (sh.I / 64);
-  const size_t lds = std::max(size_t(sh.H) * kRowsChunk * 2, size_t(4) * kRowsChunk * 2 * 64 * 4);
+  const bool dense = part == StreamPart::Dense && sh.D > 0;
+  const int ud = dense ? (sh.D / 64) * 2 * kStreamKS : 0;
+  const int max_active = part == StreamPart::Routed ? std::min(sh.E, sh.T * sh.k) : 0;
+  const int units = ud + max_active * (sh.I / 64) * 2 * kStreamKS;
+  if (units == 0) return hipSuccess;
+  const size_t kl = size_t(sh.H) / kStreamKS;
+  const size_t lds = std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * 64 * 4);
   hipLaunchKernelGGL(k_stream_gateup, dim3(units), dim3(kThreads), lds, s, a, ws, ud);
+  const long long n4 = dense ? (long long)sh.T * sh.D / 4 : (long long)sh.T * sh.k * sh.I / 4;
+  const int gblocks = int(std::min<long long>(1024, (n4 + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(k_stream_geglu, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, dense ? 0 : 1, dense ? 1 : 0);
   return hipGetLastError();
 }
 
-hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
+hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s) {
   const Shape& sh = a.sh;
-  const int nblk = sh.H / 256;
-  const int ud = sh.D > 0 ? nblk : 0;
-  const int max_active = std::min(sh.E, sh.T * sh.k);
+  const int nblk = sh.H / 128;
+  const bool dense = part == StreamPart::Dense && sh.D > 0;
+  const int ud = dense ? nblk * kDenseDownKS : 0;
+  const int max_active = part == StreamPart::Routed ? std::min(sh.E, sh.T * sh.k) : 0;
   const int units = ud + max_active * nblk;
+  if (units == 0) return hipSuccess;
   const int kmax = std::max(sh.I, sh.D);
-  const size_t lds = std::max(size_t(kmax) * kRowsChunk * 2, size_t(4) * kRowsChunk * 256 * 4);
+  const size_t lds = std::max(size_t(kmax) * kRowsChunk * 2, size_t(5) * kRowsChunk * 128 * 4);
   hipLaunchKernelGGL(k_stream_down, dim3(units), dim3(kThreads), lds, s, a, ws, ud);
   return hipGetLastError();
 }

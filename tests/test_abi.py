@@ -55,7 +55,10 @@ def test_workspace_bytes_valid_config(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(hidden=2800), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(hidden=4352), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(expert_dim=4160), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(num_experts=0), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(num_experts=126), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(num_experts=300), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(top_k=0), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(top_k=17), binding.MOE_FFN_ERR_UNSUPPORTED),

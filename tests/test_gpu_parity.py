@@ -128,6 +128,17 @@ def test_mfma_router_and_bias(torch, T):
         full_check(s, x, w, bias, out, r, inter)
 
 
+@pytest.mark.parametrize("H,E,k,T", [(512, 4, 2, 5), (2816, 256, 8, 8), (512, 24, 3, 7), (512, 16, 4, 8),
+                                     (256, 8, 8, 8)])
+def test_router_shapes(torch, H, E, k, T):
+    """Small-T router variants: 8-expert chunks (E/8 a power of two, several
+    row batches at E = 256), and the per-expert path for other E."""
+    s = synth.FFNShape("rt", T, H, E, k, 64, 64)
+    x, w, _ = G.make_inputs(s, seed=E)
+    out, r, inter, _ = run_gpu(torch, s, x, w, None, AUTO)
+    full_check(s, x, w, None, out, r, inter)
+
+
 def test_no_dense_branch(torch):
     s = synth.FFNShape("nodense", 70, 256, 8, 2, 64, 0)
     x, w, _ = G.make_inputs(s)
@@ -168,8 +179,9 @@ def test_duplicate_router_columns_tie_break(torch):
     G.assert_block_close(out, ref["out"])
 
 
-def test_determinism(torch):
-    s = MID.with_tokens(333)
+@pytest.mark.parametrize("T", [8, 333])
+def test_determinism(torch, T):
+    s = MID.with_tokens(T)
     x, w, bias = G.make_inputs(s)
     for variant in (STREAM, MFMA):
         ffn = ffn_for(s, variant)
