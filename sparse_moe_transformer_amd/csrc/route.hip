@@ -37,34 +37,65 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-// Wave-wide arg-max with the lower index winning ties.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float ov = __shfl_xor(v, off, kWave);
-    int oi = __shfl_xor(i, off, kWave);
-    if (better(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-}
-
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
 
-// One wave routes one token whose E logits are in z (LDS or global).
-// Lane l owns experts l, l+64, l+128, l+192.
+// DPP lane moves (gfx9 encodings): swap neighbours, swap pairs, mirror
+// inside 8 lanes, mirror inside 16 lanes.
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, false);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Wave-wide arg-max, lower index winning ties; the result is wave-uniform.
+// Inside each 16-lane row: two quad swaps, then mirrors (after each step
+// the lanes of a group agree, so a mirror reaches the other group); the 4
+// row winners are then compared through readlane.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<kDppXor1>(v, i);
+  argmax_step<kDppXor2>(v, i);
+  argmax_step<kDppHalfMirror>(v, i);
+  argmax_step<kDppMirror>(v, i);
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+    const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+    if (better(rv, ri, bv, bi)) {
+      bv = rv;
+      bi = ri;
+    }
+  }
+  v = bv;
+  i = bi;
+}
+
+// One wave routes one token whose E logits are in z (LDS or global).  Lane
+// l owns experts l, l+64, l+128, l+192.  k rounds of wave arg-max pick the
+// experts (equal logits: lower id first); p = softmax over all experts;
+// w = p_S / sum(p_S), written in ascending expert id.
 __device__ void wave_route_token(const float* z, int E, int k, int32_t* out_idx, float* out_w) {
   const int lane = threadIdx.x & (kWave - 1);
+  const int nj = (E + kWave - 1) / kWave;  // wave-uniform
   float zv[4];
   bool sel[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int e = lane + j * kWave;
+    const int e = lane + j * kWave;
     zv[j] = (e < E) ? z[e] : -INFINITY;
     sel[j] = false;
   }
@@ -74,8 +105,8 @@ __device__ void wave_route_token(const float* z, int E, int k, int32_t* out_idx,
     int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int e = lane + j * kWave;
-      if (e < E && !sel[j] && better(zv[j], e, bv, bi)) {
+      const int e = lane + j * kWave;
+      if (j < nj && e < E && !sel[j] && better(zv[j], e, bv, bi)) {
         bv = zv[j];
         bi = e;
       }
@@ -100,16 +131,15 @@ __device__ void wave_route_token(const float* z, int E, int k, int32_t* out_idx,
     ps += p[j];
   }
   ps = wave_sum(ps);
-  // ascending expert id order: rank = selected ids below this one
+  // ascending expert id order: position = selected ids below this one
   int base = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint64_t m = __ballot(sel[j]);
+    const uint64_t m = __ballot(sel[j]);
     if (sel[j]) {
-      uint64_t below = m & ((1ull << lane) - 1ull);
-      int rank = base + __popcll(below);
-      out_idx[rank] = lane + j * kWave;
-      out_w[rank] = p[j] / ps;
+      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+      out_idx[pos] = lane + j * kWave;
+      out_w[pos] = p[j] / ps;
     }
     base += __popcll(m);
   }
@@ -123,7 +153,7 @@ __device__ int block_exclusive_scan(int v, int* scratch /* [BLOCK/kWave + 1] */,
   int incl = v;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
-    int o = __shfl_up(incl, off, kWave);
+    const int o = __shfl_up(incl, off, kWave);
     if (lane >= off) incl += o;
   }
   if (lane == kWave - 1) scratch[wid] = incl;
@@ -131,55 +161,90 @@ __device__ int block_exclusive_scan(int v, int* scratch /* [BLOCK/kWave + 1] */,
   if (threadIdx.x == 0) {
     int run = 0;
     for (int w = 0; w < BLOCK / kWave; ++w) {
-      int c = scratch[w];
+      const int c = scratch[w];
       scratch[w] = run;
       run += c;
     }
     scratch[BLOCK / kWave] = run;
   }
   __syncthreads();
-  int excl = scratch[wid] + incl - v;
+  const int excl = scratch[wid] + incl - v;
   total = scratch[BLOCK / kWave];
   __syncthreads();
   return excl;
+}
+
+// Block-wide exclusive scan of three ints per thread in one pass.
+template <int BLOCK>
+__device__ int3 block_exclusive_scan3(int3 v, int3* scratch /* [BLOCK/kWave + 1] */, int3& total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  int3 incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int ox = __shfl_up(incl.x, off, kWave);
+    const int oy = __shfl_up(incl.y, off, kWave);
+    const int oz = __shfl_up(incl.z, off, kWave);
+    if (lane >= off) {
+      incl.x += ox;
+      incl.y += oy;
+      incl.z += oz;
+    }
+  }
+  if (lane == kWave - 1) scratch[wid] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int3 run = make_int3(0, 0, 0);
+    for (int w = 0; w < BLOCK / kWave; ++w) {
+      const int3 c = scratch[w];
+      scratch[w] = run;
+      run.x += c.x;
+      run.y += c.y;
+      run.z += c.z;
+    }
+    scratch[BLOCK / kWave] = run;
+  }
+  __syncthreads();
+  const int3 base = scratch[wid];
+  total = scratch[BLOCK / kWave];
+  __syncthreads();
+  return make_int3(base.x + incl.x - v.x, base.y + incl.y - v.y, base.z + incl.z - v.z);
 }
 
 // Given counts[e] (one per thread e < E), write counts, offsets, the MFMA
 // tile list and the active-expert list; returns the thread's offset.  Called
 // by one whole block of BLOCK >= E threads.
 template <int BLOCK>
-__device__ int build_offsets_and_tiles(const int cnt_e, int E, const Workspace& ws, int* scratch) {
+__device__ int build_offsets_and_tiles(const int cnt_e, int E, const Workspace& ws, int* /*unused*/) {
+  __shared__ int3 scratch3[BLOCK / kWave + 1];
   const int e = threadIdx.x;
   const int c = (e < E) ? cnt_e : 0;
-  int total;
-  const int off = block_exclusive_scan<BLOCK>(c, scratch, total);
+  const int nm = (c + kGemmBM - 1) / kGemmBM;
+  int3 total;
+  const int3 ex = block_exclusive_scan3<BLOCK>(make_int3(c, nm, c > 0 ? 1 : 0), scratch3, total);
+  const int off = ex.x;
   if (e < E) {
     ws.counts[e] = c;
     ws.offsets[e] = off;
   }
-  if (e == 0) ws.offsets[E] = total;
-  const int nm = (c + kGemmBM - 1) / kGemmBM;
-  int ntile;
-  const int m0 = block_exclusive_scan<BLOCK>(nm, scratch, ntile);
+  if (e == 0) {
+    ws.offsets[E] = total.x;
+    ws.meta[0] = total.y;
+    ws.meta[1] = total.z;
+  }
   for (int m = 0; m < nm; ++m) {
-    int32_t* t = ws.mtiles + 4 * (m0 + m);
+    int32_t* t = ws.mtiles + 4 * (ex.y + m);
     t[0] = e;
     t[1] = off + m * kGemmBM;
     t[2] = min(kGemmBM, c - m * kGemmBM);
     t[3] = 0;
   }
-  int nact;
-  const int a0 = block_exclusive_scan<BLOCK>(c > 0 ? 1 : 0, scratch, nact);
   if (c > 0) {
-    int32_t* t = ws.active + 4 * a0;
+    int32_t* t = ws.active + 4 * ex.z;
     t[0] = e;
     t[1] = off;
     t[2] = c;
     t[3] = 0;
-  }
-  if (e == 0) {
-    ws.meta[0] = ntile;
-    ws.meta[1] = nact;
   }
   return off;
 }
@@ -281,12 +346,18 @@ __global__ __launch_bounds__(kThreads) void k_route_part8(Shape sh, const bf16_t
       }
     }
     if (b + MAXR < R) continue;
-    // fold row groups inside each wave, then across the 4 waves
+    // fold row groups inside each wave (lane bits >= log2(EC); the step
+    // test is uniform, so every step unrolls), then across the 4 waves
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int st = 0; st < 6; ++st) {
+      const int off = 1 << st;
+      if (off >= EC) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        for (int off = EC; off < kWave; off <<= 1) acc[t][c] += __shfl_xor(acc[t][c], off, kWave);
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[t][c] += __shfl_xor(acc[t][c], off, kWave);
+      }
+    }
     __syncthreads();  // red aliases xs
     float* red = smem;  // [4 waves][8][E]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -350,14 +421,16 @@ __global__ __launch_bounds__(kThreads) void k_route_part(Shape sh, const bf16_t*
   }
 }
 
-// one block: sum the K-slices in fixed order (+ bias), route, group
-__global__ __launch_bounds__(kThreads) void k_route_finish(Shape sh, int nparts, const float* __restrict__ bias,
+// one block of 512 threads (one wave per token for T <= 8): sum the K-slices
+// in fixed order (+ bias), route, group
+constexpr int kFinishThreads = 512;
+__global__ __launch_bounds__(kFinishThreads) void k_route_finish(Shape sh, int nparts, const float* __restrict__ bias,
                                                           Workspace ws) {
   const int T = sh.T, E = sh.E;
   extern __shared__ float zl[];  // [T][E]
   const int E4 = E / 4;
   const size_t stride = size_t(kRouteSmallT) * E / 4;  // float4s between parts
-  for (int i = threadIdx.x; i < T * E4; i += kThreads) {
+  for (int i = threadIdx.x; i < T * E4; i += kFinishThreads) {
     const int t = i / E4, e4 = (i % E4) * 4;
     const float4* p = reinterpret_cast<const float4*>(ws.route_part + size_t(t) * E + e4);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -385,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void k_route_finish(Shape sh, int nparts,
     zl[t * E + e4 + 3] = s.w;
   }
   __syncthreads();
-  route_and_group<kThreads>(sh, ws, zl);
+  route_and_group<kFinishThreads>(sh, ws, zl);
 }
 
 // ---------------------------------------------------------------------------
@@ -507,8 +580,8 @@ hipError_t launch_route_small(const Shape& sh, const bf16_t* x, const bf16_t* wr
     const size_t lds = size_t(64) * rows * sizeof(float);
     hipLaunchKernelGGL(k_route_part, dim3(nsplit), dim3(kThreads), lds, s, sh, x, wr, ws);
   }
-  hipLaunchKernelGGL(k_route_finish, dim3(1), dim3(kThreads), size_t(sh.T) * sh.E * sizeof(float), s, sh, nsplit,
-                     bias, ws);
+  hipLaunchKernelGGL(k_route_finish, dim3(1), dim3(kFinishThreads), size_t(sh.T) * sh.E * sizeof(float), s, sh,
+                     nsplit, bias, ws);
   return hipGetLastError();
 }
 
