@@ -224,16 +224,23 @@ def moe_ffn(x, router_w, w_gate, w_up, w_down, d_gate=None, d_up=None, d_down=No
     if tokens is not None:
         tokens = np.asarray(tokens, dtype=np.int64)
         out = np.zeros((len(tokens), H))
+        cache = {}  # expert -> its three fp64 matrices (each decoded once per call)
+
+        def mats(e):
+            if e not in cache:
+                cache[e] = (_matrix(w_gate, e), _matrix(w_up, e), _matrix(w_down, e))
+            return cache[e]
+
+        dense_m = ((_dense_matrix(d_gate), _dense_matrix(d_up), _dense_matrix(d_down))
+                   if have_dense else None)
         for i, t in enumerate(tokens):
             acc = np.zeros(H)
             for j in range(top_k):
                 e = int(r["topk_idx"][t, j])
-                _, ye = geglu(X[t:t + 1], _matrix(w_gate, e), _matrix(w_up, e),
-                              _matrix(w_down, e))
+                _, ye = geglu(X[t:t + 1], *mats(e))
                 acc += r["topk_w"][t, j] * ye[0]
             if have_dense:
-                _, yd = geglu(X[t:t + 1], _dense_matrix(d_gate), _dense_matrix(d_up),
-                              _dense_matrix(d_down))
+                _, yd = geglu(X[t:t + 1], *dense_m)
                 acc += yd[0]
             out[i] = acc
         res["out"] = out

@@ -37,10 +37,10 @@ namespace moe {
 namespace {
 
 constexpr int BM = kGemmBM;  // 128
-constexpr int BN = 128;      // B columns per tile
+constexpr int BN = 256;      // B columns per tile
 constexpr int BK = 64;
 constexpr int LDSK = BK + 8;  // padded row (elements)
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 8 waves: 2 (rows) x 4 (columns), 64 x 64 outputs each
 constexpr int kXcd = 8;
 
 enum { MODE_PLAIN_BF16 = 0, MODE_PLAIN_F32 = 1, MODE_GATEUP = 2 };
@@ -94,7 +94,7 @@ __device__ __forceinline__ float e4m3_f32(uint32_t b) {
 }
 
 template <int MODE, int WF>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0, int units_total) {
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0, int units_total) {
   // ---- logical tile of this block (XCD-aware remap) ----
   const int per = (units_total + kXcd - 1) / kXcd;
   const int u = (blockIdx.x % kXcd) * per + blockIdx.x / kXcd;
@@ -116,8 +116,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0
     row0 = mt * BM;
     rows = min(BM, S.host_rows - row0);
   }
-  const int K = S.K;
-  // output columns of this tile
+  const int K = S.K, N = S.N;
+  // output columns of this tile: gate/up pairs 128 gate with 128 up columns
   constexpr int OUTN = (MODE == MODE_GATEUP) ? BN / 2 : BN;
   const int n0 = nt * OUTN;
 
@@ -127,80 +127,69 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  // ---- A rows this thread loads: chunks c = tid + 256 i, row c/8, k-chunk c%8
-  const bf16_t* arow[4];
-  int akc[4];
-  bool aval[4];
+  // ---- A: 16-byte chunks c = tid + 512 i, row c/8, k-chunk c%8.  Rows past
+  // the tile's end read a valid row (their results are never stored), so the
+  // loads need no branches.
+  const bf16_t* arow[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int c = tid + kThreads * i;
-    int r = c >> 3;
-    akc[i] = (c & 7) * 8;
-    aval[i] = r < rows;
-    long long gr = aval[i] ? (S.gather ? S.gather[row0 + r] : row0 + r) : 0;
-    arow[i] = S.A + gr * S.lda;
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = (c >> 3) < rows ? (c >> 3) : 0;
+    const long long gr = S.gather ? S.gather[row0 + r] : row0 + r;
+    arow[i] = S.A + gr * S.lda + (c & 7) * 8;
   }
 
-  // ---- B source of this thread
-  const bf16_t* bsrc = nullptr;  // bf16: 4 rows x 8 cols at (kb*4, col)
+  // ---- B source of this thread (columns past N read column 0; discarded)
+  const bf16_t* bsrc = nullptr;  // bf16: 4 rows x 8 columns at (bkb*4, bcol)
   int bkb = 0, bcol = 0;
-  const uint8_t* fq = nullptr;   // fp4: 32 codes (16 bytes) of one column
+  const uint8_t* fq = nullptr;   // NVFP4: 32 codes (16 bytes) of one column
   const uint8_t* fs = nullptr;
   int fn = 0, fkh = 0;
   if (WF == W_BF16) {
-    const int nb = tid >> 4;  // 16 groups of 8 columns
+    const int nb = tid >> 4;  // 32 groups of 8 columns
     bkb = tid & 15;           // 16 groups of 4 k
     bcol = nb * 8;
     const bf16_t* Bm = S.B0;
     int ncol = n0 + nb * 8;
-    if (MODE == MODE_GATEUP && nb >= 8) {
+    if (MODE == MODE_GATEUP && nb >= 16) {
       Bm = S.B1;
-      ncol = n0 + (nb - 8) * 8;
+      ncol = n0 + (nb - 16) * 8;
     }
-    bsrc = Bm + grp * S.b_gstride + ncol;
+    bsrc = Bm + grp * S.b_gstride + (ncol < N ? ncol : 0);
   } else {
-    fn = tid >> 1;   // LDS column 0..127
-    fkh = tid & 1;   // which 32-k half of the 64-k step
+    fn = tid >> 1;  // LDS column 0..255
+    fkh = tid & 1;  // which 32-k half of the 64-k step
     const Fp4Mat* F = &S.F0;
     int ncol = n0 + fn;
-    if (MODE == MODE_GATEUP && fn >= 64) {
+    if (MODE == MODE_GATEUP && fn >= 128) {
       F = &S.F1;
-      ncol = n0 + fn - 64;
+      ncol = n0 + fn - 128;
     }
     const long long NN = S.N;
-    fq = F->q + (grp * NN + ncol) * (long long)(K / 2) + fkh * 16;
-    fs = F->scale + (grp * NN + ncol) * (long long)(K / 16) + fkh * 2;
+    const long long col = ncol < N ? ncol : 0;
+    fq = F->q + (grp * NN + col) * (long long)(K / 2) + fkh * 16;
+    fs = F->scale + (grp * NN + col) * (long long)(K / 16) + fkh * 2;
   }
 
-  u32x4_t ra[4];
-  u32x4_t rb[4];
-
-  auto load_tile = [&](int k0) {
+  auto load_tile = [&](int k0, u32x4_t(&ra)[2], u32x4_t(&rb)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (aval[i])
-        ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + k0 + akc[i]);
-      else
-        ra[i] = u32x4_t{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + k0);
     if (WF == W_BF16) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        rb[r] = *reinterpret_cast<const u32x4_t*>(bsrc + (long long)(k0 + bkb * 4 + r) * S.ldb);
+      for (int r = 0; r < 4; ++r) rb[r] = *reinterpret_cast<const u32x4_t*>(bsrc + (long long)(k0 + bkb * 4 + r) * S.ldb);
     } else {
       rb[0] = *reinterpret_cast<const u32x4_t*>(fq + k0 / 2);
-      uint32_t sc = *reinterpret_cast<const uint16_t*>(fs + k0 / 16);
-      rb[1] = u32x4_t{sc, 0, 0, 0};
+      rb[1] = u32x4_t{uint32_t(*reinterpret_cast<const uint16_t*>(fs + k0 / 16)), 0, 0, 0};
     }
   };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, const u32x4_t(&ra)[2], const u32x4_t(&rb)[4]) {
     bf16_t* as = As[buf];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + kThreads * i;
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + kThreads * i;
       *reinterpret_cast<u32x4_t*>(as + (c >> 3) * LDSK + (c & 7) * 8) = ra[i];
     }
     bf16_t* bs = Bs[buf];
@@ -208,10 +197,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0
       // rb[r] holds k = 4kb + r, columns bcol..bcol+7 (2 per dword)
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        uint32_t r0 = rb[0][d], r1 = rb[1][d], r2 = rb[2][d], r3 = rb[3][d];
-        // column 2d: lo halves; column 2d+1: hi halves
-        u32x2_t c0 = {perm_lo16(r0, r1), perm_lo16(r2, r3)};
-        u32x2_t c1 = {perm_hi16(r0, r1), perm_hi16(r2, r3)};
+        const uint32_t r0 = rb[0][d], r1 = rb[1][d], r2 = rb[2][d], r3 = rb[3][d];
+        const u32x2_t c0 = {perm_lo16(r0, r1), perm_lo16(r2, r3)};  // column 2d
+        const u32x2_t c1 = {perm_hi16(r0, r1), perm_hi16(r2, r3)};  // column 2d+1
         *reinterpret_cast<u32x2_t*>(bs + (bcol + 2 * d) * LDSK + bkb * 4) = c0;
         *reinterpret_cast<u32x2_t*>(bs + (bcol + 2 * d + 1) * LDSK + bkb * 4) = c1;
       }
@@ -222,14 +210,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0
       uint32_t outw[16];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        uint32_t q = rb[0][d];  // 8 codes, k = 8d .. 8d+7 (low nibble first)
-        float sv = d < 2 ? s0v : s1v;
+        const uint32_t q = rb[0][d];  // 8 codes, k = 8d .. 8d+7 (low nibble first)
+        const float sv = d < 2 ? s0v : s1v;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          uint32_t clo = (q >> (8 * p)) & 0xFu;
-          uint32_t chi = (q >> (8 * p + 4)) & 0xFu;
-          float vlo = __uint_as_float(e2m1_f32_bits(clo)) * sv;
-          float vhi = __uint_as_float(e2m1_f32_bits(chi)) * sv;
+          const float vlo = __uint_as_float(e2m1_f32_bits((q >> (8 * p)) & 0xFu)) * sv;
+          const float vhi = __uint_as_float(e2m1_f32_bits((q >> (8 * p + 4)) & 0xFu)) * sv;
           // exact in bf16: keep the top 16 bits
           outw[d * 4 + p] = (__float_as_uint(vlo) >> 16) | (__float_as_uint(vhi) & 0xFFFF0000u);
         }
@@ -250,31 +236,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // LDS rows of this lane's operands
+  // this wave's 32 x 32 blocks: rows wm*64 + 32i; columns (gate/up: gate and
+  // up at wn*32; else wn*64 + 32j).  The K loop computes every block;
+  // blocks past the tile's rows or the matrix's columns are dropped in the
+  // epilogue.
   const int kofs = (lane >> 5) * 8;
   int arow_l[2], brow_l[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) arow_l[i] = (wm * 64 + i * 32 + (lane & 31)) * LDSK + kofs;
   if (MODE == MODE_GATEUP) {
     brow_l[0] = (wn * 32 + (lane & 31)) * LDSK + kofs;
-    brow_l[1] = (64 + wn * 32 + (lane & 31)) * LDSK + kofs;
+    brow_l[1] = (BN / 2 + wn * 32 + (lane & 31)) * LDSK + kofs;
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) brow_l[j] = (wn * 64 + j * 32 + (lane & 31)) * LDSK + kofs;
   }
 
-  // K-steps of this tile's slice
-  const int nk_all = K / BK;
-  const int kt0 = ks * nk_all / S.ksplit;
-  const int nk = (ks + 1) * nk_all / S.ksplit - kt0;
-  load_tile(kt0 * BK);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tile((kt0 + kt + 1) * BK);
-    const bf16_t* as = As[cur];
-    const bf16_t* bs = Bs[cur];
+  auto compute = [&](int buf) {
+    const bf16_t* as = As[buf];
+    const bf16_t* bs = Bs[buf];
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
       bf16x8_t a[2], b[2];
@@ -288,8 +268,48 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tile(cur ^ 1);
+  };
+
+  // K-steps of this tile's slice.  Global loads run two steps ahead of the
+  // MFMAs (two register stages), LDS is double-buffered; the steady state is
+  // straight-line code (tail loads re-read the last step), so the compiler
+  // can wait on exactly the loads it needs.
+  const int nk_all = K / BK;
+  const int kt0 = ks * nk_all / S.ksplit;
+  const int nk = (ks + 1) * nk_all / S.ksplit - kt0;
+  const int klast = (kt0 + nk - 1) * BK;
+  u32x4_t ra0[2], rb0[4], ra1[2], rb1[4];
+  load_tile(kt0 * BK, ra0, rb0);
+  load_tile(min((kt0 + 1) * BK, klast), ra1, rb1);
+  store_tile(0, ra0, rb0);
+  __syncthreads();
+  int kt = 0;
+  // sched_barrier keeps the scheduler from sinking the next step's loads
+  // below the wait for the current step's registers
+  for (; kt + 1 < nk; kt += 2) {
+    load_tile(min((kt0 + kt + 2) * BK, klast), ra0, rb0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    __builtin_amdgcn_sched_barrier(0);
+    store_tile(1, ra1, rb1);
     __syncthreads();
+    load_tile(min((kt0 + kt + 3) * BK, klast), ra1, rb1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_tile(0, ra0, rb0);
+    __syncthreads();
+  }
+  if (kt < nk) compute(0);  // odd step count: LDS buffer 0 holds the last step
+
+  bool mval[2], nval[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) mval[i] = wm * 64 + i * 32 < rows;
+  if (MODE == MODE_GATEUP) {
+    nval[0] = nval[1] = n0 + wn * 32 < N;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) nval[j] = n0 + wn * 64 + j * 32 < N;
   }
 
   // ---- epilogue: lane holds column (lane & 31); rows 8(r/4) + 4(lane/32) + r%4
@@ -300,21 +320,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Seg s0, Seg s1, int units0
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
+    if (!mval[i]) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (row >= rows) continue;
       const long long orow = (long long)(row0 + row) * S.ldc + ks * S.c_slice;
       if (MODE == MODE_GATEUP) {
+        if (!nval[0]) continue;
         const int col = n0 + wn * 32 + (lane & 31);
-        float g = acc[i][0][r] * ts0;
-        float up = acc[i][1][r] * ts1;
+        const float g = acc[i][0][r] * ts0;
+        const float up = acc[i][1][r] * ts1;
         reinterpret_cast<bf16_t*>(S.C)[orow + col] = (bf16_t)f32_to_bf16_bits(gelu_tanh(g) * up);
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
+          if (!nval[j]) continue;
           const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-          float v = acc[i][j][r] * ts0;
+          const float v = acc[i][j][r] * ts0;
           if (MODE == MODE_PLAIN_F32)
             reinterpret_cast<float*>(S.C)[orow + col] = v;
           else
@@ -358,7 +381,7 @@ hipError_t launch_gemm_router(const Shape& sh, const bf16_t* x, const bf16_t* wr
   r.N = sh.E;
   r.C = logits;
   r.ldc = sh.E;
-  r.n_ntiles = sh.E / BN;
+  r.n_ntiles = (sh.E + BN - 1) / BN;
   r.host_rows = sh.T;
   r.ksplit = ksplit;
   r.c_slice = (long long)sh.T * sh.E;
@@ -382,7 +405,7 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
     d.N = sh.D;
     d.C = ws.h_d;
     d.ldc = sh.D;
-    d.n_ntiles = sh.D / (BN / 2);
+    d.n_ntiles = (sh.D + BN / 2 - 1) / (BN / 2);
     d.host_rows = sh.T;
   }
   // routed experts: rows gathered through perm
@@ -399,7 +422,7 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
   e.N = sh.I;
   e.C = ws.h;
   e.ldc = sh.I;
-  e.n_ntiles = sh.I / (BN / 2);
+  e.n_ntiles = (sh.I + BN / 2 - 1) / (BN / 2);
   e.mtiles = ws.mtiles;
   e.n_mtiles = ws.meta;
   e.max_mtiles = max_mtiles;
@@ -421,7 +444,7 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
     d.N = sh.H;
     d.C = ws.y_d;
     d.ldc = sh.H;
-    d.n_ntiles = sh.H / BN;
+    d.n_ntiles = (sh.H + BN - 1) / BN;
     d.host_rows = sh.T;
   }
   e.A = ws.h;
@@ -434,7 +457,7 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
   e.N = sh.H;
   e.C = ws.y;
   e.ldc = sh.H;
-  e.n_ntiles = sh.H / BN;
+  e.n_ntiles = (sh.H + BN - 1) / BN;
   e.mtiles = ws.mtiles;
   e.n_mtiles = ws.meta;
   e.max_mtiles = max_mtiles;
