@@ -12,7 +12,8 @@
  *     (archdb fields "FFN activation": GeGLU with tanh-approximate GELU;
  *     "FFN projections have bias terms": No; expert width 704).
  *   - always-on dense branch: the same GeGLU form with width 2112
- *     (gemma-llm API page gm.nn.Gemma4_26B_A4B: "a dense shared MLP branch").
+ *     (gemma-llm API page gm.nn.Gemma4_26B_A4B, model description: every
+ *     layer also has one dense MLP of width 2112 that all tokens pass through).
  *   - output: out[t] = sum_j w[t,j] * E_{e_j}(x_t) + Dense(x_t).
  *
  * Data layout (all row-major, all caller-owned DEVICE memory unless noted):
@@ -148,14 +149,20 @@ int moe_ffn_forward_nvfp4(moe_ffn_handle *h, int32_t T, const void *x, const voi
  *   topk_idx [T, k] int32 (ascending expert id per token), topk_w [T, k]
  *   fp32 (aligned with topk_idx), counts [E] int32, offsets [E+1] int32,
  *   perm [T*k] int32 (token of each expert-grouped row), pos [T*k] int32
- *   (row of slot (t, j)).  topk_w is not written by moe_ffn_align_only. */
+ *   (row of slot (t, j)).  topk_w is not written by moe_ffn_align_only.
+ * The weight-streaming variant never builds the grouping tables (its
+ * kernels derive each expert's rows from topk_idx); after such a forward
+ * this call first queues the grouping kernels on `stream`. */
 int moe_ffn_get_routing(moe_ffn_handle *h, int32_t *topk_idx, float *topk_w, int32_t *counts,
                         int32_t *offsets, int32_t *perm, int32_t *pos, void *stream);
 
-/* Device-to-device copies of the intermediates of the last forward; any
- * destination may be NULL.  h [T*k, I] bf16 (GeGLU hidden of each routed
- * row, expert-grouped order), y [T*k, H] bf16 (expert output per row),
- * h_d [T, D] bf16 and y_d [T, H] bf16 (dense branch). */
+/* Intermediates of the last forward copied into caller device buffers;
+ * any destination may be NULL.  h [T*k, I] bf16 (GeGLU hidden of each
+ * routed row, expert-grouped order), y [T*k, H] bf16 (expert output per
+ * row, same order), h_d [T, D] bf16 and y_d [T, H] bf16 (dense branch).
+ * The weight-streaming variant keeps routed rows in (token, slot) order;
+ * after such a forward this call queues the grouping kernels and a copy
+ * into grouped order on `stream`. */
 int moe_ffn_get_intermediates(moe_ffn_handle *h, void *h_rows, void *y_rows, void *h_dense,
                               void *y_dense, void *stream);
 
@@ -167,10 +174,13 @@ int moe_ffn_align_only(moe_ffn_handle *h, int32_t T, const int32_t *topk_idx, vo
 /* Per-stage timing with HIP events recorded on the forward's stream.
  * Stages: */
 enum {
-  MOE_FFN_STAGE_ROUTE = 0,   /* router logits + top-k (+ grouping when T <= 64) */
-  MOE_FFN_STAGE_ALIGN = 1,   /* grouping kernels (T > 64) */
-  MOE_FFN_STAGE_GATEUP = 2,  /* routed + dense gate/up GEMMs with GeGLU */
-  MOE_FFN_STAGE_DOWN = 3,    /* routed + dense down GEMMs */
+  MOE_FFN_STAGE_ROUTE = 0,   /* router logits + top-k */
+  MOE_FFN_STAGE_ALIGN = 1,   /* grouping kernels (MFMA variant only) */
+  MOE_FFN_STAGE_GATEUP = 2,  /* gate/up: MFMA = routed + dense GEMM with GeGLU;
+                                streaming = the routed partial-sum kernel and
+                                its GeGLU kernel (the dense branch runs on a
+                                side stream, unmeasured) */
+  MOE_FFN_STAGE_DOWN = 3,    /* down: as for gate/up */
   MOE_FFN_STAGE_COMBINE = 4, /* weighted sum + dense add */
   MOE_FFN_NUM_STAGES = 5
 };

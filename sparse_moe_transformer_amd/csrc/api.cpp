@@ -29,6 +29,10 @@ struct moe_ffn_handle {
   int variant;
   int max_mtiles;
   int last_T;
+  // the last forward ran the streaming path: its grouping tables (counts,
+  // offsets, perm, pos) were never built and its h / h_d / y rows are not
+  // in grouped order; the diagnostic getters rebuild them on request
+  bool last_stream;
   bool sync_mode;
   uint32_t prof_mask;
   int prof_max;
@@ -92,7 +96,7 @@ Layout layout(const moe_ffn_config& c) {
   L.max_mtiles = int((T * k + moe::kGemmBM - 1) / moe::kGemmBM + E);
   const size_t sizes[19] = {
       size_t(moe::kRouterSlices) * T * E * 4,     // logits (K-slices)
-      size_t(moe::kRouteSplits) * 256 * 64 * 4,   // route_part (slices x phases x 64 x E)
+      size_t(moe::kRouteSlices) * 64 * E * 4,     // route_part (K-slices, T <= 64)
       T * k * 4,                                  // topk_idx
       T * k * 4,                                  // topk_w
       E * 4,                                      // counts
@@ -103,13 +107,13 @@ Layout layout(const moe_ffn_config& c) {
       T * k * 4,                                  // pos
       size_t(L.max_mtiles) * 16,                  // mtiles
       E * 16,                                     // active
-      512 * 4,                                    // meta: counters and tickets
+      512 * 4,                                    // meta: counters
       T * k * I * 2,                              // h
       T * (D ? D : 1) * 2,                        // h_d
       T * k * H * 2,                              // y
       T * H * 2,                                  // y_d
-      size_t(moe::kStreamKS) * 2 *                // streaming gate/up partials
-          (size_t(moe::kStreamRows) * I + size_t(moe::kRouteSmallT) * (D ? D : 1)) * 4,
+      (size_t(moe::kStreamKS) * moe::kStreamRows * I +  // streaming gate/up partials
+       size_t(moe::kDenseKS) * moe::kRouteSmallT * (D ? D : 1)) * 2 * 4,
       size_t(moe::kDenseDownKS) * moe::kRouteSmallT * H * 4,  // streaming dense down partials
   };
   size_t o = 0;
@@ -236,7 +240,9 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "route");
   }
-  if (T > moe::kRouteSmallT) {
+  if (!stream) {
+    // the MFMA tiles read the grouped rows and the tile list; the streaming
+    // kernels derive their experts' rows from topk_idx themselves
     StageTimer tm(h, MOE_FFN_STAGE_ALIGN, s, timing);
     e = moe::launch_align(sh, ws, s);
     tm.stop();
@@ -262,12 +268,13 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   {
     StageTimer tm(h, MOE_FFN_STAGE_COMBINE, s, timing);
     e = moe::launch_combine(sh, ws, static_cast<moe::bf16_t*>(out), (h->cfg.flags & MOE_FFN_ACCUMULATE) != 0,
-                            stream ? moe::kDenseDownKS : 0, s);
+                            stream && sh.D > 0 ? moe::dense_down_slices(sh) : 0, stream, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "combine");
   }
   if (timing) ++h->prof_fwd;
   h->last_T = T;
+  h->last_stream = stream;
   return finish(h, s, "forward");
 }
 
@@ -500,6 +507,10 @@ int moe_ffn_get_routing(moe_ffn_handle* h, int32_t* topk_idx, float* topk_w, int
     if (int r = check_handle(h)) return r;
     DeviceGuard g(h->device);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (h->last_stream && h->last_T > 0) {
+      hipError_t e = moe::launch_align(shape_of(h, h->last_T), h->ws, s);
+      if (e != hipSuccess) return hip_fail(e, "align");
+    }
     const size_t Tk = size_t(h->last_T) * h->cfg.top_k;
     const size_t E = size_t(h->cfg.num_experts);
     struct C {
@@ -528,6 +539,16 @@ int moe_ffn_get_intermediates(moe_ffn_handle* h, void* h_rows, void* y_rows, voi
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t T = size_t(h->last_T), k = size_t(h->cfg.top_k);
     const size_t H = size_t(h->cfg.hidden), I = size_t(h->cfg.expert_dim), D = size_t(h->cfg.dense_dim);
+    if (h->last_stream && T > 0) {
+      // rebuild perm / pos, then write h and y in grouped order
+      const moe::Shape sh = shape_of(h, int(T));
+      hipError_t e = moe::launch_align(sh, h->ws, s);
+      if (e == hipSuccess)
+        e = moe::launch_stream_export(sh, h->ws, static_cast<moe::bf16_t*>(h_rows), static_cast<moe::bf16_t*>(y_rows), s);
+      if (e != hipSuccess) return hip_fail(e, "get_intermediates export");
+      h_rows = nullptr;
+      y_rows = nullptr;
+    }
     struct C {
       void* dst;
       const void* src;
@@ -556,6 +577,7 @@ int moe_ffn_align_only(moe_ffn_handle* h, int32_t T, const int32_t* topk_idx, vo
       return fail(MOE_FFN_ERR_INVALID_ARG, "topk_idx must be 4-byte aligned");
     if (T == 0) {
       h->last_T = 0;
+      h->last_stream = false;
       g_err.clear();
       return MOE_FFN_OK;
     }
@@ -567,6 +589,7 @@ int moe_ffn_align_only(moe_ffn_handle* h, int32_t T, const int32_t* topk_idx, vo
     e = moe::launch_align(shape_of(h, T), h->ws, s);
     if (e != hipSuccess) return hip_fail(e, "align");
     h->last_T = T;
+    h->last_stream = false;
     return finish(h, s, "align_only");
   } catch (...) {
     return fail(MOE_FFN_ERR_HIP, "unknown exception");

@@ -1,9 +1,11 @@
 // Output of the MoE block: the routing-weighted sum of the token's expert
 // rows plus the always-on dense branch (gemma-llm API page
-// gm.nn.Gemma4_26B_A4B: every layer has a MoE branch and a dense shared MLP
-// branch; the sum carries no extra weight on the dense term).
+// gm.nn.Gemma4_26B_A4B, model description: each layer runs the expert
+// mixture and one dense MLP side by side; no weight on the dense term is
+// stated, so it is a plain sum).
 //
-//   out[t] = sum_{j < k} w[t, j] * y[pos[t, j]] + y_d[t]     (fp32, j ascending)
+//   out[t] = sum_{j < k} w[t, j] * y[row(t, j)] + y_d[t]     (fp32, j ascending)
+//   row(t, j) = pos[t, j] (grouped rows) or t * k + j (slot-ordered rows)
 //   (y_d is bf16, or the sum of fp32 K-slices of the dense down projection)
 //   with the accumulate flag: out[t] = out_old[t] + (the above)
 //
@@ -19,13 +21,13 @@ constexpr int kThreads = 128;
 
 // grid (T, ceil(H / (8 * kThreads))): one token per blockIdx.x, 8 columns per thread
 __global__ __launch_bounds__(kThreads) void k_combine(Shape sh, Workspace ws, bf16_t* __restrict__ out,
-                                                      int accumulate, int yd_slices) {
+                                                      int accumulate, int yd_slices, int slot_rows) {
   const int t = blockIdx.x;
   const int H = sh.H, k = sh.k;
   __shared__ int prow[16];
   __shared__ float pw[16];
   if (threadIdx.x < k) {
-    prow[threadIdx.x] = ws.pos[(long long)t * k + threadIdx.x];
+    prow[threadIdx.x] = slot_rows ? t * k + threadIdx.x : ws.pos[(long long)t * k + threadIdx.x];
     pw[threadIdx.x] = ws.topk_w[(long long)t * k + threadIdx.x];
   }
   __syncthreads();
@@ -47,11 +49,22 @@ __global__ __launch_bounds__(kThreads) void k_combine(Shape sh, Workspace ws, bf
       yd[2 * d + 1] = bf16_hi(vd[d]);
     }
   } else if (sh.D > 0) {
-    for (int sl = 0; sl < yd_slices; ++sl) {
-      const float4* p = reinterpret_cast<const float4*>(ws.ydp + ((long long)sl * kRouteSmallT + t) * H + c);
-      const float4 a = p[0], b = p[1];
-      yd[0] += a.x; yd[1] += a.y; yd[2] += a.z; yd[3] += a.w;
-      yd[4] += b.x; yd[5] += b.y; yd[6] += b.z; yd[7] += b.w;
+    // issue every slice's loads, then sum in slice order
+    float4 pa[kDenseDownKS], pb[kDenseDownKS];
+#pragma unroll
+    for (int sl = 0; sl < kDenseDownKS; ++sl) {
+      if (sl < yd_slices) {
+        const float4* p = reinterpret_cast<const float4*>(ws.ydp + ((long long)sl * kRouteSmallT + t) * H + c);
+        pa[sl] = p[0];
+        pb[sl] = p[1];
+      }
+    }
+#pragma unroll
+    for (int sl = 0; sl < kDenseDownKS; ++sl) {
+      if (sl < yd_slices) {
+        yd[0] += pa[sl].x; yd[1] += pa[sl].y; yd[2] += pa[sl].z; yd[3] += pa[sl].w;
+        yd[4] += pb[sl].x; yd[5] += pb[sl].y; yd[6] += pb[sl].z; yd[7] += pb[sl].w;
+      }
     }
     // the dense branch's output, rounded to bf16, kept for inspection; the
     // sum below uses the same rounded values as the bf16 path
@@ -96,9 +109,10 @@ __global__ __launch_bounds__(kThreads) void k_combine(Shape sh, Workspace ws, bf
 }  // namespace
 
 hipError_t launch_combine(const Shape& sh, const Workspace& ws, bf16_t* out, bool accumulate, int yd_slices,
-                          hipStream_t s) {
+                          bool slot_rows, hipStream_t s) {
   const int cols = (sh.H + 8 * kThreads - 1) / (8 * kThreads);
-  hipLaunchKernelGGL(k_combine, dim3(sh.T, cols), dim3(kThreads), 0, s, sh, ws, out, accumulate ? 1 : 0, yd_slices);
+  hipLaunchKernelGGL(k_combine, dim3(sh.T, cols), dim3(kThreads), 0, s, sh, ws, out, accumulate ? 1 : 0, yd_slices,
+                     slot_rows ? 1 : 0);
   return hipGetLastError();
 }
 

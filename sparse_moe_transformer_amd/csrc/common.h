@@ -48,7 +48,7 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 // Workspace of one handle (device pointers), laid out once at create.
 struct Workspace {
   float* logits;        // [kRouterSlices, Tmax, E] fp32 partial router logits (large-T path)
-  float* route_part;    // [kRouteSplits * 256 / E, 64, E] partial logits (small-T path)
+  float* route_part;    // [kRouteSlices, 64, E] fp32 partial router logits (T <= 64)
   int32_t* topk_idx;    // [Tmax, k]
   float* topk_w;        // [Tmax, k]
   int32_t* counts;      // [E]
@@ -59,27 +59,33 @@ struct Workspace {
   int32_t* pos;         // [Tmax*k]
   int32_t* mtiles;      // [max_mtiles, 4] (expert, row0, rows, 0) for MFMA tiles
   int32_t* active;      // [E, 4] (expert, row0, rows, 0) per expert with rows
-  int32_t* meta;        // [512]: 0 = #mtiles, 1 = #active; tickets: 8 router, 9 dense
-                        // gate/up, 16 + e expert e's gate/up
-  bf16_t* h;            // [Tmax*k, I]
+  int32_t* meta;        // [512]: 0 = #mtiles, 1 = #active experts
+  bf16_t* h;            // [Tmax*k, I] perm order (MFMA path) or slot order (streaming path)
   bf16_t* h_d;          // [Tmax, D]
-  bf16_t* y;            // [Tmax*k, H]
+  bf16_t* y;            // [Tmax*k, H] perm order (MFMA path) or slot order (streaming path)
   bf16_t* y_d;          // [Tmax, H]
-  float* part;          // [kStreamKS][kStreamRows][2][I] + [kStreamKS][64][2][D] gate/up partials
+  float* part;          // [kStreamKS][kStreamRows][2][I] (rows = slots) + [kDenseKS][64][2][D]
+                        // (rows = tokens) gate/up partials of the streaming path
   float* ydp;           // [kDenseDownKS][64][H] dense down partials (streaming path)
 };
 
-constexpr int kRouteSplits = 16;   // K-slices (blocks) of the small-T router
 constexpr int kRouterSlices = 16;  // most K-slices of the large-T router logits
-constexpr int kRouteSmallT = 64;   // largest T of the fused single-block router
+constexpr int kRouteSlices = 32;   // K-slices of the small-T router logits
+constexpr int kRouteSmallT = 64;   // largest T of the one-block-per-token router and the streaming path
 constexpr int kGemmBM = 128;       // MFMA tile rows (tokens)
-constexpr int kStreamKS = 2;       // K-slices of the streaming gate/up units
-constexpr int kDenseDownKS = 4;    // K-slices of the streaming dense down units
+constexpr int kStreamKS = 2;       // K-slices of the streaming routed gate/up units
+constexpr int kDenseKS = 8;        // K-slices of the streaming dense gate/up units
+constexpr int kDenseDownKS = 16;   // K-slices of the streaming dense down units
 constexpr int kStreamRows = kRouteSmallT * 16;  // routed rows of the streaming path (T <= 64, k <= 16)
 
 struct Shape {
   int T, H, E, k, I, D;
 };
+
+// K-slices of the streaming dense-branch units: whole 64-row groups, at
+// most the constants above (no empty slice)
+__host__ __device__ inline int dense_gateup_slices(const Shape& sh) { return sh.H / 64 < kDenseKS ? sh.H / 64 : kDenseKS; }
+__host__ __device__ inline int dense_down_slices(const Shape& sh) { return sh.D / 64 < kDenseDownKS ? sh.D / 64 : kDenseDownKS; }
 
 // NVFP4 matrix stack
 struct Fp4Mat {
@@ -109,14 +115,19 @@ struct StreamArgs {
 enum class StreamPart { Routed, Dense };
 hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s);
 hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s);
+// h and y rows of the last streamed forward into caller buffers in grouped
+// (perm) order; needs ws.pos from launch_align; either pointer may be null
+hipError_t launch_stream_export(const Shape& sh, const Workspace& ws, bf16_t* h_rows, bf16_t* y_rows, hipStream_t s);
 
 // MFMA tiles (large T)
 hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s);
 hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s);
 
 // yd_slices: 0 = dense output in ws.y_d (bf16); n > 0 = n fp32 slices in
-// ws.ydp, summed in order (and stored to ws.y_d as bf16)
+// ws.ydp, summed in order (and stored to ws.y_d as bf16).  slot_rows: the
+// expert rows of token t are ws.y rows t*k .. t*k+k-1 (streaming path);
+// else rows ws.pos[t*k + j] (grouped order).
 hipError_t launch_combine(const Shape& sh, const Workspace& ws, bf16_t* out, bool accumulate, int yd_slices,
-                          hipStream_t s);
+                          bool slot_rows, hipStream_t s);
 
 }  // namespace moe

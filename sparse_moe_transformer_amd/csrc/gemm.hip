@@ -30,6 +30,8 @@
 // Block ids are remapped so consecutive logical tiles (the N-tiles of one
 // M-tile, then the next M-tile of the same expert) run on one XCD and share
 // its L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -252,21 +254,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     for (int j = 0; j < 2; ++j) brow_l[j] = (wn * 64 + j * 32 + (lane & 31)) * LDSK + kofs;
   }
 
-  auto compute = [&](int buf) {
+  // MFMA blocks of this wave inside the tile's rows and the matrix's
+  // columns (wave-uniform): blocks past either are skipped, so the ragged
+  // last M-tile of an expert and the last N-tile cost only their valid part
+  bool mval[2], nval[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) mval[i] = wm * 64 + i * 32 < rows;
+  if (MODE == MODE_GATEUP) {
+    nval[0] = nval[1] = n0 + wn * 32 < N;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) nval[j] = n0 + wn * 64 + j * 32 < N;
+  }
+  const bool full = __builtin_amdgcn_readfirstlane(mval[0] && mval[1] && nval[0] && nval[1]);
+
+  // Fragments of sub-step kk + 1 are read from LDS while the MFMAs of kk run.
+  auto compute = [&](int buf, auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
     const bf16_t* as = As[buf];
     const bf16_t* bs = Bs[buf];
+    bf16x8_t a[2][2], b[2][2];
+    auto frags = [&](int kk, bf16x8_t(&af)[2], bf16x8_t(&bf)[2]) {
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8_t a[2], b[2];
+      for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(as + arow_l[i] + kk);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(as + arow_l[i] + kk);
+      for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const bf16x8_t*>(bs + brow_l[j] + kk);
+    };
+    frags(0, a[0], b[0]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8_t*>(bs + brow_l[j] + kk);
+    for (int s = 0; s < BK / 16; ++s) {
+      if (s + 1 < BK / 16) frags((s + 1) * 16, a[(s + 1) & 1], b[(s + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          if (FULL || (mval[i] && nval[j]))
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
     }
   };
 
@@ -279,38 +302,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   const int nk = (ks + 1) * nk_all / S.ksplit - kt0;
   const int klast = (kt0 + nk - 1) * BK;
   u32x4_t ra0[2], rb0[4], ra1[2], rb1[4];
-  load_tile(kt0 * BK, ra0, rb0);
-  load_tile(min((kt0 + 1) * BK, klast), ra1, rb1);
-  store_tile(0, ra0, rb0);
-  __syncthreads();
-  int kt = 0;
-  // sched_barrier keeps the scheduler from sinking the next step's loads
-  // below the wait for the current step's registers
-  for (; kt + 1 < nk; kt += 2) {
-    load_tile(min((kt0 + kt + 2) * BK, klast), ra0, rb0);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(0);
-    __builtin_amdgcn_sched_barrier(0);
-    store_tile(1, ra1, rb1);
-    __syncthreads();
-    load_tile(min((kt0 + kt + 3) * BK, klast), ra1, rb1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1);
-    __builtin_amdgcn_sched_barrier(0);
+  auto kloop = [&](auto full_c) {
+    load_tile(kt0 * BK, ra0, rb0);
+    load_tile(min((kt0 + 1) * BK, klast), ra1, rb1);
     store_tile(0, ra0, rb0);
     __syncthreads();
-  }
-  if (kt < nk) compute(0);  // odd step count: LDS buffer 0 holds the last step
-
-  bool mval[2], nval[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) mval[i] = wm * 64 + i * 32 < rows;
-  if (MODE == MODE_GATEUP) {
-    nval[0] = nval[1] = n0 + wn * 32 < N;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) nval[j] = n0 + wn * 64 + j * 32 < N;
-  }
+    int kt = 0;
+    // sched_barrier keeps the scheduler from sinking the next step's loads
+    // below the wait for the current step's registers
+    for (; kt + 1 < nk; kt += 2) {
+      load_tile(min((kt0 + kt + 2) * BK, klast), ra0, rb0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0, full_c);
+      __builtin_amdgcn_sched_barrier(0);
+      store_tile(1, ra1, rb1);
+      __syncthreads();
+      load_tile(min((kt0 + kt + 3) * BK, klast), ra1, rb1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(1, full_c);
+      __builtin_amdgcn_sched_barrier(0);
+      store_tile(0, ra0, rb0);
+      __syncthreads();
+    }
+    if (kt < nk) compute(0, full_c);  // odd step count: LDS buffer 0 holds the last step
+  };
+  if (full)
+    kloop(std::true_type{});
+  else
+    kloop(std::false_type{});
 
   // ---- epilogue: lane holds column (lane & 31); rows 8(r/4) + 4(lane/32) + r%4
   float ts0 = 1.f, ts1 = 1.f;

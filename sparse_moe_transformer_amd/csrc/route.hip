@@ -13,17 +13,18 @@
 // is a deterministic function of topk_idx (no atomics decide positions).
 //
 // Two routes:
-//   T <= 64: a K-sliced partial-logit kernel (for T <= 8 with 16-byte
-//     loads of 8 experts x up to 16 rows per thread, all in flight at once),
-//     then one block that sums the slices in fixed order, routes and groups.  (No in-kernel hand-off
-//     between blocks: on this multi-XCD part a device-scope release writes
-//     back the L2, which costs more than a second launch.)
+//   T <= 64: partial logits of kRouteSlices K-slices (many small blocks,
+//     so W_r streams at full bandwidth), then one block per token sums the
+//     slices in fixed order and routes it.  (An in-kernel hand-off between
+//     blocks would need a device-scope release, which on this multi-XCD
+//     part writes back the L2 and costs more than a second launch.)
 //   large T: split-K logits (MFMA tiles when E % 128 == 0, else an FMA
-//     kernel), a top-k kernel that sums the K-slices in fixed order, then
-//     three grouping kernels: per-64-token membership masks, a per-expert
-//     scan over the token blocks, and the scatter (which also rebuilds the
-//     expert offsets and the tile lists).
+//     kernel), a top-k kernel that sums the K-slices in fixed order.
+// Grouping (any T): per-64-token membership masks, a per-expert scan over
+// the token blocks, and the scatter (which also rebuilds the expert offsets
+// and the tile lists).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -253,212 +254,94 @@ __device__ int build_offsets_and_tiles(const int cnt_e, int E, const Workspace& 
 // small T (<= 64)
 // ---------------------------------------------------------------------------
 
-// Route T <= 64 tokens from logits zl[T][E] (LDS) and group them (one
-// 64-token block); run by one whole block of BLOCK threads (BLOCK >= E).
-template <int BLOCK>
-__device__ void route_and_group(const Shape& sh, const Workspace& ws, const float* zl) {
-  const int T = sh.T, E = sh.E, k = sh.k;
-  __shared__ int32_t tk[kRouteSmallT * 16];
-  __shared__ float tw[kRouteSmallT * 16];
-  __shared__ unsigned long long mask[256];
-  __shared__ int offs[256];
-  __shared__ int scratch[BLOCK / kWave + 1];
-  const int wid = threadIdx.x / kWave;
-  for (int t = wid; t < T; t += BLOCK / kWave) wave_route_token(zl + t * E, E, k, tk + t * k, tw + t * k);
-  if (threadIdx.x < E) mask[threadIdx.x] = 0;
-  __syncthreads();
-  for (int i = threadIdx.x; i < T * k; i += BLOCK) {
-    ws.topk_idx[i] = tk[i];
-    ws.topk_w[i] = tw[i];
-    atomicOr(&mask[tk[i]], 1ull << (i / k));
+// Partial logits of one K-slice for a group of tokens:
+//   part[s][t][e] = sum over the slice's rows k of x[t][k] * W_r[k][e].
+// Block (slice s, token group of TB tokens); thread = (chunk ec of CW
+// experts, token tl, row group rg); row group rg owns the slice's rows
+// rg, rg + RG, ..., so one wave's 16-byte loads cover whole rows of W_r
+// (several tokens' lanes read the same row: one fetch serves them).  All of
+// a thread's rows are loaded at once; the slice's x rows are staged in LDS
+// as fp32 while the loads are in flight.  Row groups are summed in a fixed
+// order through LDS.
+constexpr int kRouteMaxRows = 16;  // rows of a slice per thread
+template <int CW>
+__global__ __launch_bounds__(kThreads) void k_route_part(Shape sh, int slice_rows, int TB,
+                                                        const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr,
+                                                        float* __restrict__ part) {
+  typedef typename std::conditional<CW == 8, u32x4_t, u32x2_t>::type vec_t;
+  const int H = sh.H, E = sh.E, T = sh.T;
+  const int EC = E / CW;
+  const int RG = kThreads / (EC * TB);
+  const int tid = threadIdx.x;
+  const int ec = tid % EC, tl = (tid / EC) % TB, rg = tid / (EC * TB);
+  const bool live = rg < RG;
+  const int s = blockIdx.x, t0 = blockIdx.y * TB;
+  const int k0 = s * slice_rows;
+  const int nrow = live && rg < slice_rows ? (slice_rows - 1 - rg) / RG + 1 : 0;
+  __shared__ float xs[kThreads * kRouteMaxRows];  // [TB][slice_rows]
+  __shared__ float red[kThreads * 8];              // [RG][TB][E]
+  const bf16_t* pw = wr + size_t(k0 + (live ? rg : 0)) * E + ec * CW;
+  vec_t vw[kRouteMaxRows];
+#pragma unroll
+  for (int i = 0; i < kRouteMaxRows; ++i)
+    vw[i] = i < nrow ? *reinterpret_cast<const vec_t*>(pw + size_t(i) * RG * E) : vec_t{};
+  const int nch = slice_rows / 8;
+  for (int c = tid; c < TB * nch; c += kThreads) {
+    const int tt = c / nch, kc = (c % nch) * 8;
+    u32x4_t v = {0, 0, 0, 0};
+    if (t0 + tt < T) v = *reinterpret_cast<const u32x4_t*>(x + size_t(t0 + tt) * H + k0 + kc);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      xs[tt * slice_rows + kc + 2 * d] = bf16_lo(v[d]);
+      xs[tt * slice_rows + kc + 2 * d + 1] = bf16_hi(v[d]);
+    }
   }
   __syncthreads();
-  const uint64_t m = threadIdx.x < E ? mask[threadIdx.x] : 0;
-  const int off = build_offsets_and_tiles<BLOCK>(__popcll(m), E, ws, scratch);
-  if (threadIdx.x < E) offs[threadIdx.x] = off;
+  float acc[CW];
+#pragma unroll
+  for (int c = 0; c < CW; ++c) acc[c] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRouteMaxRows; ++i) {
+    const float xv = xs[tl * slice_rows + min(rg + RG * i, slice_rows - 1)];  // past nrow: zero weights
+#pragma unroll
+    for (int d = 0; d < CW / 2; ++d) {
+      acc[2 * d] += xv * bf16_lo(vw[i][d]);
+      acc[2 * d + 1] += xv * bf16_hi(vw[i][d]);
+    }
+  }
+  if (live) {
+#pragma unroll
+    for (int c = 0; c < CW; ++c) red[(rg * TB + tl) * E + ec * CW + c] = acc[c];
+  }
   __syncthreads();
-  for (int i = threadIdx.x; i < T * k; i += BLOCK) {
-    const int t = i / k;
-    const int ee = tk[i];
-    const int p = offs[ee] + __popcll(mask[ee] & ((1ull << t) - 1ull));
-    ws.perm[p] = t;
-    ws.pos[i] = p;
+  for (int o = tid; o < TB * E; o += kThreads) {
+    const int tt = o / E;
+    if (t0 + tt >= T) continue;
+    float z = 0.f;
+    for (int g = 0; g < RG; ++g) z += red[g * TB * E + o];
+    part[(size_t(s) * kRouteSmallT + t0 + tt) * E + (o % E)] = z;
   }
 }
 
-// T <= 8 and E / 8 a power of two: partial logits of one K-slice per block.
-// Thread = (8-expert chunk ec, row group rg owning a contiguous run of the
-// slice's rows); all of its rows' 16-byte pieces of W_r are loaded at once
-// (<= 16 rows), 8 tokens x 8 experts accumulators.  The 8 token rows of the
-// slice are staged in LDS as fp32.  Row groups fold by shuffles and across
-// waves in LDS; the block writes route_part[block][t][e].
-__global__ __launch_bounds__(kThreads) void k_route_part8(Shape sh, const bf16_t* __restrict__ x,
-                                                         const bf16_t* __restrict__ wr, Workspace ws) {
-  const int T = sh.T, H = sh.H, E = sh.E;
-  const int rows = H / gridDim.x;  // multiple of 16
-  const int k0 = blockIdx.x * rows;
-  const int EC = E / 8, RG = kThreads / EC;
-  const int ec = threadIdx.x % EC, rg = threadIdx.x / EC;
-  const int R = (rows + RG - 1) / RG;
-  const int kb = min(rows, rg * R), ke = min(rows, kb + R);
-  extern __shared__ float smem[];
-  float* xs = smem;  // [8][rows]
-  constexpr int MAXR = 16;
-  const bf16_t* pw = wr + size_t(k0 + kb) * E + ec * 8;
-  float acc[8][8];
+// One block per token: z = sum of the slices in order (+ b), then one wave
+// routes the token.
+__global__ __launch_bounds__(kThreads) void k_route_fin(Shape sh, int nslices, const float* __restrict__ part,
+                                                       const float* __restrict__ bias, Workspace ws) {
+  const int t = blockIdx.x, E = sh.E;
+  __shared__ float zs[256];
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const float* p = part + size_t(t) * E + e;
+    float v[kRouteSlices];
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+    for (int j = 0; j < kRouteSlices; ++j) v[j] = j < nslices ? p[size_t(j) * kRouteSmallT * E] : 0.f;
+    float z = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[t][c] = 0.f;
-  for (int b = 0; b < R; b += MAXR) {  // same trip count in every thread
-    u32x4_t vw[MAXR];
-#pragma unroll
-    for (int i = 0; i < MAXR; ++i)
-      vw[i] = kb + b + i < ke ? *reinterpret_cast<const u32x4_t*>(pw + size_t(b + i) * E) : u32x4_t{0, 0, 0, 0};
-    if (b == 0) {  // stage x while the first rows are in flight
-      const int nch = rows / 8;
-      for (int i = threadIdx.x; i < 8 * nch; i += kThreads) {
-        const int t = i / nch, kc = (i % nch) * 8;
-        u32x4_t v = {0, 0, 0, 0};
-        if (t < T) v = *reinterpret_cast<const u32x4_t*>(x + size_t(t) * H + k0 + kc);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          xs[t * rows + kc + 2 * d] = bf16_lo(v[d]);
-          xs[t * rows + kc + 2 * d + 1] = bf16_hi(v[d]);
-        }
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < MAXR; ++i) {
-      const int kk = min(kb + b + i, rows - 1);  // past ke: zero weights
-      float w[8];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        w[2 * d] = bf16_lo(vw[i][d]);
-        w[2 * d + 1] = bf16_hi(vw[i][d]);
-      }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float xv = xs[t * rows + kk];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[t][c] += xv * w[c];
-      }
-    }
-    if (b + MAXR < R) continue;
-    // fold row groups inside each wave (lane bits >= log2(EC); the step
-    // test is uniform, so every step unrolls), then across the 4 waves
-#pragma unroll
-    for (int st = 0; st < 6; ++st) {
-      const int off = 1 << st;
-      if (off >= EC) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) acc[t][c] += __shfl_xor(acc[t][c], off, kWave);
-      }
-    }
-    __syncthreads();  // red aliases xs
-    float* red = smem;  // [4 waves][8][E]
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane < EC) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) red[(wave * 8 + t) * E + lane * 8 + c] = acc[t][c];
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < T * E; i += kThreads) {
-      float z = 0.f;
-#pragma unroll
-      for (int wv = 0; wv < 4; ++wv) z += red[wv * 8 * E + i];
-      ws.route_part[size_t(blockIdx.x) * kRouteSmallT * E + i] = z;
-    }
-  }
-}
-
-// 8 < T <= 64 (or other E): partial logits of one K-slice per block.
-// Thread = (expert e, token group g); rows' loads issued 16 at a time.
-__global__ __launch_bounds__(kThreads) void k_route_part(Shape sh, const bf16_t* __restrict__ x,
-                                                        const bf16_t* __restrict__ wr, Workspace ws) {
-  constexpr int TT = 64;
-  const int T = sh.T, H = sh.H, E = sh.E;
-  const int rows = H / gridDim.x;
-  const int k0 = blockIdx.x * rows;
-  const int TG = kThreads / E;
-  const int e = threadIdx.x % E;
-  const int g = threadIdx.x / E;
-  extern __shared__ float smem[];
-  float* xs = smem;  // [TT][rows]
-  for (int i = threadIdx.x; i < TT * rows; i += kThreads) {
-    const int t = i / rows, kk = i % rows;
-    xs[i] = (t < T) ? bf16_to_f32(x[size_t(t) * H + k0 + kk]) : 0.f;
+    for (int j = 0; j < kRouteSlices; ++j) z += v[j];
+    zs[e] = bias ? z + bias[e] : z;
   }
   __syncthreads();
-  if (g >= TG) return;
-  float acc[TT];
-#pragma unroll
-  for (int i = 0; i < TT; ++i) acc[i] = 0.f;
-  constexpr int B = 16;
-  for (int kb = 0; kb < rows; kb += B) {
-    float w[B];
-#pragma unroll
-    for (int j = 0; j < B; ++j) w[j] = kb + j < rows ? bf16_to_f32(wr[size_t(k0 + kb + j) * E + e]) : 0.f;
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const float* xr = xs + min(kb + j, rows - 1);  // past the slice: zero weight
-#pragma unroll
-      for (int i = 0; i < TT; ++i) {
-        const int t = g + i * TG;
-        if (t < TT) acc[i] += xr[t * rows] * w[j];
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < TT; ++i) {
-    const int t = g + i * TG;
-    if (t < T) ws.route_part[(size_t(blockIdx.x) * kRouteSmallT + t) * E + e] = acc[i];
-  }
-}
-
-// one block of 512 threads (one wave per token for T <= 8): sum the K-slices
-// in fixed order (+ bias), route, group
-constexpr int kFinishThreads = 512;
-__global__ __launch_bounds__(kFinishThreads) void k_route_finish(Shape sh, int nparts, const float* __restrict__ bias,
-                                                          Workspace ws) {
-  const int T = sh.T, E = sh.E;
-  extern __shared__ float zl[];  // [T][E]
-  const int E4 = E / 4;
-  const size_t stride = size_t(kRouteSmallT) * E / 4;  // float4s between parts
-  for (int i = threadIdx.x; i < T * E4; i += kFinishThreads) {
-    const int t = i / E4, e4 = (i % E4) * 4;
-    const float4* p = reinterpret_cast<const float4*>(ws.route_part + size_t(t) * E + e4);
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int b0 = 0; b0 < nparts; b0 += 16) {
-      float4 v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = (b0 + j < nparts) ? p[(b0 + j) * stride] : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        s.x += v[j].x;
-        s.y += v[j].y;
-        s.z += v[j].z;
-        s.w += v[j].w;
-      }
-    }
-    if (bias) {
-      s.x += bias[e4];
-      s.y += bias[e4 + 1];
-      s.z += bias[e4 + 2];
-      s.w += bias[e4 + 3];
-    }
-    zl[t * E + e4] = s.x;
-    zl[t * E + e4 + 1] = s.y;
-    zl[t * E + e4 + 2] = s.z;
-    zl[t * E + e4 + 3] = s.w;
-  }
-  __syncthreads();
-  route_and_group<kFinishThreads>(sh, ws, zl);
+  if (threadIdx.x < kWave)
+    wave_route_token(zs, E, sh.k, ws.topk_idx + size_t(t) * sh.k, ws.topk_w + size_t(t) * sh.k);
 }
 
 // ---------------------------------------------------------------------------
@@ -570,18 +453,27 @@ __global__ __launch_bounds__(kThreads) void k_align_scatter(Shape sh, Workspace 
 
 hipError_t launch_route_small(const Shape& sh, const bf16_t* x, const bf16_t* wr, const float* bias,
                               const Workspace& ws, hipStream_t s) {
-  const int nsplit = kRouteSplits;  // H % 256 == 0: every slice has a multiple of 16 rows
-  const int rows = sh.H / nsplit;
-  const int ec = sh.E / 8;
-  if (sh.T <= 8 && sh.E % 8 == 0 && (ec & (ec - 1)) == 0) {
-    const size_t lds = std::max(size_t(8) * rows, size_t(4) * 8 * sh.E) * sizeof(float);
-    hipLaunchKernelGGL(k_route_part8, dim3(nsplit), dim3(kThreads), lds, s, sh, x, wr, ws);
-  } else {
-    const size_t lds = size_t(64) * rows * sizeof(float);
-    hipLaunchKernelGGL(k_route_part, dim3(nsplit), dim3(kThreads), lds, s, sh, x, wr, ws);
-  }
-  hipLaunchKernelGGL(k_route_finish, dim3(1), dim3(kFinishThreads), size_t(sh.T) * sh.E * sizeof(float), s, sh,
-                     nsplit, bias, ws);
+  if (sh.T == 0) return hipSuccess;
+  // kRouteSlices slices of a multiple of 8 rows (H % 256 == 0); enough row
+  // groups that a thread loads at most kRouteMaxRows rows, the rest of the
+  // block's threads spread over tokens
+  const int cw = sh.E % 8 == 0 ? 8 : 4;
+  const int ec = sh.E / cw;
+  int nslices = kRouteSlices;
+  while (nslices > 1 && (sh.H % nslices || (sh.H / nslices) % 8)) nslices /= 2;
+  const int slice_rows = sh.H / nslices;
+  int rg_need = 1;
+  while (rg_need * kRouteMaxRows < slice_rows) rg_need *= 2;
+  const int tb = std::max(1, std::min(sh.T, kThreads / (ec * rg_need)));
+  const int rg = kThreads / (ec * tb);
+  if (rg < 1 || (slice_rows + rg - 1) / rg > kRouteMaxRows || tb * slice_rows > kThreads * kRouteMaxRows)
+    return hipErrorInvalidValue;
+  const dim3 grid(nslices, (sh.T + tb - 1) / tb);
+  if (cw == 8)
+    hipLaunchKernelGGL(k_route_part<8>, grid, dim3(kThreads), 0, s, sh, slice_rows, tb, x, wr, ws.route_part);
+  else
+    hipLaunchKernelGGL(k_route_part<4>, grid, dim3(kThreads), 0, s, sh, slice_rows, tb, x, wr, ws.route_part);
+  hipLaunchKernelGGL(k_route_fin, dim3(sh.T), dim3(kThreads), 0, s, sh, nslices, ws.route_part, bias, ws);
   return hipGetLastError();
 }
 

@@ -5,28 +5,34 @@
 // bandwidth.  Both kernels are built from one unit routine:
 //
 //   unit = (weight matrix, NCOLS output columns, K rows [kbeg, kend)),
-//   applied to <= 8 activation rows (bf16, in global memory).
+//   applied to <= 8 activation rows.
 //   Thread = (column group of 8 columns = one 16-byte load per weight row,
-//   row group owning a contiguous run of R rows).  16 (1-2 rows) or 8 (more
-//   rows) weight rows' loads are in flight per thread.  For 1-2 activation rows each thread loads its own
-//   activation values alongside the weights (no LDS staging, no barrier);
-//   for more rows they are staged in LDS transposed ([k][row], one 16-byte
-//   read feeds 8 rows) while the first weight batch is already in flight.
-//   Row-group partial sums are folded with shuffles, then across waves.
+//   row group owning a contiguous run of R rows).  4 to 16 weight rows'
+//   loads are in flight per thread (more for fewer activation rows).  For
+//   1-2 x rows each thread loads its own activation values alongside the
+//   weights (no LDS staging, no barrier); otherwise the rows are staged in
+//   LDS transposed ([k][row], one 16-byte read feeds 8 rows) while the first
+//   weight batch is already in flight.  Row-group partial sums are folded
+//   with shuffles, then across waves.
 //
 //   gate/up (k_stream_gateup): units are (expert or dense branch, gate or up
-//     matrix, 64 columns, one of kStreamKS K-slices) over the group's token
-//     rows (x gathered through perm).  Each unit writes fp32 partial
-//     pre-activations; a small kernel then sums the slices in fixed order
-//     and writes h = gelu_tanh(G) * U (the GeGLU) in bf16.  (No in-kernel
-//     hand-off between blocks: on this multi-XCD part a device-scope
-//     release writes back the L2, which is far dearer than a launch.)
+//     matrix, 64 columns, one K-slice of whole 64-row groups) over the
+//     group's token rows (x gathered by token).  Each unit writes fp32
+//     partial pre-activations; k_stream_geglu then sums the slices in fixed
+//     order and writes h = gelu_tanh(G) * U (the GeGLU) in bf16.  (No
+//     in-kernel hand-off between blocks: on this multi-XCD part a
+//     device-scope release writes back the L2, which is far dearer than a
+//     launch.)
 //   down (k_stream_down): units are (expert, 128 columns) over the expert's
 //     h rows, output rows y in bf16; the dense branch's longer K is cut into
-//     kDenseDownKS slices whose fp32 partial outputs the combine sums.
+//     K-slices whose fp32 partial outputs the combine sums.
 //
-// Grids are sized by the upper bound on active experts; units past the
-// device-side active list exit at once.  Dense-branch units come first.
+// Routed units need no grouping tables: each block derives its expert's
+// rows from topk_idx (at most 64 tokens) with a few LDS atomics.  Routed
+// rows are indexed by slot s = t * k + j, so the combine reads a token's k
+// rows at s = t * k .. t * k + k - 1.  Grids are sized by the upper bound on
+// active experts; units past the last active expert exit at once.  Dense
+// and routed units are separate kernel instances.
 #include <algorithm>
 #include <type_traits>
 
@@ -52,8 +58,31 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
 __device__ __forceinline__ float* part_ptr(const Workspace& ws, const Shape& sh, bool dense, int ks, int row,
                                            int mat) {
   if (!dense) return ws.part + ((size_t(ks) * kStreamRows + row) * 2 + mat) * sh.I;
-  float* base = ws.part + size_t(kStreamKS) * kStreamRows * 2 * sh.I;
+  float* base = ws.part + size_t(kStreamKS) * kStreamRows * 2 * sh.I;  // then [kDenseKS][64][2][D]
   return base + ((size_t(ks) * kRouteSmallT + row) * 2 + mat) * sh.D;
+}
+
+// Weight and activation rows are read through buffer resources: a 32-bit
+// per-thread byte offset plus a uniform (scalar) row offset, so the unrolled
+// loads share one address register instead of a 64-bit address each.  The
+// base pointers must be block-uniform.
+constexpr int kPolicyNT = 2;  // nontemporal: weights are streamed once
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
+}
+template <class V, int POLICY>
+__device__ __forceinline__ V bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (sizeof(V) == 16)
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
+  else
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POLICY));
+}
+// a pointer that is the same in every lane, moved to scalar registers
+__device__ __forceinline__ const bf16_t* uniform_ptr(const bf16_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const bf16_t*>((uint64_t(hi) << 32) | lo);
 }
 
 // Fold acc over the row groups of the block; returns [NT][NCOLS] sums in LDS.
@@ -115,20 +144,28 @@ __device__ const float* unit_direct(const bf16_t* __restrict__ w, int ldw, int k
   for (int r = 0; r < NT; ++r)
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
-  const bf16_t* pw = w + (long long)k0 * ldw + cg * 8;
+  const __amdgpu_buffer_rsrc_t rw = rsrc_of(w);
+  const uint32_t wrow = uint32_t(ldw) * 2, wv = uint32_t(k0) * wrow + cg * 16;
+  __amdgpu_buffer_rsrc_t rx[NT];
+  bool has[NT];
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    const bf16_t* p = uniform_ptr(act[r]);
+    has[r] = p != nullptr;
+    rx[r] = rsrc_of(p);
+  }
   for (int b = 0; b < R; b += kU) {
     u32x4_t vw[kU];
     u32x2_t va[NT][kU / 4];
 #pragma unroll
     for (int i = 0; i < kU; ++i)
-      vw[i] = (b + i < R) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pw + (long long)(b + i) * ldw))
-                          : u32x4_t{0, 0, 0, 0};
+      vw[i] = (b + i < R) ? bload<u32x4_t, kPolicyNT>(rw, wv, uint32_t(b + i) * wrow) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < NT; ++r)
 #pragma unroll
       for (int q = 0; q < kU / 4; ++q)
-        va[r][q] = (act[r] && b + 4 * q < R) ? *reinterpret_cast<const u32x2_t*>(act[r] + k0 + b + 4 * q)
-                                              : u32x2_t{0, 0};
+        va[r][q] = (has[r] && b + 4 * q < R) ? bload<u32x2_t, 0>(rx[r], uint32_t(k0) * 2, uint32_t(b + 4 * q) * 2)
+                                             : u32x2_t{0, 0};
     // rows past R hold zero weights: no branch, so the loop fully unrolls
 #pragma unroll
     for (int i = 0; i < kU; i += 2)
@@ -138,11 +175,41 @@ __device__ const float* unit_direct(const bf16_t* __restrict__ w, int ldw, int k
   return fold_rows<NT, NCOLS, 8>(acc, red);
 }
 
-// NT in (2, 8] rows: activations staged in LDS as xs[k - kbeg][8]; the first
-// weight batch is issued before the staging.
-template <int NT, int NCOLS, int CPT, int U>
-__device__ const float* unit_staged(const bf16_t* __restrict__ w, int ldw, int kbeg, int kend,
-                                    const bf16_t* const* act, bf16_t* xs, float* red) {
+// Staging of NT <= 8 activation rows into LDS as xs[k - kbeg][8] (bf16):
+// rows read from global memory (x rows of the gate/up units).  A thread
+// loads one 8-k piece of every row (two halves of 4 rows) and transposes it
+// in registers into 16-bit runs of xs[k][0..8).
+struct StageRows {
+  const bf16_t* const* act;  // [8] row pointers, null = zero row
+  __device__ void operator()(bf16_t* xs, int kbeg, int kend) const {
+    const int nch = (kend - kbeg) / 8;
+#pragma unroll 1
+    for (int c = threadIdx.x; c < nch; c += kThreads) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4_t v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bf16_t* src = act[4 * hf + r];
+          v[r] = src ? *reinterpret_cast<const u32x4_t*>(src + kbeg + c * 8) : u32x4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32x2_t lo = {perm_lo16(v[0][d], v[1][d]), perm_lo16(v[2][d], v[3][d])};
+          const u32x2_t hi = {perm_hi16(v[0][d], v[1][d]), perm_hi16(v[2][d], v[3][d])};
+          *reinterpret_cast<u32x2_t*>(xs + (c * 8 + 2 * d) * kRowsChunk + 4 * hf) = lo;
+          *reinterpret_cast<u32x2_t*>(xs + (c * 8 + 2 * d + 1) * kRowsChunk + 4 * hf) = hi;
+        }
+      }
+    }
+  }
+};
+
+// NT <= 8 rows staged in LDS as xs[k - kbeg][8] by `stage`; the first weight
+// batch is issued before the staging so that it overlaps it.
+template <int NT, int NCOLS, int CPT, int U, class Stage>
+__device__ const float* unit_staged(const bf16_t* __restrict__ w, int ldw, int kbeg, int kend, const Stage& stage,
+                                    bf16_t* xs, float* red) {
   constexpr int CG = NCOLS / CPT, RG = kThreads / CG;
   typedef typename std::conditional<CPT == 8, u32x4_t, u32x2_t>::type vec_t;
   const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
@@ -153,33 +220,12 @@ __device__ const float* unit_staged(const bf16_t* __restrict__ w, int ldw, int k
   for (int r = 0; r < NT; ++r)
 #pragma unroll
     for (int c = 0; c < CPT; ++c) acc[r][c] = 0.f;
-  const bf16_t* pw = w + (long long)k0 * ldw + cg * CPT;
+  const __amdgpu_buffer_rsrc_t rw = rsrc_of(w);
+  const uint32_t wrow = uint32_t(ldw) * 2, wv = uint32_t(k0) * wrow + cg * CPT * 2;
   vec_t vw[U];
 #pragma unroll
-  for (int i = 0; i < U; ++i)
-    vw[i] = (i < R) ? __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(pw + (long long)i * ldw)) : vec_t{};
-  // stage: a thread loads one 8-k piece of every row (two halves of 4 rows)
-  // and transposes it in registers into 16-bit runs of xs[k][0..8)
-  const int nch = (kend - kbeg) / 8;
-#pragma unroll 1
-  for (int c = threadIdx.x; c < nch; c += kThreads) {
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      u32x4_t v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bf16_t* src = act[4 * hf + r];
-        v[r] = src ? *reinterpret_cast<const u32x4_t*>(src + kbeg + c * 8) : u32x4_t{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const u32x2_t lo = {perm_lo16(v[0][d], v[1][d]), perm_lo16(v[2][d], v[3][d])};
-        const u32x2_t hi = {perm_hi16(v[0][d], v[1][d]), perm_hi16(v[2][d], v[3][d])};
-        *reinterpret_cast<u32x2_t*>(xs + (c * 8 + 2 * d) * kRowsChunk + 4 * hf) = lo;
-        *reinterpret_cast<u32x2_t*>(xs + (c * 8 + 2 * d + 1) * kRowsChunk + 4 * hf) = hi;
-      }
-    }
-  }
+  for (int i = 0; i < U; ++i) vw[i] = (i < R) ? bload<vec_t, kPolicyNT>(rw, wv, uint32_t(i) * wrow) : vec_t{};
+  stage(xs, kbeg, kend);
   __syncthreads();
   for (int b = 0;;) {
 #pragma unroll
@@ -199,103 +245,127 @@ __device__ const float* unit_staged(const bf16_t* __restrict__ w, int ldw, int k
     if (b >= R) break;
 #pragma unroll
     for (int i = 0; i < U; ++i)
-      vw[i] = (b + i < R) ? __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(pw + (long long)(b + i) * ldw))
-                          : vec_t{};
+      vw[i] = (b + i < R) ? bload<vec_t, kPolicyNT>(rw, wv, uint32_t(b + i) * wrow) : vec_t{};
   }
   return fold_rows<NT, NCOLS, CPT>(acc, red);
 }
 
-// one chunk of nr <= 8 rows: sums [nr][NCOLS] in LDS
+// One chunk of nr <= 8 activation rows: sums [nr][NCOLS] in LDS
 template <int NCOLS>
-__device__ const float* stream_unit(int nr, const bf16_t* w, int ldw, int kbeg, int kend, const bf16_t* const* act,
+__device__ const float* unit_x_rows(int nr, const bf16_t* w, int ldw, int kbeg, int kend, const bf16_t* const* act,
                                     bf16_t* xs, float* red) {
   if (nr <= 1) return unit_direct<1, NCOLS>(w, ldw, kbeg, kend, act, red);
   if (nr <= 2) return unit_direct<2, NCOLS>(w, ldw, kbeg, kend, act, red);
-  if (nr <= 4) return unit_staged<4, NCOLS, 8, 8>(w, ldw, kbeg, kend, act, xs, red);
-  return unit_staged<8, NCOLS, 8, 4>(w, ldw, kbeg, kend, act, xs, red);
+  const StageRows st{act};
+  if (nr <= 4) return unit_staged<4, NCOLS, 8, 8>(w, ldw, kbeg, kend, st, xs, red);
+  return unit_staged<8, NCOLS, 8, 4>(w, ldw, kbeg, kend, st, xs, red);
+}
+
+// ---------------------------------------------------------------------------
+// routing, derived in the block
+// ---------------------------------------------------------------------------
+
+// The rows of the ai-th expert that has tokens (experts in ascending id),
+// derived from topk_idx of the T <= 64 tokens by the block itself, so no
+// grouping tables (and no kernel to build them) are needed.  Row r is the
+// slot s = t * k + j of its r-th token t (ascending), j being the expert's
+// place in the token's list; slot[r] receives s.  Returns the expert id
+// (-1 when fewer than ai + 1 experts have tokens) and its row count.  Every
+// thread of the block must call it.
+struct ExpertRows {
+  int e, rows;
+};
+__device__ ExpertRows expert_rows(const Shape& sh, const int32_t* __restrict__ topk, int ai, int* slot) {
+  __shared__ unsigned long long mask[256];  // bit t: token t picked the expert
+  __shared__ unsigned long long pres[4];    // bit e: expert e has tokens
+  const int tid = threadIdx.x, E = sh.E, k = sh.k, n = sh.T * sh.k;
+  for (int i = tid; i < E; i += kThreads) mask[i] = 0;
+  if (tid < 4) pres[tid] = 0;
+  __syncthreads();
+  for (int s = tid; s < n; s += kThreads) {
+    const int e = topk[s];
+    atomicOr(&mask[e], 1ull << (s / k));
+    atomicOr(&pres[e >> 6], 1ull << (e & 63));
+  }
+  __syncthreads();
+  int e = -1, left = ai;  // block-uniform
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    unsigned long long m = pres[wd];
+    const int c = __popcll(m);
+    if (e < 0 && left < c) {
+      for (int i = 0; i < left; ++i) m &= m - 1;
+      e = wd * 64 + __builtin_ctzll(m);
+    }
+    if (e < 0) left -= c;
+  }
+  e = __builtin_amdgcn_readfirstlane(e);
+  if (e < 0) return {-1, 0};
+  const unsigned long long m = mask[e];
+  if (tid < sh.T && ((m >> tid) & 1ull)) {
+    int j = 0;
+    for (int jj = 0; jj < k; ++jj)
+      if (topk[tid * k + jj] == e) j = jj;
+    slot[__popcll(m & ((1ull << tid) - 1ull))] = tid * k + j;
+  }
+  __syncthreads();
+  return {e, __builtin_amdgcn_readfirstlane(int(__popcll(m)))};
 }
 
 // ---------------------------------------------------------------------------
 // gate/up
 // ---------------------------------------------------------------------------
 
-// blocks [0, units_dense) are dense-branch units, the rest routed units
-__global__ __launch_bounds__(kThreads) void k_stream_gateup(StreamArgs a, Workspace ws, int units_dense) {
+// DENSE: units (gate or up matrix, 64 columns, K-slice) over the T rows of x.
+// Routed: units (ai-th active expert, ...) over the expert's rows, x gathered
+// by token.  Writes fp32 partial pre-activations per K-slice, indexed by
+// slot (routed) or token (dense).
+// (3 waves per SIMD: the register budget of 168 holds every unit variant)
+template <bool DENSE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_gateup(StreamArgs a, Workspace ws, int KS) {
   const Shape& sh = a.sh;
   const int H = sh.H;
-  int u = blockIdx.x;
-  bool dense;
-  int grp = -1, row0 = 0, rows, N;
-  if (u < units_dense) {
-    dense = true;
-    rows = sh.T;
-    N = sh.D;
-  } else {
-    u -= units_dense;
-    const int per = (sh.I / 64) * 2 * kStreamKS;
-    const int ai = u / per;
-    if (ai >= ws.meta[1]) return;
+  const int N = DENSE ? sh.D : sh.I;
+  const int per = (N / 64) * 2 * KS;
+  __shared__ int slot[kRouteSmallT];
+  int u = blockIdx.x, grp = 0, rows = sh.T;
+  if (!DENSE) {
+    const ExpertRows er = expert_rows(sh, ws.topk_idx, u / per, slot);
+    if (er.e < 0) return;
+    grp = er.e;
+    rows = er.rows;
     u %= per;
-    dense = false;
-    grp = ws.active[4 * ai];
-    row0 = ws.active[4 * ai + 1];
-    rows = ws.active[4 * ai + 2];
-    N = sh.I;
   }
   // u -> (n-block, matrix, K-slice), K-slice fastest
-  const int ks = u % kStreamKS;
-  const int mat = (u / kStreamKS) & 1;
-  const int n0 = (u / (2 * kStreamKS)) * 64;
-  const int kbeg = ks * H / kStreamKS, kend = (ks + 1) * H / kStreamKS;
-  const bf16_t* w = dense ? (mat ? a.du : a.dg) + n0 : (mat ? a.wu : a.wg) + (long long)grp * H * sh.I + n0;
+  // K-slices of whole 64-row groups (a thread's share of rows stays even)
+  const int ks = u % KS;
+  const int mat = (u / KS) & 1;
+  const int n0 = (u / (2 * KS)) * 64;
+  const int g64 = H / 64;
+  const int kbeg = (ks * g64 / KS) * 64, kend = ((ks + 1) * g64 / KS) * 64;
+  const bf16_t* w = DENSE ? (mat ? a.du : a.dg) + n0 : (mat ? a.wu : a.wg) + (long long)grp * H * sh.I + n0;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16_t* xs = reinterpret_cast<bf16_t*>(smem_raw);  // [kend-kbeg][8] staged rows
   float* red = reinterpret_cast<float*>(smem_raw);   // [5][8][64]
   __shared__ const bf16_t* act[kRowsChunk];
+  __shared__ float* dst[kRowsChunk];
 
   for (int c0 = 0; c0 < rows; c0 += kRowsChunk) {
     const int nr = min(kRowsChunk, rows - c0);
     if (threadIdx.x < kRowsChunk) {
       const int r = threadIdx.x;
-      act[r] = r < nr ? a.x + (long long)(dense ? c0 + r : ws.perm[row0 + c0 + r]) * H : nullptr;
+      const int row = r < nr ? (DENSE ? c0 + r : slot[c0 + r]) : 0;
+      act[r] = r < nr ? a.x + (long long)(DENSE ? row : row / sh.k) * H : nullptr;
+      dst[r] = part_ptr(ws, sh, DENSE, ks, row, mat) + n0;
     }
     __syncthreads();
     const bf16_t* rowp[kRowsChunk];
 #pragma unroll
     for (int r = 0; r < kRowsChunk; ++r) rowp[r] = act[r];
-    const float* sums = stream_unit<64>(nr, w, N, kbeg, kend, rowp, xs, red);
-    float* out = part_ptr(ws, sh, dense, ks, (dense ? 0 : row0) + c0, mat) + n0;
-    for (int o = threadIdx.x; o < nr * 64; o += kThreads) out[(long long)(o >> 6) * 2 * N + (o & 63)] = sums[o];
+    const float* sums = unit_x_rows<64>(nr, w, N, kbeg, kend, rowp, xs, red);
+    for (int o = threadIdx.x; o < nr * 64; o += kThreads) dst[o >> 6][o & 63] = sums[o];
     __syncthreads();
-  }
-
-}
-
-// GeGLU of the streamed rows: h = gelu_tanh(sum G) * (sum U), K-slices in
-// fixed order, bf16.  Rows: the T*k routed rows (expert-grouped order) and/or
-// the T dense rows; 4 columns per thread.
-__global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace ws, int routed, int dense_rows) {
-  const int rrows = routed ? sh.T * sh.k : 0;
-  const long long nr4 = (long long)rrows * (sh.I / 4);
-  const long long nd4 = dense_rows ? (long long)sh.T * (sh.D / 4) : 0;
-  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < nr4 + nd4;
-       i += (long long)gridDim.x * kThreads) {
-    const bool dense = i >= nr4;
-    const long long j = dense ? i - nr4 : i;
-    const int N = dense ? sh.D : sh.I;
-    const int row = int(j / (N / 4)), n4 = int(j % (N / 4)) * 4;
-    float4 g = make_float4(0.f, 0.f, 0.f, 0.f), up = g;
-#pragma unroll
-    for (int s = 0; s < kStreamKS; ++s) {
-      const float4 pg = *reinterpret_cast<const float4*>(part_ptr(ws, sh, dense, s, row, 0) + n4);
-      const float4 pu = *reinterpret_cast<const float4*>(part_ptr(ws, sh, dense, s, row, 1) + n4);
-      g.x += pg.x; g.y += pg.y; g.z += pg.z; g.w += pg.w;
-      up.x += pu.x; up.y += pu.y; up.z += pu.z; up.w += pu.w;
-    }
-    bf16_t* hout = (dense ? ws.h_d : ws.h) + (long long)row * N + n4;
-    *reinterpret_cast<u32x2_t*>(hout) = u32x2_t{pack_bf16x2(gelu_tanh(g.x) * up.x, gelu_tanh(g.y) * up.y),
-                                                pack_bf16x2(gelu_tanh(g.z) * up.z, gelu_tanh(g.w) * up.w)};
   }
 }
 
@@ -303,60 +373,92 @@ __global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace w
 // down
 // ---------------------------------------------------------------------------
 
-// blocks [0, units_dense) are dense-branch units, the rest routed units
-__global__ __launch_bounds__(kThreads) void k_stream_down(StreamArgs a, Workspace ws, int units_dense) {
+// GeGLU of the streamed rows: h = gelu_tanh(sum G) * (sum U), K-slices in
+// fixed order, bf16.  Routed: the T*k slot rows of ws.part into ws.h (slot
+// order); dense: the T token rows into ws.h_d.  4 columns per thread.
+template <bool DENSE>
+__global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace ws, int KS) {
+  const int N = DENSE ? sh.D : sh.I;
+  const int rows = DENSE ? sh.T : sh.T * sh.k;
+  const long long n4 = (long long)rows * (N / 4);
+  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n4; i += (long long)gridDim.x * kThreads) {
+    const int row = int(i / (N / 4)), c = int(i % (N / 4)) * 4;
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f), up = g;
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 pg = *reinterpret_cast<const float4*>(part_ptr(ws, sh, DENSE, ks, row, 0) + c);
+      const float4 pu = *reinterpret_cast<const float4*>(part_ptr(ws, sh, DENSE, ks, row, 1) + c);
+      g.x += pg.x; g.y += pg.y; g.z += pg.z; g.w += pg.w;
+      up.x += pu.x; up.y += pu.y; up.z += pu.z; up.w += pu.w;
+    }
+    bf16_t* hout = (DENSE ? ws.h_d : ws.h) + (long long)row * N + c;
+    *reinterpret_cast<u32x2_t*>(hout) = u32x2_t{pack_bf16x2(gelu_tanh(g.x) * up.x, gelu_tanh(g.y) * up.y),
+                                                pack_bf16x2(gelu_tanh(g.z) * up.z, gelu_tanh(g.w) * up.w)};
+  }
+}
+
+// DENSE: units (128 columns, K-slice of whole 64-row groups of D) over the T
+// rows of h_d; fp32 partial outputs per K-slice (summed by the combine).
+// Routed: units (ai-th active expert, 128 columns) over the expert's rows of
+// h (slot order), bf16 output rows y indexed by slot.
+template <bool DENSE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_down(StreamArgs a, Workspace ws) {
   const Shape& sh = a.sh;
   const int H = sh.H;
   const int nblk = H / 128;
-  int u = blockIdx.x;
-  bool dense;
-  int grp = -1, row0 = 0, rows, K, kbeg = 0, kend;
-  if (u < units_dense) {
-    // dense branch: (column block, K-slice of whole 64-row groups), fp32 partials
-    dense = true;
-    rows = sh.T;
-    K = sh.D;
-    const int ks = u % kDenseDownKS, g64 = sh.D / 64;
-    u /= kDenseDownKS;
-    kbeg = (ks * g64 / kDenseDownKS) * 64;
-    kend = ((ks + 1) * g64 / kDenseDownKS) * 64;
-    (void)ks;
+  __shared__ int slot[kRouteSmallT];
+  int u = blockIdx.x, grp = 0, rows = sh.T, kbeg = 0, kend = sh.I, ksd = 0;
+  if (DENSE) {
+    const int g64 = sh.D / 64, KS = dense_down_slices(sh);
+    ksd = u % KS;
+    u /= KS;
+    kbeg = (ksd * g64 / KS) * 64;
+    kend = ((ksd + 1) * g64 / KS) * 64;
   } else {
-    u -= units_dense;
-    const int ai = u / nblk;
-    if (ai >= ws.meta[1]) return;
+    const ExpertRows er = expert_rows(sh, ws.topk_idx, u / nblk, slot);
+    if (er.e < 0) return;
+    grp = er.e;
+    rows = er.rows;
     u %= nblk;
-    dense = false;
-    grp = ws.active[4 * ai];
-    row0 = ws.active[4 * ai + 1];
-    rows = ws.active[4 * ai + 2];
-    K = sh.I;
-    kend = K;
   }
   const int n0 = u * 128;
-  const bf16_t* wd = (dense ? a.dd : a.wd + (long long)grp * sh.I * H) + n0;
-  const bf16_t* hin = dense ? ws.h_d : ws.h + (long long)row0 * sh.I;
-  const int ksd = dense ? (blockIdx.x % kDenseDownKS) : 0;
+  const int K = DENSE ? sh.D : sh.I;  // row length of h / h_d
+  const bf16_t* wd = (DENSE ? a.dd : a.wd + (long long)grp * sh.I * H) + n0;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  bf16_t* hs = reinterpret_cast<bf16_t*>(smem_raw);  // [K][8] staged rows
+  bf16_t* hs = reinterpret_cast<bf16_t*>(smem_raw);  // [kend-kbeg][8] staged rows
   float* red = reinterpret_cast<float*>(smem_raw);   // [5][8][128]
+  __shared__ const bf16_t* act[kRowsChunk];
   for (int c0 = 0; c0 < rows; c0 += kRowsChunk) {
     const int nr = min(kRowsChunk, rows - c0);
+    if (threadIdx.x < kRowsChunk) {
+      const int r = threadIdx.x;
+      act[r] = r < nr ? (DENSE ? ws.h_d : ws.h) + (long long)(DENSE ? c0 + r : slot[c0 + r]) * K : nullptr;
+    }
+    __syncthreads();
     const bf16_t* rowp[kRowsChunk];
 #pragma unroll
-    for (int r = 0; r < kRowsChunk; ++r) rowp[r] = r < nr ? hin + (long long)(c0 + r) * K : nullptr;
-    const float* sums = stream_unit<128>(nr, wd, H, kbeg, kend, rowp, hs, red);
-    if (dense) {
+    for (int r = 0; r < kRowsChunk; ++r) rowp[r] = act[r];
+    const float* sums = unit_x_rows<128>(nr, wd, H, kbeg, kend, rowp, hs, red);
+    if (DENSE) {
       float* o = ws.ydp + ((long long)ksd * kRouteSmallT + c0) * H + n0;
       for (int i = threadIdx.x; i < nr * 128; i += kThreads) o[(long long)(i >> 7) * H + (i & 127)] = sums[i];
     } else {
-      bf16_t* o = ws.y + (long long)(row0 + c0) * H + n0;
       for (int i = threadIdx.x; i < nr * 128; i += kThreads)
-        o[(long long)(i >> 7) * H + (i & 127)] = (bf16_t)f32_to_bf16_bits(sums[i]);
+        ws.y[(long long)slot[c0 + (i >> 7)] * H + n0 + (i & 127)] = (bf16_t)f32_to_bf16_bits(sums[i]);
     }
     __syncthreads();
   }
+}
+
+// h and y rows of the last streamed forward (slot order) copied to grouped
+// (perm) order: block b handles slot b.  Diagnostic only.
+__global__ __launch_bounds__(kThreads) void k_stream_export(Shape sh, Workspace ws, bf16_t* h_rows, bf16_t* y_rows) {
+  const int b = blockIdx.x;
+  const int p = ws.pos[b];
+  if (h_rows)
+    for (int c = threadIdx.x; c < sh.I; c += kThreads) h_rows[(long long)p * sh.I + c] = ws.h[(long long)b * sh.I + c];
+  if (y_rows)
+    for (int c = threadIdx.x; c < sh.H; c += kThreads) y_rows[(long long)p * sh.H + c] = ws.y[(long long)b * sh.H + c];
 }
 
 }  // namespace
@@ -365,31 +467,47 @@ __global__ __launch_bounds__(kThreads) void k_stream_down(StreamArgs a, Workspac
 // routing, so the caller may run it on another stream)
 hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s) {
   const Shape& sh = a.sh;
-  const bool dense = part == StreamPart::Dense && sh.D > 0;
-  const int ud = dense ? (sh.D / 64) * 2 * kStreamKS : 0;
-  const int max_active = part == StreamPart::Routed ? std::min(sh.E, sh.T * sh.k) : 0;
-  const int units = ud + max_active * (sh.I / 64) * 2 * kStreamKS;
-  if (units == 0) return hipSuccess;
-  const size_t kl = size_t(sh.H) / kStreamKS;
+  const bool dense = part == StreamPart::Dense;
+  if (dense ? sh.D == 0 : sh.T == 0) return hipSuccess;
+  const int ks = dense ? dense_gateup_slices(sh) : kStreamKS;
+  const size_t kl = size_t((sh.H / 64 + ks - 1) / ks) * 64;  // longest slice
   const size_t lds = std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * 64 * 4);
-  hipLaunchKernelGGL(k_stream_gateup, dim3(units), dim3(kThreads), lds, s, a, ws, ud);
+  if (dense) {
+    hipLaunchKernelGGL(k_stream_gateup<true>, dim3((sh.D / 64) * 2 * ks), dim3(kThreads), lds, s, a, ws, ks);
+  } else {
+    const int max_active = std::min(sh.E, sh.T * sh.k);
+    hipLaunchKernelGGL(k_stream_gateup<false>, dim3(max_active * (sh.I / 64) * 2 * ks), dim3(kThreads), lds, s, a,
+                       ws, ks);
+  }
   const long long n4 = dense ? (long long)sh.T * sh.D / 4 : (long long)sh.T * sh.k * sh.I / 4;
   const int gblocks = int(std::min<long long>(1024, (n4 + kThreads - 1) / kThreads));
-  hipLaunchKernelGGL(k_stream_geglu, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, dense ? 0 : 1, dense ? 1 : 0);
+  if (dense)
+    hipLaunchKernelGGL(k_stream_geglu<true>, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, ks);
+  else
+    hipLaunchKernelGGL(k_stream_geglu<false>, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, ks);
   return hipGetLastError();
 }
 
 hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s) {
   const Shape& sh = a.sh;
   const int nblk = sh.H / 128;
-  const bool dense = part == StreamPart::Dense && sh.D > 0;
-  const int ud = dense ? nblk * kDenseDownKS : 0;
-  const int max_active = part == StreamPart::Routed ? std::min(sh.E, sh.T * sh.k) : 0;
-  const int units = ud + max_active * nblk;
-  if (units == 0) return hipSuccess;
-  const int kmax = std::max(sh.I, sh.D);
+  const bool dense = part == StreamPart::Dense;
+  if (dense ? sh.D == 0 : sh.T == 0) return hipSuccess;
+  const int kmax = dense ? (sh.D / 64 + dense_down_slices(sh) - 1) / dense_down_slices(sh) * 64 : sh.I;
   const size_t lds = std::max(size_t(kmax) * kRowsChunk * 2, size_t(5) * kRowsChunk * 128 * 4);
-  hipLaunchKernelGGL(k_stream_down, dim3(units), dim3(kThreads), lds, s, a, ws, ud);
+  if (dense) {
+    hipLaunchKernelGGL(k_stream_down<true>, dim3(nblk * dense_down_slices(sh)), dim3(kThreads), lds, s, a, ws);
+  } else {
+    const int max_active = std::min(sh.E, sh.T * sh.k);
+    hipLaunchKernelGGL(k_stream_down<false>, dim3(max_active * nblk), dim3(kThreads), lds, s, a, ws);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_export(const Shape& sh, const Workspace& ws, bf16_t* h_rows, bf16_t* y_rows, hipStream_t s) {
+  const int blocks = sh.T * sh.k;
+  if (blocks == 0 || (!h_rows && !y_rows)) return hipSuccess;
+  hipLaunchKernelGGL(k_stream_export, dim3(blocks), dim3(kThreads), 0, s, sh, ws, h_rows, y_rows);
   return hipGetLastError();
 }
 
