@@ -26,7 +26,8 @@ What the block computes, with the passage each step follows:
   terms": No, "Intermediate width of one routed expert": 704; NVFP4 config
   ``hidden_activation: gelu_pytorch_tanh``).
 * The always-on dense branch is the same GeGLU form H -> D -> H with
-  D = 2112 (API page: "A dense shared MLP branch (intermediate_dim=2112)";
+  D = 2112 (API page, model description: one dense MLP branch of
+  intermediate width 2112 beside the experts;
   archdb fields "Always-on experts per MoE layer": 1, "Total intermediate
   width of the shared expert(s)": 2,112).
 * The block output is the plain sum of the routed mixture and the dense
