@@ -315,6 +315,28 @@ def test_token_subset_mode_matches_full():
     assert rel_err(rs["out"], r["out"][toks]) < 1e-12
 
 
+def test_residual_layer_with_zero_down_is_identity():
+    """Pin of the stack step x + FFN(x): with every down projection zero the
+    block contributes exactly 0 (both branches end in a down matmul), so the
+    layer returns its input; with the dense branch alone left on, the layer
+    adds exactly the torch GeGLU MLP of x."""
+    shape, x, w = tiny_inputs()
+    wz = dict(w)
+    wz["down"] = np.zeros_like(w["down"])
+    wz["ddown"] = np.zeros_like(w["ddown"])
+    y, _ = oracle.moe_ffn_layer_residual(x, wz, shape.top_k)
+    assert np.array_equal(y, oracle.widen_bf16(x))
+    wd = dict(w)
+    wd["down"] = np.zeros_like(w["down"])
+    y, _ = oracle.moe_ffn_layer_residual(x, wd, shape.top_k)
+    X = torch.from_numpy(oracle.widen_bf16(x))
+    g = X @ torch.from_numpy(oracle.widen_bf16(w["dgate"]))
+    u = X @ torch.from_numpy(oracle.widen_bf16(w["dup"]))
+    ref = X + (torch.nn.functional.gelu(g, approximate="tanh") * u) @ torch.from_numpy(
+        oracle.widen_bf16(w["ddown"]))
+    assert rel_err(y, ref.numpy()) < 1e-12
+
+
 def test_force_routing_reproduces_own_routing():
     shape, x, w = tiny_inputs()
     r = run(shape, x, w)
