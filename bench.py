@@ -40,6 +40,11 @@ def parse():
     p.add_argument("--copies", type=int, default=4, help="weight copies rotated at decode")
     p.add_argument("--graph", action="store_true", help="replay each step from a HIP graph")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-skew", action="store_true")
+    p.add_argument("--skew-steps", type=int, default=10)
+    p.add_argument("--no-nvfp4", action="store_true")
+    p.add_argument("--nvfp4-steps", type=int, default=10, help="chains of --nvfp4-layers layers")
+    p.add_argument("--nvfp4-layers", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -76,24 +81,57 @@ def step_flops(shape):
     return T * (2 * H * E + k * 2 * 3 * H * I + 2 * 3 * H * D)
 
 
-def run_workload(torch, shape, steps, warmup, copies, graph):
-    """Time `steps` forwards; returns a dict of measurements."""
+def upload_nvfp4(torch, pk):
+    out = {"router": to_dev_bf16(torch, pk["router"])}
+    for n in ("gate", "up", "down", "dgate", "dup", "ddown"):
+        m = pk.get(n)
+        out[n] = None if m is None else {
+            "q": torch.from_numpy(np.ascontiguousarray(m["q"])).cuda(),
+            "scale": torch.from_numpy(np.ascontiguousarray(m["scale"])).cuda(),
+            "tensor_scale": torch.from_numpy(np.ascontiguousarray(m["tensor_scale"])).cuda()}
+    return out
+
+
+def nvfp4_layer_weight_bytes(shape):
+    """Packed bytes of one NVFP4 layer: 0.5 B codes + 1/16 B scales per weight,
+    4 B per matrix tensor scale, plus the bf16 router."""
+    H, I, D, E = shape.hidden, shape.expert_dim, shape.dense_dim, shape.experts
+    nw = E * 3 * H * I + 3 * H * D
+    return nw // 2 + nw // 16 + (3 * E + 3) * 4 + H * E * 2
+
+
+def run_workload(torch, shape, steps, warmup, copies, graph, layers=1):
+    """Time `steps` forwards; returns a dict of measurements.
+
+    bf16 workloads rotate `copies` bit-identical weight copies.  The NVFP4
+    stack chains `layers` residual layers (x <- x + FFN_l(x), in place) over
+    `copies` distinct seeded layers; a step is one layer."""
     import synth
     from sparse_moe_transformer_amd import MoeFFN, binding
 
     x = synth.make_x(shape)
-    w = synth.make_weights(shape)
-    bias = synth.zipf_bias(shape.experts) if shape.skew else None
     xd = to_dev_bf16(torch, x)
-    base = {k: to_dev_bf16(torch, v) for k, v in w.items() if v is not None}
-    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+    bias = synth.zipf_bias(shape.experts) if shape.skew else None
     bd = torch.from_numpy(bias).cuda() if bias is not None else None
-    out = torch.empty_like(xd)
-    ffn = MoeFFN.for_shape(shape)
-    torch.cuda.synchronize()
+    w = None
+    if shape.nvfp4:
+        sets = [upload_nvfp4(torch, synth.make_nvfp4_weights(shape, layer=l)) for l in range(copies)]
+        ffn = MoeFFN.for_shape(shape, accumulate=True)
+        x0 = xd.clone()
+        out = xd
 
-    def fwd(i):
-        ffn.forward(xd, sets[i % copies], out, bd)
+        def fwd(i):
+            ffn.forward_nvfp4(xd, sets[i % copies], xd, bd)
+    else:
+        w = synth.make_weights(shape)
+        base = {k: to_dev_bf16(torch, v) for k, v in w.items() if v is not None}
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+        out = torch.empty_like(xd)
+        ffn = MoeFFN.for_shape(shape)
+
+        def fwd(i):
+            ffn.forward(xd, sets[i % copies], out, bd)
+    torch.cuda.synchronize()
 
     graphs = None
     if graph:
@@ -114,19 +152,29 @@ def run_workload(torch, shape, steps, warmup, copies, graph):
         else:
             fwd(i)
 
+    def restart():
+        # the stack runs in place: restart each chain of `layers` from x
+        if shape.nvfp4:
+            xd.copy_(x0)
+
     for i in range(warmup):
+        if i % layers == 0:
+            restart()
         step(i)
     torch.cuda.synchronize()
     counts = ffn.routing(shape.tokens)["counts"].cpu().numpy()
     n_act = int((counts > 0).sum())
 
-    # timed region
+    # timed region: `steps` forwards (chains of `layers` for the stack; the
+    # restarts copy 2.3 MB and are timed too)
     t0 = time.perf_counter()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record()
     for i in range(steps):
+        if layers > 1 and i % layers == 0:
+            restart()
         step(i)
     ev1.record()
     torch.cuda.synchronize()
@@ -139,6 +187,8 @@ def run_workload(torch, shape, steps, warmup, copies, graph):
     stage_mask = (1 << binding.MOE_FFN_NUM_STAGES) - 1
     binding.check(binding.moe_ffn_profile_begin(ffn.h, stage_mask, steps))
     for i in range(steps):
+        if layers > 1 and i % layers == 0:
+            restart()
         fwd(i)
     rc, stage_ms, stage_n = binding.moe_ffn_profile_end(ffn.h)
     binding.check(rc)
@@ -146,6 +196,34 @@ def run_workload(torch, shape, steps, warmup, copies, graph):
     ffn.close()
     return {"ms_per_step": ms_step, "wall_s": wall, "n_act": n_act, "counts": counts,
             "stage_avg_us": stage_avg_us, "x": x, "w": w, "bias": bias}
+
+
+STAGES = ["route", "align", "gateup", "down", "combine"]
+
+# HBM traffic of a roofline kernel, from the committed rocprofv3 --pmc summary;
+# valid only while the kernel's sources are unchanged (their hash is stored)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "sparse_moe_transformer_amd", "csrc")
+
+
+def source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_of(kernel):
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if source_hash(rec["sources"]) != rec["source_hash"]:
+        return None
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(shape, x, w, bias, seconds):
@@ -213,9 +291,9 @@ def main():
         "step_hbm": {"algorithmic_bytes": step_bytes(dec, r["n_act"]),
                      "GBps": step_bytes(dec, r["n_act"]) / (r["ms_per_step"] * 1e-3) / 1e9,
                      "frac": step_bytes(dec, r["n_act"]) / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "stage_avg_us": dict(zip(["route", "align", "gateup", "down", "combine"],
-                                 [round(v, 2) for v in r["stage_avg_us"]])),
+        "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in r["stage_avg_us"]])),
     }
+    line["roofline"]["traffic"] = traffic_of("k_stream_gateup<false>")
     if not args.no_prefill:
         pre = synth.PREFILL
         rp = run_workload(torch, pre, args.prefill_steps, max(3, args.warmup // 4), 2, args.graph)
@@ -229,10 +307,37 @@ def main():
             "step_tflops": step_tf, "step_mfma_frac": step_tf / BF16_PEAK_TFLOPS,
             "roofline": {"bound": "mfma", "kernel": "k_gemm<2,0> (gate/up MFMA GEMM: routed + dense, GeGLU)",
                          "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
+                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": traffic_of("k_gemm<2, 0>"),
                          "algorithmic_flops": gateup_flops(pre), "avg_us": gu_us},
-            "stage_avg_us": dict(zip(["route", "align", "gateup", "down", "combine"],
-                                     [round(v, 2) for v in rp["stage_avg_us"]])),
+            "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rp["stage_avg_us"]])),
+        }
+    if not args.no_skew:
+        sk = synth.SKEW
+        rs = run_workload(torch, sk, args.skew_steps, 2, 2, args.graph)
+        c = rs["counts"]
+        line["skew"] = {
+            "workload": "same layer, T=16384, Zipf(1.2) expert loads via a router logit bias",
+            "tokens": sk.tokens, "value": sk.tokens / (rs["ms_per_step"] * 1e-3), "unit": "tokens/s",
+            "ms_per_step": rs["ms_per_step"], "steps": args.skew_steps,
+            "step_mfma_frac": step_flops(sk) / (rs["ms_per_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "load_max": int(c.max()), "load_min": int(c.min()),
+            "load_max_over_mean": float(c.max() / c.mean()),
+            "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rs["stage_avg_us"]])),
+        }
+    if not args.no_nvfp4:
+        st = synth.NVFP4_STACK
+        L = args.nvfp4_layers
+        rn = run_workload(torch, st, args.nvfp4_steps * L, 2 * L, 2, False, layers=L)
+        us = rn["ms_per_step"] * 1e3
+        wbytes = nvfp4_layer_weight_bytes(st)
+        line["nvfp4_stack"] = {
+            "workload": f"NVFP4 weight-only layer of the 30-layer residual stack, T=1024 "
+                        f"(chains of {L} layers over 2 distinct seeded layers)",
+            "tokens": st.tokens, "value": st.tokens / (us * 1e-6), "unit": "tokens/s per layer",
+            "us_per_layer": us, "stack_ms_30_layers": 30 * us * 1e-3,
+            "layer_weight_bytes": wbytes, "hbm_frac": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "mfma_frac": step_flops(st) / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+            "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rn["stage_avg_us"]])),
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(dec, r["x"], r["w"], r["bias"], args.cpu_seconds)

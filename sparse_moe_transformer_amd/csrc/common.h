@@ -12,6 +12,7 @@ typedef uint16_t bf16_t;  // raw bf16 storage
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;  // MFMA A/B operand
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;  // dot2 operand
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;  // 32x32 MFMA accumulator
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;  // 16-byte load/store
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;

@@ -78,14 +78,6 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-// e2m1 code (4 bits) -> fp32 bits
-__device__ __forceinline__ uint32_t e2m1_f32_bits(uint32_t c) {
-  uint32_t s = (c & 8u) << 28;
-  uint32_t e = (c >> 1) & 3u;
-  uint32_t m = c & 1u;
-  uint32_t mag = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
-  return s | mag;
-}
 // float8_e4m3fn byte -> fp32 (finite codes): bit 7 sign, bits 6..3 exponent
 // (bias 7), bits 2..0 mantissa; exponent 0 is subnormal, m * 2^-9
 __device__ __forceinline__ float e4m3_f32(uint32_t b) {
@@ -214,13 +206,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       for (int d = 0; d < 4; ++d) {
         const uint32_t q = rb[0][d];  // 8 codes, k = 8d .. 8d+7 (low nibble first)
         const float sv = d < 2 ? s0v : s1v;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float vlo = __uint_as_float(e2m1_f32_bits((q >> (8 * p)) & 0xFu)) * sv;
-          const float vhi = __uint_as_float(e2m1_f32_bits((q >> (8 * p + 4)) & 0xFu)) * sv;
-          // exact in bf16: keep the top 16 bits
-          outw[d * 4 + p] = (__float_as_uint(vlo) >> 16) | (__float_as_uint(vhi) & 0xFFFF0000u);
-        }
+        // byte p: codes k = 8d+2p (low nibble), 8d+2p+1, decoded exactly by
+        // the gfx950 e2m1 pair conversion (unit scale); e2m1 x e4m3 is exact
+        // in bf16, so the top 16 bits of each product are kept
+        const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+        const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+        const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+        const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+        outw[d * 4 + 0] = perm_hi16(__float_as_uint(v0.x * sv), __float_as_uint(v0.y * sv));
+        outw[d * 4 + 1] = perm_hi16(__float_as_uint(v1.x * sv), __float_as_uint(v1.y * sv));
+        outw[d * 4 + 2] = perm_hi16(__float_as_uint(v2.x * sv), __float_as_uint(v2.y * sv));
+        outw[d * 4 + 3] = perm_hi16(__float_as_uint(v3.x * sv), __float_as_uint(v3.y * sv));
       }
       bf16_t* dst = bs + fn * LDSK + fkh * 32;
 #pragma unroll

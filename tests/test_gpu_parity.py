@@ -307,6 +307,31 @@ def test_nvfp4_26b_sampled(torch):
     sampled_check(s, x, pk, None, out, r, sample_tokens(s.tokens, 12), nvfp4_w=pk)
 
 
+def test_nvfp4_stack_teacher_forced(torch):
+    """Two layers of the NVFP4 residual stack at T=1024, in place
+    (x <- x + FFN_l(x) with the accumulate flag, out == x).  Each layer is
+    checked teacher-forced: the oracle takes the GPU's own layer input (the
+    bf16 values the GPU stored), on sampled tokens."""
+    from sparse_moe_transformer_amd import MoeFFN
+    s = synth.NVFP4_STACK
+    ffn = MoeFFN.for_shape(s, accumulate=True)
+    xd = G.up_bf16(synth.make_x(s))
+    toks = sample_tokens(s.tokens, 10)
+    for layer in range(2):
+        pk = synth.make_nvfp4_weights(s, layer=layer)
+        x_in = G.to_np(xd.view(torch.int16)).view(np.uint16).copy()
+        ffn.forward_nvfp4(xd, G.up_nvfp4_weights(pk), xd)
+        torch.cuda.synchronize()
+        r = {n: G.to_np(v) for n, v in ffn.routing(s.tokens).items()}
+        rt = oracle.route(x_in, pk["router"], s.top_k)
+        G.check_routing(r["topk_idx"], r["topk_w"], rt)
+        ref = oracle.moe_ffn(x_in, pk["router"], pk["gate"], pk["up"], pk["down"], pk["dgate"],
+                             pk["dup"], pk["ddown"], top_k=s.top_k, force_routing=r["topk_idx"],
+                             tokens=toks)
+        expect = oracle.widen_bf16(x_in[toks]) + ref["out"]
+        G.assert_block_close(G.to_f64(xd)[toks], expect, what=f"layer {layer}")
+
+
 # ---------------------------------------------------------------------------
 # argument validation with a live handle
 # ---------------------------------------------------------------------------
