@@ -198,7 +198,7 @@ def run_workload(torch, shape, steps, warmup, copies, graph, layers=1):
             "stage_avg_us": stage_avg_us, "x": x, "w": w, "bias": bias}
 
 
-STAGES = ["route", "align", "gateup", "down", "combine"]
+STAGES = ["route", "align", "gateup", "down", "combine", "geglu"]
 
 # HBM traffic of a roofline kernel, from the committed rocprofv3 --pmc summary;
 # valid only while the kernel's sources are unchanged (their hash is stored)

@@ -176,13 +176,14 @@ int moe_ffn_align_only(moe_ffn_handle *h, int32_t T, const int32_t *topk_idx, vo
 enum {
   MOE_FFN_STAGE_ROUTE = 0,   /* router logits + top-k */
   MOE_FFN_STAGE_ALIGN = 1,   /* grouping kernels (MFMA variant only) */
-  MOE_FFN_STAGE_GATEUP = 2,  /* gate/up: MFMA = routed + dense GEMM with GeGLU;
-                                streaming = the routed partial-sum kernel and
-                                its GeGLU kernel (the dense branch runs on a
-                                side stream, unmeasured) */
+  MOE_FFN_STAGE_GATEUP = 2,  /* gate/up: MFMA = the routed + dense GEMM with the
+                                GeGLU fused; streaming = the routed partial-sum
+                                kernel alone (the dense branch runs on a side
+                                stream, unmeasured) */
   MOE_FFN_STAGE_DOWN = 3,    /* down: as for gate/up */
   MOE_FFN_STAGE_COMBINE = 4, /* weighted sum + dense add */
-  MOE_FFN_NUM_STAGES = 5
+  MOE_FFN_STAGE_GEGLU = 5,   /* streaming only: GeGLU of the summed partials */
+  MOE_FFN_NUM_STAGES = 6
 };
 /* Start recording an event pair around every stage in stage_mask (bit s =
  * stage s) for each of the next max_samples forwards (later forwards are

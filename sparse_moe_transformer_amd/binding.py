@@ -35,7 +35,8 @@ EXPORTS = (
     "moe_ffn_profile_end", "moe_ffn_last_error",
 )
 MOE_FFN_STAGE_ROUTE, MOE_FFN_STAGE_ALIGN, MOE_FFN_STAGE_GATEUP = 0, 1, 2
-MOE_FFN_STAGE_DOWN, MOE_FFN_STAGE_COMBINE, MOE_FFN_NUM_STAGES = 3, 4, 5
+MOE_FFN_STAGE_DOWN, MOE_FFN_STAGE_COMBINE, MOE_FFN_STAGE_GEGLU = 3, 4, 5
+MOE_FFN_NUM_STAGES = 6
 
 
 class moe_ffn_config(ctypes.Structure):

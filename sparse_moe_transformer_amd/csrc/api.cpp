@@ -229,6 +229,7 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
     e = hipEventRecord(h->ev_fork, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_fork, 0);
     if (e == hipSuccess) e = moe::launch_stream_gateup(args, ws, moe::StreamPart::Dense, h->side);
+    if (e == hipSuccess) e = moe::launch_stream_geglu(args, ws, moe::StreamPart::Dense, h->side);
     if (e == hipSuccess) e = moe::launch_stream_down(args, ws, moe::StreamPart::Dense, h->side);
     if (e == hipSuccess) e = hipEventRecord(h->ev_join, h->side);
     if (e != hipSuccess) return hip_fail(e, "dense branch");
@@ -254,6 +255,12 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
                : moe::launch_gemm_gateup(args, ws, mt, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "gate/up");
+  }
+  if (stream) {
+    StageTimer tm(h, MOE_FFN_STAGE_GEGLU, s, timing);
+    e = moe::launch_stream_geglu(args, ws, moe::StreamPart::Routed, s);
+    tm.stop();
+    if (e != hipSuccess) return hip_fail(e, "geglu");
   }
   {
     StageTimer tm(h, MOE_FFN_STAGE_DOWN, s, timing);

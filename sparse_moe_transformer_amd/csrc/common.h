@@ -75,8 +75,8 @@ constexpr int kRouteSlices = 32;   // K-slices of the small-T router logits
 constexpr int kRouteSmallT = 64;   // largest T of the one-block-per-token router and the streaming path
 constexpr int kGemmBM = 128;       // MFMA tile rows (tokens)
 constexpr int kStreamKS = 2;       // K-slices of the streaming routed gate/up units
-constexpr int kDenseKS = 8;        // K-slices of the streaming dense gate/up units
-constexpr int kDenseDownKS = 16;   // K-slices of the streaming dense down units
+constexpr int kDenseKS = 4;        // K-slices of the streaming dense gate/up units
+constexpr int kDenseDownKS = 1;    // K-slices of the streaming dense down units
 constexpr int kStreamRows = kRouteSmallT * 16;  // routed rows of the streaming path (T <= 64, k <= 16)
 
 struct Shape {
@@ -114,7 +114,9 @@ struct StreamArgs {
   bool nvfp4;
 };
 enum class StreamPart { Routed, Dense };
+// gate/up partial sums, then the GeGLU of the summed slices (bf16 h rows)
 hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s);
+hipError_t launch_stream_geglu(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s);
 hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s);
 // h and y rows of the last streamed forward into caller buffers in grouped
 // (perm) order; needs ws.pos from launch_align; either pointer may be null

@@ -45,6 +45,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsChunk = 8;
 constexpr int kU = 16;  // weight rows in flight per thread
+constexpr int kRoutedDownCols = 128;  // output columns of a routed down unit
 
 __device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);  // a.lo | b.lo << 16
@@ -404,7 +405,8 @@ template <bool DENSE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_down(StreamArgs a, Workspace ws) {
   const Shape& sh = a.sh;
   const int H = sh.H;
-  const int nblk = H / 128;
+  constexpr int NC = DENSE ? 128 : kRoutedDownCols;  // output columns of a unit
+  const int nblk = H / NC;
   __shared__ int slot[kRouteSmallT];
   int u = blockIdx.x, grp = 0, rows = sh.T, kbeg = 0, kend = sh.I, ksd = 0;
   if (DENSE) {
@@ -420,13 +422,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     rows = er.rows;
     u %= nblk;
   }
-  const int n0 = u * 128;
+  const int n0 = u * NC;
   const int K = DENSE ? sh.D : sh.I;  // row length of h / h_d
   const bf16_t* wd = (DENSE ? a.dd : a.wd + (long long)grp * sh.I * H) + n0;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16_t* hs = reinterpret_cast<bf16_t*>(smem_raw);  // [kend-kbeg][8] staged rows
-  float* red = reinterpret_cast<float*>(smem_raw);   // [5][8][128]
+  float* red = reinterpret_cast<float*>(smem_raw);   // [5][8][NC]
   __shared__ const bf16_t* act[kRowsChunk];
   for (int c0 = 0; c0 < rows; c0 += kRowsChunk) {
     const int nr = min(kRowsChunk, rows - c0);
@@ -438,13 +440,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     const bf16_t* rowp[kRowsChunk];
 #pragma unroll
     for (int r = 0; r < kRowsChunk; ++r) rowp[r] = act[r];
-    const float* sums = unit_x_rows<128>(nr, wd, H, kbeg, kend, rowp, hs, red);
+    const float* sums = unit_x_rows<NC>(nr, wd, H, kbeg, kend, rowp, hs, red);
     if (DENSE) {
       float* o = ws.ydp + ((long long)ksd * kRouteSmallT + c0) * H + n0;
-      for (int i = threadIdx.x; i < nr * 128; i += kThreads) o[(long long)(i >> 7) * H + (i & 127)] = sums[i];
+      for (int i = threadIdx.x; i < nr * NC; i += kThreads) o[(long long)(i / NC) * H + (i % NC)] = sums[i];
     } else {
-      for (int i = threadIdx.x; i < nr * 128; i += kThreads)
-        ws.y[(long long)slot[c0 + (i >> 7)] * H + n0 + (i & 127)] = (bf16_t)f32_to_bf16_bits(sums[i]);
+      for (int i = threadIdx.x; i < nr * NC; i += kThreads)
+        ws.y[(long long)slot[c0 + i / NC] * H + n0 + (i % NC)] = (bf16_t)f32_to_bf16_bits(sums[i]);
     }
     __syncthreads();
   }
@@ -479,6 +481,14 @@ hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, Stream
     hipLaunchKernelGGL(k_stream_gateup<false>, dim3(max_active * (sh.I / 64) * 2 * ks), dim3(kThreads), lds, s, a,
                        ws, ks);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_geglu(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s) {
+  const Shape& sh = a.sh;
+  const bool dense = part == StreamPart::Dense;
+  if (dense ? sh.D == 0 : sh.T == 0) return hipSuccess;
+  const int ks = dense ? dense_gateup_slices(sh) : kStreamKS;
   const long long n4 = dense ? (long long)sh.T * sh.D / 4 : (long long)sh.T * sh.k * sh.I / 4;
   const int gblocks = int(std::min<long long>(1024, (n4 + kThreads - 1) / kThreads));
   if (dense)
@@ -490,11 +500,12 @@ hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, Stream
 
 hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s) {
   const Shape& sh = a.sh;
-  const int nblk = sh.H / 128;
   const bool dense = part == StreamPart::Dense;
+  const int nblk = sh.H / (dense ? 128 : kRoutedDownCols);
   if (dense ? sh.D == 0 : sh.T == 0) return hipSuccess;
   const int kmax = dense ? (sh.D / 64 + dense_down_slices(sh) - 1) / dense_down_slices(sh) * 64 : sh.I;
-  const size_t lds = std::max(size_t(kmax) * kRowsChunk * 2, size_t(5) * kRowsChunk * 128 * 4);
+  const size_t lds = std::max(size_t(kmax) * kRowsChunk * 2,
+                              size_t(5) * kRowsChunk * (dense ? 128 : kRoutedDownCols) * 4);
   if (dense) {
     hipLaunchKernelGGL(k_stream_down<true>, dim3(nblk * dense_down_slices(sh)), dim3(kThreads), lds, s, a, ws);
   } else {

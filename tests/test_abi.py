@@ -40,6 +40,15 @@ def test_library_exports_every_declared_symbol(lib):
         assert getattr(lib, name) is not None
 
 
+def test_header_constants_match_binding():
+    """Every MOE_FFN_* enum value in the header equals the binding's constant."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    consts = dict(re.findall(r"\b(MOE_FFN_[A-Z0-9_]+)\s*=\s*(-?\d+)", src))
+    assert "MOE_FFN_NUM_STAGES" in consts and "MOE_FFN_STAGE_GEGLU" in consts
+    for name, val in consts.items():
+        assert getattr(binding, name) == int(val), name
+
+
 def cfg(**kw):
     base = dict(hidden=2816, num_experts=128, top_k=8, expert_dim=704, dense_dim=2112, max_tokens=16)
     base.update(kw)
