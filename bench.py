@@ -284,7 +284,7 @@ def main():
                    "top_k": dec.top_k, "expert_dim": dec.expert_dim, "dense_dim": dec.dense_dim,
                    "weight_copies": args.copies, "graph": bool(args.graph),
                    "active_experts": r["n_act"]},
-        "roofline": {"bound": "hbm", "kernel": "k_stream_gateup<false> (routed gate/up weight streaming)",
+        "roofline": {"bound": "hbm", "kernel": "k_stream_gateup (routed gate/up weight streaming)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes": gu_bytes, "avg_us": gu_us},
@@ -293,7 +293,7 @@ def main():
                      "frac": step_bytes(dec, r["n_act"]) / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in r["stage_avg_us"]])),
     }
-    line["roofline"]["traffic"] = traffic_of("k_stream_gateup<false>")
+    line["roofline"]["traffic"] = traffic_of("k_stream_gateup")
     if not args.no_prefill:
         pre = synth.PREFILL
         rp = run_workload(torch, pre, args.prefill_steps, max(3, args.warmup // 4), 2, args.graph)

@@ -174,15 +174,15 @@ int moe_ffn_align_only(moe_ffn_handle *h, int32_t T, const int32_t *topk_idx, vo
 /* Per-stage timing with HIP events recorded on the forward's stream.
  * Stages: */
 enum {
-  MOE_FFN_STAGE_ROUTE = 0,   /* router logits + top-k */
+  MOE_FFN_STAGE_ROUTE = 0,   /* router logits + top-k; streaming: the same
+                                launch also runs the dense branch's gate/up */
   MOE_FFN_STAGE_ALIGN = 1,   /* grouping kernels (MFMA variant only) */
   MOE_FFN_STAGE_GATEUP = 2,  /* gate/up: MFMA = the routed + dense GEMM with the
-                                GeGLU fused; streaming = the routed partial-sum
-                                kernel alone (the dense branch runs on a side
-                                stream, unmeasured) */
-  MOE_FFN_STAGE_DOWN = 3,    /* down: as for gate/up */
+                                GeGLU fused; streaming = the routed partial sums */
+  MOE_FFN_STAGE_DOWN = 3,    /* down projections, routed + dense */
   MOE_FFN_STAGE_COMBINE = 4, /* weighted sum + dense add */
-  MOE_FFN_STAGE_GEGLU = 5,   /* streaming only: GeGLU of the summed partials */
+  MOE_FFN_STAGE_GEGLU = 5,   /* streaming only: GeGLU of the summed partials
+                                (routed and dense rows) */
   MOE_FFN_NUM_STAGES = 6
 };
 /* Start recording an event pair around every stage in stage_mask (bit s =

@@ -38,10 +38,6 @@ struct moe_ffn_handle {
   int prof_max;
   int prof_fwd;  // forwards timed so far
   StageProfile prof[MOE_FFN_NUM_STAGES];
-  // the dense branch of the streaming path runs on this stream, forked from
-  // and joined back to the caller's stream with the two events
-  hipStream_t side;
-  hipEvent_t ev_fork, ev_join;
 };
 
 namespace {
@@ -83,7 +79,7 @@ int validate_config(const moe_ffn_config* c) {
 
 // Workspace layout: every buffer 256-byte aligned.
 struct Layout {
-  size_t off[19];
+  size_t off[20];
   size_t total;
   int max_mtiles;
 };
@@ -94,7 +90,7 @@ Layout layout(const moe_ffn_config& c) {
   const size_t nb = (T + 63) / 64;
   Layout L{};
   L.max_mtiles = int((T * k + moe::kGemmBM - 1) / moe::kGemmBM + E);
-  const size_t sizes[19] = {
+  const size_t sizes[20] = {
       size_t(moe::kRouterSlices) * T * E * 4,     // logits (K-slices)
       size_t(moe::kRouteSlices) * 64 * E * 4,     // route_part (K-slices, T <= 64)
       T * k * 4,                                  // topk_idx
@@ -115,9 +111,10 @@ Layout layout(const moe_ffn_config& c) {
       (size_t(moe::kStreamKS) * moe::kStreamRows * I +  // streaming gate/up partials
        size_t(moe::kDenseKS) * moe::kRouteSmallT * (D ? D : 1)) * 2 * 4,
       size_t(moe::kDenseDownKS) * moe::kRouteSmallT * H * 4,  // streaming dense down partials
+      size_t(moe::kArriveInts) * 4,               // arrival counters (zero between forwards)
   };
   size_t o = 0;
-  for (int i = 0; i < 19; ++i) {
+  for (int i = 0; i < 20; ++i) {
     L.off[i] = o;
     o += (sizes[i] + 255) & ~size_t(255);
   }
@@ -147,6 +144,7 @@ moe::Workspace bind(void* base, const Layout& L) {
   w.y_d = reinterpret_cast<moe::bf16_t*>(b + L.off[16]);
   w.part = reinterpret_cast<float*>(b + L.off[17]);
   w.ydp = reinterpret_cast<float*>(b + L.off[18]);
+  w.arrive = reinterpret_cast<int32_t*>(b + L.off[19]);
   return w;
 }
 
@@ -222,22 +220,12 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   if (args.nvfp4) stream = false;             // the streaming kernels read bf16 [K, N] weights only
   if (T > moe::kRouteSmallT) stream = false;  // their scratch holds at most 64 tokens' rows
   const int mt = int((size_t(T) * sh.k + moe::kGemmBM - 1) / moe::kGemmBM + sh.E);
-  const bool fork = stream && sh.D > 0;
-  if (fork) {
-    // the always-on dense branch does not depend on the routing: run it on
-    // the side stream while the router runs here
-    e = hipEventRecord(h->ev_fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_fork, 0);
-    if (e == hipSuccess) e = moe::launch_stream_gateup(args, ws, moe::StreamPart::Dense, h->side);
-    if (e == hipSuccess) e = moe::launch_stream_geglu(args, ws, moe::StreamPart::Dense, h->side);
-    if (e == hipSuccess) e = moe::launch_stream_down(args, ws, moe::StreamPart::Dense, h->side);
-    if (e == hipSuccess) e = hipEventRecord(h->ev_join, h->side);
-    if (e != hipSuccess) return hip_fail(e, "dense branch");
-  }
   {
+    // streaming: the router and the dense branch's gate/up share one launch
     StageTimer tm(h, MOE_FFN_STAGE_ROUTE, s, timing);
-    e = (T <= moe::kRouteSmallT) ? moe::launch_route_small(sh, xb, wr, bias, ws, s)
-                                 : moe::launch_route_large(sh, xb, wr, bias, ws, s);
+    e = stream ? moe::launch_route_dense(args, wr, bias, ws, s)
+        : (T <= moe::kRouteSmallT) ? moe::launch_route_small(sh, xb, wr, bias, ws, s)
+                                   : moe::launch_route_large(sh, xb, wr, bias, ws, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "route");
   }
@@ -251,26 +239,21 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   }
   {
     StageTimer tm(h, MOE_FFN_STAGE_GATEUP, s, timing);
-    e = stream ? moe::launch_stream_gateup(args, ws, moe::StreamPart::Routed, s)
-               : moe::launch_gemm_gateup(args, ws, mt, s);
+    e = stream ? moe::launch_stream_gateup(args, ws, s) : moe::launch_gemm_gateup(args, ws, mt, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "gate/up");
   }
   if (stream) {
     StageTimer tm(h, MOE_FFN_STAGE_GEGLU, s, timing);
-    e = moe::launch_stream_geglu(args, ws, moe::StreamPart::Routed, s);
+    e = moe::launch_stream_geglu(args, ws, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "geglu");
   }
   {
     StageTimer tm(h, MOE_FFN_STAGE_DOWN, s, timing);
-    e = stream ? moe::launch_stream_down(args, ws, moe::StreamPart::Routed, s) : moe::launch_gemm_down(args, ws, mt, s);
+    e = stream ? moe::launch_stream_down(args, ws, s) : moe::launch_gemm_down(args, ws, mt, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "down");
-  }
-  if (fork) {
-    e = hipStreamWaitEvent(s, h->ev_join, 0);
-    if (e != hipSuccess) return hip_fail(e, "join dense branch");
   }
   {
     StageTimer tm(h, MOE_FFN_STAGE_COMBINE, s, timing);
@@ -383,14 +366,6 @@ int moe_ffn_create(const moe_ffn_config* cfg, moe_ffn_handle** out_handle) {
     h->last_T = 0;
     const char* sm = std::getenv("MOE_FFN_SYNC");
     h->sync_mode = sm && std::strcmp(sm, "1") == 0;
-    e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      (void)hipFree(base);
-      delete h;
-      return hip_fail(e, "side stream/events");
-    }
     *out_handle = h;
     g_err.clear();
     return MOE_FFN_OK;
@@ -409,9 +384,6 @@ int moe_ffn_destroy(moe_ffn_handle* h) {
     DeviceGuard g(h->device);
     hipError_t e = hipDeviceSynchronize();
     profile_release(h);
-    (void)hipEventDestroy(h->ev_fork);
-    (void)hipEventDestroy(h->ev_join);
-    (void)hipStreamDestroy(h->side);
     hipError_t f = hipFree(h->ws_base);
     delete h;
     if (e != hipSuccess) return hip_fail(e, "destroy: device sync");

@@ -68,6 +68,8 @@ struct Workspace {
   float* part;          // [kStreamKS][kStreamRows][2][I] (rows = slots) + [kDenseKS][64][2][D]
                         // (rows = tokens) gate/up partials of the streaming path
   float* ydp;           // [kDenseDownKS][64][H] dense down partials (streaming path)
+  int32_t* arrive;      // [kArriveInts] arrival counters of the last-block hand-offs; every
+                        // kernel that counts leaves them at zero (zeroed at create)
 };
 
 constexpr int kRouterSlices = 16;  // most K-slices of the large-T router logits
@@ -76,8 +78,10 @@ constexpr int kRouteSmallT = 64;   // largest T of the one-block-per-token route
 constexpr int kGemmBM = 128;       // MFMA tile rows (tokens)
 constexpr int kStreamKS = 2;       // K-slices of the streaming routed gate/up units
 constexpr int kDenseKS = 4;        // K-slices of the streaming dense gate/up units
-constexpr int kDenseDownKS = 1;    // K-slices of the streaming dense down units
+constexpr int kDenseDownKS = 4;    // K-slices of the streaming dense down units
 constexpr int kStreamRows = kRouteSmallT * 16;  // routed rows of the streaming path (T <= 64, k <= 16)
+constexpr int kArriveRoute = 0;                 // [64] token groups of the small-T router
+constexpr int kArriveInts = 64;
 
 struct Shape {
   int T, H, E, k, I, D;
@@ -113,11 +117,15 @@ struct StreamArgs {
   Fp4Mat fg, fu, fd, fdg, fdu, fdd;
   bool nvfp4;
 };
-enum class StreamPart { Routed, Dense };
-// gate/up partial sums, then the GeGLU of the summed slices (bf16 h rows)
-hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s);
-hipError_t launch_stream_geglu(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s);
-hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s);
+// Streaming path (T <= 64, bf16 weights).  The router and the dense
+// branch's gate/up units share one launch; then the routed gate/up partial
+// sums, the GeGLU of the summed slices (routed and dense rows), and the
+// down units (routed and dense).
+hipError_t launch_route_dense(const StreamArgs& a, const bf16_t* wr, const float* bias, const Workspace& ws,
+                              hipStream_t s);
+hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, hipStream_t s);
+hipError_t launch_stream_geglu(const StreamArgs& a, const Workspace& ws, hipStream_t s);
+hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStream_t s);
 // h and y rows of the last streamed forward into caller buffers in grouped
 // (perm) order; needs ws.pos from launch_align; either pointer may be null
 hipError_t launch_stream_export(const Shape& sh, const Workspace& ws, bf16_t* h_rows, bf16_t* y_rows, hipStream_t s);

@@ -14,10 +14,9 @@
 //
 // Two routes:
 //   T <= 64: partial logits of kRouteSlices K-slices (many small blocks,
-//     so W_r streams at full bandwidth), then one block per token sums the
-//     slices in fixed order and routes it.  (An in-kernel hand-off between
-//     blocks would need a device-scope release, which on this multi-XCD
-//     part writes back the L2 and costs more than a second launch.)
+//     so W_r streams at full bandwidth); the last slice block of a token
+//     group sums the slices in fixed order and routes the group
+//     (route_dev.h).
 //   large T: split-K logits (MFMA tiles when E % 128 == 0, else an FMA
 //     kernel), a top-k kernel that sums the K-slices in fixed order.
 // Grouping (any T): per-64-token membership masks, a per-expert scan over
@@ -27,124 +26,13 @@
 #include <type_traits>
 
 #include "common.h"
+#include "route_dev.h"
 
 namespace moe {
 
 namespace {
 
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
-// DPP lane moves (gfx9 encodings): swap neighbours, swap pairs, mirror
-// inside 8 lanes, mirror inside 16 lanes.
-constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;
-constexpr int kDppMirror = 0x140;
-
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-  const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, false);
-  if (better(ov, oi, v, i)) {
-    v = ov;
-    i = oi;
-  }
-}
-
-// Wave-wide arg-max, lower index winning ties; the result is wave-uniform.
-// Inside each 16-lane row: two quad swaps, then mirrors (after each step
-// the lanes of a group agree, so a mirror reaches the other group); the 4
-// row winners are then compared through readlane.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  argmax_step<kDppXor1>(v, i);
-  argmax_step<kDppXor2>(v, i);
-  argmax_step<kDppHalfMirror>(v, i);
-  argmax_step<kDppMirror>(v, i);
-  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
-    const int ri = __builtin_amdgcn_readlane(i, 16 * r);
-    if (better(rv, ri, bv, bi)) {
-      bv = rv;
-      bi = ri;
-    }
-  }
-  v = bv;
-  i = bi;
-}
-
-// One wave routes one token whose E logits are in z (LDS or global).  Lane
-// l owns experts l, l+64, l+128, l+192.  k rounds of wave arg-max pick the
-// experts (equal logits: lower id first); p = softmax over all experts;
-// w = p_S / sum(p_S), written in ascending expert id.
-__device__ void wave_route_token(const float* z, int E, int k, int32_t* out_idx, float* out_w) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int nj = (E + kWave - 1) / kWave;  // wave-uniform
-  float zv[4];
-  bool sel[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + j * kWave;
-    zv[j] = (e < E) ? z[e] : -INFINITY;
-    sel[j] = false;
-  }
-  float zmax = -INFINITY;
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + j * kWave;
-      if (j < nj && e < E && !sel[j] && better(zv[j], e, bv, bi)) {
-        bv = zv[j];
-        bi = e;
-      }
-    }
-    wave_argmax(bv, bi);
-    if (r == 0) zmax = bv;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + j * kWave == bi) sel[j] = true;
-  }
-  // softmax over all experts, then renormalise the selected weights
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (lane + j * kWave < E) s += __expf(zv[j] - zmax);
-  s = wave_sum(s);
-  float p[4];
-  float ps = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    p[j] = sel[j] ? __expf(zv[j] - zmax) / s : 0.f;
-    ps += p[j];
-  }
-  ps = wave_sum(ps);
-  // ascending expert id order: position = selected ids below this one
-  int base = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint64_t m = __ballot(sel[j]);
-    if (sel[j]) {
-      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-      out_idx[pos] = lane + j * kWave;
-      out_w[pos] = p[j] / ps;
-    }
-    base += __popcll(m);
-  }
-}
 
 // Block-wide exclusive scan of one int per thread (BLOCK threads).
 template <int BLOCK>
@@ -251,97 +139,14 @@ __device__ int build_offsets_and_tiles(const int cnt_e, int E, const Workspace& 
 }
 
 // ---------------------------------------------------------------------------
-// small T (<= 64)
+// small T (<= 64): the K-sliced router of route_dev.h
 // ---------------------------------------------------------------------------
 
-// Partial logits of one K-slice for a group of tokens:
-//   part[s][t][e] = sum over the slice's rows k of x[t][k] * W_r[k][e].
-// Block (slice s, token group of TB tokens); thread = (chunk ec of CW
-// experts, token tl, row group rg); row group rg owns the slice's rows
-// rg, rg + RG, ..., so one wave's 16-byte loads cover whole rows of W_r
-// (several tokens' lanes read the same row: one fetch serves them).  All of
-// a thread's rows are loaded at once; the slice's x rows are staged in LDS
-// as fp32 while the loads are in flight.  Row groups are summed in a fixed
-// order through LDS.
-constexpr int kRouteMaxRows = 16;  // rows of a slice per thread
 template <int CW>
-__global__ __launch_bounds__(kThreads) void k_route_part(Shape sh, int slice_rows, int TB,
-                                                        const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr,
-                                                        float* __restrict__ part) {
-  typedef typename std::conditional<CW == 8, u32x4_t, u32x2_t>::type vec_t;
-  const int H = sh.H, E = sh.E, T = sh.T;
-  const int EC = E / CW;
-  const int RG = kThreads / (EC * TB);
-  const int tid = threadIdx.x;
-  const int ec = tid % EC, tl = (tid / EC) % TB, rg = tid / (EC * TB);
-  const bool live = rg < RG;
-  const int s = blockIdx.x, t0 = blockIdx.y * TB;
-  const int k0 = s * slice_rows;
-  const int nrow = live && rg < slice_rows ? (slice_rows - 1 - rg) / RG + 1 : 0;
-  __shared__ float xs[kThreads * kRouteMaxRows];  // [TB][slice_rows]
-  __shared__ float red[kThreads * 8];              // [RG][TB][E]
-  const bf16_t* pw = wr + size_t(k0 + (live ? rg : 0)) * E + ec * CW;
-  vec_t vw[kRouteMaxRows];
-#pragma unroll
-  for (int i = 0; i < kRouteMaxRows; ++i)
-    vw[i] = i < nrow ? *reinterpret_cast<const vec_t*>(pw + size_t(i) * RG * E) : vec_t{};
-  const int nch = slice_rows / 8;
-  for (int c = tid; c < TB * nch; c += kThreads) {
-    const int tt = c / nch, kc = (c % nch) * 8;
-    u32x4_t v = {0, 0, 0, 0};
-    if (t0 + tt < T) v = *reinterpret_cast<const u32x4_t*>(x + size_t(t0 + tt) * H + k0 + kc);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      xs[tt * slice_rows + kc + 2 * d] = bf16_lo(v[d]);
-      xs[tt * slice_rows + kc + 2 * d + 1] = bf16_hi(v[d]);
-    }
-  }
-  __syncthreads();
-  float acc[CW];
-#pragma unroll
-  for (int c = 0; c < CW; ++c) acc[c] = 0.f;
-#pragma unroll
-  for (int i = 0; i < kRouteMaxRows; ++i) {
-    const float xv = xs[tl * slice_rows + min(rg + RG * i, slice_rows - 1)];  // past nrow: zero weights
-#pragma unroll
-    for (int d = 0; d < CW / 2; ++d) {
-      acc[2 * d] += xv * bf16_lo(vw[i][d]);
-      acc[2 * d + 1] += xv * bf16_hi(vw[i][d]);
-    }
-  }
-  if (live) {
-#pragma unroll
-    for (int c = 0; c < CW; ++c) red[(rg * TB + tl) * E + ec * CW + c] = acc[c];
-  }
-  __syncthreads();
-  for (int o = tid; o < TB * E; o += kThreads) {
-    const int tt = o / E;
-    if (t0 + tt >= T) continue;
-    float z = 0.f;
-    for (int g = 0; g < RG; ++g) z += red[g * TB * E + o];
-    part[(size_t(s) * kRouteSmallT + t0 + tt) * E + (o % E)] = z;
-  }
-}
-
-// One block per token: z = sum of the slices in order (+ b), then one wave
-// routes the token.
-__global__ __launch_bounds__(kThreads) void k_route_fin(Shape sh, int nslices, const float* __restrict__ part,
-                                                       const float* __restrict__ bias, Workspace ws) {
-  const int t = blockIdx.x, E = sh.E;
-  __shared__ float zs[256];
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    const float* p = part + size_t(t) * E + e;
-    float v[kRouteSlices];
-#pragma unroll
-    for (int j = 0; j < kRouteSlices; ++j) v[j] = j < nslices ? p[size_t(j) * kRouteSmallT * E] : 0.f;
-    float z = 0.f;
-#pragma unroll
-    for (int j = 0; j < kRouteSlices; ++j) z += v[j];
-    zs[e] = bias ? z + bias[e] : z;
-  }
-  __syncthreads();
-  if (threadIdx.x < kWave)
-    wave_route_token(zs, E, sh.k, ws.topk_idx + size_t(t) * sh.k, ws.topk_w + size_t(t) * sh.k);
+__global__ __launch_bounds__(kThreads) void k_route_part(Shape sh, int slice_rows, int TB, const bf16_t* __restrict__ x,
+                                                        const bf16_t* __restrict__ wr, const float* __restrict__ bias,
+                                                        Workspace ws) {
+  route_slice<CW>(sh, slice_rows, TB, int(gridDim.x), blockIdx.x, blockIdx.y, x, wr, bias, ws);
 }
 
 // ---------------------------------------------------------------------------
@@ -454,26 +259,13 @@ __global__ __launch_bounds__(kThreads) void k_align_scatter(Shape sh, Workspace 
 hipError_t launch_route_small(const Shape& sh, const bf16_t* x, const bf16_t* wr, const float* bias,
                               const Workspace& ws, hipStream_t s) {
   if (sh.T == 0) return hipSuccess;
-  // kRouteSlices slices of a multiple of 8 rows (H % 256 == 0); enough row
-  // groups that a thread loads at most kRouteMaxRows rows, the rest of the
-  // block's threads spread over tokens
-  const int cw = sh.E % 8 == 0 ? 8 : 4;
-  const int ec = sh.E / cw;
-  int nslices = kRouteSlices;
-  while (nslices > 1 && (sh.H % nslices || (sh.H / nslices) % 8)) nslices /= 2;
-  const int slice_rows = sh.H / nslices;
-  int rg_need = 1;
-  while (rg_need * kRouteMaxRows < slice_rows) rg_need *= 2;
-  const int tb = std::max(1, std::min(sh.T, kThreads / (ec * rg_need)));
-  const int rg = kThreads / (ec * tb);
-  if (rg < 1 || (slice_rows + rg - 1) / rg > kRouteMaxRows || tb * slice_rows > kThreads * kRouteMaxRows)
-    return hipErrorInvalidValue;
-  const dim3 grid(nslices, (sh.T + tb - 1) / tb);
-  if (cw == 8)
-    hipLaunchKernelGGL(k_route_part<8>, grid, dim3(kThreads), 0, s, sh, slice_rows, tb, x, wr, ws.route_part);
+  const RouteSmallCfg c = route_small_config(sh);
+  if (!c.ok) return hipErrorInvalidValue;
+  const dim3 grid(c.nslices, c.groups);
+  if (c.cw == 8)
+    hipLaunchKernelGGL(k_route_part<8>, grid, dim3(kThreads), 0, s, sh, c.slice_rows, c.tb, x, wr, bias, ws);
   else
-    hipLaunchKernelGGL(k_route_part<4>, grid, dim3(kThreads), 0, s, sh, slice_rows, tb, x, wr, ws.route_part);
-  hipLaunchKernelGGL(k_route_fin, dim3(sh.T), dim3(kThreads), 0, s, sh, nslices, ws.route_part, bias, ws);
+    hipLaunchKernelGGL(k_route_part<4>, grid, dim3(kThreads), 0, s, sh, c.slice_rows, c.tb, x, wr, bias, ws);
   return hipGetLastError();
 }
 

@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "route_dev.h"
 
 namespace moe {
 
@@ -45,7 +46,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsChunk = 8;
 constexpr int kU = 16;  // weight rows in flight per thread
-constexpr int kRoutedDownCols = 128;  // output columns of a routed down unit
+constexpr int kDownCols = 128;  // output columns of a down unit
 
 __device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);  // a.lo | b.lo << 16
@@ -321,15 +322,14 @@ __device__ ExpertRows expert_rows(const Shape& sh, const int32_t* __restrict__ t
 // Routed: units (ai-th active expert, ...) over the expert's rows, x gathered
 // by token.  Writes fp32 partial pre-activations per K-slice, indexed by
 // slot (routed) or token (dense).
-// (3 waves per SIMD: the register budget of 168 holds every unit variant)
 template <bool DENSE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_gateup(StreamArgs a, Workspace ws, int KS) {
+__device__ void gateup_unit(const StreamArgs& a, const Workspace& ws, int KS, int u) {
   const Shape& sh = a.sh;
   const int H = sh.H;
   const int N = DENSE ? sh.D : sh.I;
   const int per = (N / 64) * 2 * KS;
   __shared__ int slot[kRouteSmallT];
-  int u = blockIdx.x, grp = 0, rows = sh.T;
+  int grp = 0, rows = sh.T;
   if (!DENSE) {
     const ExpertRows er = expert_rows(sh, ws.topk_idx, u / per, slot);
     if (er.e < 0) return;
@@ -370,45 +370,79 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   }
 }
 
+// Routed gate/up units.  (3 waves per SIMD: the register budget of 168
+// holds every unit variant)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_gateup(StreamArgs a,
+                                                                                                      Workspace ws,
+                                                                                                      int KS) {
+  gateup_unit<false>(a, ws, KS, blockIdx.x);
+}
+
+// The router and the dense branch's gate/up units in one launch: blocks
+// [0, nroute) are the router's (K-slice, token group) blocks, the rest are
+// dense gate/up units.  The dense branch does not depend on the routing, so
+// its weights stream while the router's few blocks wait on memory latency,
+// with no second stream and no events.
+template <int CW>
+__global__ __launch_bounds__(kThreads) void k_route_dense(
+    StreamArgs a, const bf16_t* __restrict__ wr, const float* __restrict__ bias, Workspace ws, int slice_rows, int TB,
+    int nslices, int nroute, int KSd) {
+  const int b = blockIdx.x;
+  if (b < nroute)
+    route_slice<CW>(a.sh, slice_rows, TB, nslices, b % nslices, b / nslices, a.x, wr, bias, ws);
+  else
+    gateup_unit<true>(a, ws, KSd, b - nroute);
+}
+
 // ---------------------------------------------------------------------------
 // down
 // ---------------------------------------------------------------------------
 
 // GeGLU of the streamed rows: h = gelu_tanh(sum G) * (sum U), K-slices in
-// fixed order, bf16.  Routed: the T*k slot rows of ws.part into ws.h (slot
-// order); dense: the T token rows into ws.h_d.  4 columns per thread.
-template <bool DENSE>
-__global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace ws, int KS) {
-  const int N = DENSE ? sh.D : sh.I;
-  const int rows = DENSE ? sh.T : sh.T * sh.k;
-  const long long n4 = (long long)rows * (N / 4);
-  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n4; i += (long long)gridDim.x * kThreads) {
-    const int row = int(i / (N / 4)), c = int(i % (N / 4)) * 4;
-    float4 g = make_float4(0.f, 0.f, 0.f, 0.f), up = g;
-    for (int ks = 0; ks < KS; ++ks) {
-      const float4 pg = *reinterpret_cast<const float4*>(part_ptr(ws, sh, DENSE, ks, row, 0) + c);
-      const float4 pu = *reinterpret_cast<const float4*>(part_ptr(ws, sh, DENSE, ks, row, 1) + c);
-      g.x += pg.x; g.y += pg.y; g.z += pg.z; g.w += pg.w;
-      up.x += pu.x; up.y += pu.y; up.z += pu.z; up.w += pu.w;
+// fixed order, bf16.  Items [0, n4r) are the T*k routed slot rows of
+// ws.part into ws.h (slot order), items [n4r, n4r + n4d) the T dense token
+// rows into ws.h_d.  4 columns per item.
+__device__ __forceinline__ void geglu4(const Workspace& ws, const Shape& sh, bool dense, int KS, int row, int c,
+                                       bf16_t* hout) {
+  float4 g = make_float4(0.f, 0.f, 0.f, 0.f), up = g;
+  for (int ks = 0; ks < KS; ++ks) {
+    const float4 pg = *reinterpret_cast<const float4*>(part_ptr(ws, sh, dense, ks, row, 0) + c);
+    const float4 pu = *reinterpret_cast<const float4*>(part_ptr(ws, sh, dense, ks, row, 1) + c);
+    g.x += pg.x; g.y += pg.y; g.z += pg.z; g.w += pg.w;
+    up.x += pu.x; up.y += pu.y; up.z += pu.z; up.w += pu.w;
+  }
+  *reinterpret_cast<u32x2_t*>(hout) = u32x2_t{pack_bf16x2(gelu_tanh(g.x) * up.x, gelu_tanh(g.y) * up.y),
+                                              pack_bf16x2(gelu_tanh(g.z) * up.z, gelu_tanh(g.w) * up.w)};
+}
+
+__global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace ws, long long n4r, long long n4d) {
+  const int qi = sh.I / 4, qd = sh.D / 4;
+  const int ksd = dense_gateup_slices(sh);
+  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n4r + n4d;
+       i += (long long)gridDim.x * kThreads) {
+    if (i < n4r) {
+      const int row = int(i / qi), c = int(i % qi) * 4;
+      geglu4(ws, sh, false, kStreamKS, row, c, ws.h + (long long)row * sh.I + c);
+    } else {
+      const long long j = i - n4r;
+      const int row = int(j / qd), c = int(j % qd) * 4;
+      geglu4(ws, sh, true, ksd, row, c, ws.h_d + (long long)row * sh.D + c);
     }
-    bf16_t* hout = (DENSE ? ws.h_d : ws.h) + (long long)row * N + c;
-    *reinterpret_cast<u32x2_t*>(hout) = u32x2_t{pack_bf16x2(gelu_tanh(g.x) * up.x, gelu_tanh(g.y) * up.y),
-                                                pack_bf16x2(gelu_tanh(g.z) * up.z, gelu_tanh(g.w) * up.w)};
   }
 }
 
-// DENSE: units (128 columns, K-slice of whole 64-row groups of D) over the T
-// rows of h_d; fp32 partial outputs per K-slice (summed by the combine).
-// Routed: units (ai-th active expert, 128 columns) over the expert's rows of
-// h (slot order), bf16 output rows y indexed by slot.
+// Down units.  DENSE: unit u = (128 columns, K-slice of whole 64-row groups
+// of D) over the T rows of h_d, fp32 partial outputs per slice (summed by
+// the combine).  Routed: unit u = (ai-th active expert, 128 columns) over
+// the expert's rows of h (slot order), bf16 output rows y indexed by slot.
 template <bool DENSE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_down(StreamArgs a, Workspace ws) {
+__device__ void down_unit(const StreamArgs& a, const Workspace& ws, int u) {
   const Shape& sh = a.sh;
   const int H = sh.H;
-  constexpr int NC = DENSE ? 128 : kRoutedDownCols;  // output columns of a unit
+  constexpr int NC = kDownCols;  // output columns of a unit
   const int nblk = H / NC;
   __shared__ int slot[kRouteSmallT];
-  int u = blockIdx.x, grp = 0, rows = sh.T, kbeg = 0, kend = sh.I, ksd = 0;
+  int grp = 0, rows = sh.T, kbeg = 0, kend = sh.I, ksd = 0;
   if (DENSE) {
     const int g64 = sh.D / 64, KS = dense_down_slices(sh);
     ksd = u % KS;
@@ -423,7 +457,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     u %= nblk;
   }
   const int n0 = u * NC;
-  const int K = DENSE ? sh.D : sh.I;  // row length of h / h_d
+  const int K = DENSE ? sh.D : sh.I;  // row length of h_d / h
   const bf16_t* wd = (DENSE ? a.dd : a.wd + (long long)grp * sh.I * H) + n0;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -452,6 +486,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   }
 }
 
+// One launch for the dense down units (blocks [0, ud)) and the routed ones.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_down(StreamArgs a,
+                                                                                                    Workspace ws,
+                                                                                                    int ud) {
+  const int u = blockIdx.x;
+  if (u < ud)
+    down_unit<true>(a, ws, u);
+  else
+    down_unit<false>(a, ws, u - ud);
+}
+
 // h and y rows of the last streamed forward (slot order) copied to grouped
 // (perm) order: block b handles slot b.  Diagnostic only.
 __global__ __launch_bounds__(kThreads) void k_stream_export(Shape sh, Workspace ws, bf16_t* h_rows, bf16_t* y_rows) {
@@ -465,53 +510,58 @@ __global__ __launch_bounds__(kThreads) void k_stream_export(Shape sh, Workspace 
 
 }  // namespace
 
-// part: which branch to queue (the dense branch does not depend on the
-// routing, so the caller may run it on another stream)
-hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s) {
+hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
   const Shape& sh = a.sh;
-  const bool dense = part == StreamPart::Dense;
-  if (dense ? sh.D == 0 : sh.T == 0) return hipSuccess;
-  const int ks = dense ? dense_gateup_slices(sh) : kStreamKS;
-  const size_t kl = size_t((sh.H / 64 + ks - 1) / ks) * 64;  // longest slice
+  if (sh.T == 0) return hipSuccess;
+  const size_t kl = size_t((sh.H / 64 + kStreamKS - 1) / kStreamKS) * 64;  // longest slice
   const size_t lds = std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * 64 * 4);
-  if (dense) {
-    hipLaunchKernelGGL(k_stream_gateup<true>, dim3((sh.D / 64) * 2 * ks), dim3(kThreads), lds, s, a, ws, ks);
-  } else {
-    const int max_active = std::min(sh.E, sh.T * sh.k);
-    hipLaunchKernelGGL(k_stream_gateup<false>, dim3(max_active * (sh.I / 64) * 2 * ks), dim3(kThreads), lds, s, a,
-                       ws, ks);
-  }
+  const int max_active = std::min(sh.E, sh.T * sh.k);
+  hipLaunchKernelGGL(k_stream_gateup, dim3(max_active * (sh.I / 64) * 2 * kStreamKS), dim3(kThreads), lds, s, a, ws,
+                     kStreamKS);
   return hipGetLastError();
 }
 
-hipError_t launch_stream_geglu(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s) {
+hipError_t launch_route_dense(const StreamArgs& a, const bf16_t* wr, const float* bias, const Workspace& ws,
+                              hipStream_t s) {
   const Shape& sh = a.sh;
-  const bool dense = part == StreamPart::Dense;
-  if (dense ? sh.D == 0 : sh.T == 0) return hipSuccess;
-  const int ks = dense ? dense_gateup_slices(sh) : kStreamKS;
-  const long long n4 = dense ? (long long)sh.T * sh.D / 4 : (long long)sh.T * sh.k * sh.I / 4;
-  const int gblocks = int(std::min<long long>(1024, (n4 + kThreads - 1) / kThreads));
-  if (dense)
-    hipLaunchKernelGGL(k_stream_geglu<true>, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, ks);
+  if (sh.T == 0) return hipSuccess;
+  const RouteSmallCfg c = route_small_config(sh);
+  if (!c.ok) return hipErrorInvalidValue;
+  const int nroute = c.nslices * c.groups;
+  const int ksd = sh.D > 0 ? dense_gateup_slices(sh) : 1;
+  const int ud = sh.D > 0 ? (sh.D / 64) * 2 * ksd : 0;
+  const size_t kl = size_t((sh.H / 64 + ksd - 1) / ksd) * 64;  // longest dense K-slice
+  const size_t lds = ud ? std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * 64 * 4) : 0;
+  if (c.cw == 8)
+    hipLaunchKernelGGL(k_route_dense<8>, dim3(nroute + ud), dim3(kThreads), lds, s, a, wr, bias, ws, c.slice_rows, c.tb,
+                       c.nslices, nroute, ksd);
   else
-    hipLaunchKernelGGL(k_stream_geglu<false>, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, ks);
+    hipLaunchKernelGGL(k_route_dense<4>, dim3(nroute + ud), dim3(kThreads), lds, s, a, wr, bias, ws, c.slice_rows, c.tb,
+                       c.nslices, nroute, ksd);
   return hipGetLastError();
 }
 
-hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, StreamPart part, hipStream_t s) {
+hipError_t launch_stream_geglu(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
   const Shape& sh = a.sh;
-  const bool dense = part == StreamPart::Dense;
-  const int nblk = sh.H / (dense ? 128 : kRoutedDownCols);
-  if (dense ? sh.D == 0 : sh.T == 0) return hipSuccess;
-  const int kmax = dense ? (sh.D / 64 + dense_down_slices(sh) - 1) / dense_down_slices(sh) * 64 : sh.I;
-  const size_t lds = std::max(size_t(kmax) * kRowsChunk * 2,
-                              size_t(5) * kRowsChunk * (dense ? 128 : kRoutedDownCols) * 4);
-  if (dense) {
-    hipLaunchKernelGGL(k_stream_down<true>, dim3(nblk * dense_down_slices(sh)), dim3(kThreads), lds, s, a, ws);
-  } else {
-    const int max_active = std::min(sh.E, sh.T * sh.k);
-    hipLaunchKernelGGL(k_stream_down<false>, dim3(max_active * nblk), dim3(kThreads), lds, s, a, ws);
-  }
+  if (sh.T == 0) return hipSuccess;
+  const long long n4r = (long long)sh.T * sh.k * sh.I / 4;
+  const long long n4d = sh.D > 0 ? (long long)sh.T * sh.D / 4 : 0;
+  const int gblocks = int(std::min<long long>(1024, (n4r + n4d + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(k_stream_geglu, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, n4r, n4d);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
+  const Shape& sh = a.sh;
+  if (sh.T == 0) return hipSuccess;
+  const int nblk = sh.H / kDownCols;
+  const int ksd = sh.D > 0 ? dense_down_slices(sh) : 1;
+  const int ud = sh.D > 0 ? nblk * ksd : 0;
+  const int max_active = std::min(sh.E, sh.T * sh.k);
+  // longest K run of a unit: a dense K-slice or the expert width
+  const int kd = ud ? (sh.D / 64 + ksd - 1) / ksd * 64 : 0;
+  const size_t lds = std::max(size_t(std::max(sh.I, kd)) * kRowsChunk * 2, size_t(5) * kRowsChunk * kDownCols * 4);
+  hipLaunchKernelGGL(k_stream_down, dim3(ud + max_active * nblk), dim3(kThreads), lds, s, a, ws, ud);
   return hipGetLastError();
 }
 
