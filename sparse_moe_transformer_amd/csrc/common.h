@@ -75,7 +75,7 @@ struct Workspace {
 constexpr int kRouterSlices = 16;  // most K-slices of the large-T router logits
 constexpr int kRouteSlices = 32;   // K-slices of the small-T router logits
 constexpr int kRouteSmallT = 64;   // largest T of the one-block-per-token router and the streaming path
-constexpr int kGemmBM = 128;       // MFMA tile rows (tokens)
+constexpr int kGemmBM = 256;       // MFMA tile rows (tokens)
 constexpr int kStreamKS = 2;       // K-slices of the streaming routed gate/up units
 constexpr int kDenseKS = 4;        // K-slices of the streaming dense gate/up units
 constexpr int kDenseDownKS = 4;    // K-slices of the streaming dense down units

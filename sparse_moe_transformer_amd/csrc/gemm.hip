@@ -11,25 +11,33 @@
 // needed to size the grid.  Routed A rows of the gate/up GEMM are gathered
 // from x through perm and never copied out.
 //
-// Tile: 128 rows x 128 B-columns x 64 K, 256 threads = 4 waves in 2 x 2,
-// each wave owning 64 x 64 outputs as 2 x 2 MFMA 32x32 blocks (fp32
-// accumulators).  For gate/up the 128 B-columns are 64 gate + 64 up
-// columns at the same output positions, so the GeGLU epilogue pairs them in
-// registers.
+// Tile: 256 rows x 256 B-columns x 64 K, 512 threads = 8 waves in two
+// groups of 4 (one wave of each group per SIMD).  Group g owns tile rows
+// [128 g, 128 g + 128); wave w of a group owns 64 B-columns (gate/up: 32
+// gate + the 32 up columns at the same output positions, so the GeGLU
+// epilogue pairs them in registers), i.e. 128 x 64 outputs as 4 x 2 MFMA
+// 32x32 blocks.  128-row wave tiles keep the LDS reads per MFMA low.
+//
+// Ping-pong: while one group runs the MFMAs of a k-step from LDS, the other
+// writes its half of a later k-step's tiles (A rows of its own half, 32 of
+// the 64 k rows of B) to LDS and issues its next global loads; a block
+// barrier swaps the roles, so each SIMD's matrix unit always has a wave to
+// feed.  LDS holds two k-steps (2 x 72 KB).
 //
 // Weights are [K, N] with N contiguous, while the MFMA B operand wants 8
 // consecutive k of one column per lane.  Each thread loads a 4(k) x 8(n)
-// block with four 16-byte loads, transposes it in registers and stores
-// 4-k runs to an LDS tile laid out [n][k] (k contiguous); MFMA operands are
-// then single 16-byte LDS reads.  Rows are padded to 72 elements (144 B) so
-// that 8 lanes of a 16-byte read hit 8 distinct 4-bank groups.  NVFP4
-// weights are already k-contiguous ([N, K/2]): each thread decodes 32
-// codes of one column to bf16 (an e2m1 x e4m3 product is exact in bf16)
-// and the fp32 tensor scale is applied in the epilogue.
+// block with four 16-byte loads, transposes it in registers and stores 4-k
+// runs to an LDS tile laid out [n][k] (k contiguous); MFMA operands are then
+// single 16-byte LDS reads.  Rows are padded to 72 elements (144 B), which
+// spreads 16 lanes of a 16-byte read over the 64 LDS banks.  NVFP4 weights
+// are already k-contiguous ([N, K/2]): each thread decodes 32 codes of one
+// column to bf16 (an e2m1 x e4m3 product is exact in bf16) and the fp32
+// tensor scale is applied in the epilogue.
 //
-// Block ids are remapped so consecutive logical tiles (the N-tiles of one
-// M-tile, then the next M-tile of the same expert) run on one XCD and share
-// its L2.
+// Block ids are remapped so that each XCD takes a contiguous run of the
+// tiles that exist (the N-tiles of one M-tile, then the next M-tile of the
+// same expert share its L2); the grid covers the worst-case tile list and
+// the surplus blocks exit at once.
 #include <type_traits>
 
 #include "common.h"
@@ -38,11 +46,13 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = kGemmBM;  // 128
+constexpr int BM = kGemmBM;  // 256
 constexpr int BN = 256;      // B columns per tile
 constexpr int BK = 64;
 constexpr int LDSK = BK + 8;  // padded row (elements)
-constexpr int kThreads = 512;  // 8 waves: 2 (rows) x 4 (columns), 64 x 64 outputs each
+constexpr int kThreads = 512;  // 8 waves: 2 (rows) x 4 (columns), 128 x 64 outputs each
+constexpr int kWI = BM / 64;   // 32-row MFMA blocks per wave
+constexpr int kALoads = BM * BK / 8 / kThreads;  // 16-byte A chunks per thread and k-step (a group moves half the tile with half the threads)
 constexpr int kXcd = 8;
 
 enum { MODE_PLAIN_BF16 = 0, MODE_PLAIN_F32 = 1, MODE_GATEUP = 2 };
@@ -90,9 +100,15 @@ __device__ __forceinline__ float e4m3_f32(uint32_t b) {
 template <int MODE, int WF>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0, int units_total) {
   // ---- logical tile of this block (XCD-aware remap) ----
-  const int per = (units_total + kXcd - 1) / kXcd;
-  const int u = (blockIdx.x % kXcd) * per + blockIdx.x / kXcd;
-  if (u >= units_total) return;
+  // The grid covers the worst-case tile list; the remap spreads only the
+  // tiles that exist (the grouped segment's count is read from the device
+  // list) evenly over the XCDs, each XCD taking a contiguous run, so no XCD
+  // is left with the empty tail of the list.  Surplus blocks exit at once.
+  const int total = s1.mtiles ? units0 + (*s1.n_mtiles) * s1.n_ntiles * s1.ksplit : units_total;
+  const int per = (total + kXcd - 1) / kXcd;
+  const int slot = blockIdx.x / kXcd;
+  const int u = (blockIdx.x % kXcd) * per + slot;
+  if (slot >= per || u >= total) return;
   const bool second = u >= units0;
   const Seg& S = second ? s1 : s0;
   int uu = second ? u - units0 : u;
@@ -120,17 +136,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  // wave-uniform by construction (an SGPR): the wave groups below branch on
+  // it around block barriers, so each wave must take exactly one path
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 3;
 
-  // ---- A: 16-byte chunks c = tid + 512 i, row c/8, k-chunk c%8.  Rows past
-  // the tile's end read a valid row (their results are never stored), so the
-  // loads need no branches.
-  const bf16_t* arow[2];
+  // ---- loads are split between the two wave groups (group g = waves
+  // 4g .. 4g+3, threads tg = tid - 256 g): group g moves A rows
+  // [128 g, 128 g + 128) and the k rows [32 g, 32 g + 32) of the B tile.
+  const int grp_w = wave >> 2;  // this wave's group (also its 128-row half of the tile)
+  const int tg = tid & 255;
+  // A: 16-byte chunks c = tg + 256 i of the group's half, row c/8, k-chunk
+  // c%8.  Rows past the tile's end read a valid row (their results are never
+  // stored), so the loads need no branches.
+  const bf16_t* arow[kALoads];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + kThreads * i;
-    const int r = (c >> 3) < rows ? (c >> 3) : 0;
+  for (int i = 0; i < kALoads; ++i) {
+    const int c = tg + 256 * i;
+    const int tr = grp_w * 128 + (c >> 3);
+    const int r = tr < rows ? tr : 0;
     const long long gr = S.gather ? S.gather[row0 + r] : row0 + r;
     arow[i] = S.A + gr * S.lda + (c & 7) * 8;
   }
@@ -138,12 +162,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   // ---- B source of this thread (columns past N read column 0; discarded)
   const bf16_t* bsrc = nullptr;  // bf16: 4 rows x 8 columns at (bkb*4, bcol)
   int bkb = 0, bcol = 0;
-  const uint8_t* fq = nullptr;   // NVFP4: 32 codes (16 bytes) of one column
+  const uint8_t* fq = nullptr;   // NVFP4: 16 codes (8 bytes) of one column
   const uint8_t* fs = nullptr;
-  int fn = 0, fkh = 0;
+  int fn = 0, fkq = 0;
   if (WF == W_BF16) {
-    const int nb = tid >> 4;  // 32 groups of 8 columns
-    bkb = tid & 15;           // 16 groups of 4 k
+    const int nb = tg >> 3;        // 32 groups of 8 columns
+    bkb = (tg & 7) + 8 * grp_w;    // 16 groups of 4 k; the group's 8
     bcol = nb * 8;
     const bf16_t* Bm = S.B0;
     int ncol = n0 + nb * 8;
@@ -153,8 +177,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     }
     bsrc = Bm + grp * S.b_gstride + (ncol < N ? ncol : 0);
   } else {
-    fn = tid >> 1;  // LDS column 0..255
-    fkh = tid & 1;  // which 32-k half of the 64-k step
+    fn = tg;                  // LDS column 0..255
+    fkq = grp_w;              // which 32-k half of the 64-k step
     const Fp4Mat* F = &S.F0;
     int ncol = n0 + fn;
     if (MODE == MODE_GATEUP && fn >= 128) {
@@ -163,13 +187,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     }
     const long long NN = S.N;
     const long long col = ncol < N ? ncol : 0;
-    fq = F->q + (grp * NN + col) * (long long)(K / 2) + fkh * 16;
-    fs = F->scale + (grp * NN + col) * (long long)(K / 16) + fkh * 2;
+    fq = F->q + (grp * NN + col) * (long long)(K / 2) + fkq * 16;
+    fs = F->scale + (grp * NN + col) * (long long)(K / 16) + fkq * 2;
   }
 
-  auto load_tile = [&](int k0, u32x4_t(&ra)[2], u32x4_t(&rb)[4]) {
+  auto load_tile = [&](int k0, u32x4_t(&ra)[kALoads], u32x4_t(&rb)[4]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + k0);
+    for (int i = 0; i < kALoads; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + k0);
     if (WF == W_BF16) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) rb[r] = *reinterpret_cast<const u32x4_t*>(bsrc + (long long)(k0 + bkb * 4 + r) * S.ldb);
@@ -179,11 +203,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     }
   };
 
-  auto store_tile = [&](int buf, const u32x4_t(&ra)[2], const u32x4_t(&rb)[4]) {
-    bf16_t* as = As[buf];
+  auto store_tile = [&](int buf, const u32x4_t(&ra)[kALoads], const u32x4_t(&rb)[4]) {
+    bf16_t* as = As[buf] + grp_w * 128 * LDSK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kThreads * i;
+    for (int i = 0; i < kALoads; ++i) {
+      const int c = tg + 256 * i;
       *reinterpret_cast<u32x4_t*>(as + (c >> 3) * LDSK + (c & 7) * 8) = ra[i];
     }
     bf16_t* bs = Bs[buf];
@@ -218,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
         outw[d * 4 + 2] = perm_hi16(__float_as_uint(v2.x * sv), __float_as_uint(v2.y * sv));
         outw[d * 4 + 3] = perm_hi16(__float_as_uint(v3.x * sv), __float_as_uint(v3.y * sv));
       }
-      bf16_t* dst = bs + fn * LDSK + fkh * 32;
+      bf16_t* dst = bs + fn * LDSK + fkq * 32;
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         *reinterpret_cast<u32x4_t*>(dst + v * 8) =
@@ -226,22 +250,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     }
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[kWI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kWI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // this wave's 32 x 32 blocks: rows wm*64 + 32i; columns (gate/up: gate and
-  // up at wn*32; else wn*64 + 32j).  The K loop computes every block;
-  // blocks past the tile's rows or the matrix's columns are dropped in the
-  // epilogue.
+  // this wave's 32 x 32 blocks: rows 128 g + 32i (g = its group); columns (gate/up: gate
+  // and up at wn*32; else wn*64 + 32j)
   const int kofs = (lane >> 5) * 8;
-  int arow_l[2], brow_l[2];
+  int arow_l[kWI], brow_l[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) arow_l[i] = (wm * 64 + i * 32 + (lane & 31)) * LDSK + kofs;
+  for (int i = 0; i < kWI; ++i) arow_l[i] = (grp_w * kWI * 32 + i * 32 + (lane & 31)) * LDSK + kofs;
   if (MODE == MODE_GATEUP) {
     brow_l[0] = (wn * 32 + (lane & 31)) * LDSK + kofs;
     brow_l[1] = (BN / 2 + wn * 32 + (lane & 31)) * LDSK + kofs;
@@ -250,29 +272,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     for (int j = 0; j < 2; ++j) brow_l[j] = (wn * 64 + j * 32 + (lane & 31)) * LDSK + kofs;
   }
 
-  // MFMA blocks of this wave inside the tile's rows and the matrix's
-  // columns (wave-uniform): blocks past either are skipped, so the ragged
-  // last M-tile of an expert and the last N-tile cost only their valid part
-  bool mval[2], nval[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) mval[i] = wm * 64 + i * 32 < rows;
-  if (MODE == MODE_GATEUP) {
-    nval[0] = nval[1] = n0 + wn * 32 < N;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) nval[j] = n0 + wn * 64 + j * 32 < N;
-  }
-  const bool full = __builtin_amdgcn_readfirstlane(mval[0] && mval[1] && nval[0] && nval[1]);
+  // Row blocks of this wave inside the tile's rows (wave-uniform): the K
+  // loop is instantiated per count NI, so the ragged last M-tile of an
+  // expert costs only its valid blocks' MFMAs; a wave with no valid rows or
+  // no valid columns only moves tiles.  (Columns past N inside a valid wave
+  // are computed from column 0 and dropped.)
+  const int wrow0 = grp_w * kWI * 32;
+  const bool wcols = (MODE == MODE_GATEUP) ? n0 + wn * 32 < N : n0 + wn * 64 < N;
+  const int ni = wcols ? __builtin_amdgcn_readfirstlane(min(kWI, max(0, (rows - wrow0 + 31) / 32))) : 0;
 
   // Fragments of sub-step kk + 1 are read from LDS while the MFMAs of kk run.
-  auto compute = [&](int buf, auto full_c) {
-    constexpr bool FULL = decltype(full_c)::value;
+  auto compute = [&](int buf, auto ni_c) {
+    constexpr int NI = decltype(ni_c)::value;
+    if (NI == 0) return;
     const bf16_t* as = As[buf];
     const bf16_t* bs = Bs[buf];
-    bf16x8_t a[2][2], b[2][2];
-    auto frags = [&](int kk, bf16x8_t(&af)[2], bf16x8_t(&bf)[2]) {
+    bf16x8_t a[2][kWI], b[2][2];
+    auto frags = [&](int kk, bf16x8_t(&af)[kWI], bf16x8_t(&bf)[2]) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(as + arow_l[i] + kk);
+      for (int i = 0; i < NI; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(as + arow_l[i] + kk);
 #pragma unroll
       for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const bf16x8_t*>(bs + brow_l[j] + kk);
     };
@@ -281,68 +299,92 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     for (int s = 0; s < BK / 16; ++s) {
       if (s + 1 < BK / 16) frags((s + 1) * 16, a[(s + 1) & 1], b[(s + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          if (FULL || (mval[i] && nval[j]))
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
     }
   };
 
-  // K-steps of this tile's slice.  Global loads run two steps ahead of the
-  // MFMAs (two register stages), LDS is double-buffered; the steady state is
-  // straight-line code (tail loads re-read the last step), so the compiler
-  // can wait on exactly the loads it needs.
+  // K-steps of this tile's slice, ping-pong between the wave groups: each
+  // SIMD holds one wave of each group, and while one group runs the MFMAs
+  // of a k-step the other writes its half of a later k-step's tiles to LDS
+  // and issues its next global loads; a block barrier swaps the roles.
+  // Intervals (C = compute, M = write my half of step s to LDS buffer s%2,
+  // then load my half of step s+1 into registers):
+  //   group 0: C(0) | M(1) | C(1) | M(2) | ... | C(nk-1)
+  //   group 1: M(1) | C(0) | M(2) | C(1) | ... | M(nk) | C(nk-1)
+  // Step s is complete in its buffer before group 0 reads it (both halves
+  // are written in the two intervals before), and a buffer is rewritten
+  // only after both groups have read it.  Both groups pass 2 nk - 1
+  // barriers.  Memory phases past the last step only keep the count.
   const int nk_all = K / BK;
   const int kt0 = ks * nk_all / S.ksplit;
   const int nk = (ks + 1) * nk_all / S.ksplit - kt0;
-  const int klast = (kt0 + nk - 1) * BK;
-  u32x4_t ra0[2], rb0[4], ra1[2], rb1[4];
-  auto kloop = [&](auto full_c) {
-    load_tile(kt0 * BK, ra0, rb0);
-    load_tile(min((kt0 + 1) * BK, klast), ra1, rb1);
-    store_tile(0, ra0, rb0);
-    __syncthreads();
-    int kt = 0;
-    // sched_barrier keeps the scheduler from sinking the next step's loads
-    // below the wait for the current step's registers
-    for (; kt + 1 < nk; kt += 2) {
-      load_tile(min((kt0 + kt + 2) * BK, klast), ra0, rb0);
+  u32x4_t ra[kALoads], rb[4];
+  // (sched_barrier: the staging registers hold one step at a time; the
+  // scheduler must not start the next loads before the stores have read them)
+  auto mem_phase = [&](int st) {  // write my half of step st, load my half of step st + 1
+    if (st < nk) {
+      store_tile(st & 1, ra, rb);
       __builtin_amdgcn_sched_barrier(0);
-      compute(0, full_c);
-      __builtin_amdgcn_sched_barrier(0);
-      store_tile(1, ra1, rb1);
-      __syncthreads();
-      load_tile(min((kt0 + kt + 3) * BK, klast), ra1, rb1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(1, full_c);
-      __builtin_amdgcn_sched_barrier(0);
-      store_tile(0, ra0, rb0);
-      __syncthreads();
+      if (st + 1 < nk) load_tile((kt0 + st + 1) * BK, ra, rb);
     }
-    if (kt < nk) compute(0, full_c);  // odd step count: LDS buffer 0 holds the last step
+    __builtin_amdgcn_sched_barrier(0);
   };
-  if (full)
-    kloop(std::true_type{});
-  else
-    kloop(std::false_type{});
+  auto kloop = [&](auto ni_c) {
+    load_tile(kt0 * BK, ra, rb);
+    store_tile(0, ra, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nk > 1) load_tile((kt0 + 1) * BK, ra, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    if (grp_w == 0) {
+      for (int kt = 0; kt < nk; ++kt) {
+        compute(kt & 1, ni_c);
+        __syncthreads();
+        if (kt + 1 < nk) {
+          mem_phase(kt + 1);
+          __syncthreads();
+        }
+      }
+    } else {
+      mem_phase(1);
+      __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+        compute(kt & 1, ni_c);
+        if (kt + 1 < nk) {
+          __syncthreads();
+          mem_phase(kt + 2);
+          __syncthreads();
+        }
+      }
+    }
+  };
+  switch (ni) {
+    case 0: kloop(std::integral_constant<int, 0>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    default: kloop(std::integral_constant<int, kWI>{}); break;
+  }
 
   // ---- epilogue: lane holds column (lane & 31); rows 8(r/4) + 4(lane/32) + r%4
+  if (!wcols) return;
   float ts0 = 1.f, ts1 = 1.f;
   if (WF == W_FP4) {
     ts0 = S.F0.tscale[grp];
     if (MODE == MODE_GATEUP) ts1 = S.F1.tscale[grp];
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (!mval[i]) continue;
+  for (int i = 0; i < kWI; ++i) {
+    if (i >= ni) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int row = wrow0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (row >= rows) continue;
       const long long orow = (long long)(row0 + row) * S.ldc + ks * S.c_slice;
       if (MODE == MODE_GATEUP) {
-        if (!nval[0]) continue;
         const int col = n0 + wn * 32 + (lane & 31);
         const float g = acc[i][0][r] * ts0;
         const float up = acc[i][1][r] * ts1;
@@ -350,8 +392,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          if (!nval[j]) continue;
           const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+          if (col >= N) continue;
           const float v = acc[i][j][r] * ts0;
           if (MODE == MODE_PLAIN_F32)
             reinterpret_cast<float*>(S.C)[orow + col] = v;
