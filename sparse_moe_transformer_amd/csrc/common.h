@@ -101,6 +101,28 @@ struct Fp4Mat {
 
 // ---- launches (each queues on `s` and returns the launch status) ----------
 
+// Buffer-resource loads: base pointer in scalar registers (it must be the
+// same in every lane), a 32-bit per-lane byte offset and a uniform one.
+// POLICY is the cache-policy immediate (0: default, 2: nontemporal).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
+}
+template <class V, int POLICY>
+__device__ __forceinline__ V bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (sizeof(V) == 16)
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
+  else
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POLICY));
+}
+// a pointer that is the same in every lane, moved to scalar registers
+template <class T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const T*>((uint64_t(hi) << 32) | lo);
+}
+
 hipError_t launch_route_small(const Shape& sh, const bf16_t* x, const bf16_t* wr, const float* bias,
                               const Workspace& ws, hipStream_t s);
 hipError_t launch_route_large(const Shape& sh, const bf16_t* x, const bf16_t* wr, const float* bias,

@@ -131,8 +131,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   constexpr int OUTN = (MODE == MODE_GATEUP) ? BN / 2 : BN;
   const int n0 = nt * OUTN;
 
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDSK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDSK];
+  // LDS: two k-steps of A [BM][LDSK] and B [BN][LDSK] tiles; after the K
+  // loop the same bytes stage the bf16 output tile
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * (BM + BN) * LDSK * 2];
+  bf16_t* const As0 = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* const Bs0 = As0 + 2 * BM * LDSK;
+  auto As = [&](int b) { return As0 + b * (BM * LDSK); };
+  auto Bs = [&](int b) { return Bs0 + b * (BN * LDSK); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,18 +154,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   // A: 16-byte chunks c = tg + 256 i of the group's half, row c/8, k-chunk
   // c%8.  Rows past the tile's end read a valid row (their results are never
   // stored), so the loads need no branches.
-  const bf16_t* arow[kALoads];
+  // A and bf16 B go through buffer resources: 32-bit byte offsets per lane,
+  // the k-step as a uniform offset (every operand matrix is below 2 GB).
+  const __amdgpu_buffer_rsrc_t ars = rsrc_of(uniform_ptr(S.A));
+  uint32_t aoff[kALoads];
 #pragma unroll
   for (int i = 0; i < kALoads; ++i) {
     const int c = tg + 256 * i;
     const int tr = grp_w * 128 + (c >> 3);
     const int r = tr < rows ? tr : 0;
-    const long long gr = S.gather ? S.gather[row0 + r] : row0 + r;
-    arow[i] = S.A + gr * S.lda + (c & 7) * 8;
+    const uint32_t gr = S.gather ? uint32_t(S.gather[row0 + r]) : uint32_t(row0 + r);
+    aoff[i] = (gr * uint32_t(S.lda) + uint32_t((c & 7) * 8)) * 2u;
   }
 
   // ---- B source of this thread (columns past N read column 0; discarded)
-  const bf16_t* bsrc = nullptr;  // bf16: 4 rows x 8 columns at (bkb*4, bcol)
+  __amdgpu_buffer_rsrc_t brs = ars;  // bf16: 4 rows x 8 columns at (bkb*4, bcol)
+  uint32_t boff = 0;
+  const uint32_t brow = uint32_t(S.ldb) * 2u;  // bytes per k row of B
   int bkb = 0, bcol = 0;
   const uint8_t* fq = nullptr;   // NVFP4: 16 codes (8 bytes) of one column
   const uint8_t* fs = nullptr;
@@ -175,7 +185,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       Bm = S.B1;
       ncol = n0 + (nb - 16) * 8;
     }
-    bsrc = Bm + grp * S.b_gstride + (ncol < N ? ncol : 0);
+    // the matrix differs between the gate and up halves, which split at a
+    // wave boundary, so the base stays wave-uniform
+    brs = rsrc_of(uniform_ptr(Bm + grp * S.b_gstride));
+    boff = uint32_t(bkb * 4) * brow + uint32_t(ncol < N ? ncol : 0) * 2u;
   } else {
     fn = tg;                  // LDS column 0..255
     fkq = grp_w;              // which 32-k half of the 64-k step
@@ -193,10 +206,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
 
   auto load_tile = [&](int k0, u32x4_t(&ra)[kALoads], u32x4_t(&rb)[4]) {
 #pragma unroll
-    for (int i = 0; i < kALoads; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + k0);
+    for (int i = 0; i < kALoads; ++i) ra[i] = bload<u32x4_t, 0>(ars, aoff[i], uint32_t(k0) * 2u);
     if (WF == W_BF16) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rb[r] = *reinterpret_cast<const u32x4_t*>(bsrc + (long long)(k0 + bkb * 4 + r) * S.ldb);
+      for (int r = 0; r < 4; ++r) rb[r] = bload<u32x4_t, 0>(brs, boff + uint32_t(r) * brow, uint32_t(k0) * brow);
     } else {
       rb[0] = *reinterpret_cast<const u32x4_t*>(fq + k0 / 2);
       rb[1] = u32x4_t{uint32_t(*reinterpret_cast<const uint16_t*>(fs + k0 / 16)), 0, 0, 0};
@@ -204,13 +217,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   };
 
   auto store_tile = [&](int buf, const u32x4_t(&ra)[kALoads], const u32x4_t(&rb)[4]) {
-    bf16_t* as = As[buf] + grp_w * 128 * LDSK;
+    bf16_t* as = As(buf) + grp_w * 128 * LDSK;
 #pragma unroll
     for (int i = 0; i < kALoads; ++i) {
       const int c = tg + 256 * i;
       *reinterpret_cast<u32x4_t*>(as + (c >> 3) * LDSK + (c & 7) * 8) = ra[i];
     }
-    bf16_t* bs = Bs[buf];
+    bf16_t* bs = Bs(buf);
     if (WF == W_BF16) {
       // rb[r] holds k = 4kb + r, columns bcol..bcol+7 (2 per dword)
 #pragma unroll
@@ -285,8 +298,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   auto compute = [&](int buf, auto ni_c) {
     constexpr int NI = decltype(ni_c)::value;
     if (NI == 0) return;
-    const bf16_t* as = As[buf];
-    const bf16_t* bs = Bs[buf];
+    const bf16_t* as = As(buf);
+    const bf16_t* bs = Bs(buf);
     bf16x8_t a[2][kWI], b[2][2];
     auto frags = [&](int kk, bf16x8_t(&af)[kWI], bf16x8_t(&bf)[2]) {
 #pragma unroll
@@ -370,38 +383,72 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   }
 
   // ---- epilogue: lane holds column (lane & 31); rows 8(r/4) + 4(lane/32) + r%4
-  if (!wcols) return;
   float ts0 = 1.f, ts1 = 1.f;
   if (WF == W_FP4) {
     ts0 = S.F0.tscale[grp];
     if (MODE == MODE_GATEUP) ts1 = S.F1.tscale[grp];
   }
+  if (MODE == MODE_PLAIN_F32) {  // router logits: fp32, written directly
+    if (!wcols) return;
 #pragma unroll
-  for (int i = 0; i < kWI; ++i) {
-    if (i >= ni) continue;
+    for (int i = 0; i < kWI; ++i) {
+      if (i >= ni) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wrow0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row >= rows) continue;
-      const long long orow = (long long)(row0 + row) * S.ldc + ks * S.c_slice;
-      if (MODE == MODE_GATEUP) {
-        const int col = n0 + wn * 32 + (lane & 31);
-        const float g = acc[i][0][r] * ts0;
-        const float up = acc[i][1][r] * ts1;
-        reinterpret_cast<bf16_t*>(S.C)[orow + col] = (bf16_t)f32_to_bf16_bits(gelu_tanh(g) * up);
-      } else {
+      for (int r = 0; r < 16; ++r) {
+        const int row = wrow0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= rows) continue;
+        const long long orow = (long long)(row0 + row) * S.ldc + ks * S.c_slice;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-          if (col >= N) continue;
-          const float v = acc[i][j][r] * ts0;
-          if (MODE == MODE_PLAIN_F32)
-            reinterpret_cast<float*>(S.C)[orow + col] = v;
-          else
-            reinterpret_cast<bf16_t*>(S.C)[orow + col] = (bf16_t)f32_to_bf16_bits(v);
+          if (col < N) reinterpret_cast<float*>(S.C)[orow + col] = acc[i][j][r] * ts0;
         }
       }
     }
+    return;
+  }
+  // bf16 outputs go through LDS so that the tile leaves in 16-byte stores.
+  // Neighbouring lanes swap values (DPP) so that each lane writes pairs of
+  // adjacent columns: even lanes rows r = 2q, odd lanes rows r = 2q + 1.
+  // Every wave passes both barriers (those without valid columns too).
+  constexpr int SP = OUTN * 2 + 16;  // staging row pitch (bytes)
+  __syncthreads();                   // every wave's last fragments are read
+  if (wcols) {
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int i = 0; i < kWI; ++i) {
+      if (i >= ni) continue;
+#pragma unroll
+      for (int j = 0; j < ((MODE == MODE_GATEUP) ? 1 : 2); ++j) {
+        uint32_t vb[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = (MODE == MODE_GATEUP) ? gelu_tanh(acc[i][0][r] * ts0) * (acc[i][1][r] * ts1)
+                                                : acc[i][j][r] * ts0;
+          vb[r] = f32_to_bf16_bits(v);
+        }
+        const int cpair = ((MODE == MODE_GATEUP) ? wn * 32 : wn * 64 + j * 32) + (lane & 30);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t send = odd ? vb[2 * q] : vb[2 * q + 1];
+          const uint32_t recv = uint32_t(__builtin_amdgcn_mov_dpp(int(send), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+          const int r = 2 * q + (odd ? 1 : 0);
+          const int row = wrow0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const uint32_t packed = odd ? (recv | (vb[2 * q + 1] << 16)) : (vb[2 * q] | (recv << 16));
+          *reinterpret_cast<uint32_t*>(smem + row * SP + cpair * 2) = packed;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = OUTN / 8;  // 16-byte chunks per staged row
+  bf16_t* C = reinterpret_cast<bf16_t*>(S.C);
+  for (int c = tid; c < BM * CPR; c += kThreads) {
+    const int row = c / CPR, ch = c % CPR;
+    const int col = n0 + ch * 8;
+    if (row < rows && col < N)
+      *reinterpret_cast<u32x4_t*>(C + (long long)(row0 + row) * S.ldc + ks * S.c_slice + col) =
+          *reinterpret_cast<const u32x4_t*>(smem + row * SP + ch * 16);
   }
 }
 

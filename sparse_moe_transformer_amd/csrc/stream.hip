@@ -64,28 +64,11 @@ __device__ __forceinline__ float* part_ptr(const Workspace& ws, const Shape& sh,
   return base + ((size_t(ks) * kRouteSmallT + row) * 2 + mat) * sh.D;
 }
 
-// Weight and activation rows are read through buffer resources: a 32-bit
-// per-thread byte offset plus a uniform (scalar) row offset, so the unrolled
-// loads share one address register instead of a 64-bit address each.  The
-// base pointers must be block-uniform.
+// Weight and activation rows are read through buffer resources (common.h):
+// a 32-bit per-thread byte offset plus a uniform (scalar) row offset, so the
+// unrolled loads share one address register instead of a 64-bit address
+// each.  The base pointers must be block-uniform.
 constexpr int kPolicyNT = 2;  // nontemporal: weights are streamed once
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
-}
-template <class V, int POLICY>
-__device__ __forceinline__ V bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  if constexpr (sizeof(V) == 16)
-    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
-  else
-    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POLICY));
-}
-// a pointer that is the same in every lane, moved to scalar registers
-__device__ __forceinline__ const bf16_t* uniform_ptr(const bf16_t* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
-  return reinterpret_cast<const bf16_t*>((uint64_t(hi) << 32) | lo);
-}
 
 // Fold acc over the row groups of the block; returns [NT][NCOLS] sums in LDS.
 template <int NT, int NCOLS, int CPT>
