@@ -11,28 +11,35 @@
 // needed to size the grid.  Routed A rows of the gate/up GEMM are gathered
 // from x through perm and never copied out.
 //
-// Tile: 256 rows x 256 B-columns x 64 K, 512 threads = 8 waves in two
-// groups of 4 (one wave of each group per SIMD).  Group g owns tile rows
-// [128 g, 128 g + 128); wave w of a group owns 64 B-columns (gate/up: 32
-// gate + the 32 up columns at the same output positions, so the GeGLU
-// epilogue pairs them in registers), i.e. 128 x 64 outputs as 4 x 2 MFMA
-// 32x32 blocks.  128-row wave tiles keep the LDS reads per MFMA low.
+// Tile: 256 rows x 256 B-columns, 512 threads = 8 waves in 2 (rows) x 4
+// (columns), each wave owning 128 x 64 outputs as 4 x 2 MFMA 32x32 blocks;
+// two waves share each SIMD.  For gate/up the 256 B-columns are 128 gate +
+// 128 up columns at the same output positions (a wave owns 32 of each), so
+// the GeGLU epilogue pairs them in registers.
 //
-// Ping-pong: while one group runs the MFMAs of a k-step from LDS, the other
-// writes its half of a later k-step's tiles (A rows of its own half, 32 of
-// the 64 k rows of B) to LDS and issues its next global loads; a block
-// barrier swaps the roles, so each SIMD's matrix unit always has a wave to
-// feed.  LDS holds two k-steps (2 x 72 KB).
+// Pipeline: K advances in stages of 32; four LDS stages (32 KB each) are in
+// flight.  Operand tiles go from global memory straight to LDS (buffer loads
+// with the lds flag, 16 bytes per lane, no registers), issued three stages
+// ahead, so a CU keeps ~96 KB of loads in flight without spending VGPRs on
+// them; each wave waits for its own copies of the stage about to be used,
+// then the block meets at a barrier.  A wave reads a whole stage's
+// fragments from LDS while the MFMAs of the previous stage run.
 //
-// Weights are [K, N] with N contiguous, while the MFMA B operand wants 8
-// consecutive k of one column per lane.  Each thread loads a 4(k) x 8(n)
-// block with four 16-byte loads, transposes it in registers and stores 4-k
-// runs to an LDS tile laid out [n][k] (k contiguous); MFMA operands are then
-// single 16-byte LDS reads.  Rows are padded to 72 elements (144 B), which
-// spreads 16 lanes of a 16-byte read over the 64 LDS banks.  NVFP4 weights
-// are already k-contiguous ([N, K/2]): each thread decodes 32 codes of one
-// column to bf16 (an e2m1 x e4m3 product is exact in bf16) and the fp32
-// tensor scale is applied in the epilogue.
+// LDS layouts (16-byte chunks XOR-swizzled so that every fragment read and
+// every copy touches the bank groups evenly):
+//   A  [256 rows][32 k]: 64 B per row, chunk c of row r at c ^ fa(r).
+//   B  bf16 weights are [K, N] (N contiguous) and stay so in LDS: two halves
+//      (gate / up, or columns 0-127 / 128-255) of [32 k][128 n], 256 B per k
+//      row, chunk c of row k at c ^ fb(k).  The MFMA B operand (8
+//      consecutive k of one column per lane) is read with the gfx950
+//      transposing LDS read: in a 16-lane group, lane i names row k0 + i / 4,
+//      columns 4 (i % 4) .. + 3, and receives column i of rows k0 .. k0 + 3.
+//   B  NVFP4 weights are [N, K/2] (k contiguous): two threads per column
+//      decode its 32 codes of a stage to bf16 (an e2m1 x e4m3 product is
+//      exact in bf16) into an A-style [256 n][32 k] tile; the fp32 tensor
+//      scale is applied in the epilogue.
+// After the K loop the same LDS stages the bf16 output tile, which leaves
+// the block in 16-byte row stores.
 //
 // Block ids are remapped so that each XCD takes a contiguous run of the
 // tiles that exist (the N-tiles of one M-tile, then the next M-tile of the
@@ -48,12 +55,12 @@ namespace {
 
 constexpr int BM = kGemmBM;  // 256
 constexpr int BN = 256;      // B columns per tile
-constexpr int BK = 64;
-constexpr int LDSK = BK + 8;  // padded row (elements)
+constexpr int BK = 32;       // k per pipeline stage
+constexpr int kStages = 4;   // LDS stages in flight
 constexpr int kThreads = 512;  // 8 waves: 2 (rows) x 4 (columns), 128 x 64 outputs each
-constexpr int kWI = BM / 64;   // 32-row MFMA blocks per wave
-constexpr int kALoads = BM * BK / 8 / kThreads;  // 16-byte A chunks per thread and k-step (a group moves half the tile with half the threads)
 constexpr int kXcd = 8;
+constexpr int kOpBytes = 256 * BK * 2;     // one operand tile of a stage: 16 KB
+constexpr int kStageBytes = 2 * kOpBytes;  // A, then B
 
 enum { MODE_PLAIN_BF16 = 0, MODE_PLAIN_F32 = 1, MODE_GATEUP = 2 };
 enum { W_BF16 = 0, W_FP4 = 1 };
@@ -97,13 +104,55 @@ __device__ __forceinline__ float e4m3_f32(uint32_t b) {
   return (b & 0x80u) ? -mag : mag;
 }
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource of a wave-uniform base pointer (moved to scalar
+// registers), no stride, 2^31 bytes of range.
+__device__ __forceinline__ i32x4_t rsrc4(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  i32x4_t r;
+  r[0] = int(__builtin_amdgcn_readfirstlane(uint32_t(v)));
+  r[1] = int(__builtin_amdgcn_readfirstlane(uint32_t(v >> 32)));
+  r[2] = 0x7FFFFFFF;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Global -> LDS copy of 16 bytes per lane (gfx950 buffer load with the lds
+// flag): the 16 bytes at (rsrc, voffset + soffset) of lane i land at LDS
+// byte address lds + 16 i; lds is wave-uniform (it goes to M0).  The copy
+// has no register result.  Written as asm so that the compiler does not
+// track it: it would otherwise wait for every copy in flight (including the
+// stages prefetched ahead) before any transposing LDS read; the kernel waits
+// for the copies itself (wait_counts before each barrier).
+__device__ __forceinline__ void copy_b128_to_lds(i32x4_t rsrc, uint32_t lds, int voffset, int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voffset), "s"(rsrc),
+               "s"(soffset)
+               : "memory");
+}
+
+// s_waitcnt with only vmcnt <= VM and lgkmcnt <= LGKM (expcnt not waited)
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_counts() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+// Workgroup barrier without a memory fence: the waits above it are explicit
+// (a fenced barrier would also wait for the copies still in flight for later
+// stages).  The memory clobber keeps LDS accesses on their side of it.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// swizzled chunk positions (see the header)
+__device__ __forceinline__ int fa(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int fb(int k) { return 4 * (k & 3); }
+
 template <int MODE, int WF>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0, int units_total) {
-  // ---- logical tile of this block (XCD-aware remap) ----
-  // The grid covers the worst-case tile list; the remap spreads only the
-  // tiles that exist (the grouped segment's count is read from the device
-  // list) evenly over the XCDs, each XCD taking a contiguous run, so no XCD
-  // is left with the empty tail of the list.  Surplus blocks exit at once.
+  // ---- logical tile of this block (XCD-aware remap over the real tiles) ----
   const int total = s1.mtiles ? units0 + (*s1.n_mtiles) * s1.n_ntiles * s1.ksplit : units_total;
   const int per = (total + kXcd - 1) / kXcd;
   const int slot = blockIdx.x / kXcd;
@@ -118,7 +167,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   const int nt = uu % S.n_ntiles;
   int grp = 0, row0, rows;
   if (S.mtiles) {
-    if (mt >= *S.n_mtiles) return;
     grp = S.mtiles[4 * mt];
     row0 = S.mtiles[4 * mt + 1];
     rows = S.mtiles[4 * mt + 2];
@@ -131,293 +179,291 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   constexpr int OUTN = (MODE == MODE_GATEUP) ? BN / 2 : BN;
   const int n0 = nt * OUTN;
 
-  // LDS: two k-steps of A [BM][LDSK] and B [BN][LDSK] tiles; after the K
-  // loop the same bytes stage the bf16 output tile
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * (BM + BN) * LDSK * 2];
-  bf16_t* const As0 = reinterpret_cast<bf16_t*>(smem);
-  bf16_t* const Bs0 = As0 + 2 * BM * LDSK;
-  auto As = [&](int b) { return As0 + b * (BM * LDSK); };
-  auto Bs = [&](int b) { return Bs0 + b * (BN * LDSK); };
+  // the four K stages; after the K loop the same bytes stage the output tile
+  constexpr int kStageArea = kStages * kStageBytes;
+  constexpr int SP = OUTN * 2 + 16;  // staging row pitch (bytes)
+  constexpr int kSmem = kStageArea > BM * SP ? kStageArea : BM * SP;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kSmem];
+  lds_u8* const lds3 = (lds_u8*)(lds);
+  const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>(lds3));  // LDS byte address of the stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // wave-uniform by construction (an SGPR): the wave groups below branch on
-  // it around block barriers, so each wave must take exactly one path
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave & 3;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int wm = wave >> 2, wn = wave & 3;
 
-  // ---- loads are split between the two wave groups (group g = waves
-  // 4g .. 4g+3, threads tg = tid - 256 g): group g moves A rows
-  // [128 g, 128 g + 128) and the k rows [32 g, 32 g + 32) of the B tile.
-  const int grp_w = wave >> 2;  // this wave's group (also its 128-row half of the tile)
-  const int tg = tid & 255;
-  // A: 16-byte chunks c = tg + 256 i of the group's half, row c/8, k-chunk
-  // c%8.  Rows past the tile's end read a valid row (their results are never
-  // stored), so the loads need no branches.
-  // A and bf16 B go through buffer resources: 32-bit byte offsets per lane,
-  // the k-step as a uniform offset (every operand matrix is below 2 GB).
-  const __amdgpu_buffer_rsrc_t ars = rsrc_of(uniform_ptr(S.A));
-  uint32_t aoff[kALoads];
+  // ---- A copies: wave w, copy q fills rows 32w + 16q .. + 15 of a stage;
+  // lane: row 32w + 16q + lane / 4, slot lane % 4 <- global chunk slot ^ fa.
+  // Rows past the tile's end copy a valid row (their results are dropped).
+  const i32x4_t arsrc = rsrc4(S.A);
+  int aoff[2];
 #pragma unroll
-  for (int i = 0; i < kALoads; ++i) {
-    const int c = tg + 256 * i;
-    const int tr = grp_w * 128 + (c >> 3);
-    const int r = tr < rows ? tr : 0;
-    const uint32_t gr = S.gather ? uint32_t(S.gather[row0 + r]) : uint32_t(row0 + r);
-    aoff[i] = (gr * uint32_t(S.lda) + uint32_t((c & 7) * 8)) * 2u;
+  for (int q = 0; q < 2; ++q) {
+    const int r = 32 * wave + 16 * q + (lane >> 2);
+    const int rr = r < rows ? r : 0;
+    const uint32_t gr = S.gather ? uint32_t(S.gather[row0 + rr]) : uint32_t(row0 + rr);
+    aoff[q] = int((gr * uint32_t(S.lda) + uint32_t(((lane & 3) ^ fa(r)) * 8)) * 2u);
   }
 
-  // ---- B source of this thread (columns past N read column 0; discarded)
-  __amdgpu_buffer_rsrc_t brs = ars;  // bf16: 4 rows x 8 columns at (bkb*4, bcol)
-  uint32_t boff = 0;
-  const uint32_t brow = uint32_t(S.ldb) * 2u;  // bytes per k row of B
-  int bkb = 0, bcol = 0;
-  const uint8_t* fq = nullptr;   // NVFP4: 16 codes (8 bytes) of one column
+  // ---- B.  bf16: waves 4h .. 4h+3 copy half h (gate / up, or the column
+  // halves); wave w, copy q: k rows 8 (w % 4) + 4q .. + 3; lane: row +
+  // lane / 16, slot lane % 16 <- global chunk slot ^ fb.  Columns past N
+  // copy column 0.
+  const int bh = wave >> 2;
+  i32x4_t brsrc = rsrc4(S.B0);
+  int boff[2] = {0, 0};
+  const uint32_t brow = uint32_t(S.ldb) * 2;  // bytes per k row
+  const uint8_t* fq = nullptr;  // NVFP4: codes and scales of LDS column tid / 2, k half tid % 2
   const uint8_t* fs = nullptr;
-  int fn = 0, fkq = 0;
+  const int fcol = tid >> 1, fkh = tid & 1;
   if (WF == W_BF16) {
-    const int nb = tg >> 3;        // 32 groups of 8 columns
-    bkb = (tg & 7) + 8 * grp_w;    // 16 groups of 4 k; the group's 8
-    bcol = nb * 8;
     const bf16_t* Bm = S.B0;
-    int ncol = n0 + nb * 8;
-    if (MODE == MODE_GATEUP && nb >= 16) {
-      Bm = S.B1;
-      ncol = n0 + (nb - 16) * 8;
+    int cbase = n0 + 128 * bh;
+    if (MODE == MODE_GATEUP) {
+      Bm = bh ? S.B1 : S.B0;
+      cbase = n0;
     }
-    // the matrix differs between the gate and up halves, which split at a
-    // wave boundary, so the base stays wave-uniform
-    brs = rsrc_of(uniform_ptr(Bm + grp * S.b_gstride));
-    boff = uint32_t(bkb * 4) * brow + uint32_t(ncol < N ? ncol : 0) * 2u;
+    brsrc = rsrc4(Bm + grp * S.b_gstride);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int k = 8 * (wave & 3) + 4 * q + (lane >> 4);
+      const int col = cbase + ((lane & 15) ^ fb(k)) * 8;
+      boff[q] = int(uint32_t(k) * brow + uint32_t(col < N ? col : 0) * 2u);
+    }
   } else {
-    fn = tg;                  // LDS column 0..255
-    fkq = grp_w;              // which 32-k half of the 64-k step
     const Fp4Mat* F = &S.F0;
-    int ncol = n0 + fn;
-    if (MODE == MODE_GATEUP && fn >= 128) {
+    int ncol = n0 + fcol;
+    if (MODE == MODE_GATEUP && fcol >= 128) {
       F = &S.F1;
-      ncol = n0 + fn - 128;
+      ncol = n0 + fcol - 128;
     }
     const long long NN = S.N;
     const long long col = ncol < N ? ncol : 0;
-    fq = F->q + (grp * NN + col) * (long long)(K / 2) + fkq * 16;
-    fs = F->scale + (grp * NN + col) * (long long)(K / 16) + fkq * 2;
+    fq = F->q + (grp * NN + col) * (long long)(K / 2) + fkh * 8;
+    fs = F->scale + (grp * NN + col) * (long long)(K / 16) + fkh;
   }
 
-  auto load_tile = [&](int k0, u32x4_t(&ra)[kALoads], u32x4_t(&rb)[4]) {
-#pragma unroll
-    for (int i = 0; i < kALoads; ++i) ra[i] = bload<u32x4_t, 0>(ars, aoff[i], uint32_t(k0) * 2u);
-    if (WF == W_BF16) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rb[r] = bload<u32x4_t, 0>(brs, boff + uint32_t(r) * brow, uint32_t(k0) * brow);
-    } else {
-      rb[0] = *reinterpret_cast<const u32x4_t*>(fq + k0 / 2);
-      rb[1] = u32x4_t{uint32_t(*reinterpret_cast<const uint16_t*>(fs + k0 / 16)), 0, 0, 0};
-    }
-  };
-
-  auto store_tile = [&](int buf, const u32x4_t(&ra)[kALoads], const u32x4_t(&rb)[4]) {
-    bf16_t* as = As(buf) + grp_w * 128 * LDSK;
-#pragma unroll
-    for (int i = 0; i < kALoads; ++i) {
-      const int c = tg + 256 * i;
-      *reinterpret_cast<u32x4_t*>(as + (c >> 3) * LDSK + (c & 7) * 8) = ra[i];
-    }
-    bf16_t* bs = Bs(buf);
-    if (WF == W_BF16) {
-      // rb[r] holds k = 4kb + r, columns bcol..bcol+7 (2 per dword)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t r0 = rb[0][d], r1 = rb[1][d], r2 = rb[2][d], r3 = rb[3][d];
-        const u32x2_t c0 = {perm_lo16(r0, r1), perm_lo16(r2, r3)};  // column 2d
-        const u32x2_t c1 = {perm_hi16(r0, r1), perm_hi16(r2, r3)};  // column 2d+1
-        *reinterpret_cast<u32x2_t*>(bs + (bcol + 2 * d) * LDSK + bkb * 4) = c0;
-        *reinterpret_cast<u32x2_t*>(bs + (bcol + 2 * d + 1) * LDSK + bkb * 4) = c1;
-      }
-    } else {
-      const uint32_t sc = rb[1][0];
-      const float s0v = e4m3_f32(sc & 0xFFu);
-      const float s1v = e4m3_f32((sc >> 8) & 0xFFu);
-      uint32_t outw[16];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t q = rb[0][d];  // 8 codes, k = 8d .. 8d+7 (low nibble first)
-        const float sv = d < 2 ? s0v : s1v;
-        // byte p: codes k = 8d+2p (low nibble), 8d+2p+1, decoded exactly by
-        // the gfx950 e2m1 pair conversion (unit scale); e2m1 x e4m3 is exact
-        // in bf16, so the top 16 bits of each product are kept
-        const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
-        const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
-        const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
-        const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
-        outw[d * 4 + 0] = perm_hi16(__float_as_uint(v0.x * sv), __float_as_uint(v0.y * sv));
-        outw[d * 4 + 1] = perm_hi16(__float_as_uint(v1.x * sv), __float_as_uint(v1.y * sv));
-        outw[d * 4 + 2] = perm_hi16(__float_as_uint(v2.x * sv), __float_as_uint(v2.y * sv));
-        outw[d * 4 + 3] = perm_hi16(__float_as_uint(v3.x * sv), __float_as_uint(v3.y * sv));
-      }
-      bf16_t* dst = bs + fn * LDSK + fkq * 32;
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        *reinterpret_cast<u32x4_t*>(dst + v * 8) =
-            u32x4_t{outw[4 * v], outw[4 * v + 1], outw[4 * v + 2], outw[4 * v + 3]};
-    }
-  };
-
-  f32x16_t acc[kWI][2];
-#pragma unroll
-  for (int i = 0; i < kWI; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // this wave's 32 x 32 blocks: rows 128 g + 32i (g = its group); columns (gate/up: gate
-  // and up at wn*32; else wn*64 + 32j)
-  const int kofs = (lane >> 5) * 8;
-  int arow_l[kWI], brow_l[2];
-#pragma unroll
-  for (int i = 0; i < kWI; ++i) arow_l[i] = (grp_w * kWI * 32 + i * 32 + (lane & 31)) * LDSK + kofs;
-  if (MODE == MODE_GATEUP) {
-    brow_l[0] = (wn * 32 + (lane & 31)) * LDSK + kofs;
-    brow_l[1] = (BN / 2 + wn * 32 + (lane & 31)) * LDSK + kofs;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) brow_l[j] = (wn * 64 + j * 32 + (lane & 31)) * LDSK + kofs;
-  }
-
-  // Row blocks of this wave inside the tile's rows (wave-uniform): the K
-  // loop is instantiated per count NI, so the ragged last M-tile of an
-  // expert costs only its valid blocks' MFMAs; a wave with no valid rows or
-  // no valid columns only moves tiles.  (Columns past N inside a valid wave
-  // are computed from column 0 and dropped.)
-  const int wrow0 = grp_w * kWI * 32;
-  const bool wcols = (MODE == MODE_GATEUP) ? n0 + wn * 32 < N : n0 + wn * 64 < N;
-  const int ni = wcols ? __builtin_amdgcn_readfirstlane(min(kWI, max(0, (rows - wrow0 + 31) / 32))) : 0;
-
-  // Fragments of sub-step kk + 1 are read from LDS while the MFMAs of kk run.
-  auto compute = [&](int buf, auto ni_c) {
-    constexpr int NI = decltype(ni_c)::value;
-    if (NI == 0) return;
-    const bf16_t* as = As(buf);
-    const bf16_t* bs = Bs(buf);
-    bf16x8_t a[2][kWI], b[2][2];
-    auto frags = [&](int kk, bf16x8_t(&af)[kWI], bf16x8_t(&bf)[2]) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(as + arow_l[i] + kk);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const bf16x8_t*>(bs + brow_l[j] + kk);
-    };
-    frags(0, a[0], b[0]);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      if (s + 1 < BK / 16) frags((s + 1) * 16, a[(s + 1) & 1], b[(s + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // K-steps of this tile's slice, ping-pong between the wave groups: each
-  // SIMD holds one wave of each group, and while one group runs the MFMAs
-  // of a k-step the other writes its half of a later k-step's tiles to LDS
-  // and issues its next global loads; a block barrier swaps the roles.
-  // Intervals (C = compute, M = write my half of step s to LDS buffer s%2,
-  // then load my half of step s+1 into registers):
-  //   group 0: C(0) | M(1) | C(1) | M(2) | ... | C(nk-1)
-  //   group 1: M(1) | C(0) | M(2) | C(1) | ... | M(nk) | C(nk-1)
-  // Step s is complete in its buffer before group 0 reads it (both halves
-  // are written in the two intervals before), and a buffer is rewritten
-  // only after both groups have read it.  Both groups pass 2 nk - 1
-  // barriers.  Memory phases past the last step only keep the count.
+  // K-stages of this tile's slice; stage indices past the last are clamped
+  // (their copies land in a buffer that is never read), so every stage
+  // issues the same number of memory instructions and the waits below are
+  // constants.
   const int nk_all = K / BK;
   const int kt0 = ks * nk_all / S.ksplit;
   const int nk = (ks + 1) * nk_all / S.ksplit - kt0;
-  u32x4_t ra[kALoads], rb[4];
-  // (sched_barrier: the staging registers hold one step at a time; the
-  // scheduler must not start the next loads before the stores have read them)
-  auto mem_phase = [&](int st) {  // write my half of step st, load my half of step st + 1
-    if (st < nk) {
-      store_tile(st & 1, ra, rb);
-      __builtin_amdgcn_sched_barrier(0);
-      if (st + 1 < nk) load_tile((kt0 + st + 1) * BK, ra, rb);
+
+  auto issue = [&](int st) {  // copies of stage st into LDS buffer st % kStages
+    const int kk = (kt0 + min(st, nk - 1)) * BK;
+    const uint32_t sbase_addr = lds_base + uint32_t((st & (kStages - 1)) * kStageBytes);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      copy_b128_to_lds(arsrc, sbase_addr + (32 * wave + 16 * q) * 64, aoff[q], kk * 2);
+    if (WF == W_BF16) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        copy_b128_to_lds(brsrc, sbase_addr + kOpBytes + bh * (kOpBytes / 2) + (8 * (wave & 3) + 4 * q) * 256,
+                         boff[q], int(uint32_t(kk) * brow));
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
-  auto kloop = [&](auto ni_c) {
-    load_tile(kt0 * BK, ra, rb);
-    store_tile(0, ra, rb);
-    __builtin_amdgcn_sched_barrier(0);
-    if (nk > 1) load_tile((kt0 + 1) * BK, ra, rb);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    if (grp_w == 0) {
-      for (int kt = 0; kt < nk; ++kt) {
-        compute(kt & 1, ni_c);
-        __syncthreads();
-        if (kt + 1 < nk) {
-          mem_phase(kt + 1);
-          __syncthreads();
-        }
-      }
+  // NVFP4: codes of a stage are loaded into registers two stages ahead and
+  // decoded into the LDS buffer when the stage is issued
+  auto fp4_load = [&](int st, u32x2_t& q, uint32_t& sc) {
+    const int kk = (kt0 + min(st, nk - 1)) * BK;
+    q = *reinterpret_cast<const u32x2_t*>(fq + kk / 2);
+    sc = *(fs + kk / 16);
+  };
+  auto fp4_store = [&](int st, const u32x2_t& q2, uint32_t sc) {
+    lds_u8* bs = lds3 + (st & (kStages - 1)) * kStageBytes + kOpBytes;
+    const float sv = e4m3_f32(sc & 0xFFu);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t q = q2[c];  // k = 16 fkh + 8c .. + 7, low nibble first
+      // byte p: codes k = 8c+2p (low nibble), 8c+2p+1, decoded exactly by
+      // the gfx950 e2m1 pair conversion (unit scale); e2m1 x e4m3 is exact
+      // in bf16, so the top 16 bits of each product are kept
+      const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+      const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+      const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+      const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+      const u32x4_t w = {perm_hi16(__float_as_uint(v0.x * sv), __float_as_uint(v0.y * sv)),
+                         perm_hi16(__float_as_uint(v1.x * sv), __float_as_uint(v1.y * sv)),
+                         perm_hi16(__float_as_uint(v2.x * sv), __float_as_uint(v2.y * sv)),
+                         perm_hi16(__float_as_uint(v3.x * sv), __float_as_uint(v3.y * sv))};
+      const int chunk = 2 * fkh + c;
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(bs + fcol * 64 + ((chunk ^ fa(fcol)) << 4)) = w;
+    }
+  };
+
+  // ---- fragment addresses of this wave's 32 x 32 blocks (bytes in a stage)
+  // A block i: rows wm*128 + 32i; lane row (lane & 31), k half lane / 32
+  const int hl = lane >> 5;
+  int afr[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = wm * 128 + 32 * i + (lane & 31);
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) afr[i][sb] = m * 64 + (((2 * sb + hl) ^ fa(m)) << 4);
+  }
+  // B block j: gate/up: gate (j = 0) and up (j = 1) columns wn*32; else
+  // columns wn*64 + 32j.  bf16 (transposing reads): 16-lane group g covers
+  // columns +16 (g % 2), k rows +8 (g / 2); lane i of the group names row
+  // i / 4, columns 4 (i % 4) .. + 3.  The sub-step and the second 4-row read
+  // are immediate offsets.
+  int bfr[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int gcol = (MODE == MODE_GATEUP) ? 128 * j + wn * 32 : wn * 64 + 32 * j;  // B-tile column 0..255
+    if (WF == W_BF16) {
+      const int h = gcol >> 7, lc = gcol & 127;
+      const int g = lane >> 4, i16 = lane & 15, qq = i16 & 3, mr = i16 >> 2;
+      const int colb = lc + 16 * (g & 1);
+      const int krow = 8 * (g >> 1) + mr;  // fb(krow + 16 s + 4 r) == fb(mr)
+      bfr[j][0] = kOpBytes + h * (kOpBytes / 2) + krow * 256 + ((((colb >> 3) + (qq >> 1)) ^ fb(mr)) << 4) +
+                  (qq & 1) * 8;
+      bfr[j][1] = 0;
     } else {
-      mem_phase(1);
-      __syncthreads();
-      for (int kt = 0; kt < nk; ++kt) {
-        compute(kt & 1, ni_c);
-        if (kt + 1 < nk) {
-          __syncthreads();
-          mem_phase(kt + 2);
-          __syncthreads();
-        }
-      }
+      const int n = gcol + (lane & 31);
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) bfr[j][sb] = kOpBytes + n * 64 + (((2 * sb + hl) ^ fa(n)) << 4);
     }
-  };
-  switch (ni) {
-    case 0: kloop(std::integral_constant<int, 0>{}); break;
-    case 1: kloop(std::integral_constant<int, 1>{}); break;
-    case 2: kloop(std::integral_constant<int, 2>{}); break;
-    case 3: kloop(std::integral_constant<int, 3>{}); break;
-    default: kloop(std::integral_constant<int, kWI>{}); break;
   }
 
-  // ---- epilogue: lane holds column (lane & 31); rows 8(r/4) + 4(lane/32) + r%4
+  // Row blocks of this wave inside the tile's rows (a prefix of the 4), and
+  // whether its columns are inside the matrix: both are wave-uniform, and
+  // each count runs its own straight-line path (same barriers in all), so
+  // the ragged last M-tile of an expert and the last N-tile cost only their
+  // valid part.
+  const int wcol0 = (MODE == MODE_GATEUP) ? n0 + wn * 32 : n0 + wn * 64;
+  int ni = (rows - wm * 128 + 31) / 32;
+  ni = ni < 0 ? 0 : (ni > 4 ? 4 : ni);
+  if (wcol0 >= N) ni = 0;
+  ni = __builtin_amdgcn_readfirstlane(ni);
+
   float ts0 = 1.f, ts1 = 1.f;
   if (WF == W_FP4) {
     ts0 = S.F0.tscale[grp];
     if (MODE == MODE_GATEUP) ts1 = S.F1.tscale[grp];
   }
-  if (MODE == MODE_PLAIN_F32) {  // router logits: fp32, written directly
-    if (!wcols) return;
+
+  auto run = [&](auto ni_c) {
+    constexpr int NI = decltype(ni_c)::value;
+    f32x16_t acc[4][2];
 #pragma unroll
-    for (int i = 0; i < kWI; ++i) {
-      if (i >= ni) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wrow0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= rows) continue;
-        const long long orow = (long long)(row0 + row) * S.ldc + ks * S.c_slice;
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Fragments of one stage (2 sub-steps of 16 k) for this wave's blocks.
+    struct Frags {
+      bf16x8_t a[2][4], b[2][2];
+    };
+    auto read_frags = [&](const lds_u8* sbase, Frags& f) {
+      if (NI == 0) return;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          f.a[sb][i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(sbase + afr[i][sb]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-          if (col < N) reinterpret_cast<float*>(S.C)[orow + col] = acc[i][j][r] * ts0;
+          if (WF == W_BF16) {
+            const lds_u8* p = sbase + bfr[j][0] + sb * 16 * 256;
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(p));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(p + 4 * 256));
+            const s16x4_t v[2] = {lo, hi};
+            f.b[sb][j] = __builtin_bit_cast(bf16x8_t, v);
+          } else {
+            f.b[sb][j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(sbase + bfr[j][sb]);
+          }
         }
       }
+    };
+    auto mfmas = [&](const Frags& f) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[sb][i], f.b[sb][j], acc[i][j], 0, 0, 0);
+    };
+
+    // Memory instructions per stage per lane: bf16 4 copies (A 2 + B 2);
+    // NVFP4 the code and scale loads of the stage two ahead, then 2 A copies.
+    constexpr int kPerStage = 4;
+    u32x2_t fcode[2];
+    uint32_t fscale[2];
+    if (WF == W_FP4) {
+      fp4_load(0, fcode[0], fscale[0]);
+      fp4_load(1, fcode[1], fscale[1]);
     }
-    return;
-  }
-  // bf16 outputs go through LDS so that the tile leaves in 16-byte stores.
-  // Neighbouring lanes swap values (DPP) so that each lane writes pairs of
-  // adjacent columns: even lanes rows r = 2q, odd lanes rows r = 2q + 1.
-  // Every wave passes both barriers (those without valid columns too).
-  constexpr int SP = OUTN * 2 + 16;  // staging row pitch (bytes)
-  __syncthreads();                   // every wave's last fragments are read
-  if (wcols) {
+    auto stage_in = [&](int st) {
+      if (WF == W_FP4) {
+        fp4_store(st, fcode[st & 1], fscale[st & 1]);
+        fp4_load(st + 2, fcode[st & 1], fscale[st & 1]);
+      }
+      issue(st);
+    };
+    // Software pipeline: iteration kt runs the MFMAs of stage kt from
+    // registers while the fragments of stage kt + 1 are read from LDS; the
+    // copies run four stages ahead (a stage's LDS buffer is refilled once
+    // every wave has read its fragments).
+    Frags fr[2];
+    stage_in(0);
+    stage_in(1);
+    stage_in(2);
+    stage_in(3);
+    wait_counts<3 * kPerStage, 0>();  // stage 0 landed (this wave's copies)
+    block_barrier();
+    read_frags(lds3, fr[0]);
+    // step kt: MFMAs of stage kt from `cur`, fragments of stage kt + 1 into `nxt`
+    auto step = [&](int kt, const Frags& cur, Frags& nxt) {
+      wait_counts<2 * kPerStage, 0>();  // stage kt + 1 landed; stage kt's fragments read
+      block_barrier();
+      stage_in(kt + 4);
+      read_frags(lds3 + ((kt + 1) & (kStages - 1)) * kStageBytes, nxt);
+      // keep the reads ahead of the MFMAs (the scheduler would otherwise sink
+      // them below and serialise LDS latency with the matrix work)
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(cur);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, fr[0], fr[1]);
+      step(kt + 1, fr[1], fr[0]);
+    }
+    if (kt < nk) step(kt, fr[0], fr[1]);
+    wait_counts<0, 0>();  // no copy may still be landing when LDS is reused
+
+    // ---- epilogue: lane holds column (lane & 31); rows 8(r/4) + 4(lane/32) + r%4
+    if (MODE == MODE_PLAIN_F32) {  // router logits: fp32, written directly
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row >= rows) continue;
+          const long long orow = (long long)(row0 + row) * S.ldc + ks * S.c_slice;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = wcol0 + 32 * j + (lane & 31);
+            if (col < N) reinterpret_cast<float*>(S.C)[orow + col] = acc[i][j][r] * ts0;
+          }
+        }
+      }
+      return;
+    }
+    // bf16 outputs go through LDS so that the tile leaves in 16-byte stores.
+    // Neighbouring lanes swap values (DPP) so that each lane writes pairs of
+    // adjacent columns: even lanes rows r = 2q, odd lanes rows r = 2q + 1.
+    block_barrier();  // every wave's last fragments are read and its copies landed
     const bool odd = lane & 1;
 #pragma unroll
-    for (int i = 0; i < kWI; ++i) {
-      if (i >= ni) continue;
+    for (int i = 0; i < NI; ++i) {
 #pragma unroll
       for (int j = 0; j < ((MODE == MODE_GATEUP) ? 1 : 2); ++j) {
         uint32_t vb[16];
@@ -433,22 +479,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
           const uint32_t send = odd ? vb[2 * q] : vb[2 * q + 1];
           const uint32_t recv = uint32_t(__builtin_amdgcn_mov_dpp(int(send), 0xB1, 0xF, 0xF, false));  // lane ^ 1
           const int r = 2 * q + (odd ? 1 : 0);
-          const int row = wrow0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const uint32_t packed = odd ? (recv | (vb[2 * q + 1] << 16)) : (vb[2 * q] | (recv << 16));
-          *reinterpret_cast<uint32_t*>(smem + row * SP + cpair * 2) = packed;
+          *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(lds3 + row * SP + cpair * 2) = packed;
         }
       }
     }
-  }
-  __syncthreads();
-  constexpr int CPR = OUTN / 8;  // 16-byte chunks per staged row
-  bf16_t* C = reinterpret_cast<bf16_t*>(S.C);
-  for (int c = tid; c < BM * CPR; c += kThreads) {
-    const int row = c / CPR, ch = c % CPR;
-    const int col = n0 + ch * 8;
-    if (row < rows && col < N)
-      *reinterpret_cast<u32x4_t*>(C + (long long)(row0 + row) * S.ldc + ks * S.c_slice + col) =
-          *reinterpret_cast<const u32x4_t*>(smem + row * SP + ch * 16);
+    __syncthreads();
+    constexpr int CPR = OUTN / 8;  // 16-byte chunks per staged row
+    bf16_t* C = reinterpret_cast<bf16_t*>(S.C);
+    for (int c = tid; c < BM * CPR; c += kThreads) {
+      const int row = c / CPR, ch = c % CPR;
+      const int col = n0 + ch * 8;
+      if (row < rows && col < N)
+        *reinterpret_cast<u32x4_t*>(C + (long long)(row0 + row) * S.ldc + ks * S.c_slice + col) =
+            *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(lds3 + row * SP + ch * 16);
+    }
+  };
+  switch (ni) {
+    case 4: run(std::integral_constant<int, 4>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    default: run(std::integral_constant<int, 0>{}); break;
   }
 }
 
