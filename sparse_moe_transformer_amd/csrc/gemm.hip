@@ -41,10 +41,10 @@
 // After the K loop the same LDS stages the bf16 output tile, which leaves
 // the block in 16-byte row stores.
 //
-// Block ids are remapped so that each XCD takes a contiguous run of the
-// tiles that exist (the N-tiles of one M-tile, then the next M-tile of the
-// same expert share its L2); the grid covers the worst-case tile list and
-// the surplus blocks exit at once.
+// Block ids are remapped so that each XCD takes an equal contiguous run of
+// each segment's tiles that exist (the N-tiles of one M-tile, then the next
+// M-tile of the same expert share its L2); the grid covers the worst-case
+// tile list and the surplus blocks exit at once.
 #include <type_traits>
 
 #include "common.h"
@@ -153,11 +153,23 @@ __device__ __forceinline__ int fb(int k) { return 4 * (k & 3); }
 template <int MODE, int WF>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0, int units_total) {
   // ---- logical tile of this block (XCD-aware remap over the real tiles) ----
-  const int total = s1.mtiles ? units0 + (*s1.n_mtiles) * s1.n_ntiles * s1.ksplit : units_total;
-  const int per = (total + kXcd - 1) / kXcd;
-  const int slot = blockIdx.x / kXcd;
-  const int u = (blockIdx.x % kXcd) * per + slot;
-  if (slot >= per || u >= total) return;
+  // Each segment is spread evenly over the XCDs on its own (its tiles can
+  // differ in K from the other segment's): XCD x takes a contiguous run of
+  // the host-sized segment's tiles, then a contiguous run of the grouped
+  // segment's tiles that exist (their count is read from the device list).
+  // The grid covers the worst case; surplus blocks exit at once.
+  const int n1 = s1.mtiles ? (*s1.n_mtiles) * s1.n_ntiles * s1.ksplit : units_total - units0;
+  const int p0 = (units0 + kXcd - 1) / kXcd, p1 = (n1 + kXcd - 1) / kXcd;
+  const int xcd = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
+  int u;
+  if (slot < p0) {
+    u = xcd * p0 + slot;
+    if (u >= units0) return;
+  } else {
+    const int j = xcd * p1 + (slot - p0);
+    if (slot - p0 >= p1 || j >= n1) return;
+    u = units0 + j;
+  }
   const bool second = u >= units0;
   const Seg& S = second ? s1 : s0;
   int uu = second ? u - units0 : u;
@@ -428,7 +440,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       // keep the reads ahead of the MFMAs (the scheduler would otherwise sink
       // them below and serialise LDS latency with the matrix work)
       __builtin_amdgcn_sched_barrier(0);
+      // while this wave feeds the matrix unit it takes issue priority over
+      // the SIMD's other wave, which is then reading fragments or copying
+      __builtin_amdgcn_s_setprio(1);
       mfmas(cur);
+      __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
     };
     int kt = 0;
@@ -516,7 +532,8 @@ template <int MODE, int WF>
 hipError_t launch(const Seg& a, const Seg& b, int units_a, int units_b, hipStream_t st) {
   const int total = units_a + units_b;
   if (total <= 0) return hipSuccess;
-  const int per = (total + kXcd - 1) / kXcd;
+  // slots per XCD: both segments' shares (the kernel's remap)
+  const int per = (units_a + kXcd - 1) / kXcd + (units_b + kXcd - 1) / kXcd;
   hipLaunchKernelGGL((k_gemm<MODE, WF>), dim3(per * kXcd), dim3(kThreads), 0, st, a, b, units_a, total);
   return hipGetLastError();
 }
