@@ -263,12 +263,14 @@ struct ExpertRows {
 __device__ ExpertRows expert_rows(const Shape& sh, const int32_t* __restrict__ topk, int ai, int* slot) {
   __shared__ unsigned long long mask[256];  // bit t: token t picked the expert
   __shared__ unsigned long long pres[4];    // bit e: expert e has tokens
+  __shared__ int tk[kStreamRows];           // topk_idx, read from global memory once
   const int tid = threadIdx.x, E = sh.E, k = sh.k, n = sh.T * sh.k;
   for (int i = tid; i < E; i += kThreads) mask[i] = 0;
   if (tid < 4) pres[tid] = 0;
   __syncthreads();
   for (int s = tid; s < n; s += kThreads) {
     const int e = topk[s];
+    tk[s] = e;
     atomicOr(&mask[e], 1ull << (s / k));
     atomicOr(&pres[e >> 6], 1ull << (e & 63));
   }
@@ -290,7 +292,7 @@ __device__ ExpertRows expert_rows(const Shape& sh, const int32_t* __restrict__ t
   if (tid < sh.T && ((m >> tid) & 1ull)) {
     int j = 0;
     for (int jj = 0; jj < k; ++jj)
-      if (topk[tid * k + jj] == e) j = jj;
+      if (tk[tid * k + jj] == e) j = jj;
     slot[__popcll(m & ((1ull << tid) - 1ull))] = tid * k + j;
   }
   __syncthreads();
