@@ -117,6 +117,24 @@ def test_ragged_tokens(torch, T, variant):
     full_check(s, x, w, bias, out, r, inter)
 
 
+# the 26B router shape (two tokens per router group at H = 2816, E = 128)
+# with narrow experts, so the oracle stays cheap
+ROUTE_WIDE = synth.FFNShape("routewide", 0, 2816, 128, 8, 64, 64)
+
+
+def test_alternating_token_counts_one_handle(torch):
+    """Forwards of different T on one handle, each checked in full.  The
+    router's arrival counters (one per group of two tokens here) must be
+    back at zero after every forward whatever the group count, and the
+    streaming (T <= 32) and MFMA variants share the workspace."""
+    ffn = ffn_for(ROUTE_WIDE.with_tokens(64), AUTO, max_tokens=64)
+    for i, T in enumerate([8, 64, 1, 33, 8, 17, 64, 3]):
+        st = ROUTE_WIDE.with_tokens(T)
+        x, w, bias = G.make_inputs(st, seed=100 + i)
+        out, r, inter, _ = run_gpu(torch, st, x, w, bias, AUTO, ffn=ffn)
+        full_check(st, x, w, bias, out, r, inter)
+
+
 @pytest.mark.parametrize("T", [40, 300])
 def test_mfma_router_and_bias(torch, T):
     """E = 128 takes the MFMA router tiles at T > 64; a logit bias shifts loads."""
