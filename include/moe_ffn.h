@@ -96,7 +96,9 @@ typedef struct {
   int32_t top_k;         /* k: 8 (1..min(E,16)) */
   int32_t expert_dim;    /* I: 704 (multiple of 64, at most 4096) */
   int32_t dense_dim;     /* D: 2112 (multiple of 64, at most 4096), or 0: no dense branch */
-  int32_t max_tokens;    /* largest T a forward on this handle may use (>= 1) */
+  int32_t max_tokens;    /* largest T a forward on this handle may use (>= 1);
+                            x [T, H], h [T*k, I] and h_d [T, D] in bf16 must each
+                            stay below 2 GiB at T = max_tokens */
   int32_t weight_format; /* MOE_FFN_W_BF16 or MOE_FFN_W_NVFP4 */
   uint32_t flags;        /* MOE_FFN_ACCUMULATE or 0 */
 } moe_ffn_config;

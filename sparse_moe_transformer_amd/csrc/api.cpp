@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <exception>
@@ -74,6 +75,12 @@ int validate_config(const moe_ffn_config* c) {
   if (c->weight_format != MOE_FFN_W_BF16 && c->weight_format != MOE_FFN_W_NVFP4)
     return fail(MOE_FFN_ERR_UNSUPPORTED, "unknown weight_format");
   if (c->flags & ~uint32_t(MOE_FFN_ACCUMULATE)) return fail(MOE_FFN_ERR_UNSUPPORTED, "unknown flag bits");
+  // the MFMA kernels address activation operands (x [T, H], h [T*k, I],
+  // h_d [T, D], bf16) with 32-bit byte offsets below 2^31
+  const long long widest = std::max({(long long)c->hidden, (long long)c->top_k * c->expert_dim,
+                                     (long long)c->dense_dim});
+  if ((long long)c->max_tokens * widest * 2 >= (1LL << 31))
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "max_tokens too large: an activation operand would reach 2 GiB");
   return MOE_FFN_OK;
 }
 

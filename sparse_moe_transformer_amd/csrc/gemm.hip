@@ -109,8 +109,13 @@ typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
+// A per-lane byte offset beyond every buffer resource's range (2^31 - 1
+// bytes); the uniform k-step offsets added to it (at most 32 MiB: K and a
+// B row are at most 4096 elements) cannot wrap it back into range.
+constexpr int kOutOfRange = int(0x80000000u);
+
 // Buffer resource of a wave-uniform base pointer (moved to scalar
-// registers), no stride, 2^31 bytes of range.
+// registers), no stride, 2^31 - 1 bytes of range.
 __device__ __forceinline__ i32x4_t rsrc4(const void* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   i32x4_t r;
@@ -206,7 +211,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
 
   // ---- A copies: wave w, copy q fills rows 32w + 16q .. + 15 of a stage;
   // lane: row 32w + 16q + lane / 4, slot lane % 4 <- global chunk slot ^ fa.
-  // Rows past the tile's end copy a valid row (their results are dropped).
+  // Lanes of rows past the tile's end get an offset beyond the resource's
+  // range (kOutOfRange):
+  // the copy returns zeros without touching memory, and every copy is still
+  // issued, so the wait counts below stay constants.  Those rows' results
+  // are dropped.
   const i32x4_t arsrc = rsrc4(S.A);
   int aoff[2];
 #pragma unroll
@@ -214,13 +223,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     const int r = 32 * wave + 16 * q + (lane >> 2);
     const int rr = r < rows ? r : 0;
     const uint32_t gr = S.gather ? uint32_t(S.gather[row0 + rr]) : uint32_t(row0 + rr);
-    aoff[q] = int((gr * uint32_t(S.lda) + uint32_t(((lane & 3) ^ fa(r)) * 8)) * 2u);
+    aoff[q] = r < rows ? int((gr * uint32_t(S.lda) + uint32_t(((lane & 3) ^ fa(r)) * 8)) * 2u) : kOutOfRange;
   }
 
   // ---- B.  bf16: waves 4h .. 4h+3 copy half h (gate / up, or the column
   // halves); wave w, copy q: k rows 8 (w % 4) + 4q .. + 3; lane: row +
   // lane / 16, slot lane % 16 <- global chunk slot ^ fb.  Columns past N
-  // copy column 0.
+  // are out of range, like A's rows past the tile.
   const int bh = wave >> 2;
   i32x4_t brsrc = rsrc4(S.B0);
   int boff[2] = {0, 0};
@@ -240,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     for (int q = 0; q < 2; ++q) {
       const int k = 8 * (wave & 3) + 4 * q + (lane >> 4);
       const int col = cbase + ((lane & 15) ^ fb(k)) * 8;
-      boff[q] = int(uint32_t(k) * brow + uint32_t(col < N ? col : 0) * 2u);
+      boff[q] = col < N ? int(uint32_t(k) * brow + uint32_t(col) * 2u) : kOutOfRange;
     }
   } else {
     const Fp4Mat* F = &S.F0;

@@ -76,6 +76,8 @@ def test_workspace_bytes_valid_config(lib):
     (dict(dense_dim=-64), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(dense_dim=100), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(max_tokens=0), binding.MOE_FFN_ERR_INVALID_ARG),
+    # 2^20 tokens: h [T*8, 704] bf16 would reach 11.8 GB (32-bit operand offsets)
+    (dict(max_tokens=1 << 20), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(weight_format=7), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(flags=2), binding.MOE_FFN_ERR_UNSUPPORTED),
 ])
@@ -85,6 +87,14 @@ def test_bad_configs_rejected(lib, kw, code):
     assert binding.moe_ffn_last_error() != ""
     rc, h = binding.moe_ffn_create(cfg(**kw))
     assert rc == code and not h
+
+
+def test_largest_addressable_token_count(lib):
+    # T*k*I*2 < 2^31 at the 26B shape: up to 190,650 tokens
+    rc, _ = binding.moe_ffn_workspace_bytes(cfg(max_tokens=190650))
+    assert rc == binding.MOE_FFN_OK
+    rc, _ = binding.moe_ffn_workspace_bytes(cfg(max_tokens=190651))
+    assert rc == binding.MOE_FFN_ERR_UNSUPPORTED
 
 
 def test_null_arguments(lib):
