@@ -65,6 +65,19 @@ def widen_bf16(bits) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def round_bf16(v) -> np.ndarray:
+    """Value -> the nearest bf16 value (ties to even), returned as fp64.
+
+    The value is first taken to fp32 (nearest), then its low 16 bits are
+    rounded away: a stored bf16 activation is decided in the precision the
+    kernels compute it in (fp32).  Finite inputs only.
+    """
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    b = f.view(np.uint32).astype(np.uint64)
+    b = (b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
 def gelu_tanh(v: np.ndarray) -> np.ndarray:
     """tanh approximation of GELU (Hendrycks & Gimpel 2016, eq. for GELU(x)
     ~ 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))))."""
@@ -273,6 +286,52 @@ def moe_ffn(x, router_w, w_gate, w_up, w_down, d_gate=None, d_up=None, d_down=No
     out += y_d
     res.update({"out": out, "h": h, "y": y, "h_d": h_d, "y_d": y_d})
     return res
+
+
+# ---------------------------------------------------------------------------
+# the sub-block with its sandwich norms
+# ---------------------------------------------------------------------------
+
+
+def rms_norm(v, scale, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: v / sqrt(mean(v^2) + eps) * scale.
+
+    archdb page "Gemma-4-26B-A4B", fields "Normalization layer type in the
+    blocks" (RMSNorm) and "Epsilon of the block normalization layers" (1e-06).
+    ``scale`` is the per-channel gain as applied (any offset a checkpoint
+    stores it with is the caller's).
+    """
+    V = np.asarray(v, dtype=np.float64)
+    return V / np.sqrt(np.mean(V * V, axis=-1, keepdims=True) + eps) * np.asarray(scale, dtype=np.float64)
+
+
+def moe_block(x, pre_scale, post_scale, eps: float, router_w, w_gate, w_up, w_down, d_gate=None,
+              d_up=None, d_down=None, top_k: int = 8, bias=None, force_routing=None, tokens=None) -> dict:
+    """The feed-forward sub-block with sandwich norms and the residual.
+
+    archdb field "Pre-norm, post-norm, or sandwich (pre and post)": sandwich;
+    API page gm.nn.Gemma4_26B_A4B ``use_post_ffw_norm=True``.  Reading taken
+    here (the pages show one norm before and one after the block, not one per
+    branch): a single pre-norm feeds the router, the experts and the dense
+    branch, a single post-norm acts on their sum, and the residual adds the
+    block input:
+
+        xn  = bf16(RMSNorm(x) * pre_scale)      (a stored bf16 activation)
+        out = x + RMSNorm(moe_ffn(xn)) * post_scale
+
+    Returns the moe_ffn details of xn plus ``xn``, ``ffn`` (the block's
+    pre-norm output rows) and ``out``; with ``tokens`` only those rows.
+    """
+    X = widen_bf16(x)
+    xn = round_bf16(rms_norm(X, pre_scale, eps))
+    r = moe_ffn(xn, router_w, w_gate, w_up, w_down, d_gate, d_up, d_down, top_k=top_k, bias=bias,
+                force_routing=force_routing, tokens=tokens, intermediates=tokens is None)
+    f = r["out"]
+    rows = X if tokens is None else X[np.asarray(tokens, dtype=np.int64)]
+    r["xn"] = xn
+    r["ffn"] = f
+    r["out"] = rows + rms_norm(f, post_scale, eps)
+    return r
 
 
 def moe_ffn_layer_residual(x, weights: dict, top_k: int, bias=None) -> tuple:

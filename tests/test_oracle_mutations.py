@@ -194,3 +194,70 @@ def test_e2m1_wrong_exponent_bias(monkeypatch, exp_bias):
     monkeypatch.setattr(on, "e2m1_value", bad)
     monkeypatch.setattr(oracle, "e2m1_value", bad)
     _expect_caught([pins.test_e2m1_decoder_matches_ocp_table])
+
+
+NORM_PINS = [pins.test_rms_norm_matches_torch_rms_norm,
+             pins.test_rms_norm_unit_rms_and_constant_rows]
+SANDWICH_PINS = [pins.test_block_with_zero_post_gain_is_identity,
+                 pins.test_block_prenorm_removes_input_scale,
+                 pins.test_block_is_norm_ffn_norm_residual_with_torch_norms]
+
+
+def test_rms_norm_sum_instead_of_mean(monkeypatch):
+    def bad(v, scale, eps):
+        V = np.asarray(v, dtype=np.float64)
+        return V / np.sqrt(np.sum(V * V, axis=-1, keepdims=True) + eps) * np.asarray(scale)
+
+    _patch(monkeypatch, "rms_norm", bad)
+    _expect_caught(NORM_PINS + SANDWICH_PINS)
+
+
+def test_rms_norm_dropped_eps(monkeypatch):
+    def bad(v, scale, eps):
+        V = np.asarray(v, dtype=np.float64)
+        return V / np.sqrt(np.mean(V * V, axis=-1, keepdims=True)) * np.asarray(scale)
+
+    _patch(monkeypatch, "rms_norm", bad)
+    _expect_caught(NORM_PINS)
+
+
+def test_bf16_truncation_instead_of_nearest(monkeypatch):
+    def bad(v):
+        f = np.asarray(v, dtype=np.float64).astype(np.float32)
+        b = f.view(np.uint32) & np.uint32(0xFFFF0000)
+        return b.view(np.float32).astype(np.float64)
+
+    _patch(monkeypatch, "round_bf16", bad)
+    _expect_caught([pins.test_round_bf16_matches_torch_cast] + SANDWICH_PINS)
+
+
+def test_post_norm_after_the_residual(monkeypatch):
+    real = om.moe_block
+
+    def bad(x, pre, post, eps, *a, **k):
+        r = real(x, pre, np.ones_like(np.asarray(post, dtype=np.float64)), eps, *a, **k)
+        X = om.widen_bf16(x)
+        rows = X if k.get("tokens") is None else X[np.asarray(k["tokens"], dtype=np.int64)]
+        r["out"] = om.rms_norm(rows + r["ffn"], post, eps)
+        return r
+
+    _patch(monkeypatch, "moe_block", bad)
+    _expect_caught(SANDWICH_PINS)
+
+
+def test_missing_pre_norm(monkeypatch):
+    real_round = om.round_bf16
+
+    def bad(x, pre, post, eps, router_w, w_gate, w_up, w_down, d_gate=None, d_up=None, d_down=None,
+            top_k=8, bias=None, force_routing=None, tokens=None):
+        X = om.widen_bf16(x)
+        xn = real_round(X)
+        r = om.moe_ffn(xn, router_w, w_gate, w_up, w_down, d_gate, d_up, d_down, top_k=top_k, bias=bias,
+                       force_routing=force_routing, tokens=tokens)
+        rows = X if tokens is None else X[np.asarray(tokens, dtype=np.int64)]
+        r["xn"], r["ffn"] = xn, r["out"]
+        r["out"] = rows + om.rms_norm(r["ffn"], post, eps)
+        return r
+
+    _patch(monkeypatch, "moe_block", bad)
+    _expect_caught(SANDWICH_PINS)

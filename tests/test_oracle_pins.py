@@ -337,6 +337,97 @@ def test_residual_layer_with_zero_down_is_identity():
     assert rel_err(y, ref.numpy()) < 1e-12
 
 
+# ---------------------------------------------------------------------------
+# sandwich norms and the residual (the block with its RMSNorms)
+# ---------------------------------------------------------------------------
+
+
+def test_rms_norm_matches_torch_rms_norm():
+    """Pin: oracle.rms_norm against torch.nn.functional.rms_norm (a library
+    routine) on random rows, random gains, two epsilons."""
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((9, 64)) * 3.0
+    g = rng.standard_normal(64)
+    for eps in (1e-6, 0.5):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(X), (64,), weight=torch.from_numpy(g), eps=eps)
+        assert rel_err(oracle.rms_norm(X, g, eps), ref.numpy()) < 1e-12
+
+
+def test_rms_norm_unit_rms_and_constant_rows():
+    """Pins: with eps = 0 and unit gain every row has mean square exactly 1
+    (up to rounding); a constant row c maps to c / sqrt(c^2 + eps) * g."""
+    rng = np.random.default_rng(8)
+    X = rng.standard_normal((5, 96)) * rng.uniform(0.01, 100.0, (5, 1))
+    y = oracle.rms_norm(X, np.ones(96), 0.0)
+    assert np.max(np.abs(np.mean(y * y, axis=1) - 1.0)) < 1e-12
+    c, eps, g = -0.75, 1e-6, rng.standard_normal(96)
+    y = oracle.rms_norm(np.full((1, 96), c), g, eps)
+    assert rel_err(y[0], c / np.sqrt(c * c + eps) * g) < 1e-14
+
+
+def test_round_bf16_matches_torch_cast():
+    """Pin: oracle.round_bf16 against torch's float32 -> bfloat16 cast (round
+    to nearest even), on random values and on exact halfway cases."""
+    rng = np.random.default_rng(9)
+    v = (rng.standard_normal(4096) * np.exp(rng.uniform(-20, 20, 4096))).astype(np.float32)
+    half = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(2.0 + 2.0 ** -7), 3.0 + 2.0 ** -7],
+                    dtype=np.float32)  # exactly between two bf16 values
+    for a in (v, half):
+        ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+        assert np.array_equal(oracle.round_bf16(a), ref)
+    assert list(oracle.round_bf16(half)) == [1.0, 1.015625, -2.0, 3.0]
+
+
+def block(shape, x, w, pre, post, eps, **kw):
+    return oracle.moe_block(x, pre, post, eps, w["router"], w["gate"], w["up"], w["down"], w["dgate"],
+                            w["dup"], w["ddown"], top_k=shape.top_k, **kw)
+
+
+def test_block_with_zero_post_gain_is_identity():
+    """Pin of the residual: with a zero post-norm gain the sub-block adds
+    exactly 0, so it returns its input."""
+    shape, x, w = tiny_inputs()
+    g = np.random.default_rng(1).standard_normal(shape.hidden)
+    r = block(shape, x, w, g, np.zeros(shape.hidden), 1e-6)
+    assert np.array_equal(r["out"], oracle.widen_bf16(x))
+
+
+def test_block_prenorm_removes_input_scale():
+    """Pin: with eps = 0 the pre-norm makes the FFN blind to a power-of-two
+    scale of x (doubling is exact in binary floating point, so xn and the FFN
+    output are bit-identical); the block output then differs from the
+    unscaled one only by the change of the residual."""
+    shape, x, w = tiny_inputs()
+    rng = np.random.default_rng(2)
+    pre, post = rng.standard_normal(shape.hidden), rng.standard_normal(shape.hidden)
+    X = oracle.widen_bf16(x)
+    r1 = block(shape, X, w, pre, post, 0.0)
+    r2 = block(shape, 4.0 * X, w, pre, post, 0.0)
+    assert np.array_equal(r1["xn"], r2["xn"])
+    assert np.array_equal(r1["ffn"], r2["ffn"])
+    assert rel_err(r2["out"] - 4.0 * X, r1["out"] - X) < 1e-12
+
+
+def test_block_is_norm_ffn_norm_residual_with_torch_norms():
+    """Pin of the composition: pre-norm and post-norm taken from
+    torch.nn.functional.rms_norm, the bf16 store from torch's cast, the FFN
+    from oracle.moe_ffn (pinned above); sampled-token mode agrees too."""
+    shape, x, w = tiny_inputs()
+    rng = np.random.default_rng(3)
+    pre, post, eps = rng.standard_normal(shape.hidden), rng.standard_normal(shape.hidden), 1e-6
+    X = torch.from_numpy(oracle.widen_bf16(x))
+    xn = torch.nn.functional.rms_norm(X, (shape.hidden,), weight=torch.from_numpy(pre), eps=eps)
+    xn = xn.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    f = run(shape, xn.numpy(), w)["out"]
+    ref = X + torch.nn.functional.rms_norm(torch.from_numpy(f), (shape.hidden,), weight=torch.from_numpy(post),
+                                           eps=eps)
+    r = block(shape, x, w, pre, post, eps)
+    assert rel_err(r["out"], ref.numpy()) < 1e-12
+    toks = [2, 17, 30]
+    rs = block(shape, x, w, pre, post, eps, tokens=toks)
+    assert rel_err(rs["out"], r["out"][toks]) < 1e-12
+
+
 def test_force_routing_reproduces_own_routing():
     shape, x, w = tiny_inputs()
     r = run(shape, x, w)
