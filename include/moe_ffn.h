@@ -146,6 +146,27 @@ int moe_ffn_forward_nvfp4(moe_ffn_handle *h, int32_t T, const void *x, const voi
                           const moe_ffn_nvfp4_t *d_gate, const moe_ffn_nvfp4_t *d_up,
                           const moe_ffn_nvfp4_t *d_down, void *out, void *stream);
 
+/* The feed-forward sub-block of a layer with its sandwich norms and the
+ * residual (archdb page "Gemma-4-26B-A4B": normalization RMSNorm, placement
+ * sandwich (pre and post), epsilon 1e-06; API page gm.nn.Gemma4_26B_A4B
+ * use_post_ffw_norm=True), bf16 weights:
+ *   xn  = bf16(RMSNorm(x) * pre_scale)            RMSNorm(v) = v / sqrt(mean(v^2) + eps)
+ *   out = x + RMSNorm(block(xn)) * post_scale     block = the forward above
+ * One pre-norm feeds the router, the experts and the dense branch; one
+ * post-norm acts on their sum (the pages show one norm on each side of the
+ * block).  pre_scale, post_scale: [H] fp32 device gains as applied (a
+ * checkpoint's stored offset, if any, is the caller's), 16-byte aligned.
+ * eps finite and >= 0 (the pages' value is 1e-6).  out may be x (in place);
+ * otherwise they must not overlap.  The handle must not carry
+ * MOE_FFN_ACCUMULATE (the sub-block adds its own residual: UNSUPPORTED).
+ * Routing and intermediates of the call describe block(xn).  The pre-norm
+ * is timed with MOE_FFN_STAGE_ROUTE, the post-norm with the combine. */
+int moe_ffn_forward_block(moe_ffn_handle *h, int32_t T, const void *x, const float *pre_scale,
+                          const float *post_scale, float eps, const void *router_w,
+                          const float *router_bias, const void *w_gate, const void *w_up,
+                          const void *w_down, const void *d_gate, const void *d_up,
+                          const void *d_down, void *out, void *stream);
+
 /* Device-to-device copies of the routing of the last forward (or of the
  * last moe_ffn_align_only) into caller buffers; any destination may be NULL.
  *   topk_idx [T, k] int32 (ascending expert id per token), topk_w [T, k]

@@ -66,6 +66,16 @@ class MoeFFN:
                                       _ptr(out), _stream()))
         return out
 
+    def forward_block(self, x, w, pre_scale, post_scale, out, eps=1e-6, bias=None):
+        """The sub-block with sandwich norms: out = x + RMSNorm(FFN(bf16(RMSNorm(x) * pre))) * post.
+        pre_scale/post_scale: [H] fp32 tensors; out may be x."""
+        T = x.shape[0]
+        check(binding.moe_ffn_forward_block(self.h, T, _ptr(x), _ptr(pre_scale), _ptr(post_scale), float(eps),
+                                            _ptr(w["router"]), _ptr(bias), _ptr(w["gate"]), _ptr(w["up"]),
+                                            _ptr(w["down"]), _ptr(w.get("dgate")), _ptr(w.get("dup")),
+                                            _ptr(w.get("ddown")), _ptr(out), _stream()))
+        return out
+
     def forward_nvfp4(self, x, w, out, bias=None):
         """w: router bf16 tensor; gate/up/down/dgate/dup/ddown dicts of q, scale, tensor_scale."""
         def d(m):

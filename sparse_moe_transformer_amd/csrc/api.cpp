@@ -86,7 +86,7 @@ int validate_config(const moe_ffn_config* c) {
 
 // Workspace layout: every buffer 256-byte aligned.
 struct Layout {
-  size_t off[20];
+  size_t off[21];
   size_t total;
   int max_mtiles;
 };
@@ -97,7 +97,7 @@ Layout layout(const moe_ffn_config& c) {
   const size_t nb = (T + 63) / 64;
   Layout L{};
   L.max_mtiles = int((T * k + moe::kGemmBM - 1) / moe::kGemmBM + E);
-  const size_t sizes[20] = {
+  const size_t sizes[21] = {
       size_t(moe::kRouterSlices) * T * E * 4,     // logits (K-slices)
       size_t(moe::kRouteSlices) * 64 * E * 4,     // route_part (K-slices, T <= 64)
       T * k * 4,                                  // topk_idx
@@ -119,9 +119,10 @@ Layout layout(const moe_ffn_config& c) {
        size_t(moe::kDenseKS) * moe::kRouteSmallT * (D ? D : 1)) * 2 * 4,
       size_t(moe::kDenseDownKS) * moe::kRouteSmallT * H * 4,  // streaming dense down partials
       size_t(moe::kArriveInts) * 4,               // arrival counters (zero between forwards)
+      T * H * 2,                                  // xn: pre-normed input (sandwich-norm forwards)
   };
   size_t o = 0;
-  for (int i = 0; i < 20; ++i) {
+  for (int i = 0; i < 21; ++i) {
     L.off[i] = o;
     o += (sizes[i] + 255) & ~size_t(255);
   }
@@ -152,6 +153,7 @@ moe::Workspace bind(void* base, const Layout& L) {
   w.part = reinterpret_cast<float*>(b + L.off[17]);
   w.ydp = reinterpret_cast<float*>(b + L.off[18]);
   w.arrive = reinterpret_cast<int32_t*>(b + L.off[19]);
+  w.xn = reinterpret_cast<moe::bf16_t*>(b + L.off[20]);
   return w;
 }
 
@@ -214,13 +216,22 @@ struct StageTimer {
   }
 };
 
+// Sandwich norms of a sub-block forward (null: the plain block)
+struct Norms {
+  const float* pre;
+  const float* post;
+  float eps;
+};
+
 int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, const float* bias,
-                const moe::StreamArgs& args, void* out, hipStream_t s) {
+                const moe::StreamArgs& args_in, void* out, hipStream_t s, const Norms* nm = nullptr) {
+  moe::StreamArgs args = args_in;
   const moe::Shape sh = args.sh;
   const moe::Workspace& ws = h->ws;
   const bool timing = h->prof_mask != 0 && h->prof_fwd < h->prof_max;
   hipError_t e;
-  const auto* xb = static_cast<const moe::bf16_t*>(x);
+  const auto* xres = static_cast<const moe::bf16_t*>(x);  // the block input (the residual)
+  const moe::bf16_t* xb = xres;                           // what the router and the experts read
   const auto* wr = static_cast<const moe::bf16_t*>(router_w);
   bool stream = (h->variant == MOE_FFN_VARIANT_STREAM) ||
                 (h->variant == MOE_FFN_VARIANT_AUTO && T <= kStreamMaxTokens);
@@ -230,6 +241,13 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   {
     // streaming: the router and the dense branch's gate/up share one launch
     StageTimer tm(h, MOE_FFN_STAGE_ROUTE, s, timing);
+    if (nm) {
+      // the pre-norm (timed with the router): everything below reads xn
+      e = moe::launch_rmsnorm(sh, xres, nm->pre, nm->eps, ws.xn, s);
+      if (e != hipSuccess) return hip_fail(e, "pre-norm");
+      xb = ws.xn;
+      args.x = ws.xn;
+    }
     e = stream ? moe::launch_route_dense(args, wr, bias, ws, s)
         : (T <= moe::kRouteSmallT) ? moe::launch_route_small(sh, xb, wr, bias, ws, s)
                                    : moe::launch_route_large(sh, xb, wr, bias, ws, s);
@@ -264,8 +282,11 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   }
   {
     StageTimer tm(h, MOE_FFN_STAGE_COMBINE, s, timing);
-    e = moe::launch_combine(sh, ws, static_cast<moe::bf16_t*>(out), (h->cfg.flags & MOE_FFN_ACCUMULATE) != 0,
-                            stream && sh.D > 0 ? moe::dense_down_slices(sh) : 0, stream, s);
+    const int yd_slices = stream && sh.D > 0 ? moe::dense_down_slices(sh) : 0;
+    e = nm ? moe::launch_combine_norm(sh, ws, xres, nm->post, nm->eps, static_cast<moe::bf16_t*>(out), yd_slices,
+                                      stream, s)
+           : moe::launch_combine(sh, ws, static_cast<moe::bf16_t*>(out), (h->cfg.flags & MOE_FFN_ACCUMULATE) != 0,
+                                 yd_slices, stream, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "combine");
   }
@@ -321,6 +342,36 @@ int check_fp4(const moe_ffn_nvfp4_t* m, bool required, const char* name) {
 moe::Fp4Mat to_mat(const moe_ffn_nvfp4_t* m) {
   if (!m) return moe::Fp4Mat{nullptr, nullptr, nullptr};
   return moe::Fp4Mat{m->q, m->scale, m->tensor_scale};
+}
+
+int bf16_weight_checks(const moe_ffn_handle* h, const void* w_gate, const void* w_up, const void* w_down,
+                       const void* d_gate, const void* d_up, const void* d_down) {
+  if (!w_gate || !w_up || !w_down) return fail(MOE_FFN_ERR_INVALID_ARG, "expert weights must not be NULL");
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down))
+    return fail(MOE_FFN_ERR_INVALID_ARG, "expert weights must be 16-byte aligned");
+  if (h->cfg.dense_dim > 0) {
+    if (!d_gate || !d_up || !d_down) return fail(MOE_FFN_ERR_INVALID_ARG, "dense weights must not be NULL");
+    if (!aligned16(d_gate) || !aligned16(d_up) || !aligned16(d_down))
+      return fail(MOE_FFN_ERR_INVALID_ARG, "dense weights must be 16-byte aligned");
+  } else if (d_gate || d_up || d_down) {
+    return fail(MOE_FFN_ERR_INVALID_ARG, "dense weights must be NULL when dense_dim == 0");
+  }
+  return MOE_FFN_OK;
+}
+
+moe::StreamArgs bf16_args(const moe_ffn_handle* h, int T, const void* x, const void* w_gate, const void* w_up,
+                          const void* w_down, const void* d_gate, const void* d_up, const void* d_down) {
+  moe::StreamArgs a{};
+  a.sh = shape_of(h, T);
+  a.x = static_cast<const moe::bf16_t*>(x);
+  a.wg = static_cast<const moe::bf16_t*>(w_gate);
+  a.wu = static_cast<const moe::bf16_t*>(w_up);
+  a.wd = static_cast<const moe::bf16_t*>(w_down);
+  a.dg = static_cast<const moe::bf16_t*>(d_gate);
+  a.du = static_cast<const moe::bf16_t*>(d_up);
+  a.dd = static_cast<const moe::bf16_t*>(d_down);
+  a.nvfp4 = false;
+  return a;
 }
 
 }  // namespace
@@ -414,34 +465,51 @@ int moe_ffn_forward(moe_ffn_handle* h, int32_t T, const void* x, const void* rou
                     const void* d_gate, const void* d_up, const void* d_down, void* out, void* stream) {
   try {
     if (int r = common_forward_checks(h, T, x, router_w, router_bias, out, MOE_FFN_W_BF16)) return r;
-    if (!w_gate || !w_up || !w_down) return fail(MOE_FFN_ERR_INVALID_ARG, "expert weights must not be NULL");
-    if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down))
-      return fail(MOE_FFN_ERR_INVALID_ARG, "expert weights must be 16-byte aligned");
-    const bool dense = h->cfg.dense_dim > 0;
-    if (dense) {
-      if (!d_gate || !d_up || !d_down) return fail(MOE_FFN_ERR_INVALID_ARG, "dense weights must not be NULL");
-      if (!aligned16(d_gate) || !aligned16(d_up) || !aligned16(d_down))
-        return fail(MOE_FFN_ERR_INVALID_ARG, "dense weights must be 16-byte aligned");
-    } else if (d_gate || d_up || d_down) {
-      return fail(MOE_FFN_ERR_INVALID_ARG, "dense weights must be NULL when dense_dim == 0");
-    }
+    if (int r = bf16_weight_checks(h, w_gate, w_up, w_down, d_gate, d_up, d_down)) return r;
     if (T == 0) {
       g_err.clear();
       return MOE_FFN_OK;
     }
     DeviceGuard g(h->device);
     if (!g.ok) return fail(MOE_FFN_ERR_HIP, "cannot make the handle's device current");
-    moe::StreamArgs a{};
-    a.sh = shape_of(h, T);
-    a.x = static_cast<const moe::bf16_t*>(x);
-    a.wg = static_cast<const moe::bf16_t*>(w_gate);
-    a.wu = static_cast<const moe::bf16_t*>(w_up);
-    a.wd = static_cast<const moe::bf16_t*>(w_down);
-    a.dg = static_cast<const moe::bf16_t*>(d_gate);
-    a.du = static_cast<const moe::bf16_t*>(d_up);
-    a.dd = static_cast<const moe::bf16_t*>(d_down);
-    a.nvfp4 = false;
+    const moe::StreamArgs a = bf16_args(h, T, x, w_gate, w_up, w_down, d_gate, d_up, d_down);
     return run_forward(h, T, x, router_w, router_bias, a, out, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return fail(MOE_FFN_ERR_HIP, ex.what());
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_forward_block(moe_ffn_handle* h, int32_t T, const void* x, const float* pre_scale,
+                          const float* post_scale, float eps, const void* router_w, const float* router_bias,
+                          const void* w_gate, const void* w_up, const void* w_down, const void* d_gate,
+                          const void* d_up, const void* d_down, void* out, void* stream) {
+  try {
+    if (int r = check_handle(h)) return r;
+    if (h->cfg.weight_format != MOE_FFN_W_BF16)
+      return fail(MOE_FFN_ERR_UNSUPPORTED, "weight format of the handle does not match this entry point");
+    if (h->cfg.flags & MOE_FFN_ACCUMULATE)
+      return fail(MOE_FFN_ERR_UNSUPPORTED,
+                  "the sub-block adds its own residual: use a handle without MOE_FFN_ACCUMULATE");
+    if (T < 0 || T > h->cfg.max_tokens) return fail(MOE_FFN_ERR_INVALID_ARG, "T must be in [0, max_tokens]");
+    if (!x || !router_w || !out || !pre_scale || !post_scale)
+      return fail(MOE_FFN_ERR_INVALID_ARG, "x, router_w, out, pre_scale and post_scale must not be NULL");
+    if (!aligned16(x) || !aligned16(router_w) || !aligned16(out) || !aligned16(pre_scale) || !aligned16(post_scale))
+      return fail(MOE_FFN_ERR_INVALID_ARG, "x, router_w, out, pre_scale and post_scale must be 16-byte aligned");
+    if (router_bias && (reinterpret_cast<uintptr_t>(router_bias) & 3u))
+      return fail(MOE_FFN_ERR_INVALID_ARG, "router_bias must be 4-byte aligned");
+    if (!(eps >= 0.f) || !(eps < 1e30f)) return fail(MOE_FFN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (int r = bf16_weight_checks(h, w_gate, w_up, w_down, d_gate, d_up, d_down)) return r;
+    if (T == 0) {
+      g_err.clear();
+      return MOE_FFN_OK;
+    }
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(MOE_FFN_ERR_HIP, "cannot make the handle's device current");
+    const moe::StreamArgs a = bf16_args(h, T, x, w_gate, w_up, w_down, d_gate, d_up, d_down);
+    const Norms nm{pre_scale, post_scale, eps};
+    return run_forward(h, T, x, router_w, router_bias, a, out, static_cast<hipStream_t>(stream), &nm);
   } catch (const std::exception& ex) {
     return fail(MOE_FFN_ERR_HIP, ex.what());
   } catch (...) {

@@ -68,6 +68,7 @@ struct Workspace {
   float* part;          // [kStreamKS][kStreamRows][2][I] (rows = slots) + [kDenseKS][64][2][D]
                         // (rows = tokens) gate/up partials of the streaming path
   float* ydp;           // [kDenseDownKS][64][H] dense down partials (streaming path)
+  bf16_t* xn;           // [Tmax, H] pre-normed block input (sandwich-norm forwards)
   int32_t* arrive;      // [kArriveInts] arrival counters of the last-block hand-offs; every
                         // kernel that counts leaves them at zero (zeroed at create)
 };
@@ -160,6 +161,11 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
 // ws.ydp, summed in order (and stored to ws.y_d as bf16).  slot_rows: the
 // expert rows of token t are ws.y rows t*k .. t*k+k-1 (streaming path);
 // else rows ws.pos[t*k + j] (grouped order).
+// sandwich norms: xn = bf16(RMSNorm(x) * pre); out = resid + RMSNorm(block) * post
+hipError_t launch_rmsnorm(const Shape& sh, const bf16_t* x, const float* pre, float eps, bf16_t* xn,
+                          hipStream_t s);
+hipError_t launch_combine_norm(const Shape& sh, const Workspace& ws, const bf16_t* resid, const float* post,
+                               float eps, bf16_t* out, int yd_slices, bool slot_rows, hipStream_t s);
 hipError_t launch_combine(const Shape& sh, const Workspace& ws, bf16_t* out, bool accumulate, int yd_slices,
                           bool slot_rows, hipStream_t s);
 

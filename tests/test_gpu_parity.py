@@ -380,3 +380,125 @@ def test_validation_with_handle(torch):
     assert B.moe_ffn_set_variant(ffn.h, 9) == B.MOE_FFN_ERR_INVALID_ARG
     assert B.moe_ffn_forward(ffn.h, 16, xd.data_ptr(), *args, out.data_ptr(), st) == B.MOE_FFN_OK
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# the sub-block with its sandwich norms and the residual
+# ---------------------------------------------------------------------------
+
+
+def norm_gains(H, seed=0):
+    """Seeded per-channel gains around 1 for the pre- and post-norm."""
+    rng = np.random.default_rng(1000 + seed)
+    return ((1.0 + 0.2 * rng.standard_normal(H)).astype(np.float32),
+            (1.0 + 0.2 * rng.standard_normal(H)).astype(np.float32))
+
+
+def run_block(torch, shape, x, w, pre, post, eps, variant, in_place=False, ffn=None):
+    T = x.shape[0]
+    ffn = ffn or ffn_for(shape, variant, max_tokens=T)
+    xd = G.up_bf16(x)
+    out = xd if in_place else torch.empty_like(xd)
+    ffn.forward_block(xd, G.up_weights(w), G.up(pre), G.up(post), out, eps=eps)
+    torch.cuda.synchronize()
+    r = {k: G.to_np(v) for k, v in ffn.routing(T).items()}
+    return G.to_f64(out), r
+
+
+# The pre-normed input is a stored bf16 activation.  Both sides decide its
+# rounding in fp32, but their fp32 operation orders differ (the hardware
+# reciprocal square root, the order of the two products), so a handful of
+# elements per thousand tokens land one bf16 step apart.  One step moves a
+# router logit by ~3e-4 (below the 1e-3 near-tie gap, so the sets stay
+# bit-exact) and a routing weight by up to ~1e-4: the weights are compared
+# to 1e-3 here instead of 1e-5.
+BLOCK_W_TOL = 1e-3
+
+
+def block_check(shape, x, w, pre, post, eps, out, r, tokens=None):
+    """Routing of the pre-normed input and the block output against
+    oracle.moe_block (every row, or the rows `tokens`)."""
+    args = (x, pre, post, eps, w["router"], w["gate"], w["up"], w["down"], w.get("dgate"), w.get("dup"),
+            w.get("ddown"))
+    ref = oracle.moe_block(*args, top_k=shape.top_k, tokens=tokens)
+    near = G.check_routing(r["topk_idx"], r["topk_w"], ref, w_tol=BLOCK_W_TOL)
+    G.check_align(r, r["topk_idx"], shape.experts)
+    if near.any() and not np.array_equal(r["topk_idx"], ref["topk_idx"]):
+        ref = oracle.moe_block(*args, top_k=shape.top_k, tokens=tokens, force_routing=r["topk_idx"])
+    G.assert_block_close(out if tokens is None else out[tokens], ref["out"])
+    return int(near.sum())
+
+
+@pytest.mark.parametrize("variant", [AUTO, STREAM, MFMA])
+def test_block_tiny(torch, variant):
+    s = synth.TINY
+    x, w, _ = G.make_inputs(s)
+    pre, post = norm_gains(s.hidden)
+    out, r = run_block(torch, s, x, w, pre, post, 1e-6, variant)
+    block_check(s, x, w, pre, post, 1e-6, out, r)
+
+
+@pytest.mark.parametrize("T", [1, 33, 200])
+def test_block_ragged(torch, T):
+    s = MID.with_tokens(T)
+    x, w, _ = G.make_inputs(s, seed=T)
+    pre, post = norm_gains(s.hidden, seed=T)
+    out, r = run_block(torch, s, x, w, pre, post, 1e-6, AUTO)
+    block_check(s, x, w, pre, post, 1e-6, out, r)
+
+
+def test_block_decode_26b(torch, w26):
+    s = synth.DECODE
+    x = synth.make_x(s)
+    pre, post = norm_gains(s.hidden)
+    out, r = run_block(torch, s, x, w26, pre, post, 1e-6, AUTO)
+    near = block_check(s, x, w26, pre, post, 1e-6, out, r)
+    print(f"block decode near-ties: {near}")
+
+
+def test_block_prefill_26b_sampled(torch, w26):
+    s = synth.PREFILL
+    x = synth.make_x(s)
+    pre, post = norm_gains(s.hidden, seed=1)
+    out, r = run_block(torch, s, x, w26, pre, post, 1e-6, AUTO)
+    near = block_check(s, x, w26, pre, post, 1e-6, out, r, tokens=sample_tokens(s.tokens))
+    print(f"block prefill near-ties: {near}")
+
+
+@pytest.mark.parametrize("variant", [STREAM, MFMA])
+def test_block_in_place(torch, variant):
+    """out = x: the residual stream updated in place."""
+    s = MID.with_tokens(16)
+    x, w, _ = G.make_inputs(s, seed=5)
+    pre, post = norm_gains(s.hidden, seed=5)
+    out, r = run_block(torch, s, x, w, pre, post, 1e-6, variant, in_place=True)
+    block_check(s, x, w, pre, post, 1e-6, out, r)
+
+
+def test_block_validation(torch):
+    from sparse_moe_transformer_amd import binding as B
+    from sparse_moe_transformer_amd import MoeFFN
+    s = MID.with_tokens(16)
+    x, w, _ = G.make_inputs(s)
+    xd, wd = G.up_bf16(x), G.up_weights(w)
+    pre, post = (G.up(g) for g in norm_gains(s.hidden))
+    out = torch.empty_like(xd)
+    p = {k: v.data_ptr() for k, v in wd.items()}
+    wargs = [p["gate"], p["up"], p["down"], p["dgate"], p["dup"], p["ddown"]]
+    st = torch.cuda.current_stream().cuda_stream
+    ffn = MoeFFN.for_shape(s)
+
+    def call(h, T=16, xp=xd.data_ptr(), pp=pre.data_ptr(), qp=post.data_ptr(), eps=1e-6, op=out.data_ptr()):
+        return B.moe_ffn_forward_block(h, T, xp, pp, qp, eps, p["router"], None, *wargs, op, st)
+
+    assert call(ffn.h) == B.MOE_FFN_OK
+    assert call(ffn.h, T=0) == B.MOE_FFN_OK
+    assert call(ffn.h, T=17) == B.MOE_FFN_ERR_INVALID_ARG
+    assert call(ffn.h, pp=None) == B.MOE_FFN_ERR_INVALID_ARG
+    assert call(ffn.h, qp=post.data_ptr() + 4) == B.MOE_FFN_ERR_INVALID_ARG
+    assert call(ffn.h, eps=-1.0) == B.MOE_FFN_ERR_INVALID_ARG
+    assert call(ffn.h, eps=float("nan")) == B.MOE_FFN_ERR_INVALID_ARG
+    assert call(ffn.h, op=xd.data_ptr()) == B.MOE_FFN_OK  # in place is allowed
+    acc = MoeFFN.for_shape(s, accumulate=True)
+    assert call(acc.h) == B.MOE_FFN_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
