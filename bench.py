@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--no-nvfp4", action="store_true")
     p.add_argument("--nvfp4-steps", type=int, default=10, help="chains of --nvfp4-layers layers")
     p.add_argument("--nvfp4-layers", type=int, default=4)
+    p.add_argument("--no-block", action="store_true", help="skip the sandwich-norm sub-block leg")
+    p.add_argument("--block-steps", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -100,7 +102,7 @@ def nvfp4_layer_weight_bytes(shape):
     return nw // 2 + nw // 16 + (3 * E + 3) * 4 + H * E * 2
 
 
-def run_workload(torch, shape, steps, warmup, copies, graph, layers=1):
+def run_workload(torch, shape, steps, warmup, copies, graph, layers=1, norms=False):
     """Time `steps` forwards; returns a dict of measurements.
 
     bf16 workloads rotate `copies` bit-identical weight copies.  The NVFP4
@@ -128,9 +130,17 @@ def run_workload(torch, shape, steps, warmup, copies, graph, layers=1):
         sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
         out = torch.empty_like(xd)
         ffn = MoeFFN.for_shape(shape)
+        if norms:
+            # the sub-block with sandwich norms: seeded gains around 1
+            rng = np.random.default_rng(1000)
+            pre = torch.from_numpy((1.0 + 0.2 * rng.standard_normal(shape.hidden)).astype(np.float32)).cuda()
+            post = torch.from_numpy((1.0 + 0.2 * rng.standard_normal(shape.hidden)).astype(np.float32)).cuda()
 
-        def fwd(i):
-            ffn.forward(xd, sets[i % copies], out, bd)
+            def fwd(i):
+                ffn.forward_block(xd, sets[i % copies], pre, post, out, 1e-6, bd)
+        else:
+            def fwd(i):
+                ffn.forward(xd, sets[i % copies], out, bd)
     torch.cuda.synchronize()
 
     graphs = None
@@ -294,6 +304,19 @@ def main():
         "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in r["stage_avg_us"]])),
     }
     line["roofline"]["traffic"] = traffic_of("k_stream_gateup")
+    if not args.no_block:
+        rb = run_workload(torch, dec, args.block_steps, args.warmup, args.copies, args.graph, norms=True)
+        line["sandwich_block"] = {
+            "workload": "same layer, decode T=8, the sub-block x + RMSNorm(FFN(RMSNorm(x))) "
+                        "(pre-norm kernel, post-norm and residual in the combine)",
+            "tokens": dec.tokens,
+            "value": dec.tokens / (rb["ms_per_step"] * 1e-3),
+            "unit": "tokens/s",
+            "ms_per_step": rb["ms_per_step"],
+            "steps": args.block_steps,
+            "us_over_plain_ffn": (rb["ms_per_step"] - r["ms_per_step"]) * 1000.0,
+            "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rb["stage_avg_us"]])),
+        }
     if not args.no_prefill:
         pre = synth.PREFILL
         rp = run_workload(torch, pre, args.prefill_steps, max(3, args.warmup // 4), 2, args.graph)
