@@ -7,13 +7,14 @@ Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 against brute force, closed forms, library routines and the parameter counts
 printed on the pages; see the docstring of each test.
 """
-from .block import (NEAR_TIE_GAP, align, gelu_tanh, geglu, geglu_hidden, moe_block, moe_ffn,
+from .block import (NEAR_TIE_GAP, align, dense_block, dense_ffn, gelu_tanh, geglu, geglu_hidden,
+                    moe_block, moe_ffn,
                       moe_ffn_layer_residual, rms_norm, round_bf16, route, router_logits,
                       routed_mixture_dense_mask, select_topk, softmax, widen_bf16)
 from .nvfp4 import E2M1_TABLE, E4M3_TABLE, dequant_matrix, e2m1_value, e4m3fn_value
 
 __all__ = [
-    "NEAR_TIE_GAP", "align", "gelu_tanh", "geglu", "geglu_hidden", "moe_block", "moe_ffn",
+    "NEAR_TIE_GAP", "align", "dense_block", "dense_ffn", "gelu_tanh", "geglu", "geglu_hidden", "moe_block", "moe_ffn",
     "moe_ffn_layer_residual", "rms_norm", "round_bf16", "route", "router_logits",
     "routed_mixture_dense_mask",
     "select_topk", "softmax", "widen_bf16", "E2M1_TABLE", "E4M3_TABLE",

@@ -334,6 +334,47 @@ def moe_block(x, pre_scale, post_scale, eps: float, router_w, w_gate, w_up, w_do
     return r
 
 
+# ---------------------------------------------------------------------------
+# the dense FFN of the E4B sibling
+# ---------------------------------------------------------------------------
+
+
+def dense_ffn(x, d_gate, d_up, d_down, tokens=None) -> dict:
+    """Feed-forward block of a model without experts: one GeGLU MLP H -> D -> H.
+
+    gemma-llm API page gm.nn.Gemma4_E4B, ``TransformerConfig``: embed_dim
+    2560, hidden_dim 10240, enable_moe False, num_experts 0, expert_dim 0.
+    The page does not name the activation; the family's tanh-approximate GeGLU
+    (the 26B-A4B's) is taken.  x [T, H]; d_gate, d_up [H, D]; d_down [D, H]
+    (bf16 bits, floats or NVFP4 packs).  Returns h_d, y_d and out (= y_d);
+    with ``tokens`` only those rows (and no h_d).
+    """
+    X = widen_bf16(x)
+    if tokens is not None:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        X = X[tokens]
+    h_d, y_d = geglu(X, _dense_matrix(d_gate), _dense_matrix(d_up), _dense_matrix(d_down))
+    return {"h_d": None if tokens is not None else h_d, "y_d": y_d, "out": y_d, "tokens": tokens}
+
+
+def dense_block(x, pre_scale, post_scale, eps: float, d_gate, d_up, d_down, tokens=None) -> dict:
+    """The dense FFN with the sandwich norms and the residual (API page
+    gm.nn.Gemma4_E4B ``use_post_ffw_norm=True``), read as for the MoE block:
+
+        xn  = bf16(RMSNorm(x) * pre_scale)
+        out = x + RMSNorm(dense_ffn(xn)) * post_scale
+    """
+    X = widen_bf16(x)
+    xn = round_bf16(rms_norm(X, pre_scale, eps))
+    r = dense_ffn(xn, d_gate, d_up, d_down, tokens=tokens)
+    f = r["out"]
+    rows = X if tokens is None else X[np.asarray(tokens, dtype=np.int64)]
+    r["xn"] = xn
+    r["ffn"] = f
+    r["out"] = rows + rms_norm(f, post_scale, eps)
+    return r
+
+
 def moe_ffn_layer_residual(x, weights: dict, top_k: int, bias=None) -> tuple:
     """One layer of a residual stack without attention: (x + FFN(x), details).
 

@@ -61,7 +61,14 @@ PREFILL = FFNShape("prefill", 4096, 2816, 128, 8, 704, 2112)
 SKEW = FFNShape("skew", 16384, 2816, 128, 8, 704, 2112, skew=True)
 NVFP4_STACK = FFNShape("nvfp4_stack", 1024, 2816, 128, 8, 704, 2112, layers=30,
                        nvfp4=True)
-SHAPES = {s.name: s for s in (TINY, DECODE, PREFILL, SKEW, NVFP4_STACK)}
+# the dense GeGLU FFN of the Gemma 4 E4B sibling (gemma-llm API page
+# gm.nn.Gemma4_E4B: embed_dim 2560, hidden_dim 10240, enable_moe False,
+# num_experts 0, expert_dim 0): no router and no experts
+E4B_TINY = FFNShape("e4b_tiny", 32, 256, 0, 0, 0, 512)
+E4B_DECODE = FFNShape("e4b_decode", 8, 2560, 0, 0, 0, 10240)
+E4B_PREFILL = FFNShape("e4b_prefill", 4096, 2560, 0, 0, 0, 10240)
+SHAPES = {s.name: s for s in (TINY, DECODE, PREFILL, SKEW, NVFP4_STACK, E4B_TINY, E4B_DECODE,
+                              E4B_PREFILL)}
 
 # tensor ids of the random streams
 TID_X, TID_ROUTER, TID_GATE, TID_UP, TID_DOWN = 0, 1, 2, 3, 4
@@ -144,15 +151,19 @@ def make_weights(shape: FFNShape, seed: int = 0, layer: int = 0) -> dict:
     """bf16 weights of one block, row-major [K, N] per matrix (N contiguous).
 
     router [H, E]; gate, up [E, H, I]; down [E, I, H]; dgate, dup [H, D];
-    ddown [D, H].  std = fan_in ** -0.5 with fan_in = the contracted size.
+    ddown [D, H] (None where the shape has no experts or no dense branch).
+    std = fan_in ** -0.5 with fan_in = the contracted size.
     """
     H, E, I, D = shape.hidden, shape.experts, shape.expert_dim, shape.dense_dim
-    w = {
-        "router": normal_bf16(seed, layer, TID_ROUTER, (H, E), H ** -0.5),
-        "gate": normal_bf16(seed, layer, TID_GATE, (E, H, I), H ** -0.5),
-        "up": normal_bf16(seed, layer, TID_UP, (E, H, I), H ** -0.5),
-        "down": normal_bf16(seed, layer, TID_DOWN, (E, I, H), I ** -0.5),
-    }
+    if E > 0:
+        w = {
+            "router": normal_bf16(seed, layer, TID_ROUTER, (H, E), H ** -0.5),
+            "gate": normal_bf16(seed, layer, TID_GATE, (E, H, I), H ** -0.5),
+            "up": normal_bf16(seed, layer, TID_UP, (E, H, I), H ** -0.5),
+            "down": normal_bf16(seed, layer, TID_DOWN, (E, I, H), I ** -0.5),
+        }
+    else:  # a dense FFN: no router, no experts
+        w = {"router": None, "gate": None, "up": None, "down": None}
     if D > 0:
         w["dgate"] = normal_bf16(seed, layer, TID_DGATE, (H, D), H ** -0.5)
         w["dup"] = normal_bf16(seed, layer, TID_DUP, (H, D), H ** -0.5)
@@ -268,7 +279,7 @@ def make_nvfp4_weights(shape: FFNShape, seed: int = 0, layer: int = 0) -> dict:
     w = make_weights(shape, seed, layer)
     out = {"router": w["router"]}
     for name in ("gate", "up", "down"):
-        out[name] = nvfp4_pack_stack(w[name])
+        out[name] = nvfp4_pack_stack(w[name]) if w[name] is not None else None
     for name in ("dgate", "dup", "ddown"):
         out[name] = nvfp4_pack_stack(w[name][None]) if w[name] is not None else None
     return out

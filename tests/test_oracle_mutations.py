@@ -261,3 +261,49 @@ def test_missing_pre_norm(monkeypatch):
 
     _patch(monkeypatch, "moe_block", bad)
     _expect_caught(SANDWICH_PINS)
+
+
+DENSE_FFN_PINS = [pins.test_dense_ffn_is_torch_geglu_mlp,
+                  pins.test_dense_ffn_token_rows_and_independence,
+                  pins.test_dense_ffn_is_moe_block_dense_branch,
+                  pins.test_dense_block_torch_norms_and_zero_post_gain]
+
+
+def test_dense_ffn_gate_and_up_swapped(monkeypatch):
+    real = om.dense_ffn
+
+    def bad(x, d_gate, d_up, d_down, tokens=None):
+        return real(x, d_up, d_gate, d_down, tokens=tokens)
+
+    _patch(monkeypatch, "dense_ffn", bad)
+    _expect_caught(DENSE_FFN_PINS)
+
+
+def test_dense_ffn_erf_gelu(monkeypatch):
+    from math import erf
+
+    verf = np.vectorize(erf)
+
+    def bad(x, d_gate, d_up, d_down, tokens=None):
+        X = om.widen_bf16(x)
+        if tokens is not None:
+            X = X[np.asarray(tokens, dtype=np.int64)]
+        G = X @ om._dense_matrix(d_gate)
+        h = 0.5 * G * (1.0 + verf(G / np.sqrt(2.0))) * (X @ om._dense_matrix(d_up))
+        y = h @ om._dense_matrix(d_down)
+        return {"h_d": h, "y_d": y, "out": y, "tokens": tokens}
+
+    _patch(monkeypatch, "dense_ffn", bad)
+    _expect_caught(DENSE_FFN_PINS)
+
+
+def test_dense_ffn_row_mixing(monkeypatch):
+    real = om.dense_ffn
+
+    def bad(x, d_gate, d_up, d_down, tokens=None):
+        r = real(x, d_gate, d_up, d_down, tokens=tokens)
+        r["out"] = r["out"] + 1e-3 * np.roll(r["out"], 1, axis=0)
+        return r
+
+    _patch(monkeypatch, "dense_ffn", bad)
+    _expect_caught(DENSE_FFN_PINS)

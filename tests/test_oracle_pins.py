@@ -564,3 +564,82 @@ def test_skew_lambda_gives_zipf_slope():
     slope, loads = load_slope(synth.SKEW_LAMBDA)
     assert abs(slope + synth.ZIPF_S) < 0.02, slope
     assert loads.sum() == synth.SKEW.tokens * synth.SKEW.top_k
+
+
+# ---------------------------------------------------------------------------
+# the dense FFN of the E4B sibling (no router, no experts)
+# ---------------------------------------------------------------------------
+
+
+def _torch_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(torch.float64)
+
+
+def test_dense_ffn_is_torch_geglu_mlp():
+    """Pin: the dense FFN is one GeGLU MLP, checked against torch fp64
+    matmuls and torch's tanh GELU (a library routine) on the tiny E4B-like
+    shape; the hidden rows h_d are the GELU(gate) * up product."""
+    shape = synth.E4B_TINY
+    x, w = synth.make_x(shape), synth.make_weights(shape)
+    assert w["router"] is None and w["gate"] is None
+    r = oracle.dense_ffn(x, w["dgate"], w["dup"], w["ddown"])
+    X = _torch_bf16(x)
+    h = torch.nn.functional.gelu(X @ _torch_bf16(w["dgate"]), approximate="tanh") * (X @ _torch_bf16(w["dup"]))
+    assert rel_err(r["h_d"], h.numpy()) < 1e-12
+    assert rel_err(r["out"], (h @ _torch_bf16(w["ddown"])).numpy()) < 1e-12
+
+
+def test_dense_ffn_shape_of_e4b_page():
+    """Pin of the shape: the E4B page gives embed_dim 2560 and hidden_dim
+    10240 with no experts, i.e. 3 * 2560 * 10240 = 78,643,200 FFN weights per
+    layer; the generated matrices have exactly those shapes."""
+    s = synth.E4B_DECODE
+    assert (s.hidden, s.dense_dim, s.experts, s.expert_dim) == (2560, 10240, 0, 0)
+    shapes = {"dgate": (2560, 10240), "dup": (2560, 10240), "ddown": (10240, 2560)}
+    assert sum(a * b for a, b in shapes.values()) == 78_643_200
+
+
+def test_dense_ffn_token_rows_and_independence():
+    """Pin: each output row depends on its own input row only (sampled-row
+    mode and a token permutation agree with the full call), and x = 0 gives 0
+    (GELU(0) = 0, no biases)."""
+    shape = synth.E4B_TINY
+    x, w = synth.make_x(shape), synth.make_weights(shape)
+    full = oracle.dense_ffn(x, w["dgate"], w["dup"], w["ddown"])["out"]
+    toks = [0, 5, 31]
+    assert rel_err(oracle.dense_ffn(x, w["dgate"], w["dup"], w["ddown"], tokens=toks)["out"], full[toks]) < 1e-12
+    p = np.random.default_rng(4).permutation(shape.tokens)
+    assert rel_err(oracle.dense_ffn(x[p], w["dgate"], w["dup"], w["ddown"])["out"], full[p]) < 1e-12
+    z = oracle.dense_ffn(np.zeros_like(x), w["dgate"], w["dup"], w["ddown"])["out"]
+    assert np.array_equal(z, np.zeros_like(z))
+
+
+def test_dense_ffn_is_moe_block_dense_branch():
+    """Pin: the dense FFN equals the dense branch y_d of the MoE block (itself
+    pinned against torch above) on the same input and dense matrices."""
+    shape, x, w = tiny_inputs()
+    r = run(shape, x, w)
+    d = oracle.dense_ffn(x, w["dgate"], w["dup"], w["ddown"])
+    assert np.array_equal(d["out"], r["y_d"])
+
+
+def test_dense_block_torch_norms_and_zero_post_gain():
+    """Pin of the sandwich around the dense FFN: pre- and post-norm from
+    torch.nn.functional.rms_norm and the bf16 store from torch's cast; a zero
+    post gain returns the input exactly."""
+    shape = synth.E4B_TINY
+    x, w = synth.make_x(shape), synth.make_weights(shape)
+    rng = np.random.default_rng(5)
+    pre, post, eps = rng.standard_normal(shape.hidden), rng.standard_normal(shape.hidden), 1e-6
+    X = torch.from_numpy(oracle.widen_bf16(x))
+    xn = torch.nn.functional.rms_norm(X, (shape.hidden,), weight=torch.from_numpy(pre), eps=eps)
+    xn = xn.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    h = torch.nn.functional.gelu(xn @ _torch_bf16(w["dgate"]), approximate="tanh") * (xn @ _torch_bf16(w["dup"]))
+    f = h @ _torch_bf16(w["ddown"])
+    ref = X + torch.nn.functional.rms_norm(f, (shape.hidden,), weight=torch.from_numpy(post), eps=eps)
+    r = oracle.dense_block(x, pre, post, eps, w["dgate"], w["dup"], w["ddown"])
+    assert rel_err(r["out"], ref.numpy()) < 1e-12
+    rs = oracle.dense_block(x, pre, post, eps, w["dgate"], w["dup"], w["ddown"], tokens=[3, 9])
+    assert rel_err(rs["out"], r["out"][[3, 9]]) < 1e-12
+    z = oracle.dense_block(x, pre, np.zeros(shape.hidden), eps, w["dgate"], w["dup"], w["ddown"])
+    assert np.array_equal(z["out"], oracle.widen_bf16(x))
