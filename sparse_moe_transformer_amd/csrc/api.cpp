@@ -34,6 +34,9 @@ struct moe_ffn_handle {
   // offsets, perm, pos) were never built and its h / h_d / y rows are not
   // in grouped order; the diagnostic getters rebuild them on request
   bool last_stream;
+  // the last forward (a dense FFN on the MFMA path) wrote its dense rows
+  // straight to out, not to the workspace
+  bool last_direct;
   bool sync_mode;
   uint32_t prof_mask;
   int prof_max;
@@ -57,6 +60,7 @@ int hip_fail(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int kMaxTokensLimit = 1 << 20;
+constexpr int kMaxDenseDim = 16384;
 
 int validate_config(const moe_ffn_config* c) {
   if (!c) return fail(MOE_FFN_ERR_INVALID_ARG, "config is NULL");
@@ -64,14 +68,21 @@ int validate_config(const moe_ffn_config* c) {
     return fail(MOE_FFN_ERR_INVALID_ARG, "max_tokens must be in [1, 2^20]");
   if (c->hidden <= 0 || c->hidden % 256 || c->hidden > 4096)
     return fail(MOE_FFN_ERR_UNSUPPORTED, "hidden must be a multiple of 256 in [256, 4096]");
-  if (c->num_experts < 4 || c->num_experts > 256 || c->num_experts % 4)
-    return fail(MOE_FFN_ERR_UNSUPPORTED, "num_experts must be a multiple of 4 in [4, 256]");
-  if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->num_experts)
-    return fail(MOE_FFN_ERR_UNSUPPORTED, "top_k must be in [1, min(num_experts, 16)]");
-  if (c->expert_dim <= 0 || c->expert_dim % 64 || c->expert_dim > 4096)
-    return fail(MOE_FFN_ERR_UNSUPPORTED, "expert_dim must be a multiple of 64 in [64, 4096]");
-  if (c->dense_dim < 0 || c->dense_dim % 64 || c->dense_dim > 4096)
-    return fail(MOE_FFN_ERR_UNSUPPORTED, "dense_dim must be 0 or a multiple of 64 in [64, 4096]");
+  if (c->num_experts == 0) {
+    // a dense FFN: no router and no experts, the dense branch alone
+    if (c->top_k != 0 || c->expert_dim != 0)
+      return fail(MOE_FFN_ERR_INVALID_ARG, "top_k and expert_dim must be 0 when num_experts == 0");
+    if (c->dense_dim <= 0) return fail(MOE_FFN_ERR_INVALID_ARG, "a config without experts needs dense_dim > 0");
+  } else {
+    if (c->num_experts < 4 || c->num_experts > 256 || c->num_experts % 4)
+      return fail(MOE_FFN_ERR_UNSUPPORTED, "num_experts must be 0 or a multiple of 4 in [4, 256]");
+    if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->num_experts)
+      return fail(MOE_FFN_ERR_UNSUPPORTED, "top_k must be in [1, min(num_experts, 16)]");
+    if (c->expert_dim <= 0 || c->expert_dim % 64 || c->expert_dim > 4096)
+      return fail(MOE_FFN_ERR_UNSUPPORTED, "expert_dim must be a multiple of 64 in [64, 4096]");
+  }
+  if (c->dense_dim < 0 || c->dense_dim % 64 || c->dense_dim > kMaxDenseDim)
+    return fail(MOE_FFN_ERR_UNSUPPORTED, "dense_dim must be 0 or a multiple of 64 in [64, 16384]");
   if (c->weight_format != MOE_FFN_W_BF16 && c->weight_format != MOE_FFN_W_NVFP4)
     return fail(MOE_FFN_ERR_UNSUPPORTED, "unknown weight_format");
   if (c->flags & ~uint32_t(MOE_FFN_ACCUMULATE)) return fail(MOE_FFN_ERR_UNSUPPORTED, "unknown flag bits");
@@ -117,7 +128,8 @@ Layout layout(const moe_ffn_config& c) {
       T * H * 2,                                  // y_d
       (size_t(moe::kStreamKS) * moe::kStreamRows * I +  // streaming gate/up partials
        size_t(moe::kDenseKS) * moe::kRouteSmallT * (D ? D : 1)) * 2 * 4,
-      size_t(moe::kDenseDownKS) * moe::kRouteSmallT * H * 4,  // streaming dense down partials
+      size_t(moe::dense_down_slices(moe::Shape{0, int(H), int(E), int(k), int(I), int(D)})) *
+          moe::kRouteSmallT * H * 4,              // streaming dense down partials
       size_t(moe::kArriveInts) * 4,               // arrival counters (zero between forwards)
       T * H * 2,                                  // xn: pre-normed input (sandwich-norm forwards)
   };
@@ -238,6 +250,9 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   if (args.nvfp4) stream = false;             // the streaming kernels read bf16 [K, N] weights only
   if (T > moe::kRouteSmallT) stream = false;  // their scratch holds at most 64 tokens' rows
   const int mt = int((size_t(T) * sh.k + moe::kGemmBM - 1) / moe::kGemmBM + sh.E);
+  const bool experts = sh.E > 0;  // else a dense FFN: no routing stages
+  // a dense FFN on the MFMA path writes its output rows from the down GEMM
+  const bool direct = !experts && !stream && !nm && !(h->cfg.flags & MOE_FFN_ACCUMULATE);
   {
     // streaming: the router and the dense branch's gate/up share one launch
     StageTimer tm(h, MOE_FFN_STAGE_ROUTE, s, timing);
@@ -249,12 +264,13 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
       args.x = ws.xn;
     }
     e = stream ? moe::launch_route_dense(args, wr, bias, ws, s)
+        : !experts                 ? hipSuccess
         : (T <= moe::kRouteSmallT) ? moe::launch_route_small(sh, xb, wr, bias, ws, s)
                                    : moe::launch_route_large(sh, xb, wr, bias, ws, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "route");
   }
-  if (!stream) {
+  if (!stream && experts) {
     // the MFMA tiles read the grouped rows and the tile list; the streaming
     // kernels derive their experts' rows from topk_idx themselves
     StageTimer tm(h, MOE_FFN_STAGE_ALIGN, s, timing);
@@ -276,11 +292,12 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   }
   {
     StageTimer tm(h, MOE_FFN_STAGE_DOWN, s, timing);
-    e = stream ? moe::launch_stream_down(args, ws, s) : moe::launch_gemm_down(args, ws, mt, s);
+    e = stream ? moe::launch_stream_down(args, ws, s)
+               : moe::launch_gemm_down(args, ws, mt, s, direct ? static_cast<moe::bf16_t*>(out) : nullptr);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "down");
   }
-  {
+  if (!direct) {
     StageTimer tm(h, MOE_FFN_STAGE_COMBINE, s, timing);
     const int yd_slices = stream && sh.D > 0 ? moe::dense_down_slices(sh) : 0;
     e = nm ? moe::launch_combine_norm(sh, ws, xres, nm->post, nm->eps, static_cast<moe::bf16_t*>(out), yd_slices,
@@ -293,6 +310,7 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   if (timing) ++h->prof_fwd;
   h->last_T = T;
   h->last_stream = stream;
+  h->last_direct = direct;
   return finish(h, s, "forward");
 }
 
@@ -309,17 +327,29 @@ void profile_release(moe_ffn_handle* h) {
   h->prof_fwd = 0;
 }
 
+// the router matrix and bias: required (bias optional) with experts, NULL without
+int router_checks(const moe_ffn_handle* h, const void* router_w, const float* bias) {
+  if (h->cfg.num_experts == 0) {
+    if (router_w || bias)
+      return fail(MOE_FFN_ERR_INVALID_ARG, "router_w and router_bias must be NULL when num_experts == 0");
+    return MOE_FFN_OK;
+  }
+  if (!router_w) return fail(MOE_FFN_ERR_INVALID_ARG, "router_w must not be NULL");
+  if (!aligned16(router_w)) return fail(MOE_FFN_ERR_INVALID_ARG, "router_w must be 16-byte aligned");
+  if (bias && (reinterpret_cast<uintptr_t>(bias) & 3u))
+    return fail(MOE_FFN_ERR_INVALID_ARG, "router_bias must be 4-byte aligned");
+  return MOE_FFN_OK;
+}
+
 int common_forward_checks(moe_ffn_handle* h, int T, const void* x, const void* router_w,
                           const float* bias, const void* out, int fmt) {
   if (int r = check_handle(h)) return r;
   if (h->cfg.weight_format != fmt)
     return fail(MOE_FFN_ERR_UNSUPPORTED, "weight format of the handle does not match this entry point");
   if (T < 0 || T > h->cfg.max_tokens) return fail(MOE_FFN_ERR_INVALID_ARG, "T must be in [0, max_tokens]");
-  if (!x || !router_w || !out) return fail(MOE_FFN_ERR_INVALID_ARG, "x, router_w and out must not be NULL");
-  if (!aligned16(x) || !aligned16(router_w) || !aligned16(out))
-    return fail(MOE_FFN_ERR_INVALID_ARG, "x, router_w and out must be 16-byte aligned");
-  if (bias && (reinterpret_cast<uintptr_t>(bias) & 3u))
-    return fail(MOE_FFN_ERR_INVALID_ARG, "router_bias must be 4-byte aligned");
+  if (!x || !out) return fail(MOE_FFN_ERR_INVALID_ARG, "x and out must not be NULL");
+  if (!aligned16(x) || !aligned16(out)) return fail(MOE_FFN_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
+  if (int r = router_checks(h, router_w, bias)) return r;
   if (!(h->cfg.flags & MOE_FFN_ACCUMULATE) && x == out)
     return fail(MOE_FFN_ERR_INVALID_ARG, "out may alias x only with MOE_FFN_ACCUMULATE");
   return MOE_FFN_OK;
@@ -328,7 +358,7 @@ int common_forward_checks(moe_ffn_handle* h, int T, const void* x, const void* r
 int check_fp4(const moe_ffn_nvfp4_t* m, bool required, const char* name) {
   if (!required) {
     if (m && (m->q || m->scale || m->tensor_scale))
-      return fail(MOE_FFN_ERR_INVALID_ARG, std::string(name) + " must be empty when dense_dim == 0");
+      return fail(MOE_FFN_ERR_INVALID_ARG, std::string(name) + " must be empty: the config has no such matrices");
     return MOE_FFN_OK;
   }
   if (!m || !m->q || !m->scale || !m->tensor_scale)
@@ -346,9 +376,14 @@ moe::Fp4Mat to_mat(const moe_ffn_nvfp4_t* m) {
 
 int bf16_weight_checks(const moe_ffn_handle* h, const void* w_gate, const void* w_up, const void* w_down,
                        const void* d_gate, const void* d_up, const void* d_down) {
-  if (!w_gate || !w_up || !w_down) return fail(MOE_FFN_ERR_INVALID_ARG, "expert weights must not be NULL");
-  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down))
-    return fail(MOE_FFN_ERR_INVALID_ARG, "expert weights must be 16-byte aligned");
+  if (h->cfg.num_experts == 0) {
+    if (w_gate || w_up || w_down)
+      return fail(MOE_FFN_ERR_INVALID_ARG, "expert weights must be NULL when num_experts == 0");
+  } else {
+    if (!w_gate || !w_up || !w_down) return fail(MOE_FFN_ERR_INVALID_ARG, "expert weights must not be NULL");
+    if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down))
+      return fail(MOE_FFN_ERR_INVALID_ARG, "expert weights must be 16-byte aligned");
+  }
   if (h->cfg.dense_dim > 0) {
     if (!d_gate || !d_up || !d_down) return fail(MOE_FFN_ERR_INVALID_ARG, "dense weights must not be NULL");
     if (!aligned16(d_gate) || !aligned16(d_up) || !aligned16(d_down))
@@ -493,12 +528,11 @@ int moe_ffn_forward_block(moe_ffn_handle* h, int32_t T, const void* x, const flo
       return fail(MOE_FFN_ERR_UNSUPPORTED,
                   "the sub-block adds its own residual: use a handle without MOE_FFN_ACCUMULATE");
     if (T < 0 || T > h->cfg.max_tokens) return fail(MOE_FFN_ERR_INVALID_ARG, "T must be in [0, max_tokens]");
-    if (!x || !router_w || !out || !pre_scale || !post_scale)
-      return fail(MOE_FFN_ERR_INVALID_ARG, "x, router_w, out, pre_scale and post_scale must not be NULL");
-    if (!aligned16(x) || !aligned16(router_w) || !aligned16(out) || !aligned16(pre_scale) || !aligned16(post_scale))
-      return fail(MOE_FFN_ERR_INVALID_ARG, "x, router_w, out, pre_scale and post_scale must be 16-byte aligned");
-    if (router_bias && (reinterpret_cast<uintptr_t>(router_bias) & 3u))
-      return fail(MOE_FFN_ERR_INVALID_ARG, "router_bias must be 4-byte aligned");
+    if (!x || !out || !pre_scale || !post_scale)
+      return fail(MOE_FFN_ERR_INVALID_ARG, "x, out, pre_scale and post_scale must not be NULL");
+    if (!aligned16(x) || !aligned16(out) || !aligned16(pre_scale) || !aligned16(post_scale))
+      return fail(MOE_FFN_ERR_INVALID_ARG, "x, out, pre_scale and post_scale must be 16-byte aligned");
+    if (int r = router_checks(h, router_w, router_bias)) return r;
     if (!(eps >= 0.f) || !(eps < 1e30f)) return fail(MOE_FFN_ERR_INVALID_ARG, "eps must be finite and >= 0");
     if (int r = bf16_weight_checks(h, w_gate, w_up, w_down, d_gate, d_up, d_down)) return r;
     if (T == 0) {
@@ -524,9 +558,10 @@ int moe_ffn_forward_nvfp4(moe_ffn_handle* h, int32_t T, const void* x, const voi
                           void* stream) {
   try {
     if (int r = common_forward_checks(h, T, x, router_w, router_bias, out, MOE_FFN_W_NVFP4)) return r;
-    if (int r = check_fp4(w_gate, true, "w_gate")) return r;
-    if (int r = check_fp4(w_up, true, "w_up")) return r;
-    if (int r = check_fp4(w_down, true, "w_down")) return r;
+    const bool experts = h->cfg.num_experts > 0;
+    if (int r = check_fp4(w_gate, experts, "w_gate")) return r;
+    if (int r = check_fp4(w_up, experts, "w_up")) return r;
+    if (int r = check_fp4(w_down, experts, "w_down")) return r;
     const bool dense = h->cfg.dense_dim > 0;
     if (int r = check_fp4(d_gate, dense, "d_gate")) return r;
     if (int r = check_fp4(d_up, dense, "d_up")) return r;
@@ -540,9 +575,9 @@ int moe_ffn_forward_nvfp4(moe_ffn_handle* h, int32_t T, const void* x, const voi
     moe::StreamArgs a{};
     a.sh = shape_of(h, T);
     a.x = static_cast<const moe::bf16_t*>(x);
-    a.fg = to_mat(w_gate);
-    a.fu = to_mat(w_up);
-    a.fd = to_mat(w_down);
+    a.fg = to_mat(experts ? w_gate : nullptr);
+    a.fu = to_mat(experts ? w_up : nullptr);
+    a.fd = to_mat(experts ? w_down : nullptr);
     a.fdg = to_mat(dense ? d_gate : nullptr);
     a.fdu = to_mat(dense ? d_up : nullptr);
     a.fdd = to_mat(dense ? d_down : nullptr);
@@ -559,6 +594,7 @@ int moe_ffn_get_routing(moe_ffn_handle* h, int32_t* topk_idx, float* topk_w, int
                         int32_t* offsets, int32_t* perm, int32_t* pos, void* stream) {
   try {
     if (int r = check_handle(h)) return r;
+    if (h->cfg.num_experts == 0) return fail(MOE_FFN_ERR_UNSUPPORTED, "a config without experts has no routing");
     DeviceGuard g(h->device);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (h->last_stream && h->last_T > 0) {
@@ -593,7 +629,9 @@ int moe_ffn_get_intermediates(moe_ffn_handle* h, void* h_rows, void* y_rows, voi
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t T = size_t(h->last_T), k = size_t(h->cfg.top_k);
     const size_t H = size_t(h->cfg.hidden), I = size_t(h->cfg.expert_dim), D = size_t(h->cfg.dense_dim);
-    if (h->last_stream && T > 0) {
+    if (y_dense && h->last_direct)
+      return fail(MOE_FFN_ERR_UNSUPPORTED, "the last forward wrote its dense rows straight to out");
+    if (h->last_stream && T > 0 && h->cfg.num_experts > 0) {
       // rebuild perm / pos, then write h and y in grouped order
       const moe::Shape sh = shape_of(h, int(T));
       hipError_t e = moe::launch_align(sh, h->ws, s);
@@ -625,6 +663,7 @@ int moe_ffn_get_intermediates(moe_ffn_handle* h, void* h_rows, void* y_rows, voi
 int moe_ffn_align_only(moe_ffn_handle* h, int32_t T, const int32_t* topk_idx, void* stream) {
   try {
     if (int r = check_handle(h)) return r;
+    if (h->cfg.num_experts == 0) return fail(MOE_FFN_ERR_UNSUPPORTED, "a config without experts has no routing");
     if (T < 0 || T > h->cfg.max_tokens) return fail(MOE_FFN_ERR_INVALID_ARG, "T must be in [0, max_tokens]");
     if (!topk_idx) return fail(MOE_FFN_ERR_INVALID_ARG, "topk_idx must not be NULL");
     if (reinterpret_cast<uintptr_t>(topk_idx) & 3u)
@@ -632,6 +671,7 @@ int moe_ffn_align_only(moe_ffn_handle* h, int32_t T, const int32_t* topk_idx, vo
     if (T == 0) {
       h->last_T = 0;
       h->last_stream = false;
+      h->last_direct = false;
       g_err.clear();
       return MOE_FFN_OK;
     }
@@ -644,6 +684,7 @@ int moe_ffn_align_only(moe_ffn_handle* h, int32_t T, const int32_t* topk_idx, vo
     if (e != hipSuccess) return hip_fail(e, "align");
     h->last_T = T;
     h->last_stream = false;
+    h->last_direct = false;
     return finish(h, s, "align_only");
   } catch (...) {
     return fail(MOE_FFN_ERR_HIP, "unknown exception");

@@ -47,21 +47,24 @@ __device__ __forceinline__ void combine8(const Shape& sh, const Workspace& ws, i
       yd[2 * d + 1] = bf16_hi(vd[d]);
     }
   } else if (sh.D > 0) {
-    // issue every slice's loads, then sum in slice order
-    float4 pa[kDenseDownKS], pb[kDenseDownKS];
+    // the slices in order, four slices' loads in flight at a time
+    for (int s0 = 0; s0 < yd_slices; s0 += 4) {
+      float4 pa[4], pb[4];
 #pragma unroll
-    for (int sl = 0; sl < kDenseDownKS; ++sl) {
-      if (sl < yd_slices) {
-        const float4* p = reinterpret_cast<const float4*>(ws.ydp + ((long long)sl * kRouteSmallT + t) * H + c);
-        pa[sl] = p[0];
-        pb[sl] = p[1];
+      for (int q = 0; q < 4; ++q) {
+        if (s0 + q < yd_slices) {
+          const float4* p =
+              reinterpret_cast<const float4*>(ws.ydp + ((long long)(s0 + q) * kRouteSmallT + t) * H + c);
+          pa[q] = p[0];
+          pb[q] = p[1];
+        }
       }
-    }
 #pragma unroll
-    for (int sl = 0; sl < kDenseDownKS; ++sl) {
-      if (sl < yd_slices) {
-        yd[0] += pa[sl].x; yd[1] += pa[sl].y; yd[2] += pa[sl].z; yd[3] += pa[sl].w;
-        yd[4] += pb[sl].x; yd[5] += pb[sl].y; yd[6] += pb[sl].z; yd[7] += pb[sl].w;
+      for (int q = 0; q < 4; ++q) {
+        if (s0 + q < yd_slices) {
+          yd[0] += pa[q].x; yd[1] += pa[q].y; yd[2] += pa[q].z; yd[3] += pa[q].w;
+          yd[4] += pb[q].x; yd[5] += pb[q].y; yd[6] += pb[q].z; yd[7] += pb[q].w;
+        }
       }
     }
     // the dense branch's output, rounded to bf16, kept for inspection; the

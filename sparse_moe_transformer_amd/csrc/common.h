@@ -67,7 +67,7 @@ struct Workspace {
   bf16_t* y_d;          // [Tmax, H]
   float* part;          // [kStreamKS][kStreamRows][2][I] (rows = slots) + [kDenseKS][64][2][D]
                         // (rows = tokens) gate/up partials of the streaming path
-  float* ydp;           // [kDenseDownKS][64][H] dense down partials (streaming path)
+  float* ydp;           // [dense_down_slices][64][H] dense down partials (streaming path)
   bf16_t* xn;           // [Tmax, H] pre-normed block input (sandwich-norm forwards)
   int32_t* arrive;      // [kArriveInts] arrival counters of the last-block hand-offs; every
                         // kernel that counts leaves them at zero (zeroed at create)
@@ -79,7 +79,7 @@ constexpr int kRouteSmallT = 64;   // largest T of the one-block-per-token route
 constexpr int kGemmBM = 256;       // MFMA tile rows (tokens)
 constexpr int kStreamKS = 2;       // K-slices of the streaming routed gate/up units
 constexpr int kDenseKS = 4;        // K-slices of the streaming dense gate/up units
-constexpr int kDenseDownKS = 4;    // K-slices of the streaming dense down units
+constexpr int kDenseDownKS = 16;   // most K-slices of the streaming dense down units
 constexpr int kStreamRows = kRouteSmallT * 16;  // routed rows of the streaming path (T <= 64, k <= 16)
 constexpr int kArriveRoute = 0;                 // [64] token groups of the small-T router
 constexpr int kArriveInts = 64;
@@ -91,7 +91,13 @@ struct Shape {
 // K-slices of the streaming dense-branch units: whole 64-row groups, at
 // most the constants above (no empty slice)
 __host__ __device__ inline int dense_gateup_slices(const Shape& sh) { return sh.H / 64 < kDenseKS ? sh.H / 64 : kDenseKS; }
-__host__ __device__ inline int dense_down_slices(const Shape& sh) { return sh.D / 64 < kDenseDownKS ? sh.D / 64 : kDenseDownKS; }
+// The dense down units: 4 K-slices, more for a wide D (about 640 rows each,
+// so that a D = 10240 branch still spreads over a few hundred blocks)
+__host__ __device__ inline int dense_down_slices(const Shape& sh) {
+  int ks = sh.D / 640 > 4 ? sh.D / 640 : 4;
+  if (ks > kDenseDownKS) ks = kDenseDownKS;
+  return sh.D / 64 < ks ? sh.D / 64 : ks;
+}
 
 // NVFP4 matrix stack
 struct Fp4Mat {
@@ -112,8 +118,10 @@ template <class V, int POLICY>
 __device__ __forceinline__ V bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   if constexpr (sizeof(V) == 16)
     return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
-  else
+  else if constexpr (sizeof(V) == 8)
     return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POLICY));
+  else
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, POLICY));
 }
 // a pointer that is the same in every lane, moved to scalar registers
 template <class T>
@@ -155,7 +163,9 @@ hipError_t launch_stream_export(const Shape& sh, const Workspace& ws, bf16_t* h_
 
 // MFMA tiles (large T)
 hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s);
-hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s);
+// yd_out: where the dense rows go (null: ws.y_d)
+hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s,
+                            bf16_t* yd_out = nullptr);
 
 // yd_slices: 0 = dense output in ws.y_d (bf16); n > 0 = n fp32 slices in
 // ws.ydp, summed in order (and stored to ws.y_d as bf16).  slot_rows: the

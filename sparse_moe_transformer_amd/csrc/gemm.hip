@@ -606,15 +606,16 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
   e.C = ws.h;
   e.ldc = sh.I;
   e.n_ntiles = (sh.I + BN / 2 - 1) / (BN / 2);
-  e.mtiles = ws.mtiles;
+  e.mtiles = sh.E > 0 ? ws.mtiles : nullptr;  // no experts: an empty second segment
   e.n_mtiles = ws.meta;
-  e.max_mtiles = max_mtiles;
+  e.max_mtiles = sh.E > 0 ? max_mtiles : 0;
   const int ud = sh.D > 0 ? host_units(d) : 0;
   if (a.nvfp4) return launch<MODE_GATEUP, W_FP4>(d, e, ud, grouped_units(e), s);
   return launch<MODE_GATEUP, W_BF16>(d, e, ud, grouped_units(e), s);
 }
 
-hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s) {
+hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s,
+                            bf16_t* yd_out) {
   const Shape& sh = a.sh;
   Seg d = empty_seg(), e = empty_seg();
   if (sh.D > 0) {
@@ -625,7 +626,7 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
     d.F0 = a.fdd;
     d.K = sh.D;
     d.N = sh.H;
-    d.C = ws.y_d;
+    d.C = yd_out ? yd_out : ws.y_d;
     d.ldc = sh.H;
     d.n_ntiles = (sh.H + BN - 1) / BN;
     d.host_rows = sh.T;
@@ -641,9 +642,9 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
   e.C = ws.y;
   e.ldc = sh.H;
   e.n_ntiles = (sh.H + BN - 1) / BN;
-  e.mtiles = ws.mtiles;
+  e.mtiles = sh.E > 0 ? ws.mtiles : nullptr;
   e.n_mtiles = ws.meta;
-  e.max_mtiles = max_mtiles;
+  e.max_mtiles = sh.E > 0 ? max_mtiles : 0;
   const int ud = sh.D > 0 ? host_units(d) : 0;
   if (a.nvfp4) return launch<MODE_PLAIN_BF16, W_FP4>(d, e, ud, grouped_units(e), s);
   return launch<MODE_PLAIN_BF16, W_BF16>(d, e, ud, grouped_units(e), s);

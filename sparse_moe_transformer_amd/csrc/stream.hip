@@ -122,7 +122,7 @@ __device__ const float* unit_direct(const bf16_t* __restrict__ w, int ldw, int k
                                     const bf16_t* const* act, float* red) {
   constexpr int CG = NCOLS / 8, RG = kThreads / CG;
   const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
-  const int R = (kend - kbeg) / RG;  // rows per thread (multiple of 4)
+  const int R = (kend - kbeg) / RG;  // rows per thread (even)
   const int k0 = kbeg + rg * R;
   float acc[NT][8];
 #pragma unroll
@@ -145,12 +145,20 @@ __device__ const float* unit_direct(const bf16_t* __restrict__ w, int ldw, int k
 #pragma unroll
     for (int i = 0; i < kU; ++i)
       vw[i] = (b + i < R) ? bload<u32x4_t, kPolicyNT>(rw, wv, uint32_t(b + i) * wrow) : u32x4_t{0, 0, 0, 0};
+    // R is even: a 4-row piece is whole or its last two rows lie past R
+    // (they are not read: for the last row group they would lie past kend)
 #pragma unroll
     for (int r = 0; r < NT; ++r)
 #pragma unroll
-      for (int q = 0; q < kU / 4; ++q)
-        va[r][q] = (has[r] && b + 4 * q < R) ? bload<u32x2_t, 0>(rx[r], uint32_t(k0) * 2, uint32_t(b + 4 * q) * 2)
-                                             : u32x2_t{0, 0};
+      for (int q = 0; q < kU / 4; ++q) {
+        const int k = b + 4 * q;
+        if (has[r] && k + 4 <= R)
+          va[r][q] = bload<u32x2_t, 0>(rx[r], uint32_t(k0) * 2, uint32_t(k) * 2);
+        else if (has[r] && k < R)
+          va[r][q] = u32x2_t{bload<uint32_t, 0>(rx[r], uint32_t(k0) * 2, uint32_t(k) * 2), 0u};
+        else
+          va[r][q] = u32x2_t{0, 0};
+      }
     // rows past R hold zero weights: no branch, so the loop fully unrolls
 #pragma unroll
     for (int i = 0; i < kU; i += 2)
@@ -497,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void k_stream_export(Shape sh, Workspace 
 
 hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
   const Shape& sh = a.sh;
-  if (sh.T == 0) return hipSuccess;
+  if (sh.T == 0 || sh.E == 0) return hipSuccess;
   const size_t kl = size_t((sh.H / 64 + kStreamKS - 1) / kStreamKS) * 64;  // longest slice
   const size_t lds = std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * 64 * 4);
   const int max_active = std::min(sh.E, sh.T * sh.k);
@@ -510,14 +518,16 @@ hipError_t launch_route_dense(const StreamArgs& a, const bf16_t* wr, const float
                               hipStream_t s) {
   const Shape& sh = a.sh;
   if (sh.T == 0) return hipSuccess;
-  const RouteSmallCfg c = route_small_config(sh);
-  if (!c.ok) return hipErrorInvalidValue;
-  const int nroute = c.nslices * c.groups;
+  // a dense FFN (no experts) launches the dense units only
+  const RouteSmallCfg c = sh.E > 0 ? route_small_config(sh) : RouteSmallCfg{};
+  if (sh.E > 0 && !c.ok) return hipErrorInvalidValue;
+  const int nroute = sh.E > 0 ? c.nslices * c.groups : 0;
   const int ksd = sh.D > 0 ? dense_gateup_slices(sh) : 1;
   const int ud = sh.D > 0 ? (sh.D / 64) * 2 * ksd : 0;
   const size_t kl = size_t((sh.H / 64 + ksd - 1) / ksd) * 64;  // longest dense K-slice
   const size_t lds = ud ? std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * 64 * 4) : 0;
-  if (c.cw == 8)
+  if (nroute + ud == 0) return hipSuccess;
+  if (c.cw != 4)
     hipLaunchKernelGGL(k_route_dense<8>, dim3(nroute + ud), dim3(kThreads), lds, s, a, wr, bias, ws, c.slice_rows, c.tb,
                        c.nslices, nroute, ksd);
   else

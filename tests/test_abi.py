@@ -66,7 +66,11 @@ def test_workspace_bytes_valid_config(lib):
     (dict(hidden=2800), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(hidden=4352), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(expert_dim=4160), binding.MOE_FFN_ERR_UNSUPPORTED),
-    (dict(num_experts=0), binding.MOE_FFN_ERR_UNSUPPORTED),
+    # no experts (a dense FFN) needs top_k = expert_dim = 0 and dense_dim > 0
+    (dict(num_experts=0), binding.MOE_FFN_ERR_INVALID_ARG),
+    (dict(num_experts=0, top_k=0), binding.MOE_FFN_ERR_INVALID_ARG),
+    (dict(num_experts=0, top_k=0, expert_dim=0, dense_dim=0), binding.MOE_FFN_ERR_INVALID_ARG),
+    (dict(dense_dim=16448), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(num_experts=126), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(num_experts=300), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(top_k=0), binding.MOE_FFN_ERR_UNSUPPORTED),
@@ -87,6 +91,17 @@ def test_bad_configs_rejected(lib, kw, code):
     assert binding.moe_ffn_last_error() != ""
     rc, h = binding.moe_ffn_create(cfg(**kw))
     assert rc == code and not h
+
+
+def test_dense_ffn_configs_accepted(lib):
+    """A config without experts is the dense FFN of the E4B model (2560 ->
+    10240 -> 2560); wide dense branches are accepted with experts too."""
+    rc, n = binding.moe_ffn_workspace_bytes(cfg(hidden=2560, num_experts=0, top_k=0, expert_dim=0,
+                                                dense_dim=10240, max_tokens=4096))
+    assert rc == binding.MOE_FFN_OK
+    assert n >= 4096 * 10240 * 2 + 4096 * 2560 * 2  # h_d and y_d rows
+    rc, _ = binding.moe_ffn_workspace_bytes(cfg(dense_dim=16384))
+    assert rc == binding.MOE_FFN_OK
 
 
 def test_largest_addressable_token_count(lib):
