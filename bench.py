@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--nvfp4-layers", type=int, default=4)
     p.add_argument("--no-block", action="store_true", help="skip the sandwich-norm sub-block leg")
     p.add_argument("--block-steps", type=int, default=100)
+    p.add_argument("--no-dense", action="store_true", help="skip the E4B dense FFN leg")
+    p.add_argument("--dense-steps", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -172,7 +174,10 @@ def run_workload(torch, shape, steps, warmup, copies, graph, layers=1, norms=Fal
             restart()
         step(i)
     torch.cuda.synchronize()
-    counts = ffn.routing(shape.tokens)["counts"].cpu().numpy()
+    if shape.experts > 0:
+        counts = ffn.routing(shape.tokens)["counts"].cpu().numpy()
+    else:  # a dense FFN: no routing
+        counts = np.zeros(0, dtype=np.int32)
     n_act = int((counts > 0).sum())
 
     # timed region: `steps` forwards (chains of `layers` for the stack; the
@@ -362,6 +367,31 @@ def main():
             "mfma_frac": step_flops(st) / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
             "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rn["stage_avg_us"]])),
         }
+    if not args.no_dense:
+        # the dense GeGLU FFN of the E4B model (2560 -> 10240 -> 2560, no experts)
+        dd, dp = synth.E4B_DECODE, synth.E4B_PREFILL
+        H, D = dd.hidden, dd.dense_dim
+        rd = run_workload(torch, dd, args.dense_steps, args.warmup, args.copies, args.graph)
+        dbytes = 3 * H * D * 2 + 2 * dd.tokens * H * 2
+        dense = {
+            "workload": "Gemma 4 E4B dense GeGLU FFN (H=2560, D=10240, no experts)",
+            "decode": {"tokens": dd.tokens, "value": dd.tokens / (rd["ms_per_step"] * 1e-3),
+                       "unit": "tokens/s", "ms_per_step": rd["ms_per_step"], "steps": args.dense_steps,
+                       "algorithmic_bytes": dbytes,
+                       "hbm_frac": dbytes / (rd["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rd["stage_avg_us"]]))},
+        }
+        if not args.no_prefill:
+            rq = run_workload(torch, dp, args.prefill_steps, max(3, args.warmup // 4), 2, args.graph)
+            fl = 2 * dp.tokens * 3 * H * D
+            gu_us = rq["stage_avg_us"][2]
+            dense["prefill"] = {
+                "tokens": dp.tokens, "value": dp.tokens / (rq["ms_per_step"] * 1e-3), "unit": "tokens/s",
+                "ms_per_step": rq["ms_per_step"], "steps": args.prefill_steps,
+                "step_mfma_frac": fl / (rq["ms_per_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                "gateup_mfma_frac": (2 * dp.tokens * 2 * H * D) / (gu_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+                "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rq["stage_avg_us"]]))}
+        line["e4b_dense"] = dense
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(dec, r["x"], r["w"], r["bias"], args.cpu_seconds)
     print(json.dumps(line), flush=True)

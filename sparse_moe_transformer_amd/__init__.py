@@ -58,10 +58,11 @@ class MoeFFN:
             pass
 
     def forward(self, x, w, out, bias=None):
-        """x [T, H] bf16; w: dict of bf16 tensors router, gate, up, down, dgate, dup, ddown."""
+        """x [T, H] bf16; w: dict of bf16 tensors router, gate, up, down, dgate, dup, ddown
+        (missing or None: absent, as in a config without experts)."""
         T = x.shape[0]
-        check(binding.moe_ffn_forward(self.h, T, _ptr(x), _ptr(w["router"]), _ptr(bias),
-                                      _ptr(w["gate"]), _ptr(w["up"]), _ptr(w["down"]),
+        check(binding.moe_ffn_forward(self.h, T, _ptr(x), _ptr(w.get("router")), _ptr(bias),
+                                      _ptr(w.get("gate")), _ptr(w.get("up")), _ptr(w.get("down")),
                                       _ptr(w.get("dgate")), _ptr(w.get("dup")), _ptr(w.get("ddown")),
                                       _ptr(out), _stream()))
         return out
@@ -71,8 +72,8 @@ class MoeFFN:
         pre_scale/post_scale: [H] fp32 tensors; out may be x."""
         T = x.shape[0]
         check(binding.moe_ffn_forward_block(self.h, T, _ptr(x), _ptr(pre_scale), _ptr(post_scale), float(eps),
-                                            _ptr(w["router"]), _ptr(bias), _ptr(w["gate"]), _ptr(w["up"]),
-                                            _ptr(w["down"]), _ptr(w.get("dgate")), _ptr(w.get("dup")),
+                                            _ptr(w.get("router")), _ptr(bias), _ptr(w.get("gate")), _ptr(w.get("up")),
+                                            _ptr(w.get("down")), _ptr(w.get("dgate")), _ptr(w.get("dup")),
                                             _ptr(w.get("ddown")), _ptr(out), _stream()))
         return out
 
@@ -83,8 +84,8 @@ class MoeFFN:
                 return None
             return (m["q"].data_ptr(), m["scale"].data_ptr(), m["tensor_scale"].data_ptr())
         T = x.shape[0]
-        check(binding.moe_ffn_forward_nvfp4(self.h, T, _ptr(x), _ptr(w["router"]), _ptr(bias),
-                                            d(w["gate"]), d(w["up"]), d(w["down"]),
+        check(binding.moe_ffn_forward_nvfp4(self.h, T, _ptr(x), _ptr(w.get("router")), _ptr(bias),
+                                            d(w.get("gate")), d(w.get("up")), d(w.get("down")),
                                             d(w.get("dgate")), d(w.get("dup")), d(w.get("ddown")),
                                             _ptr(out), _stream()))
         return out

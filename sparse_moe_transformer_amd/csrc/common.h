@@ -65,7 +65,7 @@ struct Workspace {
   bf16_t* h_d;          // [Tmax, D]
   bf16_t* y;            // [Tmax*k, H] perm order (MFMA path) or slot order (streaming path)
   bf16_t* y_d;          // [Tmax, H]
-  float* part;          // [kStreamKS][kStreamRows][2][I] (rows = slots) + [kDenseKS][64][2][D]
+  float* part;          // [kStreamKS][kStreamRows][2][I] (rows = slots) + [kDenseKSMax][64][2][D]
                         // (rows = tokens) gate/up partials of the streaming path
   float* ydp;           // [dense_down_slices][64][H] dense down partials (streaming path)
   bf16_t* xn;           // [Tmax, H] pre-normed block input (sandwich-norm forwards)
@@ -78,7 +78,9 @@ constexpr int kRouteSlices = 32;   // K-slices of the small-T router logits
 constexpr int kRouteSmallT = 64;   // largest T of the one-block-per-token router and the streaming path
 constexpr int kGemmBM = 256;       // MFMA tile rows (tokens)
 constexpr int kStreamKS = 2;       // K-slices of the streaming routed gate/up units
-constexpr int kDenseKS = 4;        // K-slices of the streaming dense gate/up units
+constexpr int kDenseKS = 4;        // K-slices of the streaming dense gate/up units (beside experts)
+constexpr int kDenseOnlyKS = 4;    // ... of a config without experts
+constexpr int kDenseKSMax = kDenseKS > kDenseOnlyKS ? kDenseKS : kDenseOnlyKS;
 constexpr int kDenseDownKS = 16;   // most K-slices of the streaming dense down units
 constexpr int kStreamRows = kRouteSmallT * 16;  // routed rows of the streaming path (T <= 64, k <= 16)
 constexpr int kArriveRoute = 0;                 // [64] token groups of the small-T router
@@ -90,9 +92,13 @@ struct Shape {
 
 // K-slices of the streaming dense-branch units: whole 64-row groups, at
 // most the constants above (no empty slice)
-__host__ __device__ inline int dense_gateup_slices(const Shape& sh) { return sh.H / 64 < kDenseKS ? sh.H / 64 : kDenseKS; }
-// The dense down units: 4 K-slices, more for a wide D (about 640 rows each,
-// so that a D = 10240 branch still spreads over a few hundred blocks)
+__host__ __device__ inline int dense_gateup_slices(const Shape& sh) {
+  const int ks = sh.E > 0 ? kDenseKS : kDenseOnlyKS;
+  return sh.H / 64 < ks ? sh.H / 64 : ks;
+}
+// The dense down units: K-slices of about 640 rows, at least 4 (so that a
+// D = 10240 branch spreads over a few hundred blocks; finer slices do not
+// stream faster and cost the combine a longer sum)
 __host__ __device__ inline int dense_down_slices(const Shape& sh) {
   int ks = sh.D / 640 > 4 ? sh.D / 640 : 4;
   if (ks > kDenseDownKS) ks = kDenseDownKS;

@@ -46,7 +46,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsChunk = 8;
 constexpr int kU = 16;  // weight rows in flight per thread
-constexpr int kDownCols = 128;  // output columns of a down unit
+constexpr int kDownCols = 128;  // output columns of a routed down unit
+constexpr int kDenseDownCols = 128;  // output columns of a dense down unit
+constexpr int kDenseOnlyCols = 256;  // output columns of a gate/up unit without experts
+constexpr int kDownColsMax = kDenseDownCols > kDownCols ? kDenseDownCols : kDownCols;
 
 __device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);  // a.lo | b.lo << 16
@@ -60,7 +63,7 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
 __device__ __forceinline__ float* part_ptr(const Workspace& ws, const Shape& sh, bool dense, int ks, int row,
                                            int mat) {
   if (!dense) return ws.part + ((size_t(ks) * kStreamRows + row) * 2 + mat) * sh.I;
-  float* base = ws.part + size_t(kStreamKS) * kStreamRows * 2 * sh.I;  // then [kDenseKS][64][2][D]
+  float* base = ws.part + size_t(kStreamKS) * kStreamRows * 2 * sh.I;  // then [kDenseKSMax][64][2][D]
   return base + ((size_t(ks) * kRouteSmallT + row) * 2 + mat) * sh.D;
 }
 
@@ -215,12 +218,13 @@ __device__ const float* unit_staged(const bf16_t* __restrict__ w, int ldw, int k
     for (int c = 0; c < CPT; ++c) acc[r][c] = 0.f;
   const __amdgpu_buffer_rsrc_t rw = rsrc_of(w);
   const uint32_t wrow = uint32_t(ldw) * 2, wv = uint32_t(k0) * wrow + cg * CPT * 2;
-  vec_t vw[U];
+  // two batches of U weight rows: the next batch's loads are issued before
+  // the current batch is consumed, so a thread always has loads in flight
+  auto load = [&](vec_t (&v)[U], int b) {
 #pragma unroll
-  for (int i = 0; i < U; ++i) vw[i] = (i < R) ? bload<vec_t, kPolicyNT>(rw, wv, uint32_t(i) * wrow) : vec_t{};
-  stage(xs, kbeg, kend);
-  __syncthreads();
-  for (int b = 0;;) {
+    for (int i = 0; i < U; ++i) v[i] = (b + i < R) ? bload<vec_t, kPolicyNT>(rw, wv, uint32_t(b + i) * wrow) : vec_t{};
+  };
+  auto consume = [&](const vec_t (&v)[U], int b) {
 #pragma unroll
     for (int i = 0; i < U; i += 2) {
       // rows past R hold zero weights; their LDS row index is clamped
@@ -231,14 +235,23 @@ __device__ const float* unit_staged(const bf16_t* __restrict__ w, int ldw, int k
       for (int r = 0; r < NT; ++r) {
         // (x[r][k], x[r][k+1]) from the two staged rows
         const uint32_t xp = (r & 1) ? perm_hi16(v0[r / 2], v1[r / 2]) : perm_lo16(v0[r / 2], v1[r / 2]);
-        dot_rows2<CPT>(acc[r], vw[i], vw[i + 1], xp);
+        dot_rows2<CPT>(acc[r], v[i], v[i + 1], xp);
       }
     }
+  };
+  vec_t va[U], vb[U];
+  load(va, 0);
+  stage(xs, kbeg, kend);
+  __syncthreads();
+  for (int b = 0;;) {
+    if (b + U < R) load(vb, b + U);
+    consume(va, b);
     b += U;
     if (b >= R) break;
-#pragma unroll
-    for (int i = 0; i < U; ++i)
-      vw[i] = (b + i < R) ? bload<vec_t, kPolicyNT>(rw, wv, uint32_t(b + i) * wrow) : vec_t{};
+    if (b + U < R) load(va, b + U);
+    consume(vb, b);
+    b += U;
+    if (b >= R) break;
   }
   return fold_rows<NT, NCOLS, CPT>(acc, red);
 }
@@ -315,12 +328,12 @@ __device__ ExpertRows expert_rows(const Shape& sh, const int32_t* __restrict__ t
 // Routed: units (ai-th active expert, ...) over the expert's rows, x gathered
 // by token.  Writes fp32 partial pre-activations per K-slice, indexed by
 // slot (routed) or token (dense).
-template <bool DENSE>
+template <bool DENSE, int NC = 64>
 __device__ void gateup_unit(const StreamArgs& a, const Workspace& ws, int KS, int u) {
   const Shape& sh = a.sh;
   const int H = sh.H;
   const int N = DENSE ? sh.D : sh.I;
-  const int per = (N / 64) * 2 * KS;
+  const int per = (N / NC) * 2 * KS;
   __shared__ int slot[kRouteSmallT];
   int grp = 0, rows = sh.T;
   if (!DENSE) {
@@ -334,14 +347,14 @@ __device__ void gateup_unit(const StreamArgs& a, const Workspace& ws, int KS, in
   // K-slices of whole 64-row groups (a thread's share of rows stays even)
   const int ks = u % KS;
   const int mat = (u / KS) & 1;
-  const int n0 = (u / (2 * KS)) * 64;
+  const int n0 = (u / (2 * KS)) * NC;
   const int g64 = H / 64;
   const int kbeg = (ks * g64 / KS) * 64, kend = ((ks + 1) * g64 / KS) * 64;
   const bf16_t* w = DENSE ? (mat ? a.du : a.dg) + n0 : (mat ? a.wu : a.wg) + (long long)grp * H * sh.I + n0;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16_t* xs = reinterpret_cast<bf16_t*>(smem_raw);  // [kend-kbeg][8] staged rows
-  float* red = reinterpret_cast<float*>(smem_raw);   // [5][8][64]
+  float* red = reinterpret_cast<float*>(smem_raw);   // [5][8][NC]
   __shared__ const bf16_t* act[kRowsChunk];
   __shared__ float* dst[kRowsChunk];
 
@@ -357,8 +370,8 @@ __device__ void gateup_unit(const StreamArgs& a, const Workspace& ws, int KS, in
     const bf16_t* rowp[kRowsChunk];
 #pragma unroll
     for (int r = 0; r < kRowsChunk; ++r) rowp[r] = act[r];
-    const float* sums = unit_x_rows<64>(nr, w, N, kbeg, kend, rowp, xs, red);
-    for (int o = threadIdx.x; o < nr * 64; o += kThreads) dst[o >> 6][o & 63] = sums[o];
+    const float* sums = unit_x_rows<NC>(nr, w, N, kbeg, kend, rowp, xs, red);
+    for (int o = threadIdx.x; o < nr * NC; o += kThreads) dst[o / NC][o % NC] = sums[o];
     __syncthreads();
   }
 }
@@ -385,6 +398,17 @@ __global__ __launch_bounds__(kThreads) void k_route_dense(
     route_slice<CW>(a.sh, slice_rows, TB, nslices, b % nslices, b / nslices, a.x, wr, bias, ws);
   else
     gateup_unit<true>(a, ws, KSd, b - nroute);
+}
+
+// The dense gate/up units alone (a config without experts: no router to
+// share the launch with), at the routed units' register budget.  NC = 256
+// columns per unit when D allows: each row piece is then 512 contiguous
+// bytes instead of 128, which a wide D (long rows) needs to stream well.
+template <int NC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_dense_gateup(StreamArgs a,
+                                                                                                     Workspace ws,
+                                                                                                     int KSd) {
+  gateup_unit<true, NC>(a, ws, KSd, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -428,12 +452,11 @@ __global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace w
 // of D) over the T rows of h_d, fp32 partial outputs per slice (summed by
 // the combine).  Routed: unit u = (ai-th active expert, 128 columns) over
 // the expert's rows of h (slot order), bf16 output rows y indexed by slot.
-template <bool DENSE>
+template <bool DENSE, int NC = kDownCols>
 __device__ void down_unit(const StreamArgs& a, const Workspace& ws, int u) {
   const Shape& sh = a.sh;
   const int H = sh.H;
-  constexpr int NC = kDownCols;  // output columns of a unit
-  const int nblk = H / NC;
+  const int nblk = H / NC;  // NC: output columns of a unit
   __shared__ int slot[kRouteSmallT];
   int grp = 0, rows = sh.T, kbeg = 0, kend = sh.I, ksd = 0;
   if (DENSE) {
@@ -485,7 +508,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
                                                                                                     int ud) {
   const int u = blockIdx.x;
   if (u < ud)
-    down_unit<true>(a, ws, u);
+    down_unit<true, kDenseDownCols>(a, ws, u);
   else
     down_unit<false>(a, ws, u - ud);
 }
@@ -527,7 +550,13 @@ hipError_t launch_route_dense(const StreamArgs& a, const bf16_t* wr, const float
   const size_t kl = size_t((sh.H / 64 + ksd - 1) / ksd) * 64;  // longest dense K-slice
   const size_t lds = ud ? std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * 64 * 4) : 0;
   if (nroute + ud == 0) return hipSuccess;
-  if (c.cw != 4)
+  if (nroute == 0 && sh.D % kDenseOnlyCols == 0) {
+    const size_t ldsw = std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * kDenseOnlyCols * 4);
+    hipLaunchKernelGGL(k_dense_gateup<kDenseOnlyCols>, dim3(ud / (kDenseOnlyCols / 64)), dim3(kThreads), ldsw, s,
+                       a, ws, ksd);
+  } else if (nroute == 0)
+    hipLaunchKernelGGL(k_dense_gateup<64>, dim3(ud), dim3(kThreads), lds, s, a, ws, ksd);
+  else if (c.cw != 4)
     hipLaunchKernelGGL(k_route_dense<8>, dim3(nroute + ud), dim3(kThreads), lds, s, a, wr, bias, ws, c.slice_rows, c.tb,
                        c.nslices, nroute, ksd);
   else
@@ -551,11 +580,11 @@ hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStrea
   if (sh.T == 0) return hipSuccess;
   const int nblk = sh.H / kDownCols;
   const int ksd = sh.D > 0 ? dense_down_slices(sh) : 1;
-  const int ud = sh.D > 0 ? nblk * ksd : 0;
+  const int ud = sh.D > 0 ? (sh.H / kDenseDownCols) * ksd : 0;
   const int max_active = std::min(sh.E, sh.T * sh.k);
   // longest K run of a unit: a dense K-slice or the expert width
   const int kd = ud ? (sh.D / 64 + ksd - 1) / ksd * 64 : 0;
-  const size_t lds = std::max(size_t(std::max(sh.I, kd)) * kRowsChunk * 2, size_t(5) * kRowsChunk * kDownCols * 4);
+  const size_t lds = std::max(size_t(std::max(sh.I, kd)) * kRowsChunk * 2, size_t(5) * kRowsChunk * kDownColsMax * 4);
   hipLaunchKernelGGL(k_stream_down, dim3(ud + max_active * nblk), dim3(kThreads), lds, s, a, ws, ud);
   return hipGetLastError();
 }
