@@ -15,11 +15,15 @@
  *     (gemma-llm API page gm.nn.Gemma4_26B_A4B, model description: every
  *     layer also has one dense MLP of width 2112 that all tokens pass through).
  *   - output: out[t] = sum_j w[t,j] * E_{e_j}(x_t) + Dense(x_t).
+ * A config with num_experts = 0 is a plain dense feed-forward block: the
+ * dense branch alone, no router (gemma-llm API page gm.nn.Gemma4_E4B:
+ * enable_moe False, num_experts 0, embed_dim 2560, hidden_dim 10240).
  *
  * Data layout (all row-major, all caller-owned DEVICE memory unless noted):
  *   x        [T, H]      bf16
  *   router_w [H, E]      bf16  (never quantised: the NVFP4 checkpoint config
- *                               lists router.proj under "ignore")
+ *                               lists router.proj under "ignore"; NULL iff
+ *                               num_experts == 0, as are router_b and w_*)
  *   router_b [E]         fp32 or NULL
  *   w_gate   [E, H, I]   bf16  (matrix e is [K=H, N=I], N contiguous)
  *   w_up     [E, H, I]   bf16
@@ -92,10 +96,12 @@ enum {
 
 typedef struct {
   int32_t hidden;        /* H: 2816 (multiple of 256, at most 4096) */
-  int32_t num_experts;   /* E: 128 (multiple of 4, 4..256) */
+  int32_t num_experts;   /* E: 128 (multiple of 4, 4..256), or 0: a dense FFN
+                            (then top_k = expert_dim = 0 and dense_dim > 0,
+                            else INVALID_ARG) */
   int32_t top_k;         /* k: 8 (1..min(E,16)) */
   int32_t expert_dim;    /* I: 704 (multiple of 64, at most 4096) */
-  int32_t dense_dim;     /* D: 2112 (multiple of 64, at most 4096), or 0: no dense branch */
+  int32_t dense_dim;     /* D: 2112 (multiple of 64, at most 16384), or 0: no dense branch */
   int32_t max_tokens;    /* largest T a forward on this handle may use (>= 1);
                             x [T, H], h [T*k, I] and h_d [T, D] in bf16 must each
                             stay below 2 GiB at T = max_tokens */
@@ -127,7 +133,9 @@ int moe_ffn_set_variant(moe_ffn_handle *h, int32_t variant);
 
 /* Forward of the block for T tokens with bf16 weights (weight_format must be
  * MOE_FFN_W_BF16).  0 <= T <= max_tokens; T == 0 queues nothing.
- * router_bias may be NULL; d_gate/d_up/d_down must be NULL iff dense_dim==0.
+ * router_bias may be NULL; d_gate/d_up/d_down must be NULL iff dense_dim==0;
+ * router_w, router_bias and w_gate/w_up/w_down must be NULL iff
+ * num_experts == 0 (INVALID_ARG otherwise).
  * With MOE_FFN_ACCUMULATE, out holds the residual on entry and receives
  * residual + block(x) (out == x allowed); otherwise out must not overlap x. */
 int moe_ffn_forward(moe_ffn_handle *h, int32_t T, const void *x, const void *router_w,
@@ -139,7 +147,8 @@ int moe_ffn_forward(moe_ffn_handle *h, int32_t T, const void *x, const void *rou
  * must be MOE_FFN_W_NVFP4).  Activations, router and output stay bf16; each
  * weight tile is decoded to bf16 on chip (an e2m1 x e4m3 product is exact in
  * bf16) and the fp32 tensor scale is applied to the fp32 accumulator.  The
- * dense descriptors must have NULL members iff dense_dim == 0. */
+ * dense descriptors must have NULL members iff dense_dim == 0, the expert
+ * descriptors (and router_w) iff num_experts == 0. */
 int moe_ffn_forward_nvfp4(moe_ffn_handle *h, int32_t T, const void *x, const void *router_w,
                           const float *router_bias, const moe_ffn_nvfp4_t *w_gate,
                           const moe_ffn_nvfp4_t *w_up, const moe_ffn_nvfp4_t *w_down,
@@ -175,7 +184,8 @@ int moe_ffn_forward_block(moe_ffn_handle *h, int32_t T, const void *x, const flo
  *   (row of slot (t, j)).  topk_w is not written by moe_ffn_align_only.
  * The weight-streaming variant never builds the grouping tables (its
  * kernels derive each expert's rows from topk_idx); after such a forward
- * this call first queues the grouping kernels on `stream`. */
+ * this call first queues the grouping kernels on `stream`.  UNSUPPORTED for
+ * a config without experts. */
 int moe_ffn_get_routing(moe_ffn_handle *h, int32_t *topk_idx, float *topk_w, int32_t *counts,
                         int32_t *offsets, int32_t *perm, int32_t *pos, void *stream);
 
@@ -185,13 +195,16 @@ int moe_ffn_get_routing(moe_ffn_handle *h, int32_t *topk_idx, float *topk_w, int
  * row, same order), h_d [T, D] bf16 and y_d [T, H] bf16 (dense branch).
  * The weight-streaming variant keeps routed rows in (token, slot) order;
  * after such a forward this call queues the grouping kernels and a copy
- * into grouped order on `stream`. */
+ * into grouped order on `stream`.  A dense FFN (num_experts == 0) forward
+ * on the MFMA tiles without MOE_FFN_ACCUMULATE writes its rows straight to
+ * out, so asking for y_dense after it returns UNSUPPORTED. */
 int moe_ffn_get_intermediates(moe_ffn_handle *h, void *h_rows, void *y_rows, void *h_dense,
                               void *y_dense, void *stream);
 
 /* Test hook: run only the expert grouping (counts, offsets, perm, pos and
  * the tile lists) on caller-given routing topk_idx [T, k] int32 (device),
- * each row holding k distinct ids in [0, E) in ascending order. */
+ * each row holding k distinct ids in [0, E) in ascending order.
+ * UNSUPPORTED for a config without experts. */
 int moe_ffn_align_only(moe_ffn_handle *h, int32_t T, const int32_t *topk_idx, void *stream);
 
 /* Per-stage timing with HIP events recorded on the forward's stream.
