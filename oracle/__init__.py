@@ -11,6 +11,7 @@ from .block import (NEAR_TIE_GAP, align, dense_block, dense_ffn, gelu_tanh, gegl
                     moe_block, moe_ffn,
                       moe_ffn_layer_residual, rms_norm, round_bf16, route, router_logits,
                       routed_mixture_dense_mask, select_topk, softmax, widen_bf16)
+from .fp8 import dequant_matrix_fp8
 from .nvfp4 import E2M1_TABLE, E4M3_TABLE, dequant_matrix, e2m1_value, e4m3fn_value
 
 __all__ = [
@@ -18,5 +19,5 @@ __all__ = [
     "moe_ffn_layer_residual", "rms_norm", "round_bf16", "route", "router_logits",
     "routed_mixture_dense_mask",
     "select_topk", "softmax", "widen_bf16", "E2M1_TABLE", "E4M3_TABLE",
-    "dequant_matrix", "e2m1_value", "e4m3fn_value",
+    "dequant_matrix", "dequant_matrix_fp8", "e2m1_value", "e4m3fn_value",
 ]

@@ -194,7 +194,10 @@ def geglu(X: np.ndarray, w_gate, w_up, w_down) -> tuple:
 
 
 def _matrix(w, g: int) -> np.ndarray:
-    """fp64 [K, N] matrix g of a weight stack (bf16 bits, floats or NVFP4)."""
+    """fp64 [K, N] matrix g of a weight stack (bf16 bits, floats, NVFP4 or FP8)."""
+    if isinstance(w, dict) and "q8" in w:
+        from .fp8 import dequant_matrix_fp8
+        return dequant_matrix_fp8(w["q8"][g], w["tensor_scale"][g])
     if isinstance(w, dict):
         from .nvfp4 import dequant_matrix
         return dequant_matrix(w["q"][g], w["scale"][g], w["tensor_scale"][g])
@@ -220,7 +223,8 @@ def moe_ffn(x, router_w, w_gate, w_up, w_down, d_gate=None, d_up=None, d_down=No
     x [T, H] (bf16 bits or floats); router_w [H, E]; w_gate, w_up [E, H, I];
     w_down [E, I, H]; d_gate, d_up [H, D]; d_down [D, H] (None: no dense
     branch).  Expert and dense matrices may be NVFP4 packs (dicts with q,
-    scale, tensor_scale), which are dequantised first.
+    scale, tensor_scale) or FP8 packs (dicts with q8, tensor_scale), which
+    are dequantised first.
 
     out[t] = sum_j w[t, j] * Expert_{e_j}(x_t) + Dense(x_t), the j-sum in
     ascending j, then the dense term.  With ``tokens`` only those output rows
@@ -261,7 +265,12 @@ def moe_ffn(x, router_w, w_gate, w_up, w_down, d_gate=None, d_up=None, d_down=No
         res["tokens"] = tokens
         return res
 
-    I = (w_down["q"].shape[2] * 2) if isinstance(w_down, dict) else np.asarray(w_down).shape[1]
+    if isinstance(w_down, dict) and "q8" in w_down:
+        I = w_down["q8"].shape[1]
+    elif isinstance(w_down, dict):
+        I = w_down["q"].shape[2] * 2
+    else:
+        I = np.asarray(w_down).shape[1]
     rows = T * top_k
     h = np.zeros((rows, I)) if intermediates else None
     y = np.zeros((rows, H))

@@ -8,7 +8,8 @@ them in the byte formats the block consumes:
 * bf16 tensors as ``uint16`` arrays of raw bits (round-to-nearest-even from
   fp32 draws), shaped exactly like the device buffers;
 * the NVFP4 weight-only packing (e2m1 codes two per byte, e4m3 group scales,
-  one fp32 scale per tensor), used as a *checkpoint producer*: both sides read
+  one fp32 scale per tensor) and the FP8 weight-only packing (e4m3fn codes,
+  one fp32 scale per matrix), used as *checkpoint producers*: both sides read
   the same packed bytes, so the rounding choices made here cannot affect
   parity.
 
@@ -49,6 +50,7 @@ class FFNShape:
     layers: int = 1
     skew: bool = False   # add a per-expert logit bias with Zipf-shaped loads
     nvfp4: bool = False  # weight-only NVFP4 packing of every expert/dense matrix
+    fp8: bool = False    # weight-only FP8 (e4m3fn + per-matrix scale) packing
 
     def with_tokens(self, t: int) -> "FFNShape":
         return replace(self, tokens=int(t))
@@ -290,3 +292,49 @@ def bf16_bits(x) -> np.ndarray:
     x = np.asarray(x)
     return x if x.dtype == np.uint16 else f32_to_bf16_bits(x.astype(np.float32))
 
+
+
+# ---------------------------------------------------------------------------
+# FP8 weight-only packing (checkpoint producer)
+# ---------------------------------------------------------------------------
+
+
+def fp8_pack(w_kn: np.ndarray) -> tuple:
+    """Pack one [K, N] weight matrix (fp32 values) as e4m3fn codes with one
+    fp32 scale: returns (q [K, N] uint8, tensor_scale float).
+
+    tensor_scale = amax / 448 (1 for an all-zero matrix); code = nearest
+    e4m3fn value of w / tensor_scale (ties to even), clamped to +-448 first.
+    The layout stays [K, N] (N contiguous), like the bf16 weights.
+    """
+    w = np.asarray(w_kn, dtype=np.float32)
+    amax = float(np.max(np.abs(w))) if w.size else 0.0
+    st = np.float32(amax / _FP8_MAX) if amax > 0 else np.float32(1.0)
+    v = np.clip(w / st, -_FP8_MAX, _FP8_MAX)
+    return _to_e4m3_bits(v).reshape(w.shape), float(st)
+
+
+def fp8_pack_stack(w_ekn_bits: np.ndarray) -> dict:
+    """Pack a stack [G, K, N] of bf16-bit matrices; one scale per matrix."""
+    G, K, N = w_ekn_bits.shape
+    q = np.empty((G, K, N), dtype=np.uint8)
+    st = np.empty((G,), dtype=np.float32)
+
+    def work(g: int) -> None:
+        q[g], st[g] = fp8_pack(bf16_bits_to_f32(w_ekn_bits[g]))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(G)))
+    return {"q8": q, "tensor_scale": st}
+
+
+def make_fp8_weights(shape: FFNShape, seed: int = 0, layer: int = 0) -> dict:
+    """bf16 N(0, 1/fan_in) weights of one layer, then FP8-packed; the router
+    stays bf16 and dense matrices are packed as stacks of one."""
+    w = make_weights(shape, seed, layer)
+    out = {"router": w["router"]}
+    for name in ("gate", "up", "down"):
+        out[name] = fp8_pack_stack(w[name]) if w[name] is not None else None
+    for name in ("dgate", "dup", "ddown"):
+        out[name] = fp8_pack_stack(w[name][None]) if w[name] is not None else None
+    return out

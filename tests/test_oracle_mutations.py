@@ -307,3 +307,24 @@ def test_dense_ffn_row_mixing(monkeypatch):
 
     _patch(monkeypatch, "dense_ffn", bad)
     _expect_caught(DENSE_FFN_PINS)
+
+
+def test_fp8_scale_dropped(monkeypatch):
+    import oracle.fp8 as of
+
+    _patch(monkeypatch, "dequant_matrix_fp8", lambda q, st: on.E4M3_TABLE[np.asarray(q, dtype=np.uint8)],
+           module=of)
+    _expect_caught([pins.test_fp8_dequant_matches_torch_and_layout])
+
+
+def test_fp8_transposed_layout(monkeypatch):
+    import oracle.fp8 as of
+
+    real = of.dequant_matrix_fp8
+
+    def bad(q, st):
+        q = np.asarray(q)
+        return real(q.reshape(q.shape[::-1]).T, st)  # reads the bytes as [N, K]
+
+    _patch(monkeypatch, "dequant_matrix_fp8", bad, module=of)
+    _expect_caught([pins.test_fp8_dequant_matches_torch_and_layout])

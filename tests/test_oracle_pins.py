@@ -551,6 +551,47 @@ def test_nvfp4_block_uses_dequantised_weights():
     assert np.array_equal(r["out"], r2["out"])
 
 
+def test_fp8_dequant_matches_torch_and_layout():
+    """Pin: the FP8 decode equals torch's float8_e4m3fn -> float64 cast times
+    the fp32 scale (a library routine), value (k, n) sits at q[k, n]; the
+    packing error is at most half an e4m3 step (3 mantissa bits, relative
+    2^-4) of the scaled value, or half the subnormal step 2^-9 * scale; and
+    packing the decoded matrix again reproduces the bytes."""
+    g = np.random.default_rng(8)
+    K, N = 64, 48
+    wv = g.standard_normal((K, N)).astype(np.float32) * 0.05
+    q, st = synth.fp8_pack(wv)
+    assert q.shape == (K, N) and q.dtype == np.uint8
+    deq = oracle.dequant_matrix_fp8(q, st)
+    ref = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy() * float(np.float32(st))
+    assert np.array_equal(deq, ref)
+    k, n = 33, 7
+    assert deq[k, n] == oracle.e4m3fn_value(q[k, n]) * float(np.float32(st))
+    err = np.abs(deq - wv)
+    bound = np.maximum(np.abs(wv) * 2.0 ** -4, 2.0 ** -10 * float(st)) + 1e-12
+    assert np.all(err <= bound)
+    assert np.max(np.abs(deq)) == 448.0 * float(np.float32(st))  # amax maps to the top code
+    q2, st2 = synth.fp8_pack(deq.astype(np.float32))
+    assert np.array_equal(q2, q) and st2 == st
+
+
+def test_fp8_block_uses_dequantised_weights():
+    """The FP8 block equals the bf16-weight path applied to the decoded
+    matrices (only the weight format changes), dense-only config included."""
+    shape, x, w = tiny_inputs()
+    pk = {n: synth.fp8_pack_stack(w[n]) for n in ("gate", "up", "down")}
+    pk.update({n: synth.fp8_pack_stack(w[n][None]) for n in ("dgate", "dup", "ddown")})
+    r = oracle.moe_ffn(x, w["router"], pk["gate"], pk["up"], pk["down"], pk["dgate"],
+                       pk["dup"], pk["ddown"], top_k=2)
+    deq = {n: np.stack([oracle.dequant_matrix_fp8(pk[n]["q8"][g], pk[n]["tensor_scale"][g])
+                        for g in range(pk[n]["q8"].shape[0])]) for n in pk}
+    r2 = oracle.moe_ffn(x, w["router"], deq["gate"], deq["up"], deq["down"], deq["dgate"][0],
+                        deq["dup"][0], deq["ddown"][0], top_k=2)
+    assert np.array_equal(r["out"], r2["out"])
+    d = oracle.dense_ffn(x, pk["dgate"], pk["dup"], pk["ddown"])
+    assert np.array_equal(d["out"], r2["y_d"])
+
+
 # ---------------------------------------------------------------------------
 # the skewed-load workload's calibration
 # ---------------------------------------------------------------------------
