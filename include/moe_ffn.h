@@ -46,6 +46,15 @@
  *   tensor_scale [G] fp32
  *   w = e2m1(code) * e4m3(scale) * tensor_scale.
  *
+ * FP8 weight-only matrices (a reading of the SFP8 footprint quoted for the
+ * 26B model on the inference-research page: 28.8 GB against 57.7 GB in
+ * BF16, i.e. one byte per weight; the page defines no encoding): OCP
+ * float8_e4m3fn codes in the bf16 weights' [K, N] layout, one fp32 scale per
+ * matrix, passed per projection as a moe_ffn_fp8_t of G matrices:
+ *   q            [G, K, N] uint8 float8_e4m3fn
+ *   tensor_scale [G] fp32
+ *   w = e4m3(q) * tensor_scale.
+ *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  * stream).  Every call that takes a stream only queues work on it and
  * returns at once; no call synchronises the device except when the
@@ -82,7 +91,7 @@ enum {
   MOE_FFN_ERR_OOM = -4          /* workspace allocation failed at create */
 };
 
-enum { MOE_FFN_W_BF16 = 0, MOE_FFN_W_NVFP4 = 1 };
+enum { MOE_FFN_W_BF16 = 0, MOE_FFN_W_NVFP4 = 1, MOE_FFN_W_FP8 = 2 };
 
 /* config flags */
 enum { MOE_FFN_ACCUMULATE = 1u << 0 }; /* out += block(x) (residual stack); out may alias x */
@@ -105,7 +114,7 @@ typedef struct {
   int32_t max_tokens;    /* largest T a forward on this handle may use (>= 1);
                             x [T, H], h [T*k, I] and h_d [T, D] in bf16 must each
                             stay below 2 GiB at T = max_tokens */
-  int32_t weight_format; /* MOE_FFN_W_BF16 or MOE_FFN_W_NVFP4 */
+  int32_t weight_format; /* MOE_FFN_W_BF16, MOE_FFN_W_NVFP4 or MOE_FFN_W_FP8 */
   uint32_t flags;        /* MOE_FFN_ACCUMULATE or 0 */
 } moe_ffn_config;
 
@@ -114,6 +123,11 @@ typedef struct {
   const uint8_t *scale;       /* [G, N, K/16] float8_e4m3fn group scales */
   const float *tensor_scale;  /* [G] fp32 per-matrix scale */
 } moe_ffn_nvfp4_t;
+
+typedef struct {
+  const uint8_t *q;           /* [G, K, N] float8_e4m3fn codes (N contiguous) */
+  const float *tensor_scale;  /* [G] fp32 per-matrix scale */
+} moe_ffn_fp8_t;
 
 /* Bytes of device workspace a handle with this config allocates at create.
  * Returns INVALID_ARG for NULL pointers, UNSUPPORTED for shapes the library
@@ -154,6 +168,20 @@ int moe_ffn_forward_nvfp4(moe_ffn_handle *h, int32_t T, const void *x, const voi
                           const moe_ffn_nvfp4_t *w_up, const moe_ffn_nvfp4_t *w_down,
                           const moe_ffn_nvfp4_t *d_gate, const moe_ffn_nvfp4_t *d_up,
                           const moe_ffn_nvfp4_t *d_down, void *out, void *stream);
+
+/* Same block with FP8 weight-only expert and dense matrices (weight_format
+ * must be MOE_FFN_W_FP8; the layout is given above).  Activations, router
+ * and output stay bf16.  Small T streams the one-byte codes (half the bytes
+ * of bf16) and widens them to fp32 in registers; the MFMA tiles convert each
+ * weight tile to bf16 on chip (exact: e4m3 has 3 mantissa bits).  The fp32
+ * per-matrix scale multiplies the fp32 sums.  Expert descriptors (and
+ * router_w) must be NULL iff num_experts == 0, dense descriptors iff
+ * dense_dim == 0; q must be 16-byte aligned, tensor_scale 4-byte aligned. */
+int moe_ffn_forward_fp8(moe_ffn_handle *h, int32_t T, const void *x, const void *router_w,
+                        const float *router_bias, const moe_ffn_fp8_t *w_gate, const moe_ffn_fp8_t *w_up,
+                        const moe_ffn_fp8_t *w_down, const moe_ffn_fp8_t *d_gate,
+                        const moe_ffn_fp8_t *d_up, const moe_ffn_fp8_t *d_down, void *out,
+                        void *stream);
 
 /* The feed-forward sub-block of a layer with its sandwich norms and the
  * residual (archdb page "Gemma-4-26B-A4B": normalization RMSNorm, placement

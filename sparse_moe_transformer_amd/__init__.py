@@ -10,10 +10,11 @@ from __future__ import annotations
 
 from . import binding
 from .binding import (MOE_FFN_ACCUMULATE, MOE_FFN_VARIANT_AUTO, MOE_FFN_VARIANT_MFMA,
-                      MOE_FFN_VARIANT_STREAM, MOE_FFN_W_BF16, MOE_FFN_W_NVFP4, MoeFFNError, check)
+                      MOE_FFN_VARIANT_STREAM, MOE_FFN_W_BF16, MOE_FFN_W_FP8, MOE_FFN_W_NVFP4, MoeFFNError,
+                      check)
 
 __all__ = ["MoeFFN", "binding", "MoeFFNError", "MOE_FFN_ACCUMULATE", "MOE_FFN_VARIANT_AUTO",
-           "MOE_FFN_VARIANT_MFMA", "MOE_FFN_VARIANT_STREAM", "MOE_FFN_W_BF16", "MOE_FFN_W_NVFP4"]
+           "MOE_FFN_VARIANT_MFMA", "MOE_FFN_VARIANT_STREAM", "MOE_FFN_W_BF16", "MOE_FFN_W_FP8", "MOE_FFN_W_NVFP4"]
 
 
 def _ptr(t):
@@ -39,7 +40,8 @@ class MoeFFN:
 
     @classmethod
     def for_shape(cls, shape, max_tokens=None, **kw):
-        fmt = MOE_FFN_W_NVFP4 if getattr(shape, "nvfp4", False) else MOE_FFN_W_BF16
+        fmt = (MOE_FFN_W_NVFP4 if getattr(shape, "nvfp4", False)
+               else MOE_FFN_W_FP8 if getattr(shape, "fp8", False) else MOE_FFN_W_BF16)
         return cls(shape.hidden, shape.experts, shape.top_k, shape.expert_dim, shape.dense_dim,
                    max_tokens or shape.tokens, weight_format=fmt, **kw)
 
@@ -88,6 +90,20 @@ class MoeFFN:
                                             d(w.get("gate")), d(w.get("up")), d(w.get("down")),
                                             d(w.get("dgate")), d(w.get("dup")), d(w.get("ddown")),
                                             _ptr(out), _stream()))
+        return out
+
+    def forward_fp8(self, x, w, out, bias=None):
+        """w: router bf16 tensor; gate/up/down/dgate/dup/ddown dicts of q8 (uint8 [G, K, N])
+        and tensor_scale (fp32 [G]), or None where the config has no such matrices."""
+        def d(m):
+            if m is None:
+                return None
+            return (m["q8"].data_ptr(), m["tensor_scale"].data_ptr())
+        T = x.shape[0]
+        check(binding.moe_ffn_forward_fp8(self.h, T, _ptr(x), _ptr(w.get("router")), _ptr(bias),
+                                          d(w.get("gate")), d(w.get("up")), d(w.get("down")),
+                                          d(w.get("dgate")), d(w.get("dup")), d(w.get("ddown")),
+                                          _ptr(out), _stream()))
         return out
 
     def routing(self, T):

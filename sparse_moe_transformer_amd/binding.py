@@ -22,6 +22,7 @@ MOE_FFN_ERR_OOM = -4
 
 MOE_FFN_W_BF16 = 0
 MOE_FFN_W_NVFP4 = 1
+MOE_FFN_W_FP8 = 2
 MOE_FFN_ACCUMULATE = 1
 
 MOE_FFN_VARIANT_AUTO = 0
@@ -30,7 +31,8 @@ MOE_FFN_VARIANT_MFMA = 2
 
 EXPORTS = (
     "moe_ffn_workspace_bytes", "moe_ffn_create", "moe_ffn_destroy", "moe_ffn_set_variant",
-    "moe_ffn_forward", "moe_ffn_forward_nvfp4", "moe_ffn_forward_block", "moe_ffn_get_routing",
+    "moe_ffn_forward", "moe_ffn_forward_nvfp4", "moe_ffn_forward_fp8", "moe_ffn_forward_block",
+    "moe_ffn_get_routing",
     "moe_ffn_get_intermediates", "moe_ffn_align_only", "moe_ffn_profile_begin",
     "moe_ffn_profile_end", "moe_ffn_last_error",
 )
@@ -49,6 +51,10 @@ class moe_ffn_config(ctypes.Structure):
 class moe_ffn_nvfp4_t(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p),
                 ("tensor_scale", ctypes.c_void_p)]
+
+
+class moe_ffn_fp8_t(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p)]
 
 
 class MoeFFNError(RuntimeError):
@@ -76,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_set_variant.argtypes = [vp, i32]
         L.moe_ffn_forward.argtypes = [vp, i32] + [vp] * 11
         L.moe_ffn_forward_nvfp4.argtypes = [vp, i32, vp, vp, vp] + [P(moe_ffn_nvfp4_t)] * 6 + [vp, vp]
+        L.moe_ffn_forward_fp8.argtypes = [vp, i32, vp, vp, vp] + [P(moe_ffn_fp8_t)] * 6 + [vp, vp]
         L.moe_ffn_forward_block.argtypes = [vp, i32, vp, vp, vp, ctypes.c_float] + [vp] * 10
         L.moe_ffn_get_routing.argtypes = [vp] + [vp] * 7
         L.moe_ffn_get_intermediates.argtypes = [vp] + [vp] * 5
@@ -142,6 +149,17 @@ def moe_ffn_forward_nvfp4(h, T, x, router_w, router_bias, w_gate, w_up, w_down, 
     return lib().moe_ffn_forward_nvfp4(h, T, x, router_w, router_bias, desc(w_gate), desc(w_up),
                                        desc(w_down), desc(d_gate), desc(d_up), desc(d_down),
                                        out, stream)
+
+
+def moe_ffn_forward_fp8(h, T, x, router_w, router_bias, w_gate, w_up, w_down, d_gate, d_up,
+                        d_down, out, stream) -> int:
+    """Weight descriptors are (q_ptr, tensor_scale_ptr) tuples or None."""
+    def desc(d):
+        if d is None:
+            return None
+        return ctypes.byref(moe_ffn_fp8_t(*d))
+    return lib().moe_ffn_forward_fp8(h, T, x, router_w, router_bias, desc(w_gate), desc(w_up),
+                                     desc(w_down), desc(d_gate), desc(d_up), desc(d_down), out, stream)
 
 
 def moe_ffn_forward_block(h, T, x, pre_scale, post_scale, eps, router_w, router_bias, w_gate, w_up,

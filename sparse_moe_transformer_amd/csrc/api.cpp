@@ -83,7 +83,8 @@ int validate_config(const moe_ffn_config* c) {
   }
   if (c->dense_dim < 0 || c->dense_dim % 64 || c->dense_dim > kMaxDenseDim)
     return fail(MOE_FFN_ERR_UNSUPPORTED, "dense_dim must be 0 or a multiple of 64 in [64, 16384]");
-  if (c->weight_format != MOE_FFN_W_BF16 && c->weight_format != MOE_FFN_W_NVFP4)
+  if (c->weight_format != MOE_FFN_W_BF16 && c->weight_format != MOE_FFN_W_NVFP4 &&
+      c->weight_format != MOE_FFN_W_FP8)
     return fail(MOE_FFN_ERR_UNSUPPORTED, "unknown weight_format");
   if (c->flags & ~uint32_t(MOE_FFN_ACCUMULATE)) return fail(MOE_FFN_ERR_UNSUPPORTED, "unknown flag bits");
   // the MFMA kernels address activation operands (x [T, H], h [T*k, I],
@@ -369,6 +370,24 @@ int check_fp4(const moe_ffn_nvfp4_t* m, bool required, const char* name) {
   return MOE_FFN_OK;
 }
 
+int check_fp8(const moe_ffn_fp8_t* m, bool required, const char* name) {
+  if (!required) {
+    if (m && (m->q || m->tensor_scale))
+      return fail(MOE_FFN_ERR_INVALID_ARG, std::string(name) + " must be empty: the config has no such matrices");
+    return MOE_FFN_OK;
+  }
+  if (!m || !m->q || !m->tensor_scale)
+    return fail(MOE_FFN_ERR_INVALID_ARG, std::string(name) + ": q and tensor_scale must not be NULL");
+  if (!aligned16(m->q) || (reinterpret_cast<uintptr_t>(m->tensor_scale) & 3u))
+    return fail(MOE_FFN_ERR_INVALID_ARG, std::string(name) + ": misaligned pointer");
+  return MOE_FFN_OK;
+}
+
+moe::Fp8Mat to_mat8(const moe_ffn_fp8_t* m) {
+  if (!m) return moe::Fp8Mat{nullptr, nullptr};
+  return moe::Fp8Mat{m->q, m->tensor_scale};
+}
+
 moe::Fp4Mat to_mat(const moe_ffn_nvfp4_t* m) {
   if (!m) return moe::Fp4Mat{nullptr, nullptr, nullptr};
   return moe::Fp4Mat{m->q, m->scale, m->tensor_scale};
@@ -582,6 +601,44 @@ int moe_ffn_forward_nvfp4(moe_ffn_handle* h, int32_t T, const void* x, const voi
     a.fdu = to_mat(dense ? d_up : nullptr);
     a.fdd = to_mat(dense ? d_down : nullptr);
     a.nvfp4 = true;
+    return run_forward(h, T, x, router_w, router_bias, a, out, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return fail(MOE_FFN_ERR_HIP, ex.what());
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_forward_fp8(moe_ffn_handle* h, int32_t T, const void* x, const void* router_w, const float* router_bias,
+                        const moe_ffn_fp8_t* w_gate, const moe_ffn_fp8_t* w_up, const moe_ffn_fp8_t* w_down,
+                        const moe_ffn_fp8_t* d_gate, const moe_ffn_fp8_t* d_up, const moe_ffn_fp8_t* d_down,
+                        void* out, void* stream) {
+  try {
+    if (int r = common_forward_checks(h, T, x, router_w, router_bias, out, MOE_FFN_W_FP8)) return r;
+    const bool experts = h->cfg.num_experts > 0;
+    if (int r = check_fp8(w_gate, experts, "w_gate")) return r;
+    if (int r = check_fp8(w_up, experts, "w_up")) return r;
+    if (int r = check_fp8(w_down, experts, "w_down")) return r;
+    const bool dense = h->cfg.dense_dim > 0;
+    if (int r = check_fp8(d_gate, dense, "d_gate")) return r;
+    if (int r = check_fp8(d_up, dense, "d_up")) return r;
+    if (int r = check_fp8(d_down, dense, "d_down")) return r;
+    if (T == 0) {
+      g_err.clear();
+      return MOE_FFN_OK;
+    }
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(MOE_FFN_ERR_HIP, "cannot make the handle's device current");
+    moe::StreamArgs a{};
+    a.sh = shape_of(h, T);
+    a.x = static_cast<const moe::bf16_t*>(x);
+    a.qg = to_mat8(experts ? w_gate : nullptr);
+    a.qu = to_mat8(experts ? w_up : nullptr);
+    a.qd = to_mat8(experts ? w_down : nullptr);
+    a.qdg = to_mat8(dense ? d_gate : nullptr);
+    a.qdu = to_mat8(dense ? d_up : nullptr);
+    a.qdd = to_mat8(dense ? d_down : nullptr);
+    a.fp8 = true;
     return run_forward(h, T, x, router_w, router_bias, a, out, static_cast<hipStream_t>(stream));
   } catch (const std::exception& ex) {
     return fail(MOE_FFN_ERR_HIP, ex.what());

@@ -112,6 +112,12 @@ struct Fp4Mat {
   const float* tscale;
 };
 
+// FP8 matrix stack: [G][K][N] float8_e4m3fn codes and [G] fp32 scales
+struct Fp8Mat {
+  const uint8_t* q;
+  const float* tscale;
+};
+
 // ---- launches (each queues on `s` and returns the launch status) ----------
 
 // Buffer-resource loads: base pointer in scalar registers (it must be the
@@ -153,6 +159,9 @@ struct StreamArgs {
   // NVFP4 weights (nvfp4 == true)
   Fp4Mat fg, fu, fd, fdg, fdu, fdd;
   bool nvfp4;
+  // FP8 weights (fp8 == true)
+  Fp8Mat qg, qu, qd, qdg, qdu, qdd;
+  bool fp8;
 };
 // Streaming path (T <= 64, bf16 weights).  The router and the dense
 // branch's gate/up units share one launch; then the routed gate/up partial

@@ -38,6 +38,10 @@
 //      decode its 32 codes of a stage to bf16 (an e2m1 x e4m3 product is
 //      exact in bf16) into an A-style [256 n][32 k] tile; the fp32 tensor
 //      scale is applied in the epilogue.
+//   B  FP8 weights are [K, N] e4m3fn codes: a thread loads 16 codes of one
+//      k row, converts them to bf16 (exact: e4m3 has 3 mantissa bits) and
+//      writes them in the bf16 layout above, so the transposing reads are
+//      shared; the fp32 per-matrix scale is applied in the epilogue.
 // After the K loop the same LDS stages the bf16 output tile, which leaves
 // the block in 16-byte row stores.
 //
@@ -63,7 +67,7 @@ constexpr int kOpBytes = 256 * BK * 2;     // one operand tile of a stage: 16 KB
 constexpr int kStageBytes = 2 * kOpBytes;  // A, then B
 
 enum { MODE_PLAIN_BF16 = 0, MODE_PLAIN_F32 = 1, MODE_GATEUP = 2 };
-enum { W_BF16 = 0, W_FP4 = 1 };
+enum { W_BF16 = 0, W_FP4 = 1, W_FP8 = 2 };
 
 struct Seg {
   const bf16_t* A;
@@ -74,6 +78,7 @@ struct Seg {
   long long b_gstride;    // elements between groups
   int ldb;
   Fp4Mat F0, F1;          // NVFP4 [G][N][K/2], [G][N][K/16], [G]
+  Fp8Mat Q0, Q1;          // FP8 [G][K][ldb] e4m3fn codes (group stride b_gstride), [G] scales
   int K;
   int N;                  // output columns
   void* C;
@@ -237,6 +242,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   const uint8_t* fq = nullptr;  // NVFP4: codes and scales of LDS column tid / 2, k half tid % 2
   const uint8_t* fs = nullptr;
   const int fcol = tid >> 1, fkh = tid & 1;
+  // FP8: thread tid loads codes k row q8k, columns q8c*16 .. +15 of the
+  // stage's 256 B-columns (half q8c / 8)
+  const int q8k = tid >> 4, q8c = tid & 15;
+  const uint8_t* q8 = nullptr;
+  if (WF == W_FP8) {
+    const int h = q8c >> 3, lc = (q8c & 7) * 16;
+    const Fp8Mat* Q = &S.Q0;
+    int col = n0 + 128 * h + lc;
+    if (MODE == MODE_GATEUP) {
+      Q = h ? &S.Q1 : &S.Q0;
+      col = n0 + lc;
+    }
+    // columns past N read column 0 instead: they only feed output columns
+    // that are never stored
+    q8 = Q->q + grp * S.b_gstride + (long long)q8k * S.ldb + (col < N ? col : 0);
+  }
   if (WF == W_BF16) {
     const bf16_t* Bm = S.B0;
     int cbase = n0 + 128 * bh;
@@ -251,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       const int col = cbase + ((lane & 15) ^ fb(k)) * 8;
       boff[q] = col < N ? int(uint32_t(k) * brow + uint32_t(col) * 2u) : kOutOfRange;
     }
-  } else {
+  } else if (WF == W_FP4) {
     const Fp4Mat* F = &S.F0;
     int ncol = n0 + fcol;
     if (MODE == MODE_GATEUP && fcol >= 128) {
@@ -291,6 +312,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     const int kk = (kt0 + min(st, nk - 1)) * BK;
     q = *reinterpret_cast<const u32x2_t*>(fq + kk / 2);
     sc = *(fs + kk / 16);
+  };
+  // FP8: the 16 codes of a stage, loaded two stages ahead, written as bf16
+  auto fp8_load = [&](int st, u32x4_t& q) {
+    const int kk = (kt0 + min(st, nk - 1)) * BK;
+    q = *reinterpret_cast<const u32x4_t*>(q8 + (long long)kk * S.ldb);
+  };
+  auto fp8_store = [&](int st, const u32x4_t& q) {
+    lds_u8* row = lds3 + (st & (kStages - 1)) * kStageBytes + kOpBytes + (q8c >> 3) * (kOpBytes / 2) + q8k * 256;
+    u32x4_t w[2];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      // bytes 0,1 and 2,3 of q[d] -> bf16 pairs (gfx950 scaled conversion, unit scale: exact)
+      w[d >> 1][2 * (d & 1)] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], 1.0f, false));
+      w[d >> 1][2 * (d & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], 1.0f, true));
+    }
+    const int c0 = (q8c & 7) * 2;  // 16-byte chunk of columns lc .. lc + 7 in the half's k row
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(row + (((c0 + c) ^ fb(q8k)) << 4)) = w[c];
   };
   auto fp4_store = [&](int st, const u32x2_t& q2, uint32_t sc) {
     lds_u8* bs = lds3 + (st & (kStages - 1)) * kStageBytes + kOpBytes;
@@ -333,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int gcol = (MODE == MODE_GATEUP) ? 128 * j + wn * 32 : wn * 64 + 32 * j;  // B-tile column 0..255
-    if (WF == W_BF16) {
+    if (WF != W_FP4) {
       const int h = gcol >> 7, lc = gcol & 127;
       const int g = lane >> 4, i16 = lane & 15, qq = i16 & 3, mr = i16 >> 2;
       const int colb = lc + 16 * (g & 1);
@@ -363,6 +403,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   if (WF == W_FP4) {
     ts0 = S.F0.tscale[grp];
     if (MODE == MODE_GATEUP) ts1 = S.F1.tscale[grp];
+  } else if (WF == W_FP8) {
+    ts0 = S.Q0.tscale[grp];
+    if (MODE == MODE_GATEUP) ts1 = S.Q1.tscale[grp];
   }
 
   auto run = [&](auto ni_c) {
@@ -388,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
           f.a[sb][i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(sbase + afr[i][sb]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          if (WF == W_BF16) {
+          if (WF != W_FP4) {
             const lds_u8* p = sbase + bfr[j][0] + sb * 16 * 256;
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4_t*)(p));
@@ -413,18 +456,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     };
 
     // Memory instructions per stage per lane: bf16 4 copies (A 2 + B 2);
-    // NVFP4 the code and scale loads of the stage two ahead, then 2 A copies.
-    constexpr int kPerStage = 4;
+    // NVFP4 the code and scale loads of the stage two ahead, then 2 A
+    // copies; FP8 one 16-byte code load of the stage two ahead, then 2 A
+    // copies.
+    constexpr int kPerStage = (WF == W_FP8) ? 3 : 4;
     u32x2_t fcode[2];
     uint32_t fscale[2];
+    u32x4_t fq8[2];
     if (WF == W_FP4) {
       fp4_load(0, fcode[0], fscale[0]);
       fp4_load(1, fcode[1], fscale[1]);
+    } else if (WF == W_FP8) {
+      fp8_load(0, fq8[0]);
+      fp8_load(1, fq8[1]);
     }
     auto stage_in = [&](int st) {
       if (WF == W_FP4) {
         fp4_store(st, fcode[st & 1], fscale[st & 1]);
         fp4_load(st + 2, fcode[st & 1], fscale[st & 1]);
+      } else if (WF == W_FP8) {
+        fp8_store(st, fq8[st & 1]);
+        fp8_load(st + 2, fq8[st & 1]);
       }
       issue(st);
     };
@@ -584,6 +636,8 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
     d.ldb = sh.D;
     d.F0 = a.fdg;
     d.F1 = a.fdu;
+    d.Q0 = a.qdg;
+    d.Q1 = a.qdu;
     d.K = sh.H;
     d.N = sh.D;
     d.C = ws.h_d;
@@ -601,6 +655,8 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
   e.ldb = sh.I;
   e.F0 = a.fg;
   e.F1 = a.fu;
+  e.Q0 = a.qg;
+  e.Q1 = a.qu;
   e.K = sh.H;
   e.N = sh.I;
   e.C = ws.h;
@@ -611,6 +667,7 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
   e.max_mtiles = sh.E > 0 ? max_mtiles : 0;
   const int ud = sh.D > 0 ? host_units(d) : 0;
   if (a.nvfp4) return launch<MODE_GATEUP, W_FP4>(d, e, ud, grouped_units(e), s);
+  if (a.fp8) return launch<MODE_GATEUP, W_FP8>(d, e, ud, grouped_units(e), s);
   return launch<MODE_GATEUP, W_BF16>(d, e, ud, grouped_units(e), s);
 }
 
@@ -624,6 +681,7 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
     d.B0 = a.dd;
     d.ldb = sh.H;
     d.F0 = a.fdd;
+    d.Q0 = a.qdd;
     d.K = sh.D;
     d.N = sh.H;
     d.C = yd_out ? yd_out : ws.y_d;
@@ -637,6 +695,7 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
   e.b_gstride = (long long)sh.I * sh.H;
   e.ldb = sh.H;
   e.F0 = a.fd;
+  e.Q0 = a.qd;
   e.K = sh.I;
   e.N = sh.H;
   e.C = ws.y;
@@ -647,6 +706,7 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
   e.max_mtiles = sh.E > 0 ? max_mtiles : 0;
   const int ud = sh.D > 0 ? host_units(d) : 0;
   if (a.nvfp4) return launch<MODE_PLAIN_BF16, W_FP4>(d, e, ud, grouped_units(e), s);
+  if (a.fp8) return launch<MODE_PLAIN_BF16, W_FP8>(d, e, ud, grouped_units(e), s);
   return launch<MODE_PLAIN_BF16, W_BF16>(d, e, ud, grouped_units(e), s);
 }
 

@@ -268,6 +268,150 @@ __device__ const float* unit_x_rows(int nr, const bf16_t* w, int ldw, int kbeg, 
 }
 
 // ---------------------------------------------------------------------------
+// FP8 weights: [K, N] float8_e4m3fn codes.  A thread reads 8 bytes (8
+// columns) per weight row and widens them with the gfx950 e4m3 -> fp32 pair
+// conversion (exact); each (activation, weight) product is one fp32 FMA.
+// The per-matrix scale is applied by the caller to the summed columns.
+// ---------------------------------------------------------------------------
+
+// the 8 weights of one row piece (codes in byte order) as fp32
+__device__ __forceinline__ void widen8(const u32x2_t& v, float (&w)[8]) {
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(v[d]), false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(v[d]), true);
+    w[4 * d] = lo.x;
+    w[4 * d + 1] = lo.y;
+    w[4 * d + 2] = hi.x;
+    w[4 * d + 3] = hi.y;
+  }
+}
+
+// NT <= 2 activation rows read directly (as unit_direct)
+template <int NT, int NCOLS>
+__device__ const float* unit8_direct(const uint8_t* __restrict__ w, int ldw, int kbeg, int kend,
+                                     const bf16_t* const* act, float* red) {
+  constexpr int CG = NCOLS / 8, RG = kThreads / CG;
+  const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
+  const int R = (kend - kbeg) / RG;  // rows per thread (even)
+  const int k0 = kbeg + rg * R;
+  float acc[NT][8];
+#pragma unroll
+  for (int r = 0; r < NT; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
+  const __amdgpu_buffer_rsrc_t rw = rsrc_of(w);
+  const uint32_t wrow = uint32_t(ldw), wv = uint32_t(k0) * wrow + cg * 8;
+  __amdgpu_buffer_rsrc_t rx[NT];
+  bool has[NT];
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    const bf16_t* p = uniform_ptr(act[r]);
+    has[r] = p != nullptr;
+    rx[r] = rsrc_of(p);
+  }
+  for (int b = 0; b < R; b += kU) {
+    u32x2_t vw[kU];
+    u32x2_t va[NT][kU / 4];
+#pragma unroll
+    for (int i = 0; i < kU; ++i)
+      vw[i] = (b + i < R) ? bload<u32x2_t, kPolicyNT>(rw, wv, uint32_t(b + i) * wrow) : u32x2_t{0, 0};
+    // R is even: a 4-row activation piece is whole or its last two rows lie past R
+#pragma unroll
+    for (int r = 0; r < NT; ++r)
+#pragma unroll
+      for (int q = 0; q < kU / 4; ++q) {
+        const int k = b + 4 * q;
+        if (has[r] && k + 4 <= R)
+          va[r][q] = bload<u32x2_t, 0>(rx[r], uint32_t(k0) * 2, uint32_t(k) * 2);
+        else if (has[r] && k < R)
+          va[r][q] = u32x2_t{bload<uint32_t, 0>(rx[r], uint32_t(k0) * 2, uint32_t(k) * 2), 0u};
+        else
+          va[r][q] = u32x2_t{0, 0};
+      }
+    // rows past R hold zero codes (value 0) and zero activations
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      float wf[8];
+      widen8(vw[i], wf);
+#pragma unroll
+      for (int r = 0; r < NT; ++r) {
+        const uint32_t xw = va[r][i / 4][(i / 2) & 1];
+        const float xv = (i & 1) ? bf16_hi(xw) : bf16_lo(xw);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(xv, wf[c], acc[r][c]);
+      }
+    }
+  }
+  return fold_rows<NT, NCOLS, 8>(acc, red);
+}
+
+// NT <= 8 activation rows staged in LDS as xs[k - kbeg][8] by `stage` (as
+// unit_staged), U weight rows per batch, the next batch in flight while the
+// current one is consumed
+template <int NT, int NCOLS, int U, class Stage>
+__device__ const float* unit8_staged(const uint8_t* __restrict__ w, int ldw, int kbeg, int kend, const Stage& stage,
+                                     bf16_t* xs, float* red) {
+  constexpr int CG = NCOLS / 8, RG = kThreads / CG;
+  const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
+  const int R = (kend - kbeg) / RG;  // even
+  const int k0 = kbeg + rg * R;
+  float acc[NT][8];
+#pragma unroll
+  for (int r = 0; r < NT; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
+  const __amdgpu_buffer_rsrc_t rw = rsrc_of(w);
+  const uint32_t wrow = uint32_t(ldw), wv = uint32_t(k0) * wrow + cg * 8;
+  auto load = [&](u32x2_t (&v)[U], int b) {
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+      v[i] = (b + i < R) ? bload<u32x2_t, kPolicyNT>(rw, wv, uint32_t(b + i) * wrow) : u32x2_t{0, 0};
+  };
+  auto consume = [&](const u32x2_t (&v)[U], int b) {
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      // rows past R hold zero codes; their LDS row index is clamped
+      const int kr = min(b + i, R - 1);
+      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + (k0 - kbeg + kr) * kRowsChunk);
+      float wf[8];
+      widen8(v[i], wf);
+#pragma unroll
+      for (int r = 0; r < NT; ++r) {
+        const float x = (r & 1) ? bf16_hi(xv[r / 2]) : bf16_lo(xv[r / 2]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(x, wf[c], acc[r][c]);
+      }
+    }
+  };
+  u32x2_t va[U], vb[U];
+  load(va, 0);
+  stage(xs, kbeg, kend);
+  __syncthreads();
+  for (int b = 0;;) {
+    if (b + U < R) load(vb, b + U);
+    consume(va, b);
+    b += U;
+    if (b >= R) break;
+    if (b + U < R) load(va, b + U);
+    consume(vb, b);
+    b += U;
+    if (b >= R) break;
+  }
+  return fold_rows<NT, NCOLS, 8>(acc, red);
+}
+
+template <int NCOLS>
+__device__ const float* unit8_x_rows(int nr, const uint8_t* w, int ldw, int kbeg, int kend,
+                                     const bf16_t* const* act, bf16_t* xs, float* red) {
+  if (nr <= 1) return unit8_direct<1, NCOLS>(w, ldw, kbeg, kend, act, red);
+  if (nr <= 2) return unit8_direct<2, NCOLS>(w, ldw, kbeg, kend, act, red);
+  const StageRows st{act};
+  if (nr <= 4) return unit8_staged<4, NCOLS, 8>(w, ldw, kbeg, kend, st, xs, red);
+  return unit8_staged<8, NCOLS, 8>(w, ldw, kbeg, kend, st, xs, red);
+}
+
+// ---------------------------------------------------------------------------
 // routing, derived in the block
 // ---------------------------------------------------------------------------
 
@@ -328,7 +472,7 @@ __device__ ExpertRows expert_rows(const Shape& sh, const int32_t* __restrict__ t
 // Routed: units (ai-th active expert, ...) over the expert's rows, x gathered
 // by token.  Writes fp32 partial pre-activations per K-slice, indexed by
 // slot (routed) or token (dense).
-template <bool DENSE, int NC = 64>
+template <bool DENSE, int NC = 64, bool W8 = false>
 __device__ void gateup_unit(const StreamArgs& a, const Workspace& ws, int KS, int u) {
   const Shape& sh = a.sh;
   const int H = sh.H;
@@ -351,6 +495,10 @@ __device__ void gateup_unit(const StreamArgs& a, const Workspace& ws, int KS, in
   const int g64 = H / 64;
   const int kbeg = (ks * g64 / KS) * 64, kend = ((ks + 1) * g64 / KS) * 64;
   const bf16_t* w = DENSE ? (mat ? a.du : a.dg) + n0 : (mat ? a.wu : a.wg) + (long long)grp * H * sh.I + n0;
+  // FP8: codes of the same [K, N] matrix and its scale
+  const Fp8Mat& Q = DENSE ? (mat ? a.qdu : a.qdg) : (mat ? a.qu : a.qg);
+  const uint8_t* w8 = W8 ? Q.q + (DENSE ? 0 : (long long)grp * H * sh.I) + n0 : nullptr;
+  const float qscale = W8 ? Q.tscale[DENSE ? 0 : grp] : 1.f;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16_t* xs = reinterpret_cast<bf16_t*>(smem_raw);  // [kend-kbeg][8] staged rows
@@ -370,18 +518,24 @@ __device__ void gateup_unit(const StreamArgs& a, const Workspace& ws, int KS, in
     const bf16_t* rowp[kRowsChunk];
 #pragma unroll
     for (int r = 0; r < kRowsChunk; ++r) rowp[r] = act[r];
-    const float* sums = unit_x_rows<NC>(nr, w, N, kbeg, kend, rowp, xs, red);
-    for (int o = threadIdx.x; o < nr * NC; o += kThreads) dst[o / NC][o % NC] = sums[o];
+    if (W8) {
+      const float* sums = unit8_x_rows<NC>(nr, w8, N, kbeg, kend, rowp, xs, red);
+      for (int o = threadIdx.x; o < nr * NC; o += kThreads) dst[o / NC][o % NC] = sums[o] * qscale;
+    } else {
+      const float* sums = unit_x_rows<NC>(nr, w, N, kbeg, kend, rowp, xs, red);
+      for (int o = threadIdx.x; o < nr * NC; o += kThreads) dst[o / NC][o % NC] = sums[o];
+    }
     __syncthreads();
   }
 }
 
 // Routed gate/up units.  (3 waves per SIMD: the register budget of 168
 // holds every unit variant)
+template <bool W8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_gateup(StreamArgs a,
                                                                                                       Workspace ws,
                                                                                                       int KS) {
-  gateup_unit<false>(a, ws, KS, blockIdx.x);
+  gateup_unit<false, 64, W8>(a, ws, KS, blockIdx.x);
 }
 
 // The router and the dense branch's gate/up units in one launch: blocks
@@ -389,7 +543,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
 // dense gate/up units.  The dense branch does not depend on the routing, so
 // its weights stream while the router's few blocks wait on memory latency,
 // with no second stream and no events.
-template <int CW>
+template <int CW, bool W8>
 __global__ __launch_bounds__(kThreads) void k_route_dense(
     StreamArgs a, const bf16_t* __restrict__ wr, const float* __restrict__ bias, Workspace ws, int slice_rows, int TB,
     int nslices, int nroute, int KSd) {
@@ -397,18 +551,18 @@ __global__ __launch_bounds__(kThreads) void k_route_dense(
   if (b < nroute)
     route_slice<CW>(a.sh, slice_rows, TB, nslices, b % nslices, b / nslices, a.x, wr, bias, ws);
   else
-    gateup_unit<true>(a, ws, KSd, b - nroute);
+    gateup_unit<true, 64, W8>(a, ws, KSd, b - nroute);
 }
 
 // The dense gate/up units alone (a config without experts: no router to
 // share the launch with), at the routed units' register budget.  NC = 256
 // columns per unit when D allows: each row piece is then 512 contiguous
 // bytes instead of 128, which a wide D (long rows) needs to stream well.
-template <int NC>
+template <int NC, bool W8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_dense_gateup(StreamArgs a,
                                                                                                      Workspace ws,
                                                                                                      int KSd) {
-  gateup_unit<true, NC>(a, ws, KSd, blockIdx.x);
+  gateup_unit<true, NC, W8>(a, ws, KSd, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -452,7 +606,7 @@ __global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace w
 // of D) over the T rows of h_d, fp32 partial outputs per slice (summed by
 // the combine).  Routed: unit u = (ai-th active expert, 128 columns) over
 // the expert's rows of h (slot order), bf16 output rows y indexed by slot.
-template <bool DENSE, int NC = kDownCols>
+template <bool DENSE, int NC = kDownCols, bool W8 = false>
 __device__ void down_unit(const StreamArgs& a, const Workspace& ws, int u) {
   const Shape& sh = a.sh;
   const int H = sh.H;
@@ -475,6 +629,9 @@ __device__ void down_unit(const StreamArgs& a, const Workspace& ws, int u) {
   const int n0 = u * NC;
   const int K = DENSE ? sh.D : sh.I;  // row length of h_d / h
   const bf16_t* wd = (DENSE ? a.dd : a.wd + (long long)grp * sh.I * H) + n0;
+  const Fp8Mat& Q = DENSE ? a.qdd : a.qd;
+  const uint8_t* w8 = W8 ? Q.q + (DENSE ? 0 : (long long)grp * sh.I * H) + n0 : nullptr;
+  const float qscale = W8 ? Q.tscale[DENSE ? 0 : grp] : 1.f;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16_t* hs = reinterpret_cast<bf16_t*>(smem_raw);  // [kend-kbeg][8] staged rows
@@ -490,27 +647,29 @@ __device__ void down_unit(const StreamArgs& a, const Workspace& ws, int u) {
     const bf16_t* rowp[kRowsChunk];
 #pragma unroll
     for (int r = 0; r < kRowsChunk; ++r) rowp[r] = act[r];
-    const float* sums = unit_x_rows<NC>(nr, wd, H, kbeg, kend, rowp, hs, red);
+    const float* sums = W8 ? unit8_x_rows<NC>(nr, w8, H, kbeg, kend, rowp, hs, red)
+                           : unit_x_rows<NC>(nr, wd, H, kbeg, kend, rowp, hs, red);
     if (DENSE) {
       float* o = ws.ydp + ((long long)ksd * kRouteSmallT + c0) * H + n0;
-      for (int i = threadIdx.x; i < nr * NC; i += kThreads) o[(long long)(i / NC) * H + (i % NC)] = sums[i];
+      for (int i = threadIdx.x; i < nr * NC; i += kThreads) o[(long long)(i / NC) * H + (i % NC)] = sums[i] * qscale;
     } else {
       for (int i = threadIdx.x; i < nr * NC; i += kThreads)
-        ws.y[(long long)slot[c0 + i / NC] * H + n0 + (i % NC)] = (bf16_t)f32_to_bf16_bits(sums[i]);
+        ws.y[(long long)slot[c0 + i / NC] * H + n0 + (i % NC)] = (bf16_t)f32_to_bf16_bits(sums[i] * qscale);
     }
     __syncthreads();
   }
 }
 
 // One launch for the dense down units (blocks [0, ud)) and the routed ones.
+template <bool W8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_down(StreamArgs a,
                                                                                                     Workspace ws,
                                                                                                     int ud) {
   const int u = blockIdx.x;
   if (u < ud)
-    down_unit<true, kDenseDownCols>(a, ws, u);
+    down_unit<true, kDenseDownCols, W8>(a, ws, u);
   else
-    down_unit<false>(a, ws, u - ud);
+    down_unit<false, kDownCols, W8>(a, ws, u - ud);
 }
 
 // h and y rows of the last streamed forward (slot order) copied to grouped
@@ -532,8 +691,11 @@ hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, hipStr
   const size_t kl = size_t((sh.H / 64 + kStreamKS - 1) / kStreamKS) * 64;  // longest slice
   const size_t lds = std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * 64 * 4);
   const int max_active = std::min(sh.E, sh.T * sh.k);
-  hipLaunchKernelGGL(k_stream_gateup, dim3(max_active * (sh.I / 64) * 2 * kStreamKS), dim3(kThreads), lds, s, a, ws,
-                     kStreamKS);
+  const dim3 grid(max_active * (sh.I / 64) * 2 * kStreamKS);
+  if (a.fp8)
+    hipLaunchKernelGGL(k_stream_gateup<true>, grid, dim3(kThreads), lds, s, a, ws, kStreamKS);
+  else
+    hipLaunchKernelGGL(k_stream_gateup<false>, grid, dim3(kThreads), lds, s, a, ws, kStreamKS);
   return hipGetLastError();
 }
 
@@ -550,18 +712,34 @@ hipError_t launch_route_dense(const StreamArgs& a, const bf16_t* wr, const float
   const size_t kl = size_t((sh.H / 64 + ksd - 1) / ksd) * 64;  // longest dense K-slice
   const size_t lds = ud ? std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * 64 * 4) : 0;
   if (nroute + ud == 0) return hipSuccess;
+  const bool w8 = a.fp8;
   if (nroute == 0 && sh.D % kDenseOnlyCols == 0) {
     const size_t ldsw = std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * kDenseOnlyCols * 4);
-    hipLaunchKernelGGL(k_dense_gateup<kDenseOnlyCols>, dim3(ud / (kDenseOnlyCols / 64)), dim3(kThreads), ldsw, s,
-                       a, ws, ksd);
-  } else if (nroute == 0)
-    hipLaunchKernelGGL(k_dense_gateup<64>, dim3(ud), dim3(kThreads), lds, s, a, ws, ksd);
-  else if (c.cw != 4)
-    hipLaunchKernelGGL(k_route_dense<8>, dim3(nroute + ud), dim3(kThreads), lds, s, a, wr, bias, ws, c.slice_rows, c.tb,
-                       c.nslices, nroute, ksd);
-  else
-    hipLaunchKernelGGL(k_route_dense<4>, dim3(nroute + ud), dim3(kThreads), lds, s, a, wr, bias, ws, c.slice_rows, c.tb,
-                       c.nslices, nroute, ksd);
+    const dim3 grid(ud / (kDenseOnlyCols / 64));
+    if (w8)
+      hipLaunchKernelGGL((k_dense_gateup<kDenseOnlyCols, true>), grid, dim3(kThreads), ldsw, s, a, ws, ksd);
+    else
+      hipLaunchKernelGGL((k_dense_gateup<kDenseOnlyCols, false>), grid, dim3(kThreads), ldsw, s, a, ws, ksd);
+  } else if (nroute == 0) {
+    if (w8)
+      hipLaunchKernelGGL((k_dense_gateup<64, true>), dim3(ud), dim3(kThreads), lds, s, a, ws, ksd);
+    else
+      hipLaunchKernelGGL((k_dense_gateup<64, false>), dim3(ud), dim3(kThreads), lds, s, a, ws, ksd);
+  } else {
+    const dim3 grid(nroute + ud);
+    if (c.cw != 4 && w8)
+      hipLaunchKernelGGL((k_route_dense<8, true>), grid, dim3(kThreads), lds, s, a, wr, bias, ws, c.slice_rows, c.tb,
+                         c.nslices, nroute, ksd);
+    else if (c.cw != 4)
+      hipLaunchKernelGGL((k_route_dense<8, false>), grid, dim3(kThreads), lds, s, a, wr, bias, ws, c.slice_rows, c.tb,
+                         c.nslices, nroute, ksd);
+    else if (w8)
+      hipLaunchKernelGGL((k_route_dense<4, true>), grid, dim3(kThreads), lds, s, a, wr, bias, ws, c.slice_rows, c.tb,
+                         c.nslices, nroute, ksd);
+    else
+      hipLaunchKernelGGL((k_route_dense<4, false>), grid, dim3(kThreads), lds, s, a, wr, bias, ws, c.slice_rows, c.tb,
+                         c.nslices, nroute, ksd);
+  }
   return hipGetLastError();
 }
 
@@ -585,7 +763,10 @@ hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStrea
   // longest K run of a unit: a dense K-slice or the expert width
   const int kd = ud ? (sh.D / 64 + ksd - 1) / ksd * 64 : 0;
   const size_t lds = std::max(size_t(std::max(sh.I, kd)) * kRowsChunk * 2, size_t(5) * kRowsChunk * kDownColsMax * 4);
-  hipLaunchKernelGGL(k_stream_down, dim3(ud + max_active * nblk), dim3(kThreads), lds, s, a, ws, ud);
+  if (a.fp8)
+    hipLaunchKernelGGL(k_stream_down<true>, dim3(ud + max_active * nblk), dim3(kThreads), lds, s, a, ws, ud);
+  else
+    hipLaunchKernelGGL(k_stream_down<false>, dim3(ud + max_active * nblk), dim3(kThreads), lds, s, a, ws, ud);
   return hipGetLastError();
 }
 

@@ -42,6 +42,14 @@ def up_nvfp4_weights(w):
     return out
 
 
+def up_fp8_weights(w):
+    out = {"router": up_bf16(w["router"])}
+    for n in ("gate", "up", "down", "dgate", "dup", "ddown"):
+        m = w.get(n)
+        out[n] = None if m is None else {"q8": up(m["q8"]), "tensor_scale": up(m["tensor_scale"])}
+    return out
+
+
 def to_f64(t):
     import torch
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)

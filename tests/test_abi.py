@@ -83,6 +83,7 @@ def test_workspace_bytes_valid_config(lib):
     # 2^20 tokens: h [T*8, 704] bf16 would reach 11.8 GB (32-bit operand offsets)
     (dict(max_tokens=1 << 20), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(weight_format=7), binding.MOE_FFN_ERR_UNSUPPORTED),
+    (dict(weight_format=3), binding.MOE_FFN_ERR_UNSUPPORTED),
     (dict(flags=2), binding.MOE_FFN_ERR_UNSUPPORTED),
 ])
 def test_bad_configs_rejected(lib, kw, code):
@@ -104,6 +105,11 @@ def test_dense_ffn_configs_accepted(lib):
     assert rc == binding.MOE_FFN_OK
 
 
+def test_fp8_config_accepted(lib):
+    rc, _ = binding.moe_ffn_workspace_bytes(cfg(weight_format=binding.MOE_FFN_W_FP8))
+    assert rc == binding.MOE_FFN_OK
+
+
 def test_largest_addressable_token_count(lib):
     # T*k*I*2 < 2^31 at the 26B shape: up to 190,650 tokens
     rc, _ = binding.moe_ffn_workspace_bytes(cfg(max_tokens=190650))
@@ -117,6 +123,7 @@ def test_null_arguments(lib):
     assert lib.moe_ffn_create(None, None) == binding.MOE_FFN_ERR_INVALID_ARG
     assert binding.moe_ffn_forward(None, 8, *([None] * 11)) == binding.MOE_FFN_ERR_INVALID_ARG
     assert binding.moe_ffn_forward_nvfp4(None, 8, *([None] * 11)) == binding.MOE_FFN_ERR_INVALID_ARG
+    assert binding.moe_ffn_forward_fp8(None, 8, *([None] * 11)) == binding.MOE_FFN_ERR_INVALID_ARG
     assert binding.moe_ffn_get_routing(None, *([None] * 7)) == binding.MOE_FFN_ERR_INVALID_ARG
     assert binding.moe_ffn_get_intermediates(None, *([None] * 5)) == binding.MOE_FFN_ERR_INVALID_ARG
     assert binding.moe_ffn_align_only(None, 4, None, None) == binding.MOE_FFN_ERR_INVALID_ARG
