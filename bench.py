@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--no-block", action="store_true", help="skip the sandwich-norm sub-block leg")
     p.add_argument("--block-steps", type=int, default=100)
     p.add_argument("--no-dense", action="store_true", help="skip the E4B dense FFN leg")
+    p.add_argument("--no-fp8", action="store_true", help="skip the FP8 weight leg")
     p.add_argument("--dense-steps", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -96,6 +97,21 @@ def upload_nvfp4(torch, pk):
     return out
 
 
+def upload_fp8(torch, pk):
+    out = {"router": to_dev_bf16(torch, pk["router"]) if pk["router"] is not None else None}
+    for n in ("gate", "up", "down", "dgate", "dup", "ddown"):
+        m = pk.get(n)
+        out[n] = None if m is None else {
+            "q8": torch.from_numpy(np.ascontiguousarray(m["q8"])).cuda(),
+            "tensor_scale": torch.from_numpy(np.ascontiguousarray(m["tensor_scale"])).cuda()}
+    return out
+
+
+def clone_fp8(w):
+    return {k: (None if v is None else v.clone() if not isinstance(v, dict) else
+                {kk: vv.clone() for kk, vv in v.items()}) for k, v in w.items()}
+
+
 def nvfp4_layer_weight_bytes(shape):
     """Packed bytes of one NVFP4 layer: 0.5 B codes + 1/16 B scales per weight,
     4 B per matrix tensor scale, plus the bf16 router."""
@@ -118,7 +134,15 @@ def run_workload(torch, shape, steps, warmup, copies, graph, layers=1, norms=Fal
     bias = synth.zipf_bias(shape.experts) if shape.skew else None
     bd = torch.from_numpy(bias).cuda() if bias is not None else None
     w = None
-    if shape.nvfp4:
+    if getattr(shape, "fp8", False):
+        base = upload_fp8(torch, synth.make_fp8_weights(shape))
+        sets = [base] + [clone_fp8(base) for _ in range(copies - 1)]
+        out = torch.empty_like(xd)
+        ffn = MoeFFN.for_shape(shape)
+
+        def fwd(i):
+            ffn.forward_fp8(xd, sets[i % copies], out, bd)
+    elif shape.nvfp4:
         sets = [upload_nvfp4(torch, synth.make_nvfp4_weights(shape, layer=l)) for l in range(copies)]
         ffn = MoeFFN.for_shape(shape, accumulate=True)
         x0 = xd.clone()
@@ -392,6 +416,32 @@ def main():
                 "gateup_mfma_frac": (2 * dp.tokens * 2 * H * D) / (gu_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
                 "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rq["stage_avg_us"]]))}
         line["e4b_dense"] = dense
+    if not args.no_fp8:
+        # FP8 weight-only (e4m3fn codes + per-matrix scale): one byte per weight
+        from dataclasses import replace
+        f8 = replace(dec, fp8=True)
+        rf = run_workload(torch, f8, args.steps, args.warmup, args.copies, args.graph)
+        H, I = f8.hidden, f8.expert_dim
+        gu8 = rf["n_act"] * 2 * H * I + f8.tokens * H * 2 + f8.tokens * f8.top_k * I * 2
+        step8 = rf["n_act"] * 3 * H * I + 3 * H * f8.dense_dim + H * f8.experts * 2 + 2 * f8.tokens * H * 2
+        gu_us8 = rf["stage_avg_us"][2]
+        fp8 = {
+            "workload": "same layer with FP8 e4m3fn expert and dense weights (per-matrix scale), router bf16",
+            "decode": {"tokens": f8.tokens, "value": f8.tokens / (rf["ms_per_step"] * 1e-3), "unit": "tokens/s",
+                       "ms_per_step": rf["ms_per_step"], "steps": args.steps, "active_experts": rf["n_act"],
+                       "gateup_hbm_frac": gu8 / (gu_us8 * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                       "step_hbm_frac": step8 / (rf["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rf["stage_avg_us"]]))},
+        }
+        if not args.no_prefill:
+            fp = replace(synth.PREFILL, fp8=True)
+            rq = run_workload(torch, fp, args.prefill_steps, max(3, args.warmup // 4), 2, args.graph)
+            fp8["prefill"] = {
+                "tokens": fp.tokens, "value": fp.tokens / (rq["ms_per_step"] * 1e-3), "unit": "tokens/s",
+                "ms_per_step": rq["ms_per_step"], "steps": args.prefill_steps,
+                "step_mfma_frac": step_flops(fp) / (rq["ms_per_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rq["stage_avg_us"]]))}
+        line["fp8"] = fp8
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(dec, r["x"], r["w"], r["bias"], args.cpu_seconds)
     print(json.dumps(line), flush=True)

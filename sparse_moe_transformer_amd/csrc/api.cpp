@@ -127,7 +127,7 @@ Layout layout(const moe_ffn_config& c) {
       T * (D ? D : 1) * 2,                        // h_d
       T * k * H * 2,                              // y
       T * H * 2,                                  // y_d
-      (size_t(moe::kStreamKS) * moe::kStreamRows * I +  // streaming gate/up partials
+      (size_t(moe::kStreamKSMax) * moe::kStreamRows * I +  // streaming gate/up partials
        size_t(moe::kDenseKSMax) * moe::kRouteSmallT * (D ? D : 1)) * 2 * 4,
       size_t(moe::dense_down_slices(moe::Shape{0, int(H), int(E), int(k), int(I), int(D)})) *
           moe::kRouteSmallT * H * 4,              // streaming dense down partials

@@ -65,7 +65,7 @@ struct Workspace {
   bf16_t* h_d;          // [Tmax, D]
   bf16_t* y;            // [Tmax*k, H] perm order (MFMA path) or slot order (streaming path)
   bf16_t* y_d;          // [Tmax, H]
-  float* part;          // [kStreamKS][kStreamRows][2][I] (rows = slots) + [kDenseKSMax][64][2][D]
+  float* part;          // [kStreamKSMax][kStreamRows][2][I] (rows = slots) + [kDenseKSMax][64][2][D]
                         // (rows = tokens) gate/up partials of the streaming path
   float* ydp;           // [dense_down_slices][64][H] dense down partials (streaming path)
   bf16_t* xn;           // [Tmax, H] pre-normed block input (sandwich-norm forwards)
@@ -77,7 +77,9 @@ constexpr int kRouterSlices = 16;  // most K-slices of the large-T router logits
 constexpr int kRouteSlices = 32;   // K-slices of the small-T router logits
 constexpr int kRouteSmallT = 64;   // largest T of the one-block-per-token router and the streaming path
 constexpr int kGemmBM = 256;       // MFMA tile rows (tokens)
-constexpr int kStreamKS = 2;       // K-slices of the streaming routed gate/up units
+constexpr int kStreamKS = 2;       // K-slices of the streaming routed gate/up units (bf16)
+constexpr int kStreamKS8 = 4;      // ... with FP8 weights (units twice as wide, so twice the slices)
+constexpr int kStreamKSMax = kStreamKS8 > kStreamKS ? kStreamKS8 : kStreamKS;
 constexpr int kDenseKS = 4;        // K-slices of the streaming dense gate/up units (beside experts)
 constexpr int kDenseOnlyKS = 4;    // ... of a config without experts
 constexpr int kDenseKSMax = kDenseKS > kDenseOnlyKS ? kDenseKS : kDenseOnlyKS;

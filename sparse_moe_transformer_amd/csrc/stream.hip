@@ -63,7 +63,7 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
 __device__ __forceinline__ float* part_ptr(const Workspace& ws, const Shape& sh, bool dense, int ks, int row,
                                            int mat) {
   if (!dense) return ws.part + ((size_t(ks) * kStreamRows + row) * 2 + mat) * sh.I;
-  float* base = ws.part + size_t(kStreamKS) * kStreamRows * 2 * sh.I;  // then [kDenseKSMax][64][2][D]
+  float* base = ws.part + size_t(kStreamKSMax) * kStreamRows * 2 * sh.I;  // then [kDenseKSMax][64][2][D]
   return base + ((size_t(ks) * kRouteSmallT + row) * 2 + mat) * sh.D;
 }
 
@@ -289,7 +289,7 @@ __device__ __forceinline__ void widen8(const u32x2_t& v, float (&w)[8]) {
 
 // NT <= 2 activation rows read directly (as unit_direct)
 template <int NT, int NCOLS>
-__device__ const float* unit8_direct(const uint8_t* __restrict__ w, int ldw, int kbeg, int kend,
+__device__ const float* unit8_direct(const uint8_t* __restrict__ w, int ldw, int kbeg, int kend, int nvalid,
                                      const bf16_t* const* act, float* red) {
   constexpr int CG = NCOLS / 8, RG = kThreads / CG;
   const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
@@ -302,6 +302,7 @@ __device__ const float* unit8_direct(const uint8_t* __restrict__ w, int ldw, int
     for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
   const __amdgpu_buffer_rsrc_t rw = rsrc_of(w);
   const uint32_t wrow = uint32_t(ldw), wv = uint32_t(k0) * wrow + cg * 8;
+  const bool colok = cg * 8 < nvalid;  // columns past the matrix's last read nothing
   __amdgpu_buffer_rsrc_t rx[NT];
   bool has[NT];
 #pragma unroll
@@ -315,7 +316,7 @@ __device__ const float* unit8_direct(const uint8_t* __restrict__ w, int ldw, int
     u32x2_t va[NT][kU / 4];
 #pragma unroll
     for (int i = 0; i < kU; ++i)
-      vw[i] = (b + i < R) ? bload<u32x2_t, kPolicyNT>(rw, wv, uint32_t(b + i) * wrow) : u32x2_t{0, 0};
+      vw[i] = (colok && b + i < R) ? bload<u32x2_t, kPolicyNT>(rw, wv, uint32_t(b + i) * wrow) : u32x2_t{0, 0};
     // R is even: a 4-row activation piece is whole or its last two rows lie past R
 #pragma unroll
     for (int r = 0; r < NT; ++r)
@@ -350,8 +351,8 @@ __device__ const float* unit8_direct(const uint8_t* __restrict__ w, int ldw, int
 // unit_staged), U weight rows per batch, the next batch in flight while the
 // current one is consumed
 template <int NT, int NCOLS, int U, class Stage>
-__device__ const float* unit8_staged(const uint8_t* __restrict__ w, int ldw, int kbeg, int kend, const Stage& stage,
-                                     bf16_t* xs, float* red) {
+__device__ const float* unit8_staged(const uint8_t* __restrict__ w, int ldw, int kbeg, int kend, int nvalid,
+                                     const Stage& stage, bf16_t* xs, float* red) {
   constexpr int CG = NCOLS / 8, RG = kThreads / CG;
   const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
   const int R = (kend - kbeg) / RG;  // even
@@ -363,10 +364,11 @@ __device__ const float* unit8_staged(const uint8_t* __restrict__ w, int ldw, int
     for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
   const __amdgpu_buffer_rsrc_t rw = rsrc_of(w);
   const uint32_t wrow = uint32_t(ldw), wv = uint32_t(k0) * wrow + cg * 8;
+  const bool colok = cg * 8 < nvalid;  // columns past the matrix's last read nothing
   auto load = [&](u32x2_t (&v)[U], int b) {
 #pragma unroll
     for (int i = 0; i < U; ++i)
-      v[i] = (b + i < R) ? bload<u32x2_t, kPolicyNT>(rw, wv, uint32_t(b + i) * wrow) : u32x2_t{0, 0};
+      v[i] = (colok && b + i < R) ? bload<u32x2_t, kPolicyNT>(rw, wv, uint32_t(b + i) * wrow) : u32x2_t{0, 0};
   };
   auto consume = [&](const u32x2_t (&v)[U], int b) {
 #pragma unroll
@@ -401,14 +403,17 @@ __device__ const float* unit8_staged(const uint8_t* __restrict__ w, int ldw, int
   return fold_rows<NT, NCOLS, 8>(acc, red);
 }
 
+// nvalid: columns of the unit inside the matrix (a unit may overhang its
+// last columns: FP8 gate/up units are 128 columns, one 128-byte line per
+// weight row, and I or D need not be a multiple of 128)
 template <int NCOLS>
-__device__ const float* unit8_x_rows(int nr, const uint8_t* w, int ldw, int kbeg, int kend,
+__device__ const float* unit8_x_rows(int nr, const uint8_t* w, int ldw, int kbeg, int kend, int nvalid,
                                      const bf16_t* const* act, bf16_t* xs, float* red) {
-  if (nr <= 1) return unit8_direct<1, NCOLS>(w, ldw, kbeg, kend, act, red);
-  if (nr <= 2) return unit8_direct<2, NCOLS>(w, ldw, kbeg, kend, act, red);
+  if (nr <= 1) return unit8_direct<1, NCOLS>(w, ldw, kbeg, kend, nvalid, act, red);
+  if (nr <= 2) return unit8_direct<2, NCOLS>(w, ldw, kbeg, kend, nvalid, act, red);
   const StageRows st{act};
-  if (nr <= 4) return unit8_staged<4, NCOLS, 8>(w, ldw, kbeg, kend, st, xs, red);
-  return unit8_staged<8, NCOLS, 8>(w, ldw, kbeg, kend, st, xs, red);
+  if (nr <= 4) return unit8_staged<4, NCOLS, 8>(w, ldw, kbeg, kend, nvalid, st, xs, red);
+  return unit8_staged<8, NCOLS, 8>(w, ldw, kbeg, kend, nvalid, st, xs, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -477,7 +482,7 @@ __device__ void gateup_unit(const StreamArgs& a, const Workspace& ws, int KS, in
   const Shape& sh = a.sh;
   const int H = sh.H;
   const int N = DENSE ? sh.D : sh.I;
-  const int per = (N / NC) * 2 * KS;
+  const int per = ((N + NC - 1) / NC) * 2 * KS;  // units per expert (the last may overhang N)
   __shared__ int slot[kRouteSmallT];
   int grp = 0, rows = sh.T;
   if (!DENSE) {
@@ -492,6 +497,7 @@ __device__ void gateup_unit(const StreamArgs& a, const Workspace& ws, int KS, in
   const int ks = u % KS;
   const int mat = (u / KS) & 1;
   const int n0 = (u / (2 * KS)) * NC;
+  const int nvalid = min(NC, N - n0);
   const int g64 = H / 64;
   const int kbeg = (ks * g64 / KS) * 64, kend = ((ks + 1) * g64 / KS) * 64;
   const bf16_t* w = DENSE ? (mat ? a.du : a.dg) + n0 : (mat ? a.wu : a.wg) + (long long)grp * H * sh.I + n0;
@@ -519,8 +525,9 @@ __device__ void gateup_unit(const StreamArgs& a, const Workspace& ws, int KS, in
 #pragma unroll
     for (int r = 0; r < kRowsChunk; ++r) rowp[r] = act[r];
     if (W8) {
-      const float* sums = unit8_x_rows<NC>(nr, w8, N, kbeg, kend, rowp, xs, red);
-      for (int o = threadIdx.x; o < nr * NC; o += kThreads) dst[o / NC][o % NC] = sums[o] * qscale;
+      const float* sums = unit8_x_rows<NC>(nr, w8, N, kbeg, kend, nvalid, rowp, xs, red);
+      for (int o = threadIdx.x; o < nr * NC; o += kThreads)
+        if (o % NC < nvalid) dst[o / NC][o % NC] = sums[o] * qscale;
     } else {
       const float* sums = unit_x_rows<NC>(nr, w, N, kbeg, kend, rowp, xs, red);
       for (int o = threadIdx.x; o < nr * NC; o += kThreads) dst[o / NC][o % NC] = sums[o];
@@ -535,7 +542,7 @@ template <bool W8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_gateup(StreamArgs a,
                                                                                                       Workspace ws,
                                                                                                       int KS) {
-  gateup_unit<false, 64, W8>(a, ws, KS, blockIdx.x);
+  gateup_unit<false, W8 ? 128 : 64, W8>(a, ws, KS, blockIdx.x);
 }
 
 // The router and the dense branch's gate/up units in one launch: blocks
@@ -551,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void k_route_dense(
   if (b < nroute)
     route_slice<CW>(a.sh, slice_rows, TB, nslices, b % nslices, b / nslices, a.x, wr, bias, ws);
   else
-    gateup_unit<true, 64, W8>(a, ws, KSd, b - nroute);
+    gateup_unit<true, W8 ? 128 : 64, W8>(a, ws, KSd, b - nroute);
 }
 
 // The dense gate/up units alone (a config without experts: no router to
@@ -586,14 +593,15 @@ __device__ __forceinline__ void geglu4(const Workspace& ws, const Shape& sh, boo
                                               pack_bf16x2(gelu_tanh(g.z) * up.z, gelu_tanh(g.w) * up.w)};
 }
 
-__global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace ws, long long n4r, long long n4d) {
+__global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace ws, long long n4r, long long n4d,
+                                                           int ksr) {
   const int qi = sh.I / 4, qd = sh.D / 4;
   const int ksd = dense_gateup_slices(sh);
   for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n4r + n4d;
        i += (long long)gridDim.x * kThreads) {
     if (i < n4r) {
       const int row = int(i / qi), c = int(i % qi) * 4;
-      geglu4(ws, sh, false, kStreamKS, row, c, ws.h + (long long)row * sh.I + c);
+      geglu4(ws, sh, false, ksr, row, c, ws.h + (long long)row * sh.I + c);
     } else {
       const long long j = i - n4r;
       const int row = int(j / qd), c = int(j % qd) * 4;
@@ -647,7 +655,7 @@ __device__ void down_unit(const StreamArgs& a, const Workspace& ws, int u) {
     const bf16_t* rowp[kRowsChunk];
 #pragma unroll
     for (int r = 0; r < kRowsChunk; ++r) rowp[r] = act[r];
-    const float* sums = W8 ? unit8_x_rows<NC>(nr, w8, H, kbeg, kend, rowp, hs, red)
+    const float* sums = W8 ? unit8_x_rows<NC>(nr, w8, H, kbeg, kend, NC, rowp, hs, red)
                            : unit_x_rows<NC>(nr, wd, H, kbeg, kend, rowp, hs, red);
     if (DENSE) {
       float* o = ws.ydp + ((long long)ksd * kRouteSmallT + c0) * H + n0;
@@ -688,14 +696,16 @@ __global__ __launch_bounds__(kThreads) void k_stream_export(Shape sh, Workspace 
 hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
   const Shape& sh = a.sh;
   if (sh.T == 0 || sh.E == 0) return hipSuccess;
-  const size_t kl = size_t((sh.H / 64 + kStreamKS - 1) / kStreamKS) * 64;  // longest slice
-  const size_t lds = std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * 64 * 4);
+  const int ks = a.fp8 ? kStreamKS8 : kStreamKS;
+  const int nc = a.fp8 ? 128 : 64;  // unit columns (gateup_unit's NC)
+  const size_t kl = size_t((sh.H / 64 + ks - 1) / ks) * 64;  // longest slice
+  const size_t lds = std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * nc * 4);
   const int max_active = std::min(sh.E, sh.T * sh.k);
-  const dim3 grid(max_active * (sh.I / 64) * 2 * kStreamKS);
+  const dim3 grid(max_active * ((sh.I + nc - 1) / nc) * 2 * ks);
   if (a.fp8)
-    hipLaunchKernelGGL(k_stream_gateup<true>, grid, dim3(kThreads), lds, s, a, ws, kStreamKS);
+    hipLaunchKernelGGL(k_stream_gateup<true>, grid, dim3(kThreads), lds, s, a, ws, ks);
   else
-    hipLaunchKernelGGL(k_stream_gateup<false>, grid, dim3(kThreads), lds, s, a, ws, kStreamKS);
+    hipLaunchKernelGGL(k_stream_gateup<false>, grid, dim3(kThreads), lds, s, a, ws, ks);
   return hipGetLastError();
 }
 
@@ -708,21 +718,23 @@ hipError_t launch_route_dense(const StreamArgs& a, const bf16_t* wr, const float
   if (sh.E > 0 && !c.ok) return hipErrorInvalidValue;
   const int nroute = sh.E > 0 ? c.nslices * c.groups : 0;
   const int ksd = sh.D > 0 ? dense_gateup_slices(sh) : 1;
-  const int ud = sh.D > 0 ? (sh.D / 64) * 2 * ksd : 0;
-  const size_t kl = size_t((sh.H / 64 + ksd - 1) / ksd) * 64;  // longest dense K-slice
-  const size_t lds = ud ? std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * 64 * 4) : 0;
-  if (nroute + ud == 0) return hipSuccess;
   const bool w8 = a.fp8;
-  if (nroute == 0 && sh.D % kDenseOnlyCols == 0) {
-    const size_t ldsw = std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * kDenseOnlyCols * 4);
-    const dim3 grid(ud / (kDenseOnlyCols / 64));
+  // dense unit columns: 64 beside the router (FP8: 128, one 128-byte line
+  // per weight row); without experts 256 when D allows
+  const bool wide = nroute == 0 && sh.D % kDenseOnlyCols == 0;
+  const int nc = wide ? kDenseOnlyCols : (w8 ? 128 : 64);
+  const int ud = sh.D > 0 ? ((sh.D + nc - 1) / nc) * 2 * ksd : 0;
+  const size_t kl = size_t((sh.H / 64 + ksd - 1) / ksd) * 64;  // longest dense K-slice
+  const size_t lds = ud ? std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * nc * 4) : 0;
+  if (nroute + ud == 0) return hipSuccess;
+  if (wide) {
     if (w8)
-      hipLaunchKernelGGL((k_dense_gateup<kDenseOnlyCols, true>), grid, dim3(kThreads), ldsw, s, a, ws, ksd);
+      hipLaunchKernelGGL((k_dense_gateup<kDenseOnlyCols, true>), dim3(ud), dim3(kThreads), lds, s, a, ws, ksd);
     else
-      hipLaunchKernelGGL((k_dense_gateup<kDenseOnlyCols, false>), grid, dim3(kThreads), ldsw, s, a, ws, ksd);
+      hipLaunchKernelGGL((k_dense_gateup<kDenseOnlyCols, false>), dim3(ud), dim3(kThreads), lds, s, a, ws, ksd);
   } else if (nroute == 0) {
     if (w8)
-      hipLaunchKernelGGL((k_dense_gateup<64, true>), dim3(ud), dim3(kThreads), lds, s, a, ws, ksd);
+      hipLaunchKernelGGL((k_dense_gateup<128, true>), dim3(ud), dim3(kThreads), lds, s, a, ws, ksd);
     else
       hipLaunchKernelGGL((k_dense_gateup<64, false>), dim3(ud), dim3(kThreads), lds, s, a, ws, ksd);
   } else {
@@ -749,7 +761,8 @@ hipError_t launch_stream_geglu(const StreamArgs& a, const Workspace& ws, hipStre
   const long long n4r = (long long)sh.T * sh.k * sh.I / 4;
   const long long n4d = sh.D > 0 ? (long long)sh.T * sh.D / 4 : 0;
   const int gblocks = int(std::min<long long>(1024, (n4r + n4d + kThreads - 1) / kThreads));
-  hipLaunchKernelGGL(k_stream_geglu, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, n4r, n4d);
+  hipLaunchKernelGGL(k_stream_geglu, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, n4r, n4d,
+                     a.fp8 ? kStreamKS8 : kStreamKS);
   return hipGetLastError();
 }
 
