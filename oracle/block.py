@@ -344,6 +344,65 @@ def moe_block(x, pre_scale, post_scale, eps: float, router_w, w_gate, w_up, w_do
 
 
 # ---------------------------------------------------------------------------
+# W4A4: NVFP4 weights and NVFP4 activations
+# ---------------------------------------------------------------------------
+
+
+def moe_ffn_w4a4(x, router_w, w_gate, w_up, w_down, d_gate, d_up, d_down, in_scale,
+                 top_k: int = 8, bias=None, force_routing=None, tokens=None) -> dict:
+    """The block with NVFP4 weights and NVFP4 activations at every Linear
+    input (checkpoint config ``input_activations``; readings in
+    ``oracle.nvfp4``).  The router is not quantised (``ignore`` lists
+    ``router.proj``) and reads x as it is.
+
+    in_scale = (s_x, s_h, s_hd): the static global scales of x (input of
+    every gate/up projection), of the routed hidden rows h (bf16, as stored)
+    and of the dense hidden rows h_d.  Each expert:
+        h = bf16(gelu_tanh(q(x)·W_g[e]) ⊙ (q(x)·W_u[e])),  y = q(h)·W_d[e]
+    with q the quantise-dequantise of ``quant_act_nvfp4`` times its scale.
+    """
+    from .nvfp4 import quant_act_nvfp4
+
+    s_x, s_h, s_hd = (float(np.float32(s)) for s in in_scale)
+    X = widen_bf16(x)
+    T, H = X.shape
+    E = np.asarray(router_w).shape[1]
+    r = route(x, router_w, top_k, bias, force_routing)
+    res = dict(r)
+    XQ = quant_act_nvfp4(X, s_x) * s_x
+    toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    cache = {}
+
+    def mats(e):
+        if e not in cache:
+            cache[e] = (_matrix(w_gate, e), _matrix(w_up, e), _matrix(w_down, e))
+        return cache[e]
+
+    def hidden_q(xq, g, u, s):
+        h = round_bf16(geglu_hidden(xq, g, u))                   # the stored bf16 hidden rows
+        return quant_act_nvfp4(h, s) * s
+
+    out = np.zeros((len(toks), H))
+    have_dense = d_gate is not None
+    if have_dense:
+        dg, du, dd = _dense_matrix(d_gate), _dense_matrix(d_up), _dense_matrix(d_down)
+        yd = hidden_q(XQ[toks], dg, du, s_hd) @ dd
+    for i, t in enumerate(toks):
+        acc = np.zeros(H)
+        for j in range(top_k):
+            e = int(r["topk_idx"][t, j])
+            g, u, dwn = mats(e)
+            acc += r["topk_w"][t, j] * (hidden_q(XQ[t:t + 1], g, u, s_h) @ dwn)[0]
+        if have_dense:
+            acc += yd[i]
+        out[i] = acc
+    res["out"] = out
+    res["xq"] = XQ
+    res["tokens"] = toks
+    return res
+
+
+# ---------------------------------------------------------------------------
 # the dense FFN of the E4B sibling
 # ---------------------------------------------------------------------------
 

@@ -328,3 +328,42 @@ def test_fp8_transposed_layout(monkeypatch):
 
     _patch(monkeypatch, "dequant_matrix_fp8", bad, module=of)
     _expect_caught([pins.test_fp8_dequant_matches_torch_and_layout])
+
+
+W4A4_PINS = [pins.test_e2m1_rounding_is_nearest_with_even_ties,
+             pins.test_activation_quantiser_worked_group,
+             pins.test_activation_quantiser_properties,
+             pins.test_w4a4_block_composition_with_torch]
+
+
+def test_e2m1_ties_away_from_zero(monkeypatch):
+    def bad(r):
+        r = np.asarray(r, dtype=np.float64)
+        a = np.abs(r)
+        up = np.floor  # ties (and everything) rounded half up
+        v = np.where(a < 2.0, up(a * 2.0 + 0.5) / 2.0, np.where(a < 4.0, up(a + 0.5), 2.0 * up(a / 2.0 + 0.5)))
+        return np.sign(r) * np.minimum(v, 6.0)
+
+    _patch(monkeypatch, "round_e2m1_sat", bad, module=on)
+    _expect_caught(W4A4_PINS)
+
+
+def test_activation_scale_ignores_global_scale(monkeypatch):
+    real = on.round_e4m3_sat
+
+    def bad_quant(v, s_in):
+        v = np.asarray(v, dtype=np.float64)
+        sh = v.shape
+        g = v.reshape(*sh[:-1], sh[-1] // 16, 16)
+        sg = real(np.max(np.abs(g), axis=-1) / 6.0)              # global scale left out
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.where(sg[..., None] > 0, on.round_e2m1_sat(g / sg[..., None]), 0.0)
+        return (q * sg[..., None]).reshape(sh)
+
+    _patch(monkeypatch, "quant_act_nvfp4", bad_quant, module=on)
+    _expect_caught(W4A4_PINS)
+
+
+def test_w4a4_hidden_not_rounded_to_bf16(monkeypatch):
+    monkeypatch.setattr(om, "round_bf16", lambda v: np.asarray(v, dtype=np.float64))
+    _expect_caught([pins.test_w4a4_block_composition_with_torch])

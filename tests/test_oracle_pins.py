@@ -684,3 +684,111 @@ def test_dense_block_torch_norms_and_zero_post_gain():
     assert rel_err(rs["out"], r["out"][[3, 9]]) < 1e-12
     z = oracle.dense_block(x, pre, np.zeros(shape.hidden), eps, w["dgate"], w["dup"], w["ddown"])
     assert np.array_equal(z["out"], oracle.widen_bf16(x))
+
+
+# ---------------------------------------------------------------------------
+# W4A4: the NVFP4 activation quantiser
+# ---------------------------------------------------------------------------
+
+
+def test_e4m3_rounding_matches_torch_cast():
+    """Pin: round_e4m3_sat equals torch's float8_e4m3fn cast (round to nearest
+    even) on fp32 values in [0, 448], including every midpoint between
+    neighbouring e4m3 values; above 448 it saturates."""
+    vals = oracle.E4M3_TABLE[:127]                               # non-negative finite values
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.default_rng(11)
+    rand = np.concatenate([rng.uniform(0, 448, 4000), 2.0 ** rng.uniform(-12, 8.8, 4000)])
+    x = np.concatenate([vals, mids, rand]).astype(np.float32)
+    x = x[x <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_e4m3_sat(x), ref)
+    assert np.all(oracle.round_e4m3_sat(np.float32([448.5, 470.0, 1e6])) == 448.0)
+
+
+def test_e2m1_rounding_is_nearest_with_even_ties():
+    """Pin: round_e2m1_sat is the nearest e2m1 value by brute force over the
+    8 magnitudes, a tie going to the even mantissa (codes 0, 2, 4, 6), and
+    values beyond 6 saturate."""
+    mags = oracle.E2M1_TABLE[:8]
+    rng = np.random.default_rng(12)
+    r = np.concatenate([rng.uniform(-8, 8, 5000), (mags[:-1] + mags[1:]) / 2, -(mags[:-1] + mags[1:]) / 2, mags])
+    got = oracle.round_e2m1_sat(r)
+    for v, g in zip(r, got):
+        d = np.abs(np.abs(v) - mags)
+        best = np.flatnonzero(d == d.min())
+        code = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+        assert g == np.sign(v) * mags[code], (v, g)
+
+
+def test_activation_quantiser_worked_group():
+    """Pin on a hand-worked group: with s_in = fp32(1/6), 6 * s_in rounds to
+    exactly 1 in fp32, the group amax 6 gives s_g = 6, s_g * s_in rounds to 1,
+    so each value is just rounded on the e2m1 grid (ties to the even
+    mantissa) and the dequantised value is that times s_g = 6."""
+    s_in = float(np.float32(1.0 / 6.0))
+    v = np.array([0, 0.25, 0.3, 0.75, 1.25, 1.75, 2.5, 3.5, 5, 6, -1, -2.9, 4.4, 0.5, 1.5, 3.0])
+    e2m1 = np.array([0, 0, 0.5, 1, 1, 2, 2, 4, 4, 6, -1, -3, 4, 0.5, 1.5, 3.0])
+    assert np.array_equal(oracle.quant_act_nvfp4(v[None], s_in)[0], e2m1 * 6.0)
+
+
+def test_activation_quantiser_properties():
+    """Pins: groups are independent (permuting whole groups permutes the
+    output), an all-zero group gives zeros, every output is an e2m1 x e4m3
+    product and so exact in bf16, and |q * s_in - v| is at most one e2m1 half
+    step at the top of the grid, s_g * s_in, per group."""
+    rng = np.random.default_rng(13)
+    v = oracle.round_bf16(rng.standard_normal((6, 64)) * np.array([1e-3, 0.1, 1, 10])[:, None].repeat(16, 1).T.reshape(-1)[None])
+    v[2, 16:32] = 0.0
+    s_in = float(np.float32(np.max(np.abs(v)) / (6 * 448)))
+    q = oracle.quant_act_nvfp4(v, s_in)
+    assert np.all(q[2, 16:32] == 0)
+    assert np.array_equal(oracle.round_bf16(q), q)
+    perm = np.array([2, 0, 3, 1])
+    vp = v.reshape(6, 4, 16)[:, perm].reshape(6, 64)
+    assert np.array_equal(oracle.quant_act_nvfp4(vp, s_in), q.reshape(6, 4, 16)[:, perm].reshape(6, 64))
+    g = v.reshape(6, 4, 16)
+    amax = np.abs(g).max(-1)
+    sg = oracle.round_e4m3_sat(np.float32(amax / np.float32(6 * np.float32(s_in))))
+    err = np.abs(q * s_in - v).reshape(6, 4, 16).max(-1)
+    assert np.all(err <= sg * s_in * (1 + 1e-6) + 1e-30)
+
+
+def test_w4a4_block_composition_with_torch():
+    """Pin of the W4A4 block: routing of the unquantised x; each expert and
+    the dense branch as torch fp64 matmuls and torch's tanh GELU on the
+    quantised activations (quantiser pinned above), the hidden rows rounded
+    to bf16 by torch's cast before their quantisation; sampled-token mode
+    agrees."""
+    shape, x, w = tiny_inputs()
+    pk = {n: synth.nvfp4_pack_stack(w[n]) for n in ("gate", "up", "down")}
+    pk.update({n: synth.nvfp4_pack_stack(w[n][None]) for n in ("dgate", "dup", "ddown")})
+    s = (0.003, 0.002, 0.001)
+    r = oracle.moe_ffn_w4a4(x, w["router"], pk["gate"], pk["up"], pk["down"], pk["dgate"], pk["dup"],
+                            pk["ddown"], s, top_k=2)
+    rt = oracle.route(x, w["router"], 2)
+    assert np.array_equal(r["topk_idx"], rt["topk_idx"])
+
+    def deq(n, g):
+        return torch.from_numpy(oracle.dequant_matrix(pk[n]["q"][g], pk[n]["scale"][g], pk[n]["tensor_scale"][g]))
+
+    def q(a, sc):
+        sc = float(np.float32(sc))
+        return torch.from_numpy(oracle.quant_act_nvfp4(a.numpy(), sc) * sc)
+
+    def bf(t):
+        return t.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+    X = q(torch.from_numpy(oracle.widen_bf16(x)), s[0])
+    ref = np.zeros((shape.tokens, shape.hidden))
+    for t in range(shape.tokens):
+        for j in range(2):
+            e = int(rt["topk_idx"][t, j])
+            h = bf(torch.nn.functional.gelu(X[t:t + 1] @ deq("gate", e), approximate="tanh") * (X[t:t + 1] @ deq("up", e)))
+            ref[t] += rt["topk_w"][t, j] * (q(h, s[1]) @ deq("down", e))[0].numpy()
+    hd = bf(torch.nn.functional.gelu(X @ deq("dgate", 0), approximate="tanh") * (X @ deq("dup", 0)))
+    ref += (q(hd, s[2]) @ deq("ddown", 0)).numpy()
+    assert rel_err(r["out"], ref) < 1e-12
+    rs = oracle.moe_ffn_w4a4(x, w["router"], pk["gate"], pk["up"], pk["down"], pk["dgate"], pk["dup"],
+                             pk["ddown"], s, top_k=2, tokens=[1, 7, 30])
+    assert rel_err(rs["out"], r["out"][[1, 7, 30]]) < 1e-12
