@@ -122,11 +122,12 @@ def round_e4m3_sat(r) -> np.ndarray:
 
 def round_e2m1_sat(r) -> np.ndarray:
     """Nearest e2m1 value of fp32 values (ties to an even mantissa),
-    saturating at +-6: steps of 0.5 below 2, 1 up to 4, 2 up to 6."""
+    saturating at +-6: steps of 0.5 below 2, 1 up to 4, 2 up to 6.  The sign
+    is kept, also for a result of zero (e2m1 has a negative zero, code 8)."""
     r = np.asarray(r, dtype=np.float64)
     a = np.abs(r)
     v = np.where(a < 2.0, np.rint(a * 2.0) / 2.0, np.where(a < 4.0, np.rint(a), 2.0 * np.rint(a / 2.0)))
-    return np.sign(r) * np.minimum(v, 6.0)
+    return np.copysign(np.minimum(v, 6.0), r)
 
 
 def quant_act_nvfp4(v, s_in) -> np.ndarray:

@@ -718,7 +718,8 @@ def test_e2m1_rounding_is_nearest_with_even_ties():
         d = np.abs(np.abs(v) - mags)
         best = np.flatnonzero(d == d.min())
         code = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
-        assert g == np.sign(v) * mags[code], (v, g)
+        assert g == np.sign(v) * mags[code] and np.signbit(g) == np.signbit(v), (v, g)
+    assert np.signbit(oracle.round_e2m1_sat(np.array([-0.0, -0.2]))).all()
 
 
 def test_activation_quantiser_worked_group():
