@@ -183,6 +183,35 @@ int moe_ffn_forward_fp8(moe_ffn_handle *h, int32_t T, const void *x, const void 
                         const moe_ffn_fp8_t *d_up, const moe_ffn_fp8_t *d_down, void *out,
                         void *stream);
 
+/* Same block with NVFP4 weights AND NVFP4 activations (W4A4; the NVFP4
+ * checkpoint config's input_activations: e2m1 values, groups of 16 along K,
+ * float8_e4m3fn group scales computed per call, a static global scale per
+ * tensor).  weight_format must be MOE_FFN_W_NVFP4 and num_experts > 0.
+ * in_scale: device fp32 [3], the static global scales of x (the input of
+ * every gate/up projection), of the routed hidden rows h and of the dense
+ * hidden rows h_d (unused when dense_dim == 0); each must be positive and
+ * finite (a NaN scale gives undefined output).  Every 16-value group of a
+ * row is quantised as
+ *   s_g = e4m3(amax / (6 s)),  q = e2m1(v / (s_g s))   (nearest, ties to
+ *   even, saturating; each operation one correctly rounded fp32 step),
+ * and the projection reads q * s_g * s.  The router reads x unquantised.
+ * Runs on the MFMA tiles for every T: the quantised values q * s_g are exact
+ * in bf16, so the bf16 MFMA computes with them exactly and s joins the
+ * weights' tensor scale on the fp32 accumulators. */
+int moe_ffn_forward_w4a4(moe_ffn_handle *h, int32_t T, const void *x, const void *router_w,
+                         const float *router_bias, const moe_ffn_nvfp4_t *w_gate, const moe_ffn_nvfp4_t *w_up,
+                         const moe_ffn_nvfp4_t *w_down, const moe_ffn_nvfp4_t *d_gate,
+                         const moe_ffn_nvfp4_t *d_up, const moe_ffn_nvfp4_t *d_down, const float *in_scale,
+                         void *out, void *stream);
+
+/* The NVFP4 activation quantiser of moe_ffn_forward_w4a4 on its own: rows x K
+ * bf16 values (row-major, K a multiple of 16) to the bf16 values q * s_g of
+ * each 16-group (the global scale *in_scale, device fp32, is not applied).
+ * in == out is allowed.  Queues one kernel on `stream` on the current device;
+ * needs no handle. */
+int moe_ffn_quant_act_nvfp4(int64_t rows, int32_t K, const void *in, void *out, const float *in_scale,
+                            void *stream);
+
 /* The feed-forward sub-block of a layer with its sandwich norms and the
  * residual (archdb page "Gemma-4-26B-A4B": normalization RMSNorm, placement
  * sandwich (pre and post), epsilon 1e-06; API page gm.nn.Gemma4_26B_A4B

@@ -92,6 +92,20 @@ class MoeFFN:
                                             _ptr(out), _stream()))
         return out
 
+    def forward_w4a4(self, x, w, in_scale, out, bias=None):
+        """NVFP4 weights (as forward_nvfp4) and NVFP4 activations; in_scale: fp32 device
+        tensor [3] (global scales of x, h, h_d)."""
+        def d(m):
+            if m is None:
+                return None
+            return (m["q"].data_ptr(), m["scale"].data_ptr(), m["tensor_scale"].data_ptr())
+        T = x.shape[0]
+        check(binding.moe_ffn_forward_w4a4(self.h, T, _ptr(x), _ptr(w.get("router")), _ptr(bias),
+                                           d(w.get("gate")), d(w.get("up")), d(w.get("down")),
+                                           d(w.get("dgate")), d(w.get("dup")), d(w.get("ddown")),
+                                           _ptr(in_scale), _ptr(out), _stream()))
+        return out
+
     def forward_fp8(self, x, w, out, bias=None):
         """w: router bf16 tensor; gate/up/down/dgate/dup/ddown dicts of q8 (uint8 [G, K, N])
         and tensor_scale (fp32 [G]), or None where the config has no such matrices."""

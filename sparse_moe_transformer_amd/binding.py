@@ -31,7 +31,9 @@ MOE_FFN_VARIANT_MFMA = 2
 
 EXPORTS = (
     "moe_ffn_workspace_bytes", "moe_ffn_create", "moe_ffn_destroy", "moe_ffn_set_variant",
-    "moe_ffn_forward", "moe_ffn_forward_nvfp4", "moe_ffn_forward_fp8", "moe_ffn_forward_block",
+    "moe_ffn_forward", "moe_ffn_forward_nvfp4", "moe_ffn_forward_fp8", "moe_ffn_forward_w4a4",
+    "moe_ffn_quant_act_nvfp4",
+    "moe_ffn_forward_block",
     "moe_ffn_get_routing",
     "moe_ffn_get_intermediates", "moe_ffn_align_only", "moe_ffn_profile_begin",
     "moe_ffn_profile_end", "moe_ffn_last_error",
@@ -82,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_set_variant.argtypes = [vp, i32]
         L.moe_ffn_forward.argtypes = [vp, i32] + [vp] * 11
         L.moe_ffn_forward_nvfp4.argtypes = [vp, i32, vp, vp, vp] + [P(moe_ffn_nvfp4_t)] * 6 + [vp, vp]
+        L.moe_ffn_quant_act_nvfp4.argtypes = [ctypes.c_int64, i32, vp, vp, vp, vp]
+        L.moe_ffn_forward_w4a4.argtypes = [vp, i32, vp, vp, vp] + [P(moe_ffn_nvfp4_t)] * 6 + [vp, vp, vp]
         L.moe_ffn_forward_fp8.argtypes = [vp, i32, vp, vp, vp] + [P(moe_ffn_fp8_t)] * 6 + [vp, vp]
         L.moe_ffn_forward_block.argtypes = [vp, i32, vp, vp, vp, ctypes.c_float] + [vp] * 10
         L.moe_ffn_get_routing.argtypes = [vp] + [vp] * 7
@@ -149,6 +153,22 @@ def moe_ffn_forward_nvfp4(h, T, x, router_w, router_bias, w_gate, w_up, w_down, 
     return lib().moe_ffn_forward_nvfp4(h, T, x, router_w, router_bias, desc(w_gate), desc(w_up),
                                        desc(w_down), desc(d_gate), desc(d_up), desc(d_down),
                                        out, stream)
+
+
+def moe_ffn_quant_act_nvfp4(rows, K, inp, out, in_scale, stream) -> int:
+    return lib().moe_ffn_quant_act_nvfp4(rows, K, inp, out, in_scale, stream)
+
+
+def moe_ffn_forward_w4a4(h, T, x, router_w, router_bias, w_gate, w_up, w_down, d_gate, d_up,
+                         d_down, in_scale, out, stream) -> int:
+    """Weight descriptors as for moe_ffn_forward_nvfp4; in_scale a device pointer to 3 fp32."""
+    def desc(d):
+        if d is None:
+            return None
+        return ctypes.byref(moe_ffn_nvfp4_t(*d))
+    return lib().moe_ffn_forward_w4a4(h, T, x, router_w, router_bias, desc(w_gate), desc(w_up),
+                                      desc(w_down), desc(d_gate), desc(d_up), desc(d_down), in_scale,
+                                      out, stream)
 
 
 def moe_ffn_forward_fp8(h, T, x, router_w, router_bias, w_gate, w_up, w_down, d_gate, d_up,

@@ -281,6 +281,13 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   }
   {
     StageTimer tm(h, MOE_FFN_STAGE_GATEUP, s, timing);
+    if (args.in_scale) {
+      // NVFP4 activations: the gate/up projections read x quantised (the
+      // router above read it as it is)
+      e = moe::launch_quant_act(static_cast<const moe::bf16_t*>(x), ws.xn, T, sh.H, sh.H, args.in_scale, s);
+      if (e != hipSuccess) return hip_fail(e, "activation quantiser");
+      args.x = ws.xn;
+    }
     e = stream ? moe::launch_stream_gateup(args, ws, s) : moe::launch_gemm_gateup(args, ws, mt, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "gate/up");
@@ -293,6 +300,12 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   }
   {
     StageTimer tm(h, MOE_FFN_STAGE_DOWN, s, timing);
+    if (args.in_scale) {
+      // NVFP4 activations: the hidden rows (bf16, as stored) quantised in place
+      e = moe::launch_quant_act(ws.h, ws.h, (long long)T * sh.k, sh.I, sh.I, args.in_scale + 1, s);
+      if (e == hipSuccess && sh.D > 0) e = moe::launch_quant_act(ws.h_d, ws.h_d, T, sh.D, sh.D, args.in_scale + 2, s);
+      if (e != hipSuccess) return hip_fail(e, "activation quantiser");
+    }
     e = stream ? moe::launch_stream_down(args, ws, s)
                : moe::launch_gemm_down(args, ws, mt, s, direct ? static_cast<moe::bf16_t*>(out) : nullptr);
     tm.stop();
@@ -642,6 +655,73 @@ int moe_ffn_forward_fp8(moe_ffn_handle* h, int32_t T, const void* x, const void*
     return run_forward(h, T, x, router_w, router_bias, a, out, static_cast<hipStream_t>(stream));
   } catch (const std::exception& ex) {
     return fail(MOE_FFN_ERR_HIP, ex.what());
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_forward_w4a4(moe_ffn_handle* h, int32_t T, const void* x, const void* router_w,
+                         const float* router_bias, const moe_ffn_nvfp4_t* w_gate, const moe_ffn_nvfp4_t* w_up,
+                         const moe_ffn_nvfp4_t* w_down, const moe_ffn_nvfp4_t* d_gate, const moe_ffn_nvfp4_t* d_up,
+                         const moe_ffn_nvfp4_t* d_down, const float* in_scale, void* out, void* stream) {
+  try {
+    if (int r = common_forward_checks(h, T, x, router_w, router_bias, out, MOE_FFN_W_NVFP4)) return r;
+    if (h->cfg.num_experts == 0)
+      return fail(MOE_FFN_ERR_UNSUPPORTED, "NVFP4 activations need a config with experts");
+    if (int r = check_fp4(w_gate, true, "w_gate")) return r;
+    if (int r = check_fp4(w_up, true, "w_up")) return r;
+    if (int r = check_fp4(w_down, true, "w_down")) return r;
+    const bool dense = h->cfg.dense_dim > 0;
+    if (int r = check_fp4(d_gate, dense, "d_gate")) return r;
+    if (int r = check_fp4(d_up, dense, "d_up")) return r;
+    if (int r = check_fp4(d_down, dense, "d_down")) return r;
+    if (!in_scale || (reinterpret_cast<uintptr_t>(in_scale) & 3u))
+      return fail(MOE_FFN_ERR_INVALID_ARG, "in_scale must be a non-NULL, 4-byte aligned device pointer");
+    if (T == 0) {
+      g_err.clear();
+      return MOE_FFN_OK;
+    }
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(MOE_FFN_ERR_HIP, "cannot make the handle's device current");
+    moe::StreamArgs a{};
+    a.sh = shape_of(h, T);
+    a.x = static_cast<const moe::bf16_t*>(x);
+    a.fg = to_mat(w_gate);
+    a.fu = to_mat(w_up);
+    a.fd = to_mat(w_down);
+    a.fdg = to_mat(dense ? d_gate : nullptr);
+    a.fdu = to_mat(dense ? d_up : nullptr);
+    a.fdd = to_mat(dense ? d_down : nullptr);
+    a.nvfp4 = true;
+    a.in_scale = in_scale;
+    return run_forward(h, T, x, router_w, router_bias, a, out, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return fail(MOE_FFN_ERR_HIP, ex.what());
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_quant_act_nvfp4(int64_t rows, int32_t K, const void* in, void* out, const float* in_scale,
+                            void* stream) {
+  try {
+    if (rows < 0 || K < 0 || K % 16) return fail(MOE_FFN_ERR_INVALID_ARG, "rows >= 0 and K a multiple of 16 required");
+    if (rows * (int64_t)K * 2 >= (int64_t(1) << 40)) return fail(MOE_FFN_ERR_UNSUPPORTED, "tensor too large");
+    if (rows == 0 || K == 0) {
+      g_err.clear();
+      return MOE_FFN_OK;
+    }
+    if (!in || !out || !in_scale) return fail(MOE_FFN_ERR_INVALID_ARG, "in, out and in_scale must not be NULL");
+    if (!aligned16(in) || !aligned16(out) || (reinterpret_cast<uintptr_t>(in_scale) & 3u))
+      return fail(MOE_FFN_ERR_INVALID_ARG, "in and out must be 16-byte aligned, in_scale 4-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = moe::launch_quant_act(static_cast<const moe::bf16_t*>(in), static_cast<moe::bf16_t*>(out), rows,
+                                         K, K, in_scale, s);
+    if (e != hipSuccess) return hip_fail(e, "activation quantiser");
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "activation quantiser");
+    g_err.clear();
+    return MOE_FFN_OK;
   } catch (...) {
     return fail(MOE_FFN_ERR_HIP, "unknown exception");
   }

@@ -164,6 +164,9 @@ struct StreamArgs {
   // FP8 weights (fp8 == true)
   Fp8Mat qg, qu, qd, qdg, qdu, qdd;
   bool fp8;
+  // NVFP4 activations (W4A4): device fp32 global scales of x (gate/up
+  // input), h (routed down input) and h_d (dense down input), or null
+  const float* in_scale;
 };
 // Streaming path (T <= 64, bf16 weights).  The router and the dense
 // branch's gate/up units share one launch; then the routed gate/up partial
@@ -193,6 +196,10 @@ hipError_t launch_rmsnorm(const Shape& sh, const bf16_t* x, const float* pre, fl
                           hipStream_t s);
 hipError_t launch_combine_norm(const Shape& sh, const Workspace& ws, const bf16_t* resid, const float* post,
                                float eps, bf16_t* out, int yd_slices, bool slot_rows, hipStream_t s);
+// NVFP4 activations: rows x K bf16 (row pitch ld elements) quantised in
+// 16-groups with the global scale *s_in (device); in == out allowed
+hipError_t launch_quant_act(const bf16_t* in, bf16_t* out, long long rows, int K, int ld, const float* s_in,
+                            hipStream_t s);
 hipError_t launch_combine(const Shape& sh, const Workspace& ws, bf16_t* out, bool accumulate, int yd_slices,
                           bool slot_rows, hipStream_t s);
 

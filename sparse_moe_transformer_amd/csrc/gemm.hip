@@ -79,6 +79,7 @@ struct Seg {
   int ldb;
   Fp4Mat F0, F1;          // NVFP4 [G][N][K/2], [G][N][K/16], [G]
   Fp8Mat Q0, Q1;          // FP8 [G][K][ldb] e4m3fn codes (group stride b_gstride), [G] scales
+  const float* in_scale;  // NVFP4 activations: the A operand's global scale (device), or null
   int K;
   int N;                  // output columns
   void* C;
@@ -407,6 +408,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     ts0 = S.Q0.tscale[grp];
     if (MODE == MODE_GATEUP) ts1 = S.Q1.tscale[grp];
   }
+  if (S.in_scale) {  // quantised activations: their global scale joins the weights'
+    const float si = *S.in_scale;
+    ts0 *= si;
+    ts1 *= si;
+  }
 
   auto run = [&](auto ni_c) {
     constexpr int NI = decltype(ni_c)::value;
@@ -638,6 +644,7 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
     d.F1 = a.fdu;
     d.Q0 = a.qdg;
     d.Q1 = a.qdu;
+    d.in_scale = a.in_scale;
     d.K = sh.H;
     d.N = sh.D;
     d.C = ws.h_d;
@@ -657,6 +664,7 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
   e.F1 = a.fu;
   e.Q0 = a.qg;
   e.Q1 = a.qu;
+  e.in_scale = a.in_scale;
   e.K = sh.H;
   e.N = sh.I;
   e.C = ws.h;
@@ -682,6 +690,7 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
     d.ldb = sh.H;
     d.F0 = a.fdd;
     d.Q0 = a.qdd;
+    d.in_scale = a.in_scale ? a.in_scale + 2 : nullptr;
     d.K = sh.D;
     d.N = sh.H;
     d.C = yd_out ? yd_out : ws.y_d;
@@ -696,6 +705,7 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
   e.ldb = sh.H;
   e.F0 = a.fd;
   e.Q0 = a.qd;
+  e.in_scale = a.in_scale ? a.in_scale + 1 : nullptr;
   e.K = sh.I;
   e.N = sh.H;
   e.C = ws.y;
