@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--block-steps", type=int, default=100)
     p.add_argument("--no-dense", action="store_true", help="skip the E4B dense FFN leg")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 weight leg")
+    p.add_argument("--no-w4a4", action="store_true", help="skip the NVFP4 W4A4 leg")
     p.add_argument("--dense-steps", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -120,7 +121,7 @@ def nvfp4_layer_weight_bytes(shape):
     return nw // 2 + nw // 16 + (3 * E + 3) * 4 + H * E * 2
 
 
-def run_workload(torch, shape, steps, warmup, copies, graph, layers=1, norms=False):
+def run_workload(torch, shape, steps, warmup, copies, graph, layers=1, norms=False, w4a4=False):
     """Time `steps` forwards; returns a dict of measurements.
 
     bf16 workloads rotate `copies` bit-identical weight copies.  The NVFP4
@@ -142,6 +143,18 @@ def run_workload(torch, shape, steps, warmup, copies, graph, layers=1, norms=Fal
 
         def fwd(i):
             ffn.forward_fp8(xd, sets[i % copies], out, bd)
+    elif shape.nvfp4 and w4a4:
+        # one NVFP4 layer with NVFP4 activations; static global scales of x,
+        # h and h_d as a min/max observer would set them (amax / (6 * 448)),
+        # taking amax 4 for the hidden rows; copies are distinct seeded layers
+        sets = [upload_nvfp4(torch, synth.make_nvfp4_weights(shape, layer=l)) for l in range(copies)]
+        ffn = MoeFFN.for_shape(shape)
+        amax_x = float(np.max(np.abs(synth.bf16_bits_to_f32(x))))
+        scales = torch.tensor([amax_x, 4.0, 4.0], dtype=torch.float32, device="cuda") / (6 * 448)
+        out = torch.empty_like(xd)
+
+        def fwd(i):
+            ffn.forward_w4a4(xd, sets[i % copies], scales, out, bd)
     elif shape.nvfp4:
         sets = [upload_nvfp4(torch, synth.make_nvfp4_weights(shape, layer=l)) for l in range(copies)]
         ffn = MoeFFN.for_shape(shape, accumulate=True)
@@ -190,7 +203,7 @@ def run_workload(torch, shape, steps, warmup, copies, graph, layers=1, norms=Fal
 
     def restart():
         # the stack runs in place: restart each chain of `layers` from x
-        if shape.nvfp4:
+        if shape.nvfp4 and not w4a4:
             xd.copy_(x0)
 
     for i in range(warmup):
@@ -442,6 +455,18 @@ def main():
                 "step_mfma_frac": step_flops(fp) / (rq["ms_per_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                 "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rq["stage_avg_us"]]))}
         line["fp8"] = fp8
+    if not args.no_w4a4:
+        from dataclasses import replace
+        st = replace(synth.NVFP4_STACK, layers=1)
+        rw = run_workload(torch, st, args.nvfp4_steps * 4, 8, 2, False, w4a4=True)
+        us = rw["ms_per_step"] * 1e3
+        line["w4a4"] = {
+            "workload": "one NVFP4 layer with NVFP4 activations (W4A4), T=1024, 2 distinct seeded layers rotated",
+            "tokens": st.tokens, "value": st.tokens / (us * 1e-6), "unit": "tokens/s per layer",
+            "us_per_layer": us, "steps": args.nvfp4_steps * 4,
+            "mfma_frac": step_flops(st) / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+            "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rw["stage_avg_us"]])),
+        }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(dec, r["x"], r["w"], r["bias"], args.cpu_seconds)
     print(json.dumps(line), flush=True)
