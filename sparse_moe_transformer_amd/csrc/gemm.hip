@@ -145,6 +145,13 @@ __device__ __forceinline__ void copy_b128_to_lds(i32x4_t rsrc, uint32_t lds, int
                : "memory");
 }
 
+// the same with 4 bytes per lane (lane i at lds + 4 i)
+__device__ __forceinline__ void copy_b32_to_lds(i32x4_t rsrc, uint32_t lds, int voffset, int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds), "v"(voffset), "s"(rsrc),
+               "s"(soffset)
+               : "memory");
+}
+
 // s_waitcnt with only vmcnt <= VM and lgkmcnt <= LGKM (expcnt not waited)
 template <int VM, int LGKM>
 __device__ __forceinline__ void wait_counts() {
@@ -202,8 +209,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   constexpr int OUTN = (MODE == MODE_GATEUP) ? BN / 2 : BN;
   const int n0 = nt * OUTN;
 
-  // the four K stages; after the K loop the same bytes stage the output tile
-  constexpr int kStageArea = kStages * kStageBytes;
+  // LDS: bf16 weights: a ring of four K stages, each A then B.  FP8 /
+  // NVFP4: a deeper ring of A and the raw codes of B (their copies run
+  // kDepth stages ahead), then two bf16 B tiles decoded from the raw codes
+  // (one is written while the other is read).  After the K loop the same
+  // bytes stage the output tile.
+  constexpr int kRaw = (WF == W_FP8) ? 8192 : (WF == W_FP4) ? 5120 : 0;
+  constexpr int kDepth = (WF == W_FP8) ? 5 : (WF == W_FP4) ? 6 : kStages;
+  constexpr int kStageStride = (WF == W_BF16) ? kStageBytes : kOpBytes + kRaw;  // one ring slot
+  constexpr int kBArea = kDepth * kStageStride;                               // FP: the two B tiles
+  constexpr int kStageArea = kBArea + ((WF == W_BF16) ? 0 : 2 * kOpBytes);
   constexpr int SP = OUTN * 2 + 16;  // staging row pitch (bytes)
   constexpr int kSmem = kStageArea > BM * SP ? kStageArea : BM * SP;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kSmem];
@@ -240,24 +255,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   i32x4_t brsrc = rsrc4(S.B0);
   int boff[2] = {0, 0};
   const uint32_t brow = uint32_t(S.ldb) * 2;  // bytes per k row
-  const uint8_t* fq = nullptr;  // NVFP4: codes and scales of LDS column tid / 2, k half tid % 2
-  const uint8_t* fs = nullptr;
-  const int fcol = tid >> 1, fkh = tid & 1;
-  // FP8: thread tid loads codes k row q8k, columns q8c*16 .. +15 of the
-  // stage's 256 B-columns (half q8c / 8)
-  const int q8k = tid >> 4, q8c = tid & 15;
-  const uint8_t* q8 = nullptr;
+  // FP8 / NVFP4: each stage's raw codes are copied into the stage's raw area
+  // (DMA like A, so the compiler tracks no weight loads in the K loop) and
+  // decoded there to the bf16 B layout two stages ahead of their use.
+  //   FP8: thread t copies 16 codes of half t / 256, k row (t % 256) / 8,
+  //        columns 16 (t % 8) .. + 15 to raw + 16 t.
+  //   NVFP4: waves 0-3: thread t copies the 16 code bytes (32 k) of B-tile
+  //        column t to raw + 16 t; waves 4-7: the dword of column t - 256's
+  //        scales that holds this stage's two, to raw + 4096 + 4 (t - 256).
+  // Columns past N are out of range (zeros); they only feed output columns
+  // that are never stored.
+  i32x4_t rrsrc = rsrc4(S.A);
+  int roff = kOutOfRange;
+  const int fcol = tid >> 1, fkh = tid & 1;  // NVFP4 decode: B-tile column tid / 2, k half tid % 2
   if (WF == W_FP8) {
-    const int h = q8c >> 3, lc = (q8c & 7) * 16;
+    const int h = tid >> 8, t2 = tid & 255, k = t2 >> 3, lc = (t2 & 7) * 16;
     const Fp8Mat* Q = &S.Q0;
     int col = n0 + 128 * h + lc;
     if (MODE == MODE_GATEUP) {
       Q = h ? &S.Q1 : &S.Q0;
       col = n0 + lc;
     }
-    // columns past N read column 0 instead: they only feed output columns
-    // that are never stored
-    q8 = Q->q + grp * S.b_gstride + (long long)q8k * S.ldb + (col < N ? col : 0);
+    rrsrc = rsrc4(Q->q + grp * S.b_gstride);
+    roff = col < N ? int(uint32_t(k) * uint32_t(S.ldb) + uint32_t(col)) : kOutOfRange;
+  } else if (WF == W_FP4) {
+    const bool scl = tid >= 256;
+    const int c = tid & 255;
+    const Fp4Mat* F = &S.F0;
+    int ncol = n0 + c;
+    if (MODE == MODE_GATEUP && c >= 128) {
+      F = &S.F1;
+      ncol = n0 + c - 128;
+    }
+    const long long rowbytes = scl ? K / 16 : K / 2;
+    const uint8_t* base = (scl ? F->scale : F->q) + (long long)grp * S.N * rowbytes;
+    rrsrc = rsrc4(base);
+    roff = ncol < N ? int(uint32_t(ncol) * uint32_t(rowbytes)) : kOutOfRange;
   }
   if (WF == W_BF16) {
     const bf16_t* Bm = S.B0;
@@ -273,17 +306,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       const int col = cbase + ((lane & 15) ^ fb(k)) * 8;
       boff[q] = col < N ? int(uint32_t(k) * brow + uint32_t(col) * 2u) : kOutOfRange;
     }
-  } else if (WF == W_FP4) {
-    const Fp4Mat* F = &S.F0;
-    int ncol = n0 + fcol;
-    if (MODE == MODE_GATEUP && fcol >= 128) {
-      F = &S.F1;
-      ncol = n0 + fcol - 128;
-    }
-    const long long NN = S.N;
-    const long long col = ncol < N ? ncol : 0;
-    fq = F->q + (grp * NN + col) * (long long)(K / 2) + fkh * 8;
-    fs = F->scale + (grp * NN + col) * (long long)(K / 16) + fkh;
   }
 
   // K-stages of this tile's slice; stage indices past the last are clamped
@@ -294,9 +316,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   const int kt0 = ks * nk_all / S.ksplit;
   const int nk = (ks + 1) * nk_all / S.ksplit - kt0;
 
-  auto issue = [&](int st) {  // copies of stage st into LDS buffer st % kStages
+  auto issue = [&](int st) {  // copies of stage st into its LDS ring slot
     const int kk = (kt0 + min(st, nk - 1)) * BK;
-    const uint32_t sbase_addr = lds_base + uint32_t((st & (kStages - 1)) * kStageBytes);
+    const uint32_t sbase_addr = lds_base + uint32_t((st % kDepth) * kStageStride);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       copy_b128_to_lds(arsrc, sbase_addr + (32 * wave + 16 * q) * 64, aoff[q], kk * 2);
@@ -307,51 +329,62 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
                          boff[q], int(uint32_t(kk) * brow));
     }
   };
-  // NVFP4: codes of a stage are loaded into registers two stages ahead and
-  // decoded into the LDS buffer when the stage is issued
-  auto fp4_load = [&](int st, u32x2_t& q, uint32_t& sc) {
-    const int kk = (kt0 + min(st, nk - 1)) * BK;
-    q = *reinterpret_cast<const u32x2_t*>(fq + kk / 2);
-    sc = *(fs + kk / 16);
-  };
-  // FP8: the 16 codes of a stage, loaded two stages ahead, written as bf16
-  auto fp8_load = [&](int st, u32x4_t& q) {
-    const int kk = (kt0 + min(st, nk - 1)) * BK;
-    q = *reinterpret_cast<const u32x4_t*>(q8 + (long long)kk * S.ldb);
-  };
-  auto fp8_store = [&](int st, const u32x4_t& q) {
-    lds_u8* row = lds3 + (st & (kStages - 1)) * kStageBytes + kOpBytes + (q8c >> 3) * (kOpBytes / 2) + q8k * 256;
-    u32x4_t w[2];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      // bytes 0,1 and 2,3 of q[d] -> bf16 pairs (gfx950 scaled conversion, unit scale: exact)
-      w[d >> 1][2 * (d & 1)] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], 1.0f, false));
-      w[d >> 1][2 * (d & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], 1.0f, true));
+  // raw codes of stage st into its raw area (one copy per lane)
+  auto issue_raw = [&](int st) {
+    const int kidx = kt0 + min(st, nk - 1);
+    const uint32_t rb = lds_base + uint32_t((st % kDepth) * kStageStride + kOpBytes);
+    if (WF == W_FP8) {
+      copy_b128_to_lds(rrsrc, rb + wave * 1024, roff, int(uint32_t(kidx * BK) * uint32_t(S.ldb)));
+    } else if (WF == W_FP4) {
+      if (wave < 4)
+        copy_b128_to_lds(rrsrc, rb + wave * 1024, roff, kidx * (BK / 2));
+      else
+        copy_b32_to_lds(rrsrc, rb + 4096 + (wave - 4) * 256, roff, 4 * (kidx >> 1));
     }
-    const int c0 = (q8c & 7) * 2;  // 16-byte chunk of columns lc .. lc + 7 in the half's k row
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(row + (((c0 + c) ^ fb(q8k)) << 4)) = w[c];
   };
-  auto fp4_store = [&](int st, const u32x2_t& q2, uint32_t sc) {
-    lds_u8* bs = lds3 + (st & (kStages - 1)) * kStageBytes + kOpBytes;
-    const float sv = e4m3_f32(sc & 0xFFu);
+  // raw codes of stage st (landed) -> the stage's bf16 B tile
+  auto decode = [&](int st) {
+    lds_u8* sb = lds3 + (st % kDepth) * kStageStride;  // A, then the raw codes at kOpBytes
+    lds_u8* bt = lds3 + kBArea + (st & 1) * kOpBytes;  // this stage's bf16 B tile
+    if (WF == W_FP8) {
+      const int h = tid >> 8, t2 = tid & 255, k = t2 >> 3, c0 = (t2 & 7) * 2;
+      const u32x4_t q = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(sb + kOpBytes + tid * 16);
+      u32x4_t w[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint32_t q = q2[c];  // k = 16 fkh + 8c .. + 7, low nibble first
-      // byte p: codes k = 8c+2p (low nibble), 8c+2p+1, decoded exactly by
-      // the gfx950 e2m1 pair conversion (unit scale); e2m1 x e4m3 is exact
-      // in bf16, so the top 16 bits of each product are kept
-      const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
-      const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
-      const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
-      const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
-      const u32x4_t w = {perm_hi16(__float_as_uint(v0.x * sv), __float_as_uint(v0.y * sv)),
-                         perm_hi16(__float_as_uint(v1.x * sv), __float_as_uint(v1.y * sv)),
-                         perm_hi16(__float_as_uint(v2.x * sv), __float_as_uint(v2.y * sv)),
-                         perm_hi16(__float_as_uint(v3.x * sv), __float_as_uint(v3.y * sv))};
-      const int chunk = 2 * fkh + c;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(bs + fcol * 64 + ((chunk ^ fa(fcol)) << 4)) = w;
+      for (int d = 0; d < 4; ++d) {
+        // bytes 0,1 and 2,3 of q[d] -> bf16 pairs (gfx950 scaled conversion, unit scale: exact)
+        w[d >> 1][2 * (d & 1)] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], 1.0f, false));
+        w[d >> 1][2 * (d & 1) + 1] =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], 1.0f, true));
+      }
+      lds_u8* row = bt + h * (kOpBytes / 2) + k * 256;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(row + (((c0 + c) ^ fb(k)) << 4)) = w[c];
+    } else if (WF == W_FP4) {
+      const int kidx = kt0 + min(st, nk - 1);
+      const u32x2_t q2 =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(sb + kOpBytes + fcol * 16 + fkh * 8);
+      const uint32_t sc = sb[kOpBytes + 4096 + fcol * 4 + 2 * (kidx & 1) + fkh];
+      lds_u8* bs = bt;
+      const float sv = e4m3_f32(sc);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t q = q2[c];  // k = 16 fkh + 8c .. + 7, low nibble first
+        // byte p: codes k = 8c+2p (low nibble), 8c+2p+1, decoded exactly by
+        // the gfx950 e2m1 pair conversion (unit scale); e2m1 x e4m3 is exact
+        // in bf16, so the top 16 bits of each product are kept
+        const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+        const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+        const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+        const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+        const u32x4_t w = {perm_hi16(__float_as_uint(v0.x * sv), __float_as_uint(v0.y * sv)),
+                           perm_hi16(__float_as_uint(v1.x * sv), __float_as_uint(v1.y * sv)),
+                           perm_hi16(__float_as_uint(v2.x * sv), __float_as_uint(v2.y * sv)),
+                           perm_hi16(__float_as_uint(v3.x * sv), __float_as_uint(v3.y * sv))};
+        const int chunk = 2 * fkh + c;
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(bs + fcol * 64 + ((chunk ^ fa(fcol)) << 4)) = w;
+      }
     }
   };
 
@@ -379,13 +412,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       const int g = lane >> 4, i16 = lane & 15, qq = i16 & 3, mr = i16 >> 2;
       const int colb = lc + 16 * (g & 1);
       const int krow = 8 * (g >> 1) + mr;  // fb(krow + 16 s + 4 r) == fb(mr)
-      bfr[j][0] = kOpBytes + h * (kOpBytes / 2) + krow * 256 + ((((colb >> 3) + (qq >> 1)) ^ fb(mr)) << 4) +
+      bfr[j][0] = h * (kOpBytes / 2) + krow * 256 + ((((colb >> 3) + (qq >> 1)) ^ fb(mr)) << 4) +
                   (qq & 1) * 8;
       bfr[j][1] = 0;
     } else {
       const int n = gcol + (lane & 31);
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) bfr[j][sb] = kOpBytes + n * 64 + (((2 * sb + hl) ^ fa(n)) << 4);
+      for (int sb = 0; sb < 2; ++sb) bfr[j][sb] = n * 64 + (((2 * sb + hl) ^ fa(n)) << 4);
     }
   }
 
@@ -428,17 +461,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     struct Frags {
       bf16x8_t a[2][4], b[2][2];
     };
-    auto read_frags = [&](const lds_u8* sbase, Frags& f) {
+    // abase: the stage's A tile; bbase: its B tile
+    auto read_frags = [&](const lds_u8* abase, const lds_u8* bbase, Frags& f) {
       if (NI == 0) return;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-          f.a[sb][i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(sbase + afr[i][sb]);
+          f.a[sb][i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(abase + afr[i][sb]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if (WF != W_FP4) {
-            const lds_u8* p = sbase + bfr[j][0] + sb * 16 * 256;
+            const lds_u8* p = bbase + bfr[j][0] + sb * 16 * 256;
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4_t*)(p));
             const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -446,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
             const s16x4_t v[2] = {lo, hi};
             f.b[sb][j] = __builtin_bit_cast(bf16x8_t, v);
           } else {
-            f.b[sb][j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(sbase + bfr[j][sb]);
+            f.b[sb][j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(bbase + bfr[j][sb]);
           }
         }
       }
@@ -462,48 +496,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     };
 
     // Memory instructions per stage per lane: bf16 4 copies (A 2 + B 2);
-    // NVFP4 the code and scale loads of the stage two ahead, then 2 A
-    // copies; FP8 one 16-byte code load of the stage two ahead, then 2 A
-    // copies.
-    constexpr int kPerStage = (WF == W_FP8) ? 3 : 4;
-    u32x2_t fcode[2];
-    uint32_t fscale[2];
-    u32x4_t fq8[2];
-    if (WF == W_FP4) {
-      fp4_load(0, fcode[0], fscale[0]);
-      fp4_load(1, fcode[1], fscale[1]);
-    } else if (WF == W_FP8) {
-      fp8_load(0, fq8[0]);
-      fp8_load(1, fq8[1]);
-    }
+    // FP8 / NVFP4 3 copies (A 2 + the raw codes).
+    constexpr int kPerStage = (WF == W_BF16) ? 4 : 3;
+    auto abase_of = [&](int st) -> const lds_u8* { return lds3 + (st % kDepth) * kStageStride; };
+    auto bbase_of = [&](int st) -> const lds_u8* {
+      return (WF == W_BF16) ? abase_of(st) + kOpBytes : lds3 + kBArea + (st & 1) * kOpBytes;
+    };
     auto stage_in = [&](int st) {
-      if (WF == W_FP4) {
-        fp4_store(st, fcode[st & 1], fscale[st & 1]);
-        fp4_load(st + 2, fcode[st & 1], fscale[st & 1]);
-      } else if (WF == W_FP8) {
-        fp8_store(st, fq8[st & 1]);
-        fp8_load(st + 2, fq8[st & 1]);
-      }
+      if (WF != W_BF16) issue_raw(st);
       issue(st);
     };
-    // Software pipeline: iteration kt runs the MFMAs of stage kt from
-    // registers while the fragments of stage kt + 1 are read from LDS; the
-    // copies run four stages ahead (a stage's LDS buffer is refilled once
-    // every wave has read its fragments).
-    Frags fr[2];
-    stage_in(0);
-    stage_in(1);
-    stage_in(2);
-    stage_in(3);
-    wait_counts<3 * kPerStage, 0>();  // stage 0 landed (this wave's copies)
-    block_barrier();
-    read_frags(lds3, fr[0]);
-    // step kt: MFMAs of stage kt from `cur`, fragments of stage kt + 1 into `nxt`
-    auto step = [&](int kt, const Frags& cur, Frags& nxt) {
-      wait_counts<2 * kPerStage, 0>();  // stage kt + 1 landed; stage kt's fragments read
-      block_barrier();
-      stage_in(kt + 4);
-      read_frags(lds3 + ((kt + 1) & (kStages - 1)) * kStageBytes, nxt);
+    // The MFMAs of stage kt and the fragment reads of stage kt + 1 ride one
+    // step; a stage's LDS buffer is refilled once every wave has read it.
+    auto mma_step = [&](int kt, const Frags& cur, Frags& nxt) {
+      read_frags(abase_of(kt + 1), bbase_of(kt + 1), nxt);
       // keep the reads ahead of the MFMAs (the scheduler would otherwise sink
       // them below and serialise LDS latency with the matrix work)
       __builtin_amdgcn_sched_barrier(0);
@@ -514,6 +520,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
     };
+    Frags fr[2];
+#pragma unroll
+    for (int st = 0; st < kDepth; ++st) stage_in(st);
+    // step kt: MFMAs of stage kt from `cur`, fragments of stage kt + 1 into `nxt`
+    auto step = [&](int kt, const Frags& cur, Frags& nxt) {
+      if (WF == W_BF16) {
+        // bf16: copies run four stages ahead
+        wait_counts<2 * kPerStage, 0>();  // stage kt + 1 landed; stage kt's fragments read
+        block_barrier();
+        stage_in(kt + 4);
+      } else {
+        // FP8 / NVFP4: stage kt + 2's raw codes are decoded in this step;
+        // stages kt + 3 .. kt + kDepth - 1 stay in flight across the barrier
+        wait_counts<(kDepth - 3) * kPerStage, 0>();  // stage kt + 2 landed; this wave's decode of kt + 1 written
+        block_barrier();
+        decode(kt + 2);
+        stage_in(kt + kDepth);
+      }
+      mma_step(kt, cur, nxt);
+    };
+    if (WF == W_BF16) {
+      wait_counts<3 * kPerStage, 0>();  // stage 0 landed (this wave's copies)
+      block_barrier();
+    } else {
+      wait_counts<(kDepth - 1) * kPerStage, 0>();  // stage 0 landed
+      block_barrier();
+      decode(0);
+      wait_counts<(kDepth - 2) * kPerStage, 0>();  // stage 1 landed; decode of 0 written
+      block_barrier();
+      decode(1);
+      wait_counts<(kDepth - 2) * kPerStage, 0>();  // decode of 1 written (no new copies)
+      block_barrier();                             // every wave's decode of stage 0 is in LDS
+    }
+    read_frags(abase_of(0), bbase_of(0), fr[0]);
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
       step(kt, fr[0], fr[1]);
