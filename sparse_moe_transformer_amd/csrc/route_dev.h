@@ -37,7 +37,8 @@ inline RouteSmallCfg route_small_config(const Shape& sh) {
   c.tb = std::max(1, std::min(sh.T, kRouteThreads / (ec * rg_need)));
   const int rg = kRouteThreads / (ec * c.tb);
   c.groups = (sh.T + c.tb - 1) / c.tb;
-  c.ok = rg >= 1 && (c.slice_rows + rg - 1) / rg <= kRouteMaxRows && c.tb * c.slice_rows <= kRouteThreads * kRouteMaxRows;
+  c.ok = rg >= 1 && (c.slice_rows + rg - 1) / rg <= kRouteMaxRows && c.tb * c.slice_rows <= kRouteThreads * kRouteMaxRows &&
+         c.tb * sh.E <= 8 * kRouteThreads;  // the routing's keys and ranks fit the slice's LDS
   return c;
 }
 
@@ -94,6 +95,40 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   i = bi;
 }
 
+// The routing of one token from a wave whose lane l holds the logits zv[j]
+// of experts l + 64 j and whether each is selected: p = softmax over all E
+// experts (zmax = the largest logit), w = p_S / sum(p_S), written in
+// ascending expert id.
+__device__ __forceinline__ void wave_emit_route(const float (&zv)[4], const bool (&sel)[4], float zmax, int E,
+                                                int32_t* out_idx, float* out_w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (lane + j * kWave < E) s += __expf(zv[j] - zmax);
+  s = wave_sum(s);
+  float p[4];
+  float ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    p[j] = sel[j] ? __expf(zv[j] - zmax) / s : 0.f;
+    ps += p[j];
+  }
+  ps = wave_sum(ps);
+  // ascending expert id order: position = selected ids below this one
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint64_t m = __ballot(sel[j]);
+    if (sel[j]) {
+      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+      out_idx[pos] = lane + j * kWave;
+      out_w[pos] = p[j] / ps;
+    }
+    base += __popcll(m);
+  }
+}
+
 // One wave routes one token whose E logits are in z (LDS or global).  Lane
 // l owns experts l, l+64, l+128, l+192.  k rounds of wave arg-max pick the
 // experts (equal logits: lower id first); p = softmax over all experts;
@@ -127,31 +162,61 @@ __device__ void wave_route_token(const float* z, int E, int k, int32_t* out_idx,
     for (int j = 0; j < 4; ++j)
       if (lane + j * kWave == bi) sel[j] = true;
   }
-  // softmax over all experts, then renormalise the selected weights
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (lane + j * kWave < E) s += __expf(zv[j] - zmax);
-  s = wave_sum(s);
-  float p[4];
-  float ps = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    p[j] = sel[j] ? __expf(zv[j] - zmax) / s : 0.f;
-    ps += p[j];
-  }
-  ps = wave_sum(ps);
-  // ascending expert id order: position = selected ids below this one
-  int base = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint64_t m = __ballot(sel[j]);
-    if (sel[j]) {
-      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-      out_idx[pos] = lane + j * kWave;
-      out_w[pos] = p[j] / ps;
+  wave_emit_route(zv, sel, zmax, E, out_idx, out_w);
+}
+
+// A total order on (logit, expert) as one unsigned key: a larger logit, or
+// an equal logit with a lower id, gives a larger key.  The logit's bits are
+// mapped so that unsigned order is float order (-0 counts as +0); the low
+// word holds E - 1 - e.  route_key_z inverts the logit part.
+__device__ __forceinline__ uint64_t route_key(float z, int e, int E) {
+  uint32_t u = __float_as_uint(z);
+  if (u == 0x80000000u) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (uint64_t(u) << 32) | uint32_t(E - 1 - e);
+}
+__device__ __forceinline__ float route_key_z(uint64_t key) {
+  const uint32_t u = uint32_t(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Routes nt tokens with the whole block at once (the latency-bound end of
+// the small-T router).  keys: LDS [nt][E] route_key values; rank: LDS
+// [nt][E] ints; zmx: LDS [nt] floats.  The rank of an expert is the number
+// of experts of its token with a larger key, so the selected set is
+// rank < k (the same set as k rounds of arg-max with lower ids winning
+// ties), found by one thread per (token, expert) in parallel.  One wave per
+// token then writes the softmax weights as wave_route_token does.  Ends
+// with the block converged; keys/rank/zmx are free afterwards.
+__device__ void block_route_group(const uint64_t* keys, int* rank, float* zmx, int nt, int E, int k,
+                                  int32_t* out_idx, float* out_w) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nt * E; i += kRouteThreads) {
+    const int t = i / E;
+    const uint64_t* kt = keys + t * E;
+    const uint64_t mine = keys[i];
+    int r = 0;
+    for (int j = 0; j < E; j += 4) {  // E % 4 == 0
+      r += kt[j] > mine;
+      r += kt[j + 1] > mine;
+      r += kt[j + 2] > mine;
+      r += kt[j + 3] > mine;
     }
-    base += __popcll(m);
+    rank[i] = r;
+    if (r == 0) zmx[t] = route_key_z(mine);
+  }
+  __syncthreads();
+  const int wid = tid / kWave, lane = tid & (kWave - 1);
+  for (int t = wid; t < nt; t += kRouteThreads / kWave) {
+    float zv[4];
+    bool sel[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + j * kWave;
+      zv[j] = e < E ? route_key_z(keys[t * E + e]) : -INFINITY;
+      sel[j] = e < E && rank[t * E + e] < k;
+    }
+    wave_emit_route(zv, sel, zmx[t], E, out_idx + size_t(t) * k, out_w + size_t(t) * k);
   }
 }
 
@@ -191,7 +256,7 @@ __device__ void route_slice(const Shape& sh, int slice_rows, int TB, int nslices
   const int t0 = group * TB;
   const int k0 = s * slice_rows;
   const int nrow = live && rg < slice_rows ? (slice_rows - 1 - rg) / RG + 1 : 0;
-  __shared__ float xs[kThreads * kRouteMaxRows];  // [TB][slice_rows]
+  __shared__ __attribute__((aligned(16))) float xs[kThreads * kRouteMaxRows];  // [TB][slice_rows]
   __shared__ float red[kThreads * 8];              // [RG][TB][E]
   const bf16_t* pw = wr + size_t(k0 + (live ? rg : 0)) * E + ec * CW;
   vec_t vw[kRouteMaxRows];
@@ -247,28 +312,30 @@ __device__ void route_slice(const Shape& sh, int slice_rows, int TB, int nslices
   }
   __syncthreads();
   if (!last) return;
-  // one wave per token: z = sum of the slices in order (+ b), then route;
-  // each wave uses its own LDS row (xs is free now)
-  const int wid = tid / kWave, lane = tid & (kWave - 1);
-  float* zs = xs + wid * 256;
-  for (int tt = wid; tt < TB && t0 + tt < T; tt += kThreads / kWave) {
-    const int t = t0 + tt;
-    for (int e = lane; e < E; e += kWave) {
-      const float* p = part + size_t(t) * E + e;
-      float v[kRouteSlices];
+  // z = sum of the slices in order (+ b): one thread per (token, expert) of
+  // the group, so the whole group's logits come back in one round trip; then
+  // the block routes the group.  xs (the keys) and red (the ranks) are free
+  // now: TB * E <= 8 * kRouteThreads.
+  const int nt = min(TB, T - t0);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(xs);
+  int* rank = reinterpret_cast<int*>(red);
+  __shared__ float zmx[kRouteSmallT];
+  for (int i = tid; i < nt * E; i += kThreads) {
+    const int e = i % E;
+    const float* p = part + size_t(t0) * E + i;  // token t0 + i / E, expert e
+    float v[kRouteSlices];
 #pragma unroll
-      for (int j = 0; j < kRouteSlices; ++j)
-        v[j] = j < nslices ? __hip_atomic_load(p + size_t(j) * kRouteSmallT * E, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT)
-                                  : 0.f;
-      float z = 0.f;
+    for (int j = 0; j < kRouteSlices; ++j)
+      v[j] = j < nslices ? __hip_atomic_load(p + size_t(j) * kRouteSmallT * E, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                : 0.f;
+    float z = 0.f;
 #pragma unroll
-      for (int j = 0; j < kRouteSlices; ++j) z += v[j];
-      zs[e] = bias ? z + bias[e] : z;
-    }
-    // the wave reads back only the entries its own lanes wrote
-    wave_route_token(zs, E, sh.k, ws.topk_idx + size_t(t) * sh.k, ws.topk_w + size_t(t) * sh.k);
+    for (int j = 0; j < kRouteSlices; ++j) z += v[j];
+    keys[i] = route_key(bias ? z + bias[e] : z, e, E);
   }
+  __syncthreads();
+  block_route_group(keys, rank, zmx, nt, E, sh.k, ws.topk_idx + size_t(t0) * sh.k, ws.topk_w + size_t(t0) * sh.k);
 }
 
 }  // namespace
