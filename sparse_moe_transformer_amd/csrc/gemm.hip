@@ -526,10 +526,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     // step kt: MFMAs of stage kt from `cur`, fragments of stage kt + 1 into `nxt`
     auto step = [&](int kt, const Frags& cur, Frags& nxt) {
       if (WF == W_BF16) {
-        // bf16: copies run four stages ahead
-        wait_counts<2 * kPerStage, 0>();  // stage kt + 1 landed; stage kt's fragments read
+        // bf16: copies run kDepth stages ahead
+        wait_counts<(kDepth - 2) * kPerStage, 0>();  // stage kt + 1 landed; stage kt's fragments read
         block_barrier();
-        stage_in(kt + 4);
+        stage_in(kt + kDepth);
       } else {
         // FP8 / NVFP4: stage kt + 2's raw codes are decoded in this step;
         // stages kt + 3 .. kt + kDepth - 1 stay in flight across the barrier
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       mma_step(kt, cur, nxt);
     };
     if (WF == W_BF16) {
-      wait_counts<3 * kPerStage, 0>();  // stage 0 landed (this wave's copies)
+      wait_counts<(kDepth - 1) * kPerStage, 0>();  // stage 0 landed (this wave's copies)
       block_barrier();
     } else {
       wait_counts<(kDepth - 1) * kPerStage, 0>();  // stage 0 landed

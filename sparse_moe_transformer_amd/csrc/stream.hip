@@ -50,6 +50,11 @@ constexpr int kDownCols = 128;  // output columns of a routed down unit
 constexpr int kDenseDownCols = 128;  // output columns of a dense down unit
 constexpr int kDenseOnlyCols = 256;  // output columns of a gate/up unit without experts
 constexpr int kDownColsMax = kDenseDownCols > kDownCols ? kDenseDownCols : kDownCols;
+// Beside experts, the dense gate/up units are split between the router's
+// launch and the routed gate/up launch: the router's hand-off is a latency
+// chain, so its launch takes only as many dense units as stream within it
+// (this share, in 1/8ths); the rest run first in the routed launch.
+constexpr int kDenseRouteEighths = 5;
 
 __device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);  // a.lo | b.lo << 16
@@ -538,17 +543,22 @@ __device__ void gateup_unit(const StreamArgs& a, const Workspace& ws, int KS, in
 
 // Routed gate/up units.  (3 waves per SIMD: the register budget of 168
 // holds every unit variant)
+// Blocks [0, udn) are the dense units ud0 .. ud0 + udn - 1 (K-slices KSd),
+// the rest the routed units.
 template <bool W8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_gateup(StreamArgs a,
-                                                                                                      Workspace ws,
-                                                                                                      int KS) {
-  gateup_unit<false, W8 ? 128 : 64, W8>(a, ws, KS, blockIdx.x);
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_gateup(
+    StreamArgs a, Workspace ws, int KS, int ud0, int udn, int KSd) {
+  const int b = blockIdx.x;
+  if (b < udn)
+    gateup_unit<true, W8 ? 128 : 64, W8>(a, ws, KSd, ud0 + b);
+  else
+    gateup_unit<false, W8 ? 128 : 64, W8>(a, ws, KS, b - udn);
 }
 
-// The router and the dense branch's gate/up units in one launch: blocks
-// [0, nroute) are the router's (K-slice, token group) blocks, the rest are
-// dense gate/up units.  The dense branch does not depend on the routing, so
-// its weights stream while the router's few blocks wait on memory latency,
+// The router and dense gate/up units in one launch: blocks [0, nroute) are
+// the router's (K-slice, token group) blocks, the rest are the first dense
+// gate/up units.  The dense branch does not depend on the routing, so its
+// weights stream while the router's few blocks wait on memory latency,
 // with no second stream and no events.
 template <int CW, bool W8>
 __global__ __launch_bounds__(kThreads) void k_route_dense(
@@ -693,19 +703,39 @@ __global__ __launch_bounds__(kThreads) void k_stream_export(Shape sh, Workspace 
 
 }  // namespace
 
+namespace {
+// The dense gate/up units of a config with experts (64 columns, FP8 128:
+// one 128-byte line per weight row), and how many the router's launch takes.
+struct DenseSplit {
+  int ksd, nc, ud, in_route;
+};
+DenseSplit dense_split(const StreamArgs& a) {
+  const Shape& sh = a.sh;
+  DenseSplit d{};
+  d.ksd = sh.D > 0 ? dense_gateup_slices(sh) : 1;
+  d.nc = a.fp8 ? 128 : 64;
+  d.ud = sh.D > 0 ? ((sh.D + d.nc - 1) / d.nc) * 2 * d.ksd : 0;
+  d.in_route = d.ud * kDenseRouteEighths / 8;
+  return d;
+}
+}  // namespace
+
 hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
   const Shape& sh = a.sh;
   if (sh.T == 0 || sh.E == 0) return hipSuccess;
   const int ks = a.fp8 ? kStreamKS8 : kStreamKS;
   const int nc = a.fp8 ? 128 : 64;  // unit columns (gateup_unit's NC)
+  const DenseSplit d = dense_split(a);
+  const int udn = d.ud - d.in_route;  // dense units left to this launch
   const size_t kl = size_t((sh.H / 64 + ks - 1) / ks) * 64;  // longest slice
-  const size_t lds = std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * nc * 4);
+  const size_t kld = udn ? size_t((sh.H / 64 + d.ksd - 1) / d.ksd) * 64 : 0;
+  const size_t lds = std::max(std::max(kl, kld) * kRowsChunk * 2, size_t(5) * kRowsChunk * nc * 4);
   const int max_active = std::min(sh.E, sh.T * sh.k);
-  const dim3 grid(max_active * ((sh.I + nc - 1) / nc) * 2 * ks);
+  const dim3 grid(udn + max_active * ((sh.I + nc - 1) / nc) * 2 * ks);
   if (a.fp8)
-    hipLaunchKernelGGL(k_stream_gateup<true>, grid, dim3(kThreads), lds, s, a, ws, ks);
+    hipLaunchKernelGGL(k_stream_gateup<true>, grid, dim3(kThreads), lds, s, a, ws, ks, d.in_route, udn, d.ksd);
   else
-    hipLaunchKernelGGL(k_stream_gateup<false>, grid, dim3(kThreads), lds, s, a, ws, ks);
+    hipLaunchKernelGGL(k_stream_gateup<false>, grid, dim3(kThreads), lds, s, a, ws, ks, d.in_route, udn, d.ksd);
   return hipGetLastError();
 }
 
@@ -719,11 +749,11 @@ hipError_t launch_route_dense(const StreamArgs& a, const bf16_t* wr, const float
   const int nroute = sh.E > 0 ? c.nslices * c.groups : 0;
   const int ksd = sh.D > 0 ? dense_gateup_slices(sh) : 1;
   const bool w8 = a.fp8;
-  // dense unit columns: 64 beside the router (FP8: 128, one 128-byte line
-  // per weight row); without experts 256 when D allows
+  // dense unit columns: beside the router those of dense_split (this launch
+  // runs its first in_route units); without experts 256 when D allows
   const bool wide = nroute == 0 && sh.D % kDenseOnlyCols == 0;
   const int nc = wide ? kDenseOnlyCols : (w8 ? 128 : 64);
-  const int ud = sh.D > 0 ? ((sh.D + nc - 1) / nc) * 2 * ksd : 0;
+  const int ud = sh.D == 0 ? 0 : nroute > 0 ? dense_split(a).in_route : ((sh.D + nc - 1) / nc) * 2 * ksd;
   const size_t kl = size_t((sh.H / 64 + ksd - 1) / ksd) * 64;  // longest dense K-slice
   const size_t lds = ud ? std::max(kl * kRowsChunk * 2, size_t(5) * kRowsChunk * nc * 4) : 0;
   if (nroute + ud == 0) return hipSuccess;
