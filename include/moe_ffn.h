@@ -271,11 +271,15 @@ enum {
                                 launch also runs the dense branch's gate/up */
   MOE_FFN_STAGE_ALIGN = 1,   /* grouping kernels (MFMA variant only) */
   MOE_FFN_STAGE_GATEUP = 2,  /* gate/up: MFMA = the routed + dense GEMM with the
-                                GeGLU fused; streaming = the routed partial sums */
-  MOE_FFN_STAGE_DOWN = 3,    /* down projections, routed + dense */
+                                GeGLU fused; streaming = the routed partial sums
+                                and the dense ones the router launch left */
+  MOE_FFN_STAGE_DOWN = 3,    /* down projections, routed + dense; streaming
+                                with experts: each down unit forms its GeGLU
+                                rows from the gate/up partial sums */
   MOE_FFN_STAGE_COMBINE = 4, /* weighted sum + dense add */
-  MOE_FFN_STAGE_GEGLU = 5,   /* streaming only: GeGLU of the summed partials
-                                (routed and dense rows) */
+  MOE_FFN_STAGE_GEGLU = 5,   /* streaming without experts only: GeGLU of the
+                                dense rows (with experts it runs inside the
+                                down stage) */
   MOE_FFN_NUM_STAGES = 6
 };
 /* Start recording an event pair around every stage in stage_mask (bit s =

@@ -177,7 +177,7 @@ struct StreamArgs {
 hipError_t launch_route_dense(const StreamArgs& a, const bf16_t* wr, const float* bias, const Workspace& ws,
                               hipStream_t s);
 hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, hipStream_t s);
-hipError_t launch_stream_geglu(const StreamArgs& a, const Workspace& ws, hipStream_t s);
+hipError_t launch_dense_geglu(const StreamArgs& a, const Workspace& ws, hipStream_t s);
 hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStream_t s);
 // h and y rows of the last streamed forward into caller buffers in grouped
 // (perm) order; needs ws.pos from launch_align; either pointer may be null

@@ -586,10 +586,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
 // down
 // ---------------------------------------------------------------------------
 
-// GeGLU of the streamed rows: h = gelu_tanh(sum G) * (sum U), K-slices in
-// fixed order, bf16.  Items [0, n4r) are the T*k routed slot rows of
-// ws.part into ws.h (slot order), items [n4r, n4r + n4d) the T dense token
-// rows into ws.h_d.  4 columns per item.
+// GeGLU of the dense rows of a config without experts: h_d = gelu_tanh(sum
+// G) * (sum U), K-slices in fixed order, bf16, 4 columns per item.  (With
+// experts the down units form their rows themselves, StageGeglu below; a
+// wide dense branch alone would have every column unit of its down re-read
+// fp32 partials of all K-slices, 16x the bytes of the bf16 rows.)
 __device__ __forceinline__ void geglu4(const Workspace& ws, const Shape& sh, bool dense, int KS, int row, int c,
                                        bf16_t* hout) {
   float4 g = make_float4(0.f, 0.f, 0.f, 0.f), up = g;
@@ -603,28 +604,92 @@ __device__ __forceinline__ void geglu4(const Workspace& ws, const Shape& sh, boo
                                               pack_bf16x2(gelu_tanh(g.z) * up.z, gelu_tanh(g.w) * up.w)};
 }
 
-__global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace ws, long long n4r, long long n4d,
-                                                           int ksr) {
-  const int qi = sh.I / 4, qd = sh.D / 4;
+__global__ __launch_bounds__(kThreads) void k_dense_geglu(Shape sh, Workspace ws, long long n4d) {
+  const int qd = sh.D / 4;
   const int ksd = dense_gateup_slices(sh);
-  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n4r + n4d;
-       i += (long long)gridDim.x * kThreads) {
-    if (i < n4r) {
-      const int row = int(i / qi), c = int(i % qi) * 4;
-      geglu4(ws, sh, false, ksr, row, c, ws.h + (long long)row * sh.I + c);
-    } else {
-      const long long j = i - n4r;
-      const int row = int(j / qd), c = int(j % qd) * 4;
-      geglu4(ws, sh, true, ksd, row, c, ws.h_d + (long long)row * sh.D + c);
+  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n4d; i += (long long)gridDim.x * kThreads) {
+    const int row = int(i / qd), c = int(i % qd) * 4;
+    geglu4(ws, sh, true, ksd, row, c, ws.h_d + (long long)row * sh.D + c);
+  }
+}
+
+// GeGLU rows of a down unit, staged for unit_staged / unit8_staged:
+// h[r][k] = bf16(gelu_tanh(G) * U) with G and U the sums of the gate/up
+// K-slice partials in slice order, for the unit's rows r < nr and k in
+// [kbeg, kend), written to xs[k - kbeg][8]; rows r >= nr are zero.  Rows
+// are part rows: slot[c0 + r] (routed) or token c0 + r (dense).  With hout
+// set (the first column unit of an expert or dense K-slice) the rows also
+// go to hout[row * ldh + k], so a streamed forward's h can be read back.
+struct StageGeglu {
+  const Workspace* ws;
+  const Shape* sh;
+  bool dense;
+  int KS;           // K-slices of the gate/up partials
+  int nr, c0;
+  const int* slot;  // routed: slot of each row of the expert (LDS)
+  bf16_t* hout;
+  int ldh;
+  __device__ void operator()(bf16_t* xs, int kbeg, int kend) const {
+    const int nq = (kend - kbeg) / 4;
+#pragma unroll 1
+    for (int c = threadIdx.x; c < nq; c += kThreads) {
+      const int k = kbeg + 4 * c;
+      uint32_t hv[kRowsChunk][2];
+#pragma unroll
+      for (int r = 0; r < kRowsChunk; ++r) {
+        hv[r][0] = hv[r][1] = 0u;
+        if (r < nr) {
+          const int row = dense ? c0 + r : slot[c0 + r];
+          float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+          for (int ks = 0; ks < KS; ++ks) {
+            const float4 pg = *reinterpret_cast<const float4*>(part_ptr(*ws, *sh, dense, ks, row, 0) + k);
+            const float4 pu = *reinterpret_cast<const float4*>(part_ptr(*ws, *sh, dense, ks, row, 1) + k);
+            g.x += pg.x; g.y += pg.y; g.z += pg.z; g.w += pg.w;
+            u.x += pu.x; u.y += pu.y; u.z += pu.z; u.w += pu.w;
+          }
+          hv[r][0] = pack_bf16x2(gelu_tanh(g.x) * u.x, gelu_tanh(g.y) * u.y);
+          hv[r][1] = pack_bf16x2(gelu_tanh(g.z) * u.z, gelu_tanh(g.w) * u.w);
+          if (hout) *reinterpret_cast<u32x2_t*>(hout + (long long)row * ldh + k) = u32x2_t{hv[r][0], hv[r][1]};
+        }
+      }
+      // k-major, the 8 rows of one k in 16 bytes
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4_t v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[q] = (j & 1) ? perm_hi16(hv[2 * q][j / 2], hv[2 * q + 1][j / 2])
+                         : perm_lo16(hv[2 * q][j / 2], hv[2 * q + 1][j / 2]);
+        *reinterpret_cast<u32x4_t*>(xs + (4 * c + j) * kRowsChunk) = v;
+      }
     }
   }
+};
+
+// A down unit's rows (nr <= 8) against its weight columns, the rows staged
+// in LDS by `st`.
+template <int NCOLS, class Stage>
+__device__ const float* unit_staged_rows(int nr, const bf16_t* w, int ldw, int kbeg, int kend, const Stage& st,
+                                         bf16_t* xs, float* red) {
+  if (nr <= 2) return unit_staged<2, NCOLS, 8, 8>(w, ldw, kbeg, kend, st, xs, red);
+  if (nr <= 4) return unit_staged<4, NCOLS, 8, 8>(w, ldw, kbeg, kend, st, xs, red);
+  return unit_staged<8, NCOLS, 8, 4>(w, ldw, kbeg, kend, st, xs, red);
+}
+template <int NCOLS, class Stage>
+__device__ const float* unit8_staged_rows(int nr, const uint8_t* w, int ldw, int kbeg, int kend, int nvalid,
+                                          const Stage& st, bf16_t* xs, float* red) {
+  if (nr <= 2) return unit8_staged<2, NCOLS, 8>(w, ldw, kbeg, kend, nvalid, st, xs, red);
+  if (nr <= 4) return unit8_staged<4, NCOLS, 8>(w, ldw, kbeg, kend, nvalid, st, xs, red);
+  return unit8_staged<8, NCOLS, 8>(w, ldw, kbeg, kend, nvalid, st, xs, red);
 }
 
 // Down units.  DENSE: unit u = (128 columns, K-slice of whole 64-row groups
 // of D) over the T rows of h_d, fp32 partial outputs per slice (summed by
 // the combine).  Routed: unit u = (ai-th active expert, 128 columns) over
 // the expert's rows of h (slot order), bf16 output rows y indexed by slot.
-template <bool DENSE, int NC = kDownCols, bool W8 = false>
+// The rows of h / h_d are formed in the unit from the gate/up partials
+// (StageGeglu): no separate GeGLU launch.
+template <bool DENSE, int NC, bool W8, bool FUSED>
 __device__ void down_unit(const StreamArgs& a, const Workspace& ws, int u) {
   const Shape& sh = a.sh;
   const int H = sh.H;
@@ -654,19 +719,23 @@ __device__ void down_unit(const StreamArgs& a, const Workspace& ws, int u) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16_t* hs = reinterpret_cast<bf16_t*>(smem_raw);  // [kend-kbeg][8] staged rows
   float* red = reinterpret_cast<float*>(smem_raw);   // [5][8][NC]
-  __shared__ const bf16_t* act[kRowsChunk];
+  // K-slices of the gate/up partials behind h / h_d
+  const int ksg = DENSE ? dense_gateup_slices(sh) : (W8 ? kStreamKS8 : kStreamKS);
+  bf16_t* hout = u == 0 ? (DENSE ? ws.h_d : ws.h) : nullptr;
   for (int c0 = 0; c0 < rows; c0 += kRowsChunk) {
     const int nr = min(kRowsChunk, rows - c0);
-    if (threadIdx.x < kRowsChunk) {
-      const int r = threadIdx.x;
-      act[r] = r < nr ? (DENSE ? ws.h_d : ws.h) + (long long)(DENSE ? c0 + r : slot[c0 + r]) * K : nullptr;
-    }
-    __syncthreads();
-    const bf16_t* rowp[kRowsChunk];
+    const float* sums;
+    if (!FUSED) {  // dense rows of a config without experts: h_d from k_dense_geglu
+      const bf16_t* rowp[kRowsChunk];
 #pragma unroll
-    for (int r = 0; r < kRowsChunk; ++r) rowp[r] = act[r];
-    const float* sums = W8 ? unit8_x_rows<NC>(nr, w8, H, kbeg, kend, NC, rowp, hs, red)
-                           : unit_x_rows<NC>(nr, wd, H, kbeg, kend, rowp, hs, red);
+      for (int r = 0; r < kRowsChunk; ++r) rowp[r] = r < nr ? ws.h_d + (long long)(c0 + r) * K : nullptr;
+      sums = W8 ? unit8_x_rows<NC>(nr, w8, H, kbeg, kend, NC, rowp, hs, red)
+                : unit_x_rows<NC>(nr, wd, H, kbeg, kend, rowp, hs, red);
+    } else {
+      const StageGeglu st{&ws, &sh, DENSE, ksg, nr, c0, slot, hout, K};
+      sums = W8 ? unit8_staged_rows<NC>(nr, w8, H, kbeg, kend, NC, st, hs, red)
+                : unit_staged_rows<NC>(nr, wd, H, kbeg, kend, st, hs, red);
+    }
     if (DENSE) {
       float* o = ws.ydp + ((long long)ksd * kRouteSmallT + c0) * H + n0;
       for (int i = threadIdx.x; i < nr * NC; i += kThreads) o[(long long)(i / NC) * H + (i % NC)] = sums[i] * qscale;
@@ -679,15 +748,18 @@ __device__ void down_unit(const StreamArgs& a, const Workspace& ws, int u) {
 }
 
 // One launch for the dense down units (blocks [0, ud)) and the routed ones.
-template <bool W8>
+// FUSED (a config with experts): the units form their GeGLU rows from the
+// gate/up partials.  Otherwise (no experts, hence no routed units) the dense
+// units read h_d, which k_dense_geglu wrote.
+template <bool W8, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_down(StreamArgs a,
                                                                                                     Workspace ws,
                                                                                                     int ud) {
   const int u = blockIdx.x;
   if (u < ud)
-    down_unit<true, kDenseDownCols, W8>(a, ws, u);
-  else
-    down_unit<false, kDownCols, W8>(a, ws, u - ud);
+    down_unit<true, kDenseDownCols, W8, FUSED>(a, ws, u);
+  else if (FUSED)
+    down_unit<false, kDownCols, W8, true>(a, ws, u - ud);
 }
 
 // h and y rows of the last streamed forward (slot order) copied to grouped
@@ -785,14 +857,12 @@ hipError_t launch_route_dense(const StreamArgs& a, const bf16_t* wr, const float
   return hipGetLastError();
 }
 
-hipError_t launch_stream_geglu(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
+hipError_t launch_dense_geglu(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
   const Shape& sh = a.sh;
-  if (sh.T == 0) return hipSuccess;
-  const long long n4r = (long long)sh.T * sh.k * sh.I / 4;
-  const long long n4d = sh.D > 0 ? (long long)sh.T * sh.D / 4 : 0;
-  const int gblocks = int(std::min<long long>(1024, (n4r + n4d + kThreads - 1) / kThreads));
-  hipLaunchKernelGGL(k_stream_geglu, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, n4r, n4d,
-                     a.fp8 ? kStreamKS8 : kStreamKS);
+  if (sh.T == 0 || sh.E > 0 || sh.D == 0) return hipSuccess;  // with experts the down units form h_d
+  const long long n4d = (long long)sh.T * sh.D / 4;
+  const int gblocks = int(std::min<long long>(1024, (n4d + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(k_dense_geglu, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, n4d);
   return hipGetLastError();
 }
 
@@ -803,13 +873,19 @@ hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStrea
   const int ksd = sh.D > 0 ? dense_down_slices(sh) : 1;
   const int ud = sh.D > 0 ? (sh.H / kDenseDownCols) * ksd : 0;
   const int max_active = std::min(sh.E, sh.T * sh.k);
+  const bool fused = sh.E > 0;  // else k_dense_geglu formed h_d
   // longest K run of a unit: a dense K-slice or the expert width
   const int kd = ud ? (sh.D / 64 + ksd - 1) / ksd * 64 : 0;
   const size_t lds = std::max(size_t(std::max(sh.I, kd)) * kRowsChunk * 2, size_t(5) * kRowsChunk * kDownColsMax * 4);
-  if (a.fp8)
-    hipLaunchKernelGGL(k_stream_down<true>, dim3(ud + max_active * nblk), dim3(kThreads), lds, s, a, ws, ud);
+  const dim3 grid(ud + max_active * nblk);
+  if (a.fp8 && fused)
+    hipLaunchKernelGGL((k_stream_down<true, true>), grid, dim3(kThreads), lds, s, a, ws, ud);
+  else if (a.fp8)
+    hipLaunchKernelGGL((k_stream_down<true, false>), grid, dim3(kThreads), lds, s, a, ws, ud);
+  else if (fused)
+    hipLaunchKernelGGL((k_stream_down<false, true>), grid, dim3(kThreads), lds, s, a, ws, ud);
   else
-    hipLaunchKernelGGL(k_stream_down<false>, dim3(ud + max_active * nblk), dim3(kThreads), lds, s, a, ws, ud);
+    hipLaunchKernelGGL((k_stream_down<false, false>), grid, dim3(kThreads), lds, s, a, ws, ud);
   return hipGetLastError();
 }
 
