@@ -61,13 +61,43 @@ def to_dev_bf16(torch, a):
     return t.to("cuda")
 
 
+# The streaming path runs the first DENSE_ROUTE_EIGHTHS/8 of the dense
+# branch's gate/up units (64 columns x one of 4 K-slices of whole 64-row
+# groups each, K-slice fastest, then gate/up, then the column block) in the
+# router's launch and the rest in the routed gate/up launch.  Mirrors the
+# library's split (kDenseRouteEighths in the streaming kernels' source).
+DENSE_ROUTE_EIGHTHS = 5
+DENSE_UNIT_COLS, DENSE_KSLICES = 64, 4
+
+
+def dense_units_in_gateup(shape):
+    """(weight bytes, output columns) of the dense gate/up units that the
+    routed gate/up launch runs."""
+    H, D = shape.hidden, shape.dense_dim
+    if D == 0:
+        return 0, 0
+    ks = min(DENSE_KSLICES, H // 64)
+    ud = -(-D // DENSE_UNIT_COLS) * 2 * ks
+    g64 = H // 64
+    wbytes = cols = 0
+    for u in range(ud * DENSE_ROUTE_EIGHTHS // 8, ud):
+        s, nb = u % ks, u // (2 * ks)
+        rows = ((s + 1) * g64 // ks - s * g64 // ks) * 64
+        nc = min(DENSE_UNIT_COLS, D - nb * DENSE_UNIT_COLS)
+        wbytes += rows * nc * 2
+        cols += nc if s == 0 else 0
+    return wbytes, cols
+
+
 def routed_gateup_bytes(shape, n_act):
     """Algorithmic HBM bytes of the routed gate/up weight-streaming launch:
-    the gate and up matrices of the n_act experts that have tokens, the T
-    input rows, and the T*k hidden rows at bf16 (the kernel's fp32 partial
-    sums are an implementation choice, not counted)."""
+    the gate and up matrices of the n_act experts that have tokens and the
+    dense gate/up units it runs, the T input rows, and the T*k hidden rows
+    plus the dense units' T output columns at bf16 (the kernel's fp32
+    partial sums are an implementation choice, not counted)."""
     H, I, T, k = shape.hidden, shape.expert_dim, shape.tokens, shape.top_k
-    return n_act * 2 * H * I * 2 + T * H * 2 + T * k * I * 2
+    dw, dc = dense_units_in_gateup(shape)
+    return n_act * 2 * H * I * 2 + dw + T * H * 2 + T * k * I * 2 + T * dc * 2
 
 
 def step_bytes(shape, n_act):
@@ -336,7 +366,8 @@ def main():
                    "top_k": dec.top_k, "expert_dim": dec.expert_dim, "dense_dim": dec.dense_dim,
                    "weight_copies": args.copies, "graph": bool(args.graph),
                    "active_experts": r["n_act"]},
-        "roofline": {"bound": "hbm", "kernel": "k_stream_gateup (routed gate/up weight streaming)",
+        "roofline": {"bound": "hbm", "kernel": "k_stream_gateup (routed gate/up + 3/8 of the dense units, "
+                                               "weight streaming)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes": gu_bytes, "avg_us": gu_us},

@@ -274,12 +274,12 @@ enum {
                                 GeGLU fused; streaming = the routed partial sums
                                 and the dense ones the router launch left */
   MOE_FFN_STAGE_DOWN = 3,    /* down projections, routed + dense; streaming
-                                with experts: each down unit forms its GeGLU
-                                rows from the gate/up partial sums */
+                                with experts and bf16 weights: each down unit
+                                forms its GeGLU rows from the gate/up partials */
   MOE_FFN_STAGE_COMBINE = 4, /* weighted sum + dense add */
-  MOE_FFN_STAGE_GEGLU = 5,   /* streaming without experts only: GeGLU of the
-                                dense rows (with experts it runs inside the
-                                down stage) */
+  MOE_FFN_STAGE_GEGLU = 5,   /* streaming with FP8 weights or without
+                                experts: GeGLU of the summed partials (else it
+                                runs inside the down stage) */
   MOE_FFN_NUM_STAGES = 6
 };
 /* Start recording an event pair around every stage in stage_mask (bit s =

@@ -292,11 +292,11 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "gate/up");
   }
-  if (stream && !experts && sh.D > 0) {
-    // without experts the dense rows get a GeGLU pass of their own; with
-    // experts the down units form their rows from the partials
+  if (stream && !moe::stream_fused_geglu(sh, args.fp8)) {
+    // a GeGLU pass over the summed partials (otherwise the down units form
+    // their rows themselves)
     StageTimer tm(h, MOE_FFN_STAGE_GEGLU, s, timing);
-    e = moe::launch_dense_geglu(args, ws, s);
+    e = moe::launch_stream_geglu(args, ws, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "geglu");
   }

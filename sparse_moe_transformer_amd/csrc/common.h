@@ -100,6 +100,14 @@ __host__ __device__ inline int dense_gateup_slices(const Shape& sh) {
   const int ks = sh.E > 0 ? kDenseKS : kDenseOnlyKS;
   return sh.H / 64 < ks ? sh.H / 64 : ks;
 }
+// Whether the streaming down units form their GeGLU rows from the gate/up
+// partials themselves (bf16 weights beside experts) instead of reading rows
+// of a GeGLU pass.  Not for FP8 weights (their down units read half the
+// bytes, so the 4 K-slices of partials they would re-read cost more than the
+// launch) nor for a dense branch alone (every down column unit would re-read
+// all K-slices of a wide branch's fp32 partials).
+inline bool stream_fused_geglu(const Shape& sh, bool fp8) { return sh.E > 0 && !fp8; }
+
 // The dense down units: K-slices of about 640 rows, at least 4 (so that a
 // D = 10240 branch spreads over a few hundred blocks; finer slices do not
 // stream faster and cost the combine a longer sum)
@@ -177,7 +185,7 @@ struct StreamArgs {
 hipError_t launch_route_dense(const StreamArgs& a, const bf16_t* wr, const float* bias, const Workspace& ws,
                               hipStream_t s);
 hipError_t launch_stream_gateup(const StreamArgs& a, const Workspace& ws, hipStream_t s);
-hipError_t launch_dense_geglu(const StreamArgs& a, const Workspace& ws, hipStream_t s);
+hipError_t launch_stream_geglu(const StreamArgs& a, const Workspace& ws, hipStream_t s);
 hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStream_t s);
 // h and y rows of the last streamed forward into caller buffers in grouped
 // (perm) order; needs ws.pos from launch_align; either pointer may be null

@@ -53,7 +53,8 @@ constexpr int kDownColsMax = kDenseDownCols > kDownCols ? kDenseDownCols : kDown
 // Beside experts, the dense gate/up units are split between the router's
 // launch and the routed gate/up launch: the router's hand-off is a latency
 // chain, so its launch takes only as many dense units as stream within it
-// (this share, in 1/8ths); the rest run first in the routed launch.
+// (this share, in 1/8ths); the rest run first in the routed launch.  FP8
+// units (half the bytes) all fit in the router's launch.
 constexpr int kDenseRouteEighths = 5;
 
 __device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
@@ -586,11 +587,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
 // down
 // ---------------------------------------------------------------------------
 
-// GeGLU of the dense rows of a config without experts: h_d = gelu_tanh(sum
-// G) * (sum U), K-slices in fixed order, bf16, 4 columns per item.  (With
-// experts the down units form their rows themselves, StageGeglu below; a
-// wide dense branch alone would have every column unit of its down re-read
-// fp32 partials of all K-slices, 16x the bytes of the bf16 rows.)
+// GeGLU pass of the streamed rows where the down units do not form them
+// (stream_fused_geglu false): h = gelu_tanh(sum G) * (sum U), K-slices in
+// fixed order, bf16.  Items [0, n4r) are the T*k routed slot rows of
+// ws.part into ws.h (slot order), items [n4r, n4r + n4d) the T dense token
+// rows into ws.h_d.  4 columns per item.
 __device__ __forceinline__ void geglu4(const Workspace& ws, const Shape& sh, bool dense, int KS, int row, int c,
                                        bf16_t* hout) {
   float4 g = make_float4(0.f, 0.f, 0.f, 0.f), up = g;
@@ -604,12 +605,20 @@ __device__ __forceinline__ void geglu4(const Workspace& ws, const Shape& sh, boo
                                               pack_bf16x2(gelu_tanh(g.z) * up.z, gelu_tanh(g.w) * up.w)};
 }
 
-__global__ __launch_bounds__(kThreads) void k_dense_geglu(Shape sh, Workspace ws, long long n4d) {
-  const int qd = sh.D / 4;
+__global__ __launch_bounds__(kThreads) void k_stream_geglu(Shape sh, Workspace ws, long long n4r, long long n4d,
+                                                           int ksr) {
+  const int qi = sh.I / 4, qd = sh.D / 4;
   const int ksd = dense_gateup_slices(sh);
-  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n4d; i += (long long)gridDim.x * kThreads) {
-    const int row = int(i / qd), c = int(i % qd) * 4;
-    geglu4(ws, sh, true, ksd, row, c, ws.h_d + (long long)row * sh.D + c);
+  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n4r + n4d;
+       i += (long long)gridDim.x * kThreads) {
+    if (i < n4r) {
+      const int row = int(i / qi), c = int(i % qi) * 4;
+      geglu4(ws, sh, false, ksr, row, c, ws.h + (long long)row * sh.I + c);
+    } else {
+      const long long j = i - n4r;
+      const int row = int(j / qd), c = int(j % qd) * 4;
+      geglu4(ws, sh, true, ksd, row, c, ws.h_d + (long long)row * sh.D + c);
+    }
   }
 }
 
@@ -725,10 +734,11 @@ __device__ void down_unit(const StreamArgs& a, const Workspace& ws, int u) {
   for (int c0 = 0; c0 < rows; c0 += kRowsChunk) {
     const int nr = min(kRowsChunk, rows - c0);
     const float* sums;
-    if (!FUSED) {  // dense rows of a config without experts: h_d from k_dense_geglu
+    if (!FUSED) {  // the rows of h / h_d from k_stream_geglu
       const bf16_t* rowp[kRowsChunk];
 #pragma unroll
-      for (int r = 0; r < kRowsChunk; ++r) rowp[r] = r < nr ? ws.h_d + (long long)(c0 + r) * K : nullptr;
+      for (int r = 0; r < kRowsChunk; ++r)
+        rowp[r] = r < nr ? (DENSE ? ws.h_d : ws.h) + (long long)(DENSE ? c0 + r : slot[c0 + r]) * K : nullptr;
       sums = W8 ? unit8_x_rows<NC>(nr, w8, H, kbeg, kend, NC, rowp, hs, red)
                 : unit_x_rows<NC>(nr, wd, H, kbeg, kend, rowp, hs, red);
     } else {
@@ -748,9 +758,8 @@ __device__ void down_unit(const StreamArgs& a, const Workspace& ws, int u) {
 }
 
 // One launch for the dense down units (blocks [0, ud)) and the routed ones.
-// FUSED (a config with experts): the units form their GeGLU rows from the
-// gate/up partials.  Otherwise (no experts, hence no routed units) the dense
-// units read h_d, which k_dense_geglu wrote.
+// FUSED (stream_fused_geglu): the units form their GeGLU rows from the
+// gate/up partials; otherwise they read the rows k_stream_geglu wrote.
 template <bool W8, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_stream_down(StreamArgs a,
                                                                                                     Workspace ws,
@@ -758,8 +767,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   const int u = blockIdx.x;
   if (u < ud)
     down_unit<true, kDenseDownCols, W8, FUSED>(a, ws, u);
-  else if (FUSED)
-    down_unit<false, kDownCols, W8, true>(a, ws, u - ud);
+  else
+    down_unit<false, kDownCols, W8, FUSED>(a, ws, u - ud);
 }
 
 // h and y rows of the last streamed forward (slot order) copied to grouped
@@ -787,7 +796,7 @@ DenseSplit dense_split(const StreamArgs& a) {
   d.ksd = sh.D > 0 ? dense_gateup_slices(sh) : 1;
   d.nc = a.fp8 ? 128 : 64;
   d.ud = sh.D > 0 ? ((sh.D + d.nc - 1) / d.nc) * 2 * d.ksd : 0;
-  d.in_route = d.ud * kDenseRouteEighths / 8;
+  d.in_route = a.fp8 ? d.ud : d.ud * kDenseRouteEighths / 8;
   return d;
 }
 }  // namespace
@@ -857,12 +866,15 @@ hipError_t launch_route_dense(const StreamArgs& a, const bf16_t* wr, const float
   return hipGetLastError();
 }
 
-hipError_t launch_dense_geglu(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
+hipError_t launch_stream_geglu(const StreamArgs& a, const Workspace& ws, hipStream_t s) {
   const Shape& sh = a.sh;
-  if (sh.T == 0 || sh.E > 0 || sh.D == 0) return hipSuccess;  // with experts the down units form h_d
-  const long long n4d = (long long)sh.T * sh.D / 4;
-  const int gblocks = int(std::min<long long>(1024, (n4d + kThreads - 1) / kThreads));
-  hipLaunchKernelGGL(k_dense_geglu, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, n4d);
+  if (sh.T == 0 || stream_fused_geglu(sh, a.fp8)) return hipSuccess;  // the down units form the rows
+  const long long n4r = sh.E > 0 ? (long long)sh.T * sh.k * sh.I / 4 : 0;
+  const long long n4d = sh.D > 0 ? (long long)sh.T * sh.D / 4 : 0;
+  const int gblocks = int(std::min<long long>(1024, (n4r + n4d + kThreads - 1) / kThreads));
+  if (gblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_stream_geglu, dim3(gblocks), dim3(kThreads), 0, s, sh, ws, n4r, n4d,
+                     a.fp8 ? kStreamKS8 : kStreamKS);
   return hipGetLastError();
 }
 
@@ -873,7 +885,7 @@ hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStrea
   const int ksd = sh.D > 0 ? dense_down_slices(sh) : 1;
   const int ud = sh.D > 0 ? (sh.H / kDenseDownCols) * ksd : 0;
   const int max_active = std::min(sh.E, sh.T * sh.k);
-  const bool fused = sh.E > 0;  // else k_dense_geglu formed h_d
+  const bool fused = stream_fused_geglu(sh, a.fp8);  // else k_stream_geglu formed h / h_d
   // longest K run of a unit: a dense K-slice or the expert width
   const int kd = ud ? (sh.D / 64 + ksd - 1) / ksd * 64 : 0;
   const size_t lds = std::max(size_t(std::max(sh.I, kd)) * kRowsChunk * 2, size_t(5) * kRowsChunk * kDownColsMax * 4);
