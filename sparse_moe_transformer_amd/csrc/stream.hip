@@ -15,17 +15,19 @@
 //   weight batch is already in flight.  Row-group partial sums are folded
 //   with shuffles, then across waves.
 //
-//   gate/up (k_stream_gateup): units are (expert or dense branch, gate or up
-//     matrix, 64 columns, one K-slice of whole 64-row groups) over the
-//     group's token rows (x gathered by token).  Each unit writes fp32
-//     partial pre-activations; k_stream_geglu then sums the slices in fixed
-//     order and writes h = gelu_tanh(G) * U (the GeGLU) in bf16.  (No
-//     in-kernel hand-off between blocks: on this multi-XCD part a
+//   gate/up (k_stream_gateup, and the dense units in the router's launch):
+//     units are (expert or dense branch, gate or up matrix, 64 columns (FP8:
+//     128), one K-slice of whole 64-row groups) over the group's token rows
+//     (x gathered by token).  Each unit writes fp32 partial pre-activations.
+//     (No in-kernel hand-off between blocks: on this multi-XCD part a
 //     device-scope release writes back the L2, which is far dearer than a
 //     launch.)
 //   down (k_stream_down): units are (expert, 128 columns) over the expert's
 //     h rows, output rows y in bf16; the dense branch's longer K is cut into
-//     K-slices whose fp32 partial outputs the combine sums.
+//     K-slices whose fp32 partial outputs the combine sums.  With bf16
+//     weights beside experts each down unit forms its rows of h = bf16(
+//     gelu_tanh(G) * U) itself from the partials (slices summed in fixed
+//     order); otherwise k_stream_geglu writes h / h_d first.
 //
 // Routed units need no grouping tables: each block derives its expert's
 // rows from topk_idx (at most 64 tokens) with a few LDS atomics.  Routed
