@@ -165,11 +165,15 @@ def test_no_dense_branch(torch):
         full_check(s, x, w, None, out, r, inter)
 
 
-def test_zero_input(torch):
-    """x = 0: every logit is 0, the set is {0..k-1} with weights 1/k, out = 0."""
-    s = MID.with_tokens(100)
+@pytest.mark.parametrize("shape", [MID.with_tokens(100), MID.with_tokens(8),
+                                   synth.FFNShape("rt256", 3, 512, 256, 16, 64, 64)])
+def test_zero_input(torch, shape):
+    """x = 0: every logit is 0, the set is {0..k-1} with weights 1/k, out = 0
+    (all experts tie: the small-T router's ranks and the large-T arg-max
+    must both fall back to the lowest ids)."""
+    s = shape
     _, w, _ = G.make_inputs(s)
-    x = np.zeros((100, s.hidden), dtype=np.uint16)
+    x = np.zeros((s.tokens, s.hidden), dtype=np.uint16)
     for variant in (STREAM, MFMA):
         out, r, _, _ = run_gpu(torch, s, x, w, None, variant)
         assert np.all(out == 0.0)
