@@ -332,7 +332,7 @@ def cpu_baseline(shape, x, w, bias, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the block shards by tokens with replicated weights; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
