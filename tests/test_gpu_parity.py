@@ -71,6 +71,7 @@ def full_check(shape, x, w, bias, out, r, inter=None, nvfp4_w=None, k=None):
         G.assert_block_close(G.to_f64(inter["h"]), ref["h"], what="h")
         G.assert_block_close(G.to_f64(inter["y"]), ref["y"], what="y")
         if shape.dense_dim:
+            G.assert_block_close(G.to_f64(inter["h_d"]), ref["h_d"], what="h_d")
             G.assert_block_close(G.to_f64(inter["y_d"]), ref["y_d"], what="y_d")
     return ref, int(near.sum())
 
