@@ -118,6 +118,18 @@ def test_ragged_tokens(torch, T, variant):
     full_check(s, x, w, bias, out, r, inter)
 
 
+def test_streaming_every_token_count(torch):
+    """Every T the streaming path takes (1..64) on one handle, each checked in
+    full: the down units' GeGLU staging sees every row-chunk remainder, and
+    the router's token groups every ragged tail."""
+    ffn = ffn_for(MID, STREAM, max_tokens=64)
+    for T in range(1, 65):
+        s = MID.with_tokens(T)
+        x, w, bias = G.make_inputs(s, seed=100 + T)
+        out, r, inter, _ = run_gpu(torch, s, x, w, bias, STREAM, ffn=ffn)
+        full_check(s, x, w, bias, out, r, inter)
+
+
 # the 26B router shape (two tokens per router group at H = 2816, E = 128)
 # with narrow experts, so the oracle stays cheap
 ROUTE_WIDE = synth.FFNShape("routewide", 0, 2816, 128, 8, 64, 64)
