@@ -109,6 +109,25 @@ def test_fp8_dense_ffn_e4b(torch, T):
     G.assert_block_close(out if tokens is None else out[tokens], ref["out"])
 
 
+def test_fp8_streaming_every_token_count(torch):
+    """FP8 streaming at every T from 1 to 64 on one handle (128-column units
+    with a ragged last unit at I = 128 + dense 192, the GeGLU pass), each
+    forward checked in full."""
+    from sparse_moe_transformer_amd import MoeFFN
+    ffn = MoeFFN.for_shape(MID, max_tokens=64, variant=STREAM)
+    w = synth.make_fp8_weights(MID.with_tokens(64), seed=5)
+    wd = G.up_fp8_weights(w)
+    for T in range(1, 65):
+        s = MID.with_tokens(T)
+        x = synth.make_x(s, seed=200 + T)
+        xd = G.up_bf16(x)
+        out = torch.empty_like(xd)
+        ffn.forward_fp8(xd, wd, out)
+        torch.cuda.synchronize()
+        r = {k: G.to_np(v) for k, v in ffn.routing(T).items()}
+        check(s, x, w, G.to_f64(out), r)
+
+
 def test_fp8_validation(torch):
     from sparse_moe_transformer_amd import MoeFFN, binding as B
     s = MID.with_tokens(16)
