@@ -92,6 +92,22 @@ def test_dense_ragged(torch, T, variant):
     G.assert_block_close(out, ref_ffn(x, w)["out"])
 
 
+def test_dense_streaming_every_token_count(torch):
+    """The dense-only streaming path at every T from 1 to 64 on one handle
+    (uneven K-slices at D = 1600), each forward checked in full."""
+    ffn = ffn_for(E4B_MID, STREAM, max_tokens=64)
+    w = synth.make_weights(E4B_MID.with_tokens(64), seed=6)
+    wd = G.up_weights(w)
+    for T in range(1, 65):
+        s = E4B_MID.with_tokens(T)
+        x = synth.make_x(s, seed=300 + T)
+        xd = G.up_bf16(x)
+        out = torch.empty_like(xd)
+        ffn.forward(xd, wd, out)
+        torch.cuda.synchronize()
+        G.assert_block_close(G.to_f64(out), ref_ffn(x, w)["out"])
+
+
 @pytest.mark.parametrize("variant", [AUTO, MFMA])
 def test_dense_e4b_decode(torch, w_e4b, variant):
     s = synth.E4B_DECODE
