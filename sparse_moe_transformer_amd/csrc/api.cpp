@@ -252,6 +252,11 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   if (T > moe::kRouteSmallT) stream = false;  // their scratch holds at most 64 tokens' rows
   const int mt = int((size_t(T) * sh.k + moe::kGemmBM - 1) / moe::kGemmBM + sh.E);
   const bool experts = sh.E > 0;  // else a dense FFN: no routing stages
+  // the small-T router's launch shape does not cover every (H, E) (wide H
+  // with E not a multiple of 8): such shapes route with the large-T kernels
+  // and run the MFMA tiles, whose routing it feeds, at any T
+  const bool small_route = experts && T <= moe::kRouteSmallT && moe::route_small_fits(sh);
+  if (experts && !small_route) stream = false;
   // a dense FFN on the MFMA path writes its output rows from the down GEMM
   const bool direct = !experts && !stream && !nm && !(h->cfg.flags & MOE_FFN_ACCUMULATE);
   {
@@ -266,7 +271,7 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
     }
     e = stream ? moe::launch_route_dense(args, wr, bias, ws, s)
         : !experts                 ? hipSuccess
-        : (T <= moe::kRouteSmallT) ? moe::launch_route_small(sh, xb, wr, bias, ws, s)
+        : small_route               ? moe::launch_route_small(sh, xb, wr, bias, ws, s)
                                    : moe::launch_route_large(sh, xb, wr, bias, ws, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "route");

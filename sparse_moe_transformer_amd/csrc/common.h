@@ -156,6 +156,9 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   return reinterpret_cast<const T*>((uint64_t(hi) << 32) | lo);
 }
 
+// whether the small-T router (and so the streaming path's fused router
+// launch) covers this shape; the large-T router covers every shape
+bool route_small_fits(const Shape& sh);
 hipError_t launch_route_small(const Shape& sh, const bf16_t* x, const bf16_t* wr, const float* bias,
                               const Workspace& ws, hipStream_t s);
 hipError_t launch_route_large(const Shape& sh, const bf16_t* x, const bf16_t* wr, const float* bias,

@@ -256,6 +256,8 @@ __global__ __launch_bounds__(kThreads) void k_align_scatter(Shape sh, Workspace 
 
 }  // namespace
 
+bool route_small_fits(const Shape& sh) { return sh.E > 0 && route_small_config(sh).ok; }
+
 hipError_t launch_route_small(const Shape& sh, const bf16_t* x, const bf16_t* wr, const float* bias,
                               const Workspace& ws, hipStream_t s) {
   if (sh.T == 0) return hipSuccess;

@@ -4,8 +4,7 @@ hidden_dim 10240, enable_moe False), through the C ABI against
 oracle.dense_ffn / oracle.dense_block.
 
 Rule: every output element within 2e-2 * (|oracle| + rms(oracle)) (bf16
-output); the full-size prefill checks a sample of rows, which the oracle
-computes one by one.
+output), at every size.
 """
 import numpy as np
 import pytest
@@ -116,13 +115,11 @@ def test_dense_e4b_decode(torch, w_e4b, variant):
     G.assert_block_close(out, ref_ffn(x, w_e4b)["out"])
 
 
-def test_dense_e4b_prefill_sampled(torch, w_e4b):
+def test_dense_e4b_prefill(torch, w_e4b):
     s = synth.E4B_PREFILL
     x = synth.make_x(s)
     out, _ = run(torch, s, x, w_e4b, AUTO)
-    tokens = np.unique(np.concatenate([[0, 1, 255, 256, s.tokens - 1],
-                                       np.random.default_rng(7).choice(s.tokens, 27, replace=False)]))
-    G.assert_block_close(out[tokens], ref_ffn(x, w_e4b, tokens=tokens)["out"])
+    G.assert_block_close(out, ref_ffn(x, w_e4b)["out"])
 
 
 @pytest.mark.parametrize("variant", [STREAM, MFMA])

@@ -151,7 +151,7 @@ def test_w4a4_saturating_scales(torch):
     check(s, x, pk, sc, out, r)
 
 
-def test_w4a4_26b_sampled(torch):
+def test_w4a4_26b(torch):
     s = synth.FFNShape("nvfp4_26b", 256, 2816, 128, 8, 704, 2112, nvfp4=True)
     x = synth.make_x(s)
     pk = synth.make_nvfp4_weights(s)
@@ -161,8 +161,7 @@ def test_w4a4_26b_sampled(torch):
                         top_k=8)
     sc = np.array([np.max(np.abs(oracle.widen_bf16(x))), np.max(np.abs(r0["h"])), np.max(np.abs(r0["h_d"]))]) / (6 * 448)
     out, r = run(torch, s, x, pk, sc)
-    tokens = np.array([0, 1, 77, 128, 254, 255])
-    print(f"w4a4 near-ties: {check(s, x, pk, sc, out, r, tokens=tokens)}")
+    print(f"w4a4 near-ties: {check(s, x, pk, sc, out, r)}")
 
 
 def test_w4a4_validation(torch):
