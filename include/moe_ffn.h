@@ -157,6 +157,26 @@ int moe_ffn_forward(moe_ffn_handle *h, int32_t T, const void *x, const void *rou
                     const void *w_down, const void *d_gate, const void *d_up,
                     const void *d_down, void *out, void *stream);
 
+/* The forward above for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no handle, no hipMalloc/hipFree, no allocating library call.
+ * Its workspace is a static device array of 64 MiB that the library holds on
+ * every GPU it runs on until the process ends (a shape and T whose workspace,
+ * moe_ffn_workspace_bytes of cfg with max_tokens = T, exceeds 64 MiB return
+ * UNSUPPORTED; at the 26B-A4B shape T <= 446 fits).  cfg (host memory) gives
+ * the shape, weight_format (must be MOE_FFN_W_BF16) and flags; T must be in
+ * [0, cfg->max_tokens]; every other argument, the validation and the result
+ * are those of moe_ffn_forward on the current device.  Each call first clears
+ * the counters the kernels need at zero.  Every call on one GPU shares that
+ * GPU's array: two calls that overlap on one GPU (two streams, or two host
+ * threads) race and give undefined results; calls on different GPUs are
+ * independent.  Nothing of the call can be read back afterwards (no routing
+ * or intermediates). */
+int moe_ffn_forward_noalloc(const moe_ffn_config *cfg, int32_t T, const void *x, const void *router_w,
+                            const float *router_bias, const void *w_gate, const void *w_up,
+                            const void *w_down, const void *d_gate, const void *d_up,
+                            const void *d_down, void *out, void *stream);
+
 /* Same block with NVFP4 weight-only expert and dense matrices (weight_format
  * must be MOE_FFN_W_NVFP4).  Activations, router and output stay bf16; each
  * weight tile is decoded to bf16 on chip (an e2m1 x e4m3 product is exact in

@@ -36,7 +36,7 @@ EXPORTS = (
     "moe_ffn_forward_block",
     "moe_ffn_get_routing",
     "moe_ffn_get_intermediates", "moe_ffn_align_only", "moe_ffn_profile_begin",
-    "moe_ffn_profile_end", "moe_ffn_last_error",
+    "moe_ffn_profile_end", "moe_ffn_forward_noalloc", "moe_ffn_last_error",
 )
 MOE_FFN_STAGE_ROUTE, MOE_FFN_STAGE_ALIGN, MOE_FFN_STAGE_GATEUP = 0, 1, 2
 MOE_FFN_STAGE_DOWN, MOE_FFN_STAGE_COMBINE, MOE_FFN_STAGE_GEGLU = 3, 4, 5
@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_destroy.argtypes = [vp]
         L.moe_ffn_set_variant.argtypes = [vp, i32]
         L.moe_ffn_forward.argtypes = [vp, i32] + [vp] * 11
+        L.moe_ffn_forward_noalloc.argtypes = [P(moe_ffn_config), i32] + [vp] * 11
         L.moe_ffn_forward_nvfp4.argtypes = [vp, i32, vp, vp, vp] + [P(moe_ffn_nvfp4_t)] * 6 + [vp, vp]
         L.moe_ffn_quant_act_nvfp4.argtypes = [ctypes.c_int64, i32, vp, vp, vp, vp]
         L.moe_ffn_forward_w4a4.argtypes = [vp, i32, vp, vp, vp] + [P(moe_ffn_nvfp4_t)] * 6 + [vp, vp, vp]
@@ -141,6 +142,13 @@ def moe_ffn_forward(h, T, x, router_w, router_bias, w_gate, w_up, w_down, d_gate
                     out, stream) -> int:
     return lib().moe_ffn_forward(h, T, x, router_w, router_bias, w_gate, w_up, w_down, d_gate,
                                  d_up, d_down, out, stream)
+
+
+def moe_ffn_forward_noalloc(cfg, T, x, router_w, router_bias, w_gate, w_up, w_down, d_gate, d_up, d_down,
+                            out, stream) -> int:
+    """cfg: a moe_ffn_config (host structure) or None."""
+    return lib().moe_ffn_forward_noalloc(ctypes.byref(cfg) if cfg is not None else None, T, x, router_w,
+                                         router_bias, w_gate, w_up, w_down, d_gate, d_up, d_down, out, stream)
 
 
 def moe_ffn_forward_nvfp4(h, T, x, router_w, router_bias, w_gate, w_up, w_down, d_gate, d_up,

@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <exception>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -450,6 +451,47 @@ moe::StreamArgs bf16_args(const moe_ffn_handle* h, int T, const void* x, const v
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// The forward that allocates nothing: its workspace is a file-scope device
+// array of fixed size (each GPU the library runs on holds its own copy until
+// the process ends).  Host code never uses the array's name as an address:
+// the device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and kept; every kernel argument and fill goes through
+// that pointer.
+// ---------------------------------------------------------------------------
+
+constexpr size_t kScratchBytes = size_t(64) << 20;  // 64 MiB per device
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device (null until set up)
+
+// Device address of this device's scratch array (looked up on the first call
+// on the device; `dev` is current).
+int scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_FFN_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_FFN_OK;
+}
+
+// clears n ints (the arrival counters) with plain stores
+__global__ void k_zero_i32(int32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+}  // namespace
+
 extern "C" {
 
 int moe_ffn_workspace_bytes(const moe_ffn_config* cfg, size_t* bytes) {
@@ -548,6 +590,59 @@ int moe_ffn_forward(moe_ffn_handle* h, int32_t T, const void* x, const void* rou
     if (!g.ok) return fail(MOE_FFN_ERR_HIP, "cannot make the handle's device current");
     const moe::StreamArgs a = bf16_args(h, T, x, w_gate, w_up, w_down, d_gate, d_up, d_down);
     return run_forward(h, T, x, router_w, router_bias, a, out, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return fail(MOE_FFN_ERR_HIP, ex.what());
+  } catch (...) {
+    return fail(MOE_FFN_ERR_HIP, "unknown exception");
+  }
+}
+
+int moe_ffn_forward_noalloc(const moe_ffn_config* cfg, int32_t T, const void* x, const void* router_w,
+                            const float* router_bias, const void* w_gate, const void* w_up, const void* w_down,
+                            const void* d_gate, const void* d_up, const void* d_down, void* out, void* stream) {
+  try {
+    if (int r = validate_config(cfg)) return r;
+    if (cfg->weight_format != MOE_FFN_W_BF16)
+      return fail(MOE_FFN_ERR_UNSUPPORTED, "moe_ffn_forward_noalloc takes bf16 weights (weight_format 0)");
+    // a handle on the stack: its profiling vectors stay empty (no allocation)
+    moe_ffn_handle hs{};
+    hs.cfg = *cfg;
+    hs.variant = MOE_FFN_VARIANT_AUTO;
+    if (int r = common_forward_checks(&hs, T, x, router_w, router_bias, out, MOE_FFN_W_BF16)) return r;
+    if (int r = bf16_weight_checks(&hs, w_gate, w_up, w_down, d_gate, d_up, d_down)) return r;
+    // the workspace of this call: the handle layout sized for T tokens
+    moe_ffn_config ct = *cfg;
+    ct.max_tokens = std::max(T, 1);
+    const Layout L = layout(ct);
+    if (L.total > kScratchBytes)
+      return fail(MOE_FFN_ERR_UNSUPPORTED, "moe_ffn_forward_noalloc: this shape and T need " +
+                                               std::to_string(L.total) + " bytes of workspace, more than the " +
+                                               std::to_string(kScratchBytes) + "-byte static scratch");
+    if (T == 0) {
+      g_err.clear();
+      return MOE_FFN_OK;
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    void* base = nullptr;
+    if (int r = scratch_on(dev, &base)) return r;
+    hs.cfg = ct;
+    hs.device = dev;
+    hs.ws_base = base;
+    hs.ws_bytes = L.total;
+    hs.ws = bind(base, L);
+    hs.max_mtiles = L.max_mtiles;
+    const char* sm = std::getenv("MOE_FFN_SYNC");
+    hs.sync_mode = sm && std::strcmp(sm, "1") == 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the array keeps the last call's contents: the router hand-off's
+    // arrival counters must start at zero (a kernel, not a memset)
+    hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(64), 0, s, hs.ws.arrive, moe::kArriveInts);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "scratch counters");
+    const moe::StreamArgs a = bf16_args(&hs, T, x, w_gate, w_up, w_down, d_gate, d_up, d_down);
+    return run_forward(&hs, T, x, router_w, router_bias, a, out, s);
   } catch (const std::exception& ex) {
     return fail(MOE_FFN_ERR_HIP, ex.what());
   } catch (...) {

@@ -134,3 +134,21 @@ def test_null_arguments(lib):
 
 def test_last_error_never_null(lib):
     assert isinstance(lib.moe_ffn_last_error(), bytes)
+
+
+def test_noalloc_validation_before_any_gpu_call(lib):
+    """The no-allocation forward validates its config, T and pointers before
+    any HIP call: NULL config, a non-bf16 format, T out of range and a
+    workspace beyond the static scratch are refused; T = 0 is a no-op."""
+    f = binding.moe_ffn_forward_noalloc
+    ptrs = [256 * (i + 1) for i in range(11)]  # never dereferenced: each call is refused or T == 0
+    assert f(None, 8, *ptrs) == binding.MOE_FFN_ERR_INVALID_ARG
+    assert f(cfg(weight_format=binding.MOE_FFN_W_NVFP4), 8, *ptrs) == binding.MOE_FFN_ERR_UNSUPPORTED
+    assert f(cfg(max_tokens=16), 17, *ptrs) == binding.MOE_FFN_ERR_INVALID_ARG
+    assert f(cfg(max_tokens=16), -1, *ptrs) == binding.MOE_FFN_ERR_INVALID_ARG
+    # 64 MiB of scratch: at the 26B shape T = 446 fits, T = 447 does not
+    assert f(cfg(max_tokens=447), 447, *ptrs) == binding.MOE_FFN_ERR_UNSUPPORTED
+    assert "static scratch" in binding.moe_ffn_last_error()
+    rc, n = binding.moe_ffn_workspace_bytes(cfg(max_tokens=446))
+    assert rc == binding.MOE_FFN_OK and n <= 64 << 20
+    assert f(cfg(max_tokens=446), 0, *ptrs) == binding.MOE_FFN_OK
