@@ -185,6 +185,16 @@ def run_workload(torch, shape, steps, warmup, copies, graph, layers=1, norms=Fal
 
         def fwd(i):
             ffn.forward_w4a4(xd, sets[i % copies], scales, out, bd)
+    elif shape.nvfp4 and layers == 0:
+        # one NVFP4 layer on its own (decode): bit-identical copies rotated
+        base = upload_nvfp4(torch, synth.make_nvfp4_weights(shape))
+        sets = [base] + [clone_fp8(base) for _ in range(copies - 1)]
+        ffn = MoeFFN.for_shape(shape)
+        out = torch.empty_like(xd)
+        layers = 1
+
+        def fwd(i):
+            ffn.forward_nvfp4(xd, sets[i % copies], out, bd)
     elif shape.nvfp4:
         sets = [upload_nvfp4(torch, synth.make_nvfp4_weights(shape, layer=l)) for l in range(copies)]
         ffn = MoeFFN.for_shape(shape, accumulate=True)
@@ -233,7 +243,7 @@ def run_workload(torch, shape, steps, warmup, copies, graph, layers=1, norms=Fal
 
     def restart():
         # the stack runs in place: restart each chain of `layers` from x
-        if shape.nvfp4 and not w4a4:
+        if shape.nvfp4 and not w4a4 and layers > 1:
             xd.copy_(x0)
 
     for i in range(warmup):
@@ -434,6 +444,20 @@ def main():
             "layer_weight_bytes": wbytes, "hbm_frac": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "mfma_frac": step_flops(st) / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
             "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rn["stage_avg_us"]])),
+        }
+    if not args.no_nvfp4:
+        # one NVFP4 layer at decode (T = 8): weights streamed into registers
+        sd = synth.NVFP4_STACK.with_tokens(8)
+        rd = run_workload(torch, sd, args.steps, args.warmup, args.copies, args.graph, layers=0)
+        H, I, D, E = sd.hidden, sd.expert_dim, sd.dense_dim, sd.experts
+        per_w = 0.5 + 1.0 / 16  # packed bytes per weight: the code nibble and its share of a group scale
+        nb = int(rd["n_act"] * 3 * H * I * per_w + 3 * H * D * per_w + H * E * 2 + 2 * sd.tokens * H * 2)
+        line["nvfp4_decode"] = {
+            "workload": "one NVFP4 weight-only layer at decode, T=8 (packed weights rotated over bit-identical copies)",
+            "tokens": sd.tokens, "value": sd.tokens / (rd["ms_per_step"] * 1e-3), "unit": "tokens/s",
+            "ms_per_step": rd["ms_per_step"], "steps": args.steps, "active_experts": rd["n_act"],
+            "algorithmic_bytes": nb, "hbm_frac": nb / (rd["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rd["stage_avg_us"]])),
         }
     if not args.no_dense:
         # the dense GeGLU FFN of the E4B model (2560 -> 10240 -> 2560, no experts)

@@ -30,6 +30,7 @@ struct moe_ffn_handle {
   moe::Workspace ws;
   int variant;
   int max_mtiles;
+  int max_mtiles128;
   int last_T;
   // the last forward ran the streaming path: its grouping tables (counts,
   // offsets, perm, pos) were never built and its h / h_d / y rows are not
@@ -99,9 +100,10 @@ int validate_config(const moe_ffn_config* c) {
 
 // Workspace layout: every buffer 256-byte aligned.
 struct Layout {
-  size_t off[21];
+  size_t off[22];
   size_t total;
   int max_mtiles;
+  int max_mtiles128;
 };
 
 Layout layout(const moe_ffn_config& c) {
@@ -110,7 +112,8 @@ Layout layout(const moe_ffn_config& c) {
   const size_t nb = (T + 63) / 64;
   Layout L{};
   L.max_mtiles = int((T * k + moe::kGemmBM - 1) / moe::kGemmBM + E);
-  const size_t sizes[21] = {
+  L.max_mtiles128 = int((T * k + moe::kFp4BM - 1) / moe::kFp4BM + E);
+  const size_t sizes[22] = {
       size_t(moe::kRouterSlices) * T * E * 4,     // logits (K-slices)
       size_t(moe::kRouteSlices) * 64 * E * 4,     // route_part (K-slices, T <= 64)
       T * k * 4,                                  // topk_idx
@@ -134,9 +137,10 @@ Layout layout(const moe_ffn_config& c) {
           moe::kRouteSmallT * H * 4,              // streaming dense down partials
       size_t(moe::kArriveInts) * 4,               // arrival counters (zero between forwards)
       T * H * 2,                                  // xn: pre-normed input (sandwich-norm forwards)
+      size_t(L.max_mtiles128) * 16,               // mtiles128
   };
   size_t o = 0;
-  for (int i = 0; i < 21; ++i) {
+  for (int i = 0; i < 22; ++i) {
     L.off[i] = o;
     o += (sizes[i] + 255) & ~size_t(255);
   }
@@ -168,6 +172,7 @@ moe::Workspace bind(void* base, const Layout& L) {
   w.ydp = reinterpret_cast<float*>(b + L.off[18]);
   w.arrive = reinterpret_cast<int32_t*>(b + L.off[19]);
   w.xn = reinterpret_cast<moe::bf16_t*>(b + L.off[20]);
+  w.mtiles128 = reinterpret_cast<int32_t*>(b + L.off[21]);
   return w;
 }
 
@@ -252,6 +257,7 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   if (args.nvfp4) stream = false;             // the streaming kernels read bf16 [K, N] weights only
   if (T > moe::kRouteSmallT) stream = false;  // their scratch holds at most 64 tokens' rows
   const int mt = int((size_t(T) * sh.k + moe::kGemmBM - 1) / moe::kGemmBM + sh.E);
+  const int mt128 = int((size_t(T) * sh.k + moe::kFp4BM - 1) / moe::kFp4BM + sh.E);
   const bool experts = sh.E > 0;  // else a dense FFN: no routing stages
   // the small-T router's launch shape does not cover every (H, E) (wide H
   // with E not a multiple of 8): such shapes route with the large-T kernels
@@ -294,7 +300,9 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
       if (e != hipSuccess) return hip_fail(e, "activation quantiser");
       args.x = ws.xn;
     }
-    e = stream ? moe::launch_stream_gateup(args, ws, s) : moe::launch_gemm_gateup(args, ws, mt, s);
+    e = stream        ? moe::launch_stream_gateup(args, ws, s)
+        : args.nvfp4 ? moe::launch_fp4_gateup(args, ws, mt128, s)
+                     : moe::launch_gemm_gateup(args, ws, mt, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "gate/up");
   }
@@ -314,8 +322,10 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
       if (e == hipSuccess && sh.D > 0) e = moe::launch_quant_act(ws.h_d, ws.h_d, T, sh.D, sh.D, args.in_scale + 2, s);
       if (e != hipSuccess) return hip_fail(e, "activation quantiser");
     }
-    e = stream ? moe::launch_stream_down(args, ws, s)
-               : moe::launch_gemm_down(args, ws, mt, s, direct ? static_cast<moe::bf16_t*>(out) : nullptr);
+    moe::bf16_t* yd_direct = direct ? static_cast<moe::bf16_t*>(out) : nullptr;
+    e = stream        ? moe::launch_stream_down(args, ws, s)
+        : args.nvfp4 ? moe::launch_fp4_down(args, ws, mt128, s, yd_direct)
+                     : moe::launch_gemm_down(args, ws, mt, s, yd_direct);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "down");
   }
@@ -385,7 +395,7 @@ int check_fp4(const moe_ffn_nvfp4_t* m, bool required, const char* name) {
   }
   if (!m || !m->q || !m->scale || !m->tensor_scale)
     return fail(MOE_FFN_ERR_INVALID_ARG, std::string(name) + ": q, scale and tensor_scale must not be NULL");
-  if (!aligned16(m->q) || (reinterpret_cast<uintptr_t>(m->scale) & 1u) ||
+  if (!aligned16(m->q) || (reinterpret_cast<uintptr_t>(m->scale) & 3u) ||
       (reinterpret_cast<uintptr_t>(m->tensor_scale) & 3u))
     return fail(MOE_FFN_ERR_INVALID_ARG, std::string(name) + ": misaligned pointer");
   return MOE_FFN_OK;
@@ -537,6 +547,7 @@ int moe_ffn_create(const moe_ffn_config* cfg, moe_ffn_handle** out_handle) {
     h->ws = bind(base, L);
     h->variant = MOE_FFN_VARIANT_AUTO;
     h->max_mtiles = L.max_mtiles;
+    h->max_mtiles128 = L.max_mtiles128;
     h->last_T = 0;
     const char* sm = std::getenv("MOE_FFN_SYNC");
     h->sync_mode = sm && std::strcmp(sm, "1") == 0;
@@ -633,6 +644,7 @@ int moe_ffn_forward_noalloc(const moe_ffn_config* cfg, int32_t T, const void* x,
     hs.ws_bytes = L.total;
     hs.ws = bind(base, L);
     hs.max_mtiles = L.max_mtiles;
+    hs.max_mtiles128 = L.max_mtiles128;
     const char* sm = std::getenv("MOE_FFN_SYNC");
     hs.sync_mode = sm && std::strcmp(sm, "1") == 0;
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -61,8 +61,9 @@ struct Workspace {
   int32_t* perm;        // [Tmax*k]
   int32_t* pos;         // [Tmax*k]
   int32_t* mtiles;      // [max_mtiles, 4] (expert, row0, rows, 0) for MFMA tiles
+  int32_t* mtiles128;   // [max_mtiles128, 4] the same with tiles of at most 128 rows (NVFP4 GEMMs)
   int32_t* active;      // [E, 4] (expert, row0, rows, 0) per expert with rows
-  int32_t* meta;        // [512]: 0 = #mtiles, 1 = #active experts
+  int32_t* meta;        // [512]: 0 = #mtiles, 1 = #active experts, 2 = #mtiles128
   bf16_t* h;            // [Tmax*k, I] perm order (MFMA path) or slot order (streaming path)
   bf16_t* h_d;          // [Tmax, D]
   bf16_t* y;            // [Tmax*k, H] perm order (MFMA path) or slot order (streaming path)
@@ -79,6 +80,8 @@ constexpr int kRouterSlices = 16;  // most K-slices of the large-T router logits
 constexpr int kRouteSlices = 32;   // K-slices of the small-T router logits
 constexpr int kRouteSmallT = 64;   // largest T of the one-block-per-token router and the streaming path
 constexpr int kGemmBM = 256;       // MFMA tile rows (tokens)
+constexpr int kFp4BM = 128;        // row tiles of the NVFP4 weight-streaming GEMMs
+constexpr int kFp4SmallT = 32;     // ... up to this T every expert's rows are one 32-row tile
 constexpr int kStreamKS = 2;       // K-slices of the streaming routed gate/up units (bf16)
 constexpr int kStreamKS8 = 4;      // ... with FP8 weights (units twice as wide, so twice the slices)
 constexpr int kStreamKSMax = kStreamKS8 > kStreamKS ? kStreamKS8 : kStreamKS;
@@ -199,6 +202,13 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
 // yd_out: where the dense rows go (null: ws.y_d)
 hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mtiles, hipStream_t s,
                             bf16_t* yd_out = nullptr);
+
+// NVFP4 weights streamed into registers (fp4mm.hip), any T: gate/up with the
+// GeGLU (routed rows and the dense branch) and down.  max_tiles128: the
+// capacity of ws.mtiles128.
+hipError_t launch_fp4_gateup(const StreamArgs& a, const Workspace& ws, int max_tiles128, hipStream_t s);
+hipError_t launch_fp4_down(const StreamArgs& a, const Workspace& ws, int max_tiles128, hipStream_t s,
+                           bf16_t* yd_out = nullptr);
 
 // yd_slices: 0 = dense output in ws.y_d (bf16); n > 0 = n fp32 slices in
 // ws.ydp, summed in order (and stored to ws.y_d as bf16).  slot_rows: the

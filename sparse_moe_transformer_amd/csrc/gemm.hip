@@ -17,13 +17,14 @@
 // 128 up columns at the same output positions (a wave owns 32 of each), so
 // the GeGLU epilogue pairs them in registers.
 //
-// Pipeline: K advances in stages of 32; four LDS stages (32 KB each) are in
-// flight.  Operand tiles go from global memory straight to LDS (buffer loads
-// with the lds flag, 16 bytes per lane, no registers), issued three stages
-// ahead, so a CU keeps ~96 KB of loads in flight without spending VGPRs on
-// them; each wave waits for its own copies of the stage about to be used,
-// then the block meets at a barrier.  A wave reads a whole stage's
-// fragments from LDS while the MFMAs of the previous stage run.
+// Pipeline: K advances in stages of 32; kStages LDS stages (32 KB each) are
+// in flight.  Operand tiles go from global memory straight to LDS (buffer
+// loads with the lds flag, 16 bytes per lane, no registers), issued
+// kStages - 1 stages ahead, without spending VGPRs on them; each wave waits
+// for its own copies of the stage about to be used, then the block meets at
+// a barrier.  Registers hold one 16-k sub-step of fragments ahead: a wave
+// reads the next sub-step's fragments from LDS while the MFMAs of the
+// current one run.
 //
 // LDS layouts (16-byte chunks XOR-swizzled so that every fragment read and
 // every copy touches the bank groups evenly):
@@ -34,14 +35,11 @@
 //      consecutive k of one column per lane) is read with the gfx950
 //      transposing LDS read: in a 16-lane group, lane i names row k0 + i / 4,
 //      columns 4 (i % 4) .. + 3, and receives column i of rows k0 .. k0 + 3.
-//   B  NVFP4 weights are [N, K/2] (k contiguous): two threads per column
-//      decode its 32 codes of a stage to bf16 (an e2m1 x e4m3 product is
-//      exact in bf16) into an A-style [256 n][32 k] tile; the fp32 tensor
-//      scale is applied in the epilogue.
-//   B  FP8 weights are [K, N] e4m3fn codes: a thread loads 16 codes of one
-//      k row, converts them to bf16 (exact: e4m3 has 3 mantissa bits) and
-//      writes them in the bf16 layout above, so the transposing reads are
-//      shared; the fp32 per-matrix scale is applied in the epilogue.
+//   B  FP8 weights are [K, N] e4m3fn codes: they are copied to LDS like A
+//      and converted there to bf16 (exact: e4m3 has 3 mantissa bits) in the
+//      bf16 layout above, so the transposing reads are shared; the fp32
+//      per-matrix scale is applied in the epilogue.
+// (NVFP4 weights, stored out-major, stream into registers instead: fp4mm.hip.)
 // After the K loop the same LDS stages the bf16 output tile, which leaves
 // the block in 16-byte row stores.
 //
@@ -67,7 +65,7 @@ constexpr int kOpBytes = 256 * BK * 2;     // one operand tile of a stage: 16 KB
 constexpr int kStageBytes = 2 * kOpBytes;  // A, then B
 
 enum { MODE_PLAIN_BF16 = 0, MODE_PLAIN_F32 = 1, MODE_GATEUP = 2 };
-enum { W_BF16 = 0, W_FP4 = 1, W_FP8 = 2 };
+enum { W_BF16 = 0, W_FP8 = 2 };
 
 struct Seg {
   const bf16_t* A;
@@ -77,7 +75,6 @@ struct Seg {
   const bf16_t* B1;       // up (gate/up mode)
   long long b_gstride;    // elements between groups
   int ldb;
-  Fp4Mat F0, F1;          // NVFP4 [G][N][K/2], [G][N][K/16], [G]
   Fp8Mat Q0, Q1;          // FP8 [G][K][ldb] e4m3fn codes (group stride b_gstride), [G] scales
   const float* in_scale;  // NVFP4 activations: the A operand's global scale (device), or null
   int K;
@@ -189,7 +186,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     u = units0 + j;
   }
   const bool second = u >= units0;
-  const Seg& S = second ? s1 : s0;
+  const Seg S = second ? s1 : s0;
   int uu = second ? u - units0 : u;
   const int ks = uu % S.ksplit;
   uu /= S.ksplit;
@@ -214,8 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   // kDepth stages ahead), then two bf16 B tiles decoded from the raw codes
   // (one is written while the other is read).  After the K loop the same
   // bytes stage the output tile.
-  constexpr int kRaw = (WF == W_FP8) ? 8192 : (WF == W_FP4) ? 5120 : 0;
-  constexpr int kDepth = (WF == W_FP8) ? 5 : (WF == W_FP4) ? 6 : kStages;
+  constexpr int kRaw = (WF == W_FP8) ? 8192 : 0;
+  constexpr int kDepth = (WF == W_FP8) ? 5 : kStages;
   constexpr int kStageStride = (WF == W_BF16) ? kStageBytes : kOpBytes + kRaw;  // one ring slot
   constexpr int kBArea = kDepth * kStageStride;                               // FP: the two B tiles
   constexpr int kStageArea = kBArea + ((WF == W_BF16) ? 0 : 2 * kOpBytes);
@@ -267,30 +264,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   // that are never stored.
   i32x4_t rrsrc = rsrc4(S.A);
   int roff = kOutOfRange;
-  const int fcol = tid >> 1, fkh = tid & 1;  // NVFP4 decode: B-tile column tid / 2, k half tid % 2
   if (WF == W_FP8) {
     const int h = tid >> 8, t2 = tid & 255, k = t2 >> 3, lc = (t2 & 7) * 16;
-    const Fp8Mat* Q = &S.Q0;
-    int col = n0 + 128 * h + lc;
-    if (MODE == MODE_GATEUP) {
-      Q = h ? &S.Q1 : &S.Q0;
-      col = n0 + lc;
-    }
-    rrsrc = rsrc4(Q->q + grp * S.b_gstride);
+    const uint8_t* q = (MODE == MODE_GATEUP && h) ? S.Q1.q : S.Q0.q;
+    const int col = (MODE == MODE_GATEUP) ? n0 + lc : n0 + 128 * h + lc;
+    rrsrc = rsrc4(q + grp * S.b_gstride);
     roff = col < N ? int(uint32_t(k) * uint32_t(S.ldb) + uint32_t(col)) : kOutOfRange;
-  } else if (WF == W_FP4) {
-    const bool scl = tid >= 256;
-    const int c = tid & 255;
-    const Fp4Mat* F = &S.F0;
-    int ncol = n0 + c;
-    if (MODE == MODE_GATEUP && c >= 128) {
-      F = &S.F1;
-      ncol = n0 + c - 128;
-    }
-    const long long rowbytes = scl ? K / 16 : K / 2;
-    const uint8_t* base = (scl ? F->scale : F->q) + (long long)grp * S.N * rowbytes;
-    rrsrc = rsrc4(base);
-    roff = ncol < N ? int(uint32_t(ncol) * uint32_t(rowbytes)) : kOutOfRange;
   }
   if (WF == W_BF16) {
     const bf16_t* Bm = S.B0;
@@ -335,11 +314,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     const uint32_t rb = lds_base + uint32_t((st % kDepth) * kStageStride + kOpBytes);
     if (WF == W_FP8) {
       copy_b128_to_lds(rrsrc, rb + wave * 1024, roff, int(uint32_t(kidx * BK) * uint32_t(S.ldb)));
-    } else if (WF == W_FP4) {
-      if (wave < 4)
-        copy_b128_to_lds(rrsrc, rb + wave * 1024, roff, kidx * (BK / 2));
-      else
-        copy_b32_to_lds(rrsrc, rb + 4096 + (wave - 4) * 256, roff, 4 * (kidx >> 1));
     }
   };
   // raw codes of stage st (landed) -> the stage's bf16 B tile
@@ -361,30 +335,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
 #pragma unroll
       for (int c = 0; c < 2; ++c)
         *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(row + (((c0 + c) ^ fb(k)) << 4)) = w[c];
-    } else if (WF == W_FP4) {
-      const int kidx = kt0 + min(st, nk - 1);
-      const u32x2_t q2 =
-          *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(sb + kOpBytes + fcol * 16 + fkh * 8);
-      const uint32_t sc = sb[kOpBytes + 4096 + fcol * 4 + 2 * (kidx & 1) + fkh];
-      lds_u8* bs = bt;
-      const float sv = e4m3_f32(sc);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint32_t q = q2[c];  // k = 16 fkh + 8c .. + 7, low nibble first
-        // byte p: codes k = 8c+2p (low nibble), 8c+2p+1, decoded exactly by
-        // the gfx950 e2m1 pair conversion (unit scale); e2m1 x e4m3 is exact
-        // in bf16, so the top 16 bits of each product are kept
-        const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
-        const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
-        const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
-        const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
-        const u32x4_t w = {perm_hi16(__float_as_uint(v0.x * sv), __float_as_uint(v0.y * sv)),
-                           perm_hi16(__float_as_uint(v1.x * sv), __float_as_uint(v1.y * sv)),
-                           perm_hi16(__float_as_uint(v2.x * sv), __float_as_uint(v2.y * sv)),
-                           perm_hi16(__float_as_uint(v3.x * sv), __float_as_uint(v3.y * sv))};
-        const int chunk = 2 * fkh + c;
-        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(bs + fcol * 64 + ((chunk ^ fa(fcol)) << 4)) = w;
-      }
     }
   };
 
@@ -403,23 +353,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   // columns +16 (g % 2), k rows +8 (g / 2); lane i of the group names row
   // i / 4, columns 4 (i % 4) .. + 3.  The sub-step and the second 4-row read
   // are immediate offsets.
-  int bfr[2][2];
+  int bfr[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int gcol = (MODE == MODE_GATEUP) ? 128 * j + wn * 32 : wn * 64 + 32 * j;  // B-tile column 0..255
-    if (WF != W_FP4) {
-      const int h = gcol >> 7, lc = gcol & 127;
-      const int g = lane >> 4, i16 = lane & 15, qq = i16 & 3, mr = i16 >> 2;
-      const int colb = lc + 16 * (g & 1);
-      const int krow = 8 * (g >> 1) + mr;  // fb(krow + 16 s + 4 r) == fb(mr)
-      bfr[j][0] = h * (kOpBytes / 2) + krow * 256 + ((((colb >> 3) + (qq >> 1)) ^ fb(mr)) << 4) +
-                  (qq & 1) * 8;
-      bfr[j][1] = 0;
-    } else {
-      const int n = gcol + (lane & 31);
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) bfr[j][sb] = n * 64 + (((2 * sb + hl) ^ fa(n)) << 4);
-    }
+    const int h = gcol >> 7, lc = gcol & 127;
+    const int g = lane >> 4, i16 = lane & 15, qq = i16 & 3, mr = i16 >> 2;
+    const int colb = lc + 16 * (g & 1);
+    const int krow = 8 * (g >> 1) + mr;  // fb(krow + 16 s + 4 r) == fb(mr)
+    bfr[j] = h * (kOpBytes / 2) + krow * 256 + ((((colb >> 3) + (qq >> 1)) ^ fb(mr)) << 4) + (qq & 1) * 8;
   }
 
   // Row blocks of this wave inside the tile's rows (a prefix of the 4), and
@@ -434,10 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   ni = __builtin_amdgcn_readfirstlane(ni);
 
   float ts0 = 1.f, ts1 = 1.f;
-  if (WF == W_FP4) {
-    ts0 = S.F0.tscale[grp];
-    if (MODE == MODE_GATEUP) ts1 = S.F1.tscale[grp];
-  } else if (WF == W_FP8) {
+  if (WF == W_FP8) {
     ts0 = S.Q0.tscale[grp];
     if (MODE == MODE_GATEUP) ts1 = S.Q1.tscale[grp];
   }
@@ -457,42 +396,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Fragments of one stage (2 sub-steps of 16 k) for this wave's blocks.
+    // Fragments of one 16-k sub-step of a stage for this wave's blocks.
     struct Frags {
-      bf16x8_t a[2][4], b[2][2];
+      bf16x8_t a[4], b[2];
     };
-    // abase: the stage's A tile; bbase: its B tile
-    auto read_frags = [&](const lds_u8* abase, const lds_u8* bbase, Frags& f) {
+    // abase: the stage's A tile; bbase: its B tile; sb: sub-step 0 or 1
+    auto read_sub = [&](const lds_u8* abase, const lds_u8* bbase, int sb, Frags& f) {
       if (NI == 0) return;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
+      for (int i = 0; i < NI; ++i)
+        f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(abase + afr[i][sb]);
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-          f.a[sb][i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(abase + afr[i][sb]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (WF != W_FP4) {
-            const lds_u8* p = bbase + bfr[j][0] + sb * 16 * 256;
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(p));
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(p + 4 * 256));
-            const s16x4_t v[2] = {lo, hi};
-            f.b[sb][j] = __builtin_bit_cast(bf16x8_t, v);
-          } else {
-            f.b[sb][j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(bbase + bfr[j][sb]);
-          }
-        }
+      for (int j = 0; j < 2; ++j) {
+        const lds_u8* p = bbase + bfr[j] + sb * 16 * 256;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+        const s16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p + 4 * 256));
+        const s16x4_t v[2] = {lo, hi};
+        f.b[j] = __builtin_bit_cast(bf16x8_t, v);
       }
     };
     auto mfmas = [&](const Frags& f) {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[sb][i], f.b[sb][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     };
 
     // Memory instructions per stage per lane: bf16 4 copies (A 2 + B 2);
@@ -506,25 +435,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       if (WF != W_BF16) issue_raw(st);
       issue(st);
     };
-    // The MFMAs of stage kt and the fragment reads of stage kt + 1 ride one
-    // step; a stage's LDS buffer is refilled once every wave has read it.
-    auto mma_step = [&](int kt, const Frags& cur, Frags& nxt) {
-      read_frags(abase_of(kt + 1), bbase_of(kt + 1), nxt);
-      // keep the reads ahead of the MFMAs (the scheduler would otherwise sink
-      // them below and serialise LDS latency with the matrix work)
+    // the fragment reads ride ahead of the MFMAs they do not feed: keep them
+    // above (the scheduler would otherwise sink them below and serialise LDS
+    // latency with the matrix work); while this wave feeds the matrix unit it
+    // takes issue priority over the SIMD's other wave, which is then reading
+    // fragments or copying
+    auto mma = [&](const Frags& f) {
       __builtin_amdgcn_sched_barrier(0);
-      // while this wave feeds the matrix unit it takes issue priority over
-      // the SIMD's other wave, which is then reading fragments or copying
       __builtin_amdgcn_s_setprio(1);
-      mfmas(cur);
+      mfmas(f);
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
     };
-    Frags fr[2];
+    Frags f0, f1;  // sub-step 0 and sub-step 1 of a stage
 #pragma unroll
     for (int st = 0; st < kDepth; ++st) stage_in(st);
-    // step kt: MFMAs of stage kt from `cur`, fragments of stage kt + 1 into `nxt`
-    auto step = [&](int kt, const Frags& cur, Frags& nxt) {
+    // Step kt: f0 holds stage kt's first sub-step.  Its second is read while
+    // the first's MFMAs run; then the block meets (every wave has read all of
+    // stage kt, so its LDS slot is refilled with stage kt + kDepth) and the
+    // first sub-step of stage kt + 1 is read while the second's MFMAs run.
+    // Registers hold one sub-step ahead, not a stage.
+    auto step = [&](int kt) {
+      read_sub(abase_of(kt), bbase_of(kt), 1, f1);
+      mma(f0);
       if (WF == W_BF16) {
         // bf16: copies run kDepth stages ahead
         wait_counts<(kDepth - 2) * kPerStage, 0>();  // stage kt + 1 landed; stage kt's fragments read
@@ -538,7 +471,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
         decode(kt + 2);
         stage_in(kt + kDepth);
       }
-      mma_step(kt, cur, nxt);
+      read_sub(abase_of(kt + 1), bbase_of(kt + 1), 0, f0);
+      mma(f1);
     };
     if (WF == W_BF16) {
       wait_counts<(kDepth - 1) * kPerStage, 0>();  // stage 0 landed (this wave's copies)
@@ -553,13 +487,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       wait_counts<(kDepth - 2) * kPerStage, 0>();  // decode of 1 written (no new copies)
       block_barrier();                             // every wave's decode of stage 0 is in LDS
     }
-    read_frags(abase_of(0), bbase_of(0), fr[0]);
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, fr[0], fr[1]);
-      step(kt + 1, fr[1], fr[0]);
-    }
-    if (kt < nk) step(kt, fr[0], fr[1]);
+    read_sub(abase_of(0), bbase_of(0), 0, f0);
+    for (int kt = 0; kt < nk; ++kt) step(kt);
     wait_counts<0, 0>();  // no copy may still be landing when LDS is reused
 
     // ---- epilogue: lane holds column (lane & 31); rows 8(r/4) + 4(lane/32) + r%4
@@ -680,8 +609,6 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
     d.B0 = a.dg;
     d.B1 = a.du;
     d.ldb = sh.D;
-    d.F0 = a.fdg;
-    d.F1 = a.fdu;
     d.Q0 = a.qdg;
     d.Q1 = a.qdu;
     d.in_scale = a.in_scale;
@@ -700,8 +627,6 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
   e.B1 = a.wu;
   e.b_gstride = (long long)sh.H * sh.I;
   e.ldb = sh.I;
-  e.F0 = a.fg;
-  e.F1 = a.fu;
   e.Q0 = a.qg;
   e.Q1 = a.qu;
   e.in_scale = a.in_scale;
@@ -714,7 +639,6 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
   e.n_mtiles = ws.meta;
   e.max_mtiles = sh.E > 0 ? max_mtiles : 0;
   const int ud = sh.D > 0 ? host_units(d) : 0;
-  if (a.nvfp4) return launch<MODE_GATEUP, W_FP4>(d, e, ud, grouped_units(e), s);
   if (a.fp8) return launch<MODE_GATEUP, W_FP8>(d, e, ud, grouped_units(e), s);
   return launch<MODE_GATEUP, W_BF16>(d, e, ud, grouped_units(e), s);
 }
@@ -728,7 +652,6 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
     d.lda = sh.D;
     d.B0 = a.dd;
     d.ldb = sh.H;
-    d.F0 = a.fdd;
     d.Q0 = a.qdd;
     d.in_scale = a.in_scale ? a.in_scale + 2 : nullptr;
     d.K = sh.D;
@@ -743,7 +666,6 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
   e.B0 = a.wd;
   e.b_gstride = (long long)sh.I * sh.H;
   e.ldb = sh.H;
-  e.F0 = a.fd;
   e.Q0 = a.qd;
   e.in_scale = a.in_scale ? a.in_scale + 1 : nullptr;
   e.K = sh.I;
@@ -755,7 +677,6 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
   e.n_mtiles = ws.meta;
   e.max_mtiles = sh.E > 0 ? max_mtiles : 0;
   const int ud = sh.D > 0 ? host_units(d) : 0;
-  if (a.nvfp4) return launch<MODE_PLAIN_BF16, W_FP4>(d, e, ud, grouped_units(e), s);
   if (a.fp8) return launch<MODE_PLAIN_BF16, W_FP8>(d, e, ud, grouped_units(e), s);
   return launch<MODE_PLAIN_BF16, W_BF16>(d, e, ud, grouped_units(e), s);
 }

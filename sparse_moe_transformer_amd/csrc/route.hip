@@ -63,54 +63,59 @@ __device__ int block_exclusive_scan(int v, int* scratch /* [BLOCK/kWave + 1] */,
   return excl;
 }
 
-// Block-wide exclusive scan of three ints per thread in one pass.
+// Block-wide exclusive scan of four ints per thread in one pass.
 template <int BLOCK>
-__device__ int3 block_exclusive_scan3(int3 v, int3* scratch /* [BLOCK/kWave + 1] */, int3& total) {
+__device__ int4 block_exclusive_scan4(int4 v, int4* scratch /* [BLOCK/kWave + 1] */, int4& total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
-  int3 incl = v;
+  int4 incl = v;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
     const int ox = __shfl_up(incl.x, off, kWave);
     const int oy = __shfl_up(incl.y, off, kWave);
     const int oz = __shfl_up(incl.z, off, kWave);
+    const int ow = __shfl_up(incl.w, off, kWave);
     if (lane >= off) {
       incl.x += ox;
       incl.y += oy;
       incl.z += oz;
+      incl.w += ow;
     }
   }
   if (lane == kWave - 1) scratch[wid] = incl;
   __syncthreads();
   if (threadIdx.x == 0) {
-    int3 run = make_int3(0, 0, 0);
+    int4 run = make_int4(0, 0, 0, 0);
     for (int w = 0; w < BLOCK / kWave; ++w) {
-      const int3 c = scratch[w];
+      const int4 c = scratch[w];
       scratch[w] = run;
       run.x += c.x;
       run.y += c.y;
       run.z += c.z;
+      run.w += c.w;
     }
     scratch[BLOCK / kWave] = run;
   }
   __syncthreads();
-  const int3 base = scratch[wid];
+  const int4 base = scratch[wid];
   total = scratch[BLOCK / kWave];
   __syncthreads();
-  return make_int3(base.x + incl.x - v.x, base.y + incl.y - v.y, base.z + incl.z - v.z);
+  return make_int4(base.x + incl.x - v.x, base.y + incl.y - v.y, base.z + incl.z - v.z, base.w + incl.w - v.w);
 }
 
 // Given counts[e] (one per thread e < E), write counts, offsets, the MFMA
-// tile list and the active-expert list; returns the thread's offset.  Called
-// by one whole block of BLOCK >= E threads.
+// tile lists (tiles of kGemmBM rows and of kFp4BM rows) and the
+// active-expert list; returns the thread's offset.  Called by one whole
+// block of BLOCK >= E threads.
 template <int BLOCK>
 __device__ int build_offsets_and_tiles(const int cnt_e, int E, const Workspace& ws, int* /*unused*/) {
-  __shared__ int3 scratch3[BLOCK / kWave + 1];
+  __shared__ int4 scratch4[BLOCK / kWave + 1];
   const int e = threadIdx.x;
   const int c = (e < E) ? cnt_e : 0;
   const int nm = (c + kGemmBM - 1) / kGemmBM;
-  int3 total;
-  const int3 ex = block_exclusive_scan3<BLOCK>(make_int3(c, nm, c > 0 ? 1 : 0), scratch3, total);
+  const int nm2 = (c + kFp4BM - 1) / kFp4BM;
+  int4 total;
+  const int4 ex = block_exclusive_scan4<BLOCK>(make_int4(c, nm, c > 0 ? 1 : 0, nm2), scratch4, total);
   const int off = ex.x;
   if (e < E) {
     ws.counts[e] = c;
@@ -120,12 +125,20 @@ __device__ int build_offsets_and_tiles(const int cnt_e, int E, const Workspace& 
     ws.offsets[E] = total.x;
     ws.meta[0] = total.y;
     ws.meta[1] = total.z;
+    ws.meta[2] = total.w;
   }
   for (int m = 0; m < nm; ++m) {
     int32_t* t = ws.mtiles + 4 * (ex.y + m);
     t[0] = e;
     t[1] = off + m * kGemmBM;
     t[2] = min(kGemmBM, c - m * kGemmBM);
+    t[3] = 0;
+  }
+  for (int m = 0; m < nm2; ++m) {
+    int32_t* t = ws.mtiles128 + 4 * (ex.w + m);
+    t[0] = e;
+    t[1] = off + m * kFp4BM;
+    t[2] = min(kFp4BM, c - m * kFp4BM);
     t[3] = 0;
   }
   if (c > 0) {

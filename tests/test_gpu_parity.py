@@ -349,6 +349,34 @@ def test_nvfp4_block(torch, T):
     full_check(s, x, w, None, out, r, inter, nvfp4_w=pk)
 
 
+def test_nvfp4_every_token_count(torch):
+    """NVFP4 weights streamed into registers at every T from 1 to 64 on one
+    handle, each forward checked in full: T <= 32 runs one 32-row tile per
+    expert with 2-wave column blocks, larger T the 128-row tiles."""
+    s64 = synth.FFNShape("mid_fp4", 64, 512, 32, 4, 128, 192, nvfp4=True)
+    _, w, pk = nvfp4_inputs(s64, seed=9)
+    from sparse_moe_transformer_amd import MoeFFN
+    ffn = MoeFFN.for_shape(s64, max_tokens=64)
+    wd = G.up_nvfp4_weights(pk)
+    for T in range(1, 65):
+        s = s64.with_tokens(T)
+        x = synth.make_x(s, seed=500 + T)
+        xd = G.up_bf16(x)
+        out = torch.empty_like(xd)
+        ffn.forward_nvfp4(xd, wd, out)
+        torch.cuda.synchronize()
+        r = {k: G.to_np(v) for k, v in ffn.routing(T).items()}
+        full_check(s, x, w, None, G.to_f64(out), r, ffn.intermediates(T), nvfp4_w=pk)
+
+
+def test_nvfp4_decode_26b(torch):
+    s = synth.NVFP4_STACK.with_tokens(8)
+    x = synth.make_x(s)
+    pk = synth.make_nvfp4_weights(s)
+    out, r, inter, _ = run_gpu(torch, s, x, pk, None, AUTO, nvfp4=True)
+    full_check(s, x, pk, None, out, r, inter, nvfp4_w=pk)
+
+
 def test_nvfp4_hot_experts(torch):
     """NVFP4 B tiles on experts with more than 512 rows (several M-tiles each)."""
     s = synth.FFNShape("mid128_fp4", HOT_T, 512, 128, 8, 128, 128, nvfp4=True)
