@@ -79,7 +79,7 @@ struct Workspace {
 constexpr int kRouterSlices = 16;  // most K-slices of the large-T router logits
 constexpr int kRouteSlices = 32;   // K-slices of the small-T router logits
 constexpr int kRouteSmallT = 64;   // largest T of the one-block-per-token router and the streaming path
-constexpr int kGemmBM = 256;       // MFMA tile rows (tokens)
+constexpr int kGemmBM = 320;       // MFMA tile rows (tokens): ~256 +- 16 rows per expert at T = 4096 fit one tile
 constexpr int kFp4BM = 128;        // row tiles of the NVFP4 weight-streaming GEMMs
 constexpr int kFp4SmallT = 32;     // ... up to this T every expert's rows are one 32-row tile
 constexpr int kStreamKS = 2;       // K-slices of the streaming routed gate/up units (bf16)

@@ -11,9 +11,11 @@
 // needed to size the grid.  Routed A rows of the gate/up GEMM are gathered
 // from x through perm and never copied out.
 //
-// Tile: 256 rows x 256 B-columns, 512 threads = 8 waves in 2 (rows) x 4
-// (columns), each wave owning 128 x 64 outputs as 4 x 2 MFMA 32x32 blocks;
-// two waves share each SIMD.  For gate/up the 256 B-columns are 128 gate +
+// Tile: 320 rows x 256 B-columns, 512 threads = 8 waves in 2 (rows) x 4
+// (columns), each wave owning 160 x 64 outputs as 5 x 2 MFMA 32x32 blocks;
+// two waves share each SIMD.  320 rows hold a whole expert at prefill
+// (256 +- 16 rows per expert at T = 4096), so its weights are streamed by
+// one M-tile instead of a full tile and a short tail tile.  For gate/up the 256 B-columns are 128 gate +
 // 128 up columns at the same output positions (a wave owns 32 of each), so
 // the GeGLU epilogue pairs them in registers.
 //
@@ -28,7 +30,7 @@
 //
 // LDS layouts (16-byte chunks XOR-swizzled so that every fragment read and
 // every copy touches the bank groups evenly):
-//   A  [256 rows][32 k]: 64 B per row, chunk c of row r at c ^ fa(r).
+//   A  [320 rows][32 k]: 64 B per row, chunk c of row r at c ^ fa(r).
 //   B  bf16 weights are [K, N] (N contiguous) and stay so in LDS: two halves
 //      (gate / up, or columns 0-127 / 128-255) of [32 k][128 n], 256 B per k
 //      row, chunk c of row k at c ^ fb(k).  The MFMA B operand (8
@@ -55,14 +57,24 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = kGemmBM;  // 256
+constexpr int BM = kGemmBM;  // 320
+constexpr int kRowBlocks = BM / 64;  // 32-row MFMA blocks per wave row (2 wave rows)
+// Host-sized segments (the dense branch, all T rows) take 256-row tiles,
+// except in the gate/up launch beside expert tiles, which take 320 (measured
+// on one GPU at T = 4096, gate/up / down us: 26B layer 466 / 262 with 256-row
+// dense tiles everywhere, 439 / 275 with 320 everywhere; the E4B dense FFN
+// alone 436 / 286 against 470 / 314)
+constexpr int kHostBMSmall = 256;
 constexpr int BN = 256;      // B columns per tile
 constexpr int BK = 32;       // k per pipeline stage
 constexpr int kStages = 4;   // LDS stages in flight
 constexpr int kThreads = 512;  // 8 waves: 2 (rows) x 4 (columns), 128 x 64 outputs each
 constexpr int kXcd = 8;
-constexpr int kOpBytes = 256 * BK * 2;     // one operand tile of a stage: 16 KB
-constexpr int kStageBytes = 2 * kOpBytes;  // A, then B
+constexpr int kAOpBytes = BM * BK * 2;          // the A tile of a stage: 20 KB
+constexpr int kBOpBytes = BN * BK * 2;          // the B tile of a stage: 16 KB
+constexpr int kStageBytes = kAOpBytes + kBOpBytes;  // A, then B
+constexpr int kACopies = 3;                     // A copies per wave per stage (1 KB each; 20 of the 24 land in A)
+constexpr int kDummyBytes = 4096;               // where the 4 surplus A copies land (never read)
 
 enum { MODE_PLAIN_BF16 = 0, MODE_PLAIN_F32 = 1, MODE_GATEUP = 2 };
 enum { W_BF16 = 0, W_FP8 = 2 };
@@ -82,7 +94,8 @@ struct Seg {
   void* C;
   int ldc;
   int n_ntiles;           // output column tiles
-  int host_rows;          // host-sized segment: number of rows (tiles at BM)
+  int host_rows;          // host-sized segment: number of rows
+  int host_bm;            // ... in tiles of this many rows (<= BM)
   const int32_t* mtiles;  // expert-grouped segment: device tile list (else null)
   const int32_t* n_mtiles;
   int max_mtiles;
@@ -198,8 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     row0 = S.mtiles[4 * mt + 1];
     rows = S.mtiles[4 * mt + 2];
   } else {
-    row0 = mt * BM;
-    rows = min(BM, S.host_rows - row0);
+    row0 = mt * S.host_bm;
+    rows = min(S.host_bm, S.host_rows - row0);
   }
   const int K = S.K, N = S.N;
   // output columns of this tile: gate/up pairs 128 gate with 128 up columns
@@ -212,12 +225,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   // (one is written while the other is read).  After the K loop the same
   // bytes stage the output tile.
   constexpr int kRaw = (WF == W_FP8) ? 8192 : 0;
-  constexpr int kDepth = (WF == W_FP8) ? 5 : kStages;
-  constexpr int kStageStride = (WF == W_BF16) ? kStageBytes : kOpBytes + kRaw;  // one ring slot
-  constexpr int kBArea = kDepth * kStageStride;                               // FP: the two B tiles
-  constexpr int kStageArea = kBArea + ((WF == W_BF16) ? 0 : 2 * kOpBytes);
-  constexpr int SP = OUTN * 2 + 16;  // staging row pitch (bytes)
-  constexpr int kSmem = kStageArea > BM * SP ? kStageArea : BM * SP;
+  constexpr int kDepth = kStages;
+  constexpr int kStageStride = (WF == W_BF16) ? kStageBytes : kAOpBytes + kRaw;  // one ring slot
+  constexpr int kBArea = kDepth * kStageStride;                                // FP8: the two B tiles
+  constexpr int kDummy = kBArea + ((WF == W_BF16) ? 0 : 2 * kBOpBytes);        // surplus A copies
+  constexpr int kStageArea = kDummy + kDummyBytes;
+  constexpr int SP = OUTN * 2 + 16;  // staging row pitch (bytes); half the tile's rows at a time
+  constexpr int kSmem = kStageArea > (BM / 2) * SP ? kStageArea : (BM / 2) * SP;
+  static_assert(kSmem <= 163840, "LDS per block");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kSmem];
   lds_u8* const lds3 = (lds_u8*)(lds);
   const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>(lds3));  // LDS byte address of the stages
@@ -227,18 +242,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int wm = wave >> 2, wn = wave & 3;
 
-  // ---- A copies: wave w, copy q fills rows 32w + 16q .. + 15 of a stage;
-  // lane: row 32w + 16q + lane / 4, slot lane % 4 <- global chunk slot ^ fa.
+  // ---- A copies: copy c = 3 w + q of wave w fills rows 16 c .. + 15 of a
+  // stage (c < 20; copies 20 .. 23 land in a dummy area, out of range);
+  // lane: row 16 c + lane / 4, slot lane % 4 <- global chunk slot ^ fa.
   // Lanes of rows past the tile's end get an offset beyond the resource's
   // range (kOutOfRange):
   // the copy returns zeros without touching memory, and every copy is still
   // issued, so the wait counts below stay constants.  Those rows' results
   // are dropped.
   const i32x4_t arsrc = rsrc4(S.A);
-  int aoff[2];
+  int aoff[kACopies];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = 32 * wave + 16 * q + (lane >> 2);
+  for (int q = 0; q < kACopies; ++q) {
+    const int r = 16 * (kACopies * wave + q) + (lane >> 2);  // r >= BM: a surplus copy (r >= rows)
     const int rr = r < rows ? r : 0;
     const uint32_t gr = S.gather ? uint32_t(S.gather[row0 + rr]) : uint32_t(row0 + rr);
     aoff[q] = r < rows ? int((gr * uint32_t(S.lda) + uint32_t(((lane & 3) ^ fa(r)) * 8)) * 2u) : kOutOfRange;
@@ -299,30 +315,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     const int kk = (kt0 + min(st, nk - 1)) * BK;
     const uint32_t sbase_addr = lds_base + uint32_t((st % kDepth) * kStageStride);
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      copy_b128_to_lds(arsrc, sbase_addr + (32 * wave + 16 * q) * 64, aoff[q], kk * 2);
+    for (int q = 0; q < kACopies; ++q) {
+      const int c = kACopies * wave + q;  // wave-uniform
+      const uint32_t dst = c < BM / 16 ? sbase_addr + c * 1024 : lds_base + uint32_t(kDummy + (c - BM / 16) * 1024);
+      copy_b128_to_lds(arsrc, dst, aoff[q], kk * 2);
+    }
     if (WF == W_BF16) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
-        copy_b128_to_lds(brsrc, sbase_addr + kOpBytes + bh * (kOpBytes / 2) + (8 * (wave & 3) + 4 * q) * 256,
+        copy_b128_to_lds(brsrc, sbase_addr + kAOpBytes + bh * (kBOpBytes / 2) + (8 * (wave & 3) + 4 * q) * 256,
                          boff[q], int(uint32_t(kk) * brow));
     }
   };
   // raw codes of stage st into its raw area (one copy per lane)
   auto issue_raw = [&](int st) {
     const int kidx = kt0 + min(st, nk - 1);
-    const uint32_t rb = lds_base + uint32_t((st % kDepth) * kStageStride + kOpBytes);
+    const uint32_t rb = lds_base + uint32_t((st % kDepth) * kStageStride + kAOpBytes);
     if (WF == W_FP8) {
       copy_b128_to_lds(rrsrc, rb + wave * 1024, roff, int(uint32_t(kidx * BK) * uint32_t(S.ldb)));
     }
   };
   // raw codes of stage st (landed) -> the stage's bf16 B tile
   auto decode = [&](int st) {
-    lds_u8* sb = lds3 + (st % kDepth) * kStageStride;  // A, then the raw codes at kOpBytes
-    lds_u8* bt = lds3 + kBArea + (st & 1) * kOpBytes;  // this stage's bf16 B tile
+    lds_u8* sb = lds3 + (st % kDepth) * kStageStride;  // A, then the raw codes at kAOpBytes
+    lds_u8* bt = lds3 + kBArea + (st & 1) * kBOpBytes;  // this stage's bf16 B tile
     if (WF == W_FP8) {
       const int h = tid >> 8, t2 = tid & 255, k = t2 >> 3, c0 = (t2 & 7) * 2;
-      const u32x4_t q = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(sb + kOpBytes + tid * 16);
+      const u32x4_t q = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(sb + kAOpBytes + tid * 16);
       u32x4_t w[2];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -331,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
         w[d >> 1][2 * (d & 1) + 1] =
             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], 1.0f, true));
       }
-      lds_u8* row = bt + h * (kOpBytes / 2) + k * 256;
+      lds_u8* row = bt + h * (kBOpBytes / 2) + k * 256;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
         *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(row + (((c0 + c) ^ fb(k)) << 4)) = w[c];
@@ -339,12 +358,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   };
 
   // ---- fragment addresses of this wave's 32 x 32 blocks (bytes in a stage)
-  // A block i: rows wm*128 + 32i; lane row (lane & 31), k half lane / 32
+  // A block i: rows wm*BM/2 + 32i; lane row (lane & 31), k half lane / 32
   const int hl = lane >> 5;
-  int afr[4][2];
+  int afr[kRowBlocks][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = wm * 128 + 32 * i + (lane & 31);
+  for (int i = 0; i < kRowBlocks; ++i) {
+    const int m = wm * (BM / 2) + 32 * i + (lane & 31);
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) afr[i][sb] = m * 64 + (((2 * sb + hl) ^ fa(m)) << 4);
   }
@@ -361,17 +380,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     const int g = lane >> 4, i16 = lane & 15, qq = i16 & 3, mr = i16 >> 2;
     const int colb = lc + 16 * (g & 1);
     const int krow = 8 * (g >> 1) + mr;  // fb(krow + 16 s + 4 r) == fb(mr)
-    bfr[j] = h * (kOpBytes / 2) + krow * 256 + ((((colb >> 3) + (qq >> 1)) ^ fb(mr)) << 4) + (qq & 1) * 8;
+    bfr[j] = h * (kBOpBytes / 2) + krow * 256 + ((((colb >> 3) + (qq >> 1)) ^ fb(mr)) << 4) + (qq & 1) * 8;
   }
 
-  // Row blocks of this wave inside the tile's rows (a prefix of the 4), and
+  // Row blocks of this wave inside the tile's rows (a prefix of the 5), and
   // whether its columns are inside the matrix: both are wave-uniform, and
   // each count runs its own straight-line path (same barriers in all), so
   // the ragged last M-tile of an expert and the last N-tile cost only their
   // valid part.
   const int wcol0 = (MODE == MODE_GATEUP) ? n0 + wn * 32 : n0 + wn * 64;
-  int ni = (rows - wm * 128 + 31) / 32;
-  ni = ni < 0 ? 0 : (ni > 4 ? 4 : ni);
+  int ni = (rows - wm * (BM / 2) + 31) / 32;
+  ni = ni < 0 ? 0 : (ni > kRowBlocks ? kRowBlocks : ni);
   if (wcol0 >= N) ni = 0;
   ni = __builtin_amdgcn_readfirstlane(ni);
 
@@ -388,9 +407,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
 
   auto run = [&](auto ni_c) {
     constexpr int NI = decltype(ni_c)::value;
-    f32x16_t acc[4][2];
+    f32x16_t acc[kRowBlocks][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kRowBlocks; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -398,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
 
     // Fragments of one 16-k sub-step of a stage for this wave's blocks.
     struct Frags {
-      bf16x8_t a[4], b[2];
+      bf16x8_t a[kRowBlocks], b[2];
     };
     // abase: the stage's A tile; bbase: its B tile; sb: sub-step 0 or 1
     auto read_sub = [&](const lds_u8* abase, const lds_u8* bbase, int sb, Frags& f) {
@@ -424,12 +443,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     };
 
-    // Memory instructions per stage per lane: bf16 4 copies (A 2 + B 2);
-    // FP8 / NVFP4 3 copies (A 2 + the raw codes).
-    constexpr int kPerStage = (WF == W_BF16) ? 4 : 3;
+    // Memory instructions per stage per lane: bf16 5 copies (A 3 + B 2);
+    // FP8 4 copies (A 3 + the raw codes).
+    constexpr int kPerStage = (WF == W_BF16) ? kACopies + 2 : kACopies + 1;
     auto abase_of = [&](int st) -> const lds_u8* { return lds3 + (st % kDepth) * kStageStride; };
     auto bbase_of = [&](int st) -> const lds_u8* {
-      return (WF == W_BF16) ? abase_of(st) + kOpBytes : lds3 + kBArea + (st & 1) * kOpBytes;
+      return (WF == W_BF16) ? abase_of(st) + kAOpBytes : lds3 + kBArea + (st & 1) * kBOpBytes;
     };
     auto stage_in = [&](int st) {
       if (WF != W_BF16) issue_raw(st);
@@ -497,7 +516,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       for (int i = 0; i < NI; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int row = wm * (BM / 2) + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (row >= rows) continue;
           const long long orow = (long long)(row0 + row) * S.ldc + ks * S.c_slice;
 #pragma unroll
@@ -509,46 +528,54 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       }
       return;
     }
-    // bf16 outputs go through LDS so that the tile leaves in 16-byte stores.
+    // bf16 outputs go through LDS so that the tile leaves in 16-byte stores,
+    // half the tile's rows at a time (the waves of wave row h stage them).
     // Neighbouring lanes swap values (DPP) so that each lane writes pairs of
     // adjacent columns: even lanes rows r = 2q, odd lanes rows r = 2q + 1.
-    block_barrier();  // every wave's last fragments are read and its copies landed
     const bool odd = lane & 1;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-#pragma unroll
-      for (int j = 0; j < ((MODE == MODE_GATEUP) ? 1 : 2); ++j) {
-        uint32_t vb[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float v = (MODE == MODE_GATEUP) ? gelu_tanh(acc[i][0][r] * ts0) * (acc[i][1][r] * ts1)
-                                                : acc[i][j][r] * ts0;
-          vb[r] = f32_to_bf16_bits(v);
-        }
-        const int cpair = ((MODE == MODE_GATEUP) ? wn * 32 : wn * 64 + j * 32) + (lane & 30);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t send = odd ? vb[2 * q] : vb[2 * q + 1];
-          const uint32_t recv = uint32_t(__builtin_amdgcn_mov_dpp(int(send), 0xB1, 0xF, 0xF, false));  // lane ^ 1
-          const int r = 2 * q + (odd ? 1 : 0);
-          const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const uint32_t packed = odd ? (recv | (vb[2 * q + 1] << 16)) : (vb[2 * q] | (recv << 16));
-          *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(lds3 + row * SP + cpair * 2) = packed;
-        }
-      }
-    }
-    __syncthreads();
     constexpr int CPR = OUTN / 8;  // 16-byte chunks per staged row
     bf16_t* C = reinterpret_cast<bf16_t*>(S.C);
-    for (int c = tid; c < BM * CPR; c += kThreads) {
-      const int row = c / CPR, ch = c % CPR;
-      const int col = n0 + ch * 8;
-      if (row < rows && col < N)
-        *reinterpret_cast<u32x4_t*>(C + (long long)(row0 + row) * S.ldc + ks * S.c_slice + col) =
-            *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(lds3 + row * SP + ch * 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      block_barrier();  // h = 0: every wave's last fragments are read; h = 1: the first half has left
+      if (wm == h) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+#pragma unroll
+          for (int j = 0; j < ((MODE == MODE_GATEUP) ? 1 : 2); ++j) {
+            uint32_t vb[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float v = (MODE == MODE_GATEUP) ? gelu_tanh(acc[i][0][r] * ts0) * (acc[i][1][r] * ts1)
+                                                    : acc[i][j][r] * ts0;
+              vb[r] = f32_to_bf16_bits(v);
+            }
+            const int cpair = ((MODE == MODE_GATEUP) ? wn * 32 : wn * 64 + j * 32) + (lane & 30);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const uint32_t send = odd ? vb[2 * q] : vb[2 * q + 1];
+              const uint32_t recv = uint32_t(__builtin_amdgcn_mov_dpp(int(send), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+              const int r = 2 * q + (odd ? 1 : 0);
+              const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // in the half
+              const uint32_t packed = odd ? (recv | (vb[2 * q + 1] << 16)) : (vb[2 * q] | (recv << 16));
+              *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(lds3 + row * SP + cpair * 2) = packed;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      for (int c = tid; c < (BM / 2) * CPR; c += kThreads) {
+        const int hrow = c / CPR, ch = c % CPR;
+        const int row = h * (BM / 2) + hrow;
+        const int col = n0 + ch * 8;
+        if (row < rows && col < N)
+          *reinterpret_cast<u32x4_t*>(C + (long long)(row0 + row) * S.ldc + ks * S.c_slice + col) =
+              *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(lds3 + hrow * SP + ch * 16);
+      }
     }
   };
   switch (ni) {
+    case 5: run(std::integral_constant<int, 5>{}); break;
     case 4: run(std::integral_constant<int, 4>{}); break;
     case 3: run(std::integral_constant<int, 3>{}); break;
     case 2: run(std::integral_constant<int, 2>{}); break;
@@ -561,6 +588,7 @@ Seg empty_seg() {
   Seg s{};
   s.n_ntiles = 1;
   s.ksplit = 1;
+  s.host_bm = BM;
   return s;
 }
 
@@ -574,7 +602,8 @@ hipError_t launch(const Seg& a, const Seg& b, int units_a, int units_b, hipStrea
   return hipGetLastError();
 }
 
-int host_units(const Seg& s) { return ((s.host_rows + BM - 1) / BM) * s.n_ntiles * s.ksplit; }
+int host_units(const Seg& s) { return ((s.host_rows + s.host_bm - 1) / s.host_bm) * s.n_ntiles * s.ksplit; }
+
 int grouped_units(const Seg& s) { return s.max_mtiles * s.n_ntiles; }
 
 }  // namespace
@@ -618,6 +647,7 @@ hipError_t launch_gemm_gateup(const StreamArgs& a, const Workspace& ws, int max_
     d.ldc = sh.D;
     d.n_ntiles = (sh.D + BN / 2 - 1) / (BN / 2);
     d.host_rows = sh.T;
+    d.host_bm = sh.E > 0 ? BM : kHostBMSmall;
   }
   // routed experts: rows gathered through perm
   e.A = a.x;
@@ -660,6 +690,7 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
     d.ldc = sh.H;
     d.n_ntiles = (sh.H + BN - 1) / BN;
     d.host_rows = sh.T;
+    d.host_bm = kHostBMSmall;
   }
   e.A = ws.h;
   e.lda = sh.I;

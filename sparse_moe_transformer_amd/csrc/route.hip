@@ -205,6 +205,145 @@ __global__ __launch_bounds__(kThreads) void k_topk(Shape sh, int nslices, const 
   wave_route_token(zs[wid], E, sh.k, ws.topk_idx + size_t(t) * sh.k, ws.topk_w + size_t(t) * sh.k);
 }
 
+// Large-T router with E = 128 or 256: one block of 4 waves per 32 tokens
+// computes their logits over all of K with v_mfma_f32_32x32x16_bf16 and
+// routes them, so no partial logits go through memory.  Per 64-k step the
+// x rows ([32][64] bf16, 128 B rows) and the W_r rows ([64][E], split in
+// 128-column halves of 256 B rows) go global -> LDS by DMA (buffer loads
+// with the lds flag) three steps ahead; 16-byte chunks are XOR-swizzled as
+// in the grouped GEMM tiles (x: chunk c of row r at c ^ (r % 8); W_r: chunk
+// c of k row at c ^ 4 (k % 4)).  The MFMA B operand (8 consecutive k of one
+// expert per lane) is read with the gfx950 transposing LDS read.  Wave w
+// owns experts 32 w .. + 31 of each half.  Then the logits (+ bias) go to
+// LDS and each wave routes 8 tokens (wave_route_token).
+constexpr int kRmStep = 64;  // k per step
+constexpr int kRouteFusedMinT = 8192;
+constexpr int kRmDepth = 4;  // LDS stages
+
+typedef int i32x4v_t __attribute__((ext_vector_type(4)));
+typedef short s16x4v_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4v_t rm_rsrc(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  i32x4v_t r;
+  r[0] = int(__builtin_amdgcn_readfirstlane(uint32_t(v)));
+  r[1] = int(__builtin_amdgcn_readfirstlane(uint32_t(v >> 32)));
+  r[2] = 0x7FFFFFFF;
+  r[3] = 0x00020000;
+  return r;
+}
+__device__ __forceinline__ void rm_copy(i32x4v_t rsrc, uint32_t lds, int voffset, int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voffset), "s"(rsrc),
+               "s"(soffset)
+               : "memory");
+}
+template <int VM>
+__device__ __forceinline__ void rm_wait() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int NH>  // 128-column halves of E
+__global__ __launch_bounds__(256) void k_route_mfma(Shape sh, const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr,
+                                                    const float* __restrict__ bias, Workspace ws) {
+  constexpr int E = 128 * NH;
+  constexpr int kA = 32 * 128;                 // x rows of a step: 4 KB
+  constexpr int kB = kRmStep * 256 * NH;       // W_r rows of a step
+  constexpr int kStage = kA + kB;
+  constexpr int CB = kB / 1024 / 4;            // W_r copies per wave per step
+  constexpr int kPer = 1 + CB;                 // copies per wave per step
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kRmDepth * kStage];
+  float* const zs = reinterpret_cast<float*>(lds);  // [32][E] logits after the K loop (the stages are free)
+  lds_u8* const l3 = (lds_u8*)lds;
+  const uint32_t lbase = uint32_t(reinterpret_cast<uintptr_t>(l3));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, lc = lane & 31;
+  const int t0 = blockIdx.x * 32;
+  const int H = sh.H, nsteps = H / kRmStep;
+
+  // x copy of wave w: rows 8 w .. + 7; lane: row 8 w + lane / 8, slot lane % 8
+  const i32x4v_t xr = rm_rsrc(x);
+  int xoff;
+  {
+    const int r = 8 * wave + (lane >> 3);
+    xoff = t0 + r < sh.T ? int((uint32_t(t0 + r) * uint32_t(H) + uint32_t(((lane & 7) ^ (r & 7)) * 8)) * 2u)
+                         : int(0x80000000u);  // past T: out of range, zeros
+  }
+  // W_r copy q of wave w: k rows 4 (CB w + q) .. + 3 of the step, across the
+  // halves: copy index c = CB w + q -> half c / 16, rows 4 (c % 16) ..;
+  // lane: row + lane / 16, slot lane % 16 <- chunk slot ^ 4 (k % 4)
+  const i32x4v_t wrs = rm_rsrc(wr);
+  int woff[CB];
+#pragma unroll
+  for (int q = 0; q < CB; ++q) {
+    const int c = CB * wave + q, half = c >> 4, k = 4 * (c & 15) + (lane >> 4);
+    woff[q] = int((uint32_t(k) * uint32_t(E) + uint32_t(128 * half + (((lane & 15) ^ (4 * (k & 3))) * 8))) * 2u);
+  }
+  auto issue = [&](int st) {
+    const int kk = min(st, nsteps - 1) * kRmStep;
+    const uint32_t sb = lbase + uint32_t((st % kRmDepth) * kStage);
+    rm_copy(xr, sb + wave * 1024, xoff, kk * 2);
+#pragma unroll
+    for (int q = 0; q < CB; ++q) {
+      const int c = CB * wave + q;
+      rm_copy(wrs, sb + kA + (c >> 4) * (kRmStep * 256) + (c & 15) * 1024, woff[q], kk * E * 2);
+    }
+  };
+  // fragment addresses: A row lc, k-step i: chunk (2 i + hf) ^ (lc % 8);
+  // B (half j, columns 32 wave ..): as in the grouped GEMM's transposing reads
+  int bfr;
+  {
+    const int g = lane >> 4, i16 = lane & 15, qq = i16 & 3, mr = i16 >> 2;
+    const int colb = 32 * wave + 16 * (g & 1);
+    const int krow = 8 * (g >> 1) + mr;
+    bfr = krow * 256 + ((((colb >> 3) + (qq >> 1)) ^ (4 * (mr & 3))) << 4) + (qq & 1) * 8;
+  }
+  f32x16_t acc[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+#pragma unroll
+  for (int st = 0; st < kRmDepth - 1; ++st) issue(st);
+  for (int s = 0; s < nsteps; ++s) {
+    rm_wait<(kRmDepth - 2) * kPer>();  // step s landed (this wave's copies)
+    __builtin_amdgcn_s_barrier();      // every wave's copies of step s landed; step s - 1's slot is free
+    issue(s + kRmDepth - 1);
+    const lds_u8* sa = l3 + (s % kRmDepth) * kStage;
+    const lds_u8* sbp = sa + kA;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8_t a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+          sa + lc * 128 + (((2 * i + hf) ^ (lc & 7)) << 4));
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const lds_u8* p = sbp + j * (kRmStep * 256) + bfr + i * 16 * 256;
+        const s16x4v_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4v_t*)(p));
+        const s16x4v_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4v_t*)(p + 4 * 256));
+        const s16x4v_t v[2] = {lo, hi};
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, v), acc[j], 0, 0, 0);
+      }
+    }
+  }
+  rm_wait<0>();
+  __syncthreads();  // every wave's last fragments are read: the stages become zs
+  // logits (+ bias) to LDS: lane holds expert 32 wave + lc of half j, tokens
+  // 8 (r / 4) + 4 hf + r % 4
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    const int e = 128 * j + 32 * wave + lc;
+    const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zs[(8 * (r >> 2) + 4 * hf + (r & 3)) * E + e] = acc[j][r] + b;
+  }
+  __syncthreads();
+  for (int t = wave; t < 32 && t0 + t < sh.T; t += 4)
+    wave_route_token(zs + t * E, E, sh.k, ws.topk_idx + size_t(t0 + t) * sh.k, ws.topk_w + size_t(t0 + t) * sh.k);
+}
+
 // per 64-token block: membership masks and counts
 __global__ __launch_bounds__(kThreads) void k_align_count(Shape sh, Workspace ws) {
   const int T = sh.T, E = sh.E, k = sh.k;
@@ -289,6 +428,17 @@ hipError_t launch_gemm_router(const Shape& sh, const bf16_t* x, const bf16_t* wr
 
 hipError_t launch_route_large(const Shape& sh, const bf16_t* x, const bf16_t* wr, const float* bias,
                               const Workspace& ws, hipStream_t s) {
+  if ((sh.E == 128 || sh.E == 256) && sh.H % kRmStep == 0 && sh.T >= kRouteFusedMinT) {
+    // logits and routing in one launch, 32 tokens per block (measured:
+    // faster than the split-K logits and the per-token top-k from about
+    // T = 8192 on; below that its few blocks leave most CUs idle)
+    const dim3 grid((sh.T + 31) / 32);
+    if (sh.E == 128)
+      hipLaunchKernelGGL(k_route_mfma<1>, grid, dim3(256), 0, s, sh, x, wr, bias, ws);
+    else
+      hipLaunchKernelGGL(k_route_mfma<2>, grid, dim3(256), 0, s, sh, x, wr, bias, ws);
+    return hipGetLastError();
+  }
   int nslices = 1;
   if (sh.E % 128 == 0 && sh.H % 64 == 0) {
     // enough K-slices for ~512 tiles, at most kRouterSlices
