@@ -12,7 +12,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_ffn.so")
+# MOE_FFN_LIB selects another build of the library (the host-sanitized one of
+# the CPU ABI tests); the default is the in-tree build
+LIB_PATH = os.environ.get("MOE_FFN_LIB") or os.path.join(_PKG, "libmoe_ffn.so")
 
 MOE_FFN_OK = 0
 MOE_FFN_ERR_INVALID_ARG = -1

@@ -63,6 +63,54 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(OBJDIR, "asan")
+SAN_LIB = os.path.join(SAN_DIR, "libmoe_ffn_asan.so")
+
+
+def asan_runtime():
+    """Path of the compiler's AddressSanitizer runtime (it also carries the
+    UndefinedBehaviorSanitizer handlers), or None."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    hits = sorted(glob.glob(os.path.join(root, "lib", "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")) +
+                  glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else None
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The library with its host code (the C ABI layer, api.cpp) built with
+    AddressSanitizer and UndefinedBehaviorSanitizer, for the CPU tests of the
+    ABI; device code is the regular build.  Load it with the sanitizer
+    runtime preloaded (asan_runtime()).  Returns its path."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        if src == "api.cpp":
+            continue
+        obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+        if not os.path.exists(obj) or os.path.getmtime(obj) < os.path.getmtime(os.path.join(CSRC, src)):
+            obj = _compile(src)
+        objs.append(obj)
+    api_obj = os.path.join(SAN_DIR, "api.o")
+    # sanitizers on the host pass only (each -fsanitize= behind -Xarch_host)
+    cmd = [hipcc(), "-xhip", *[f for f in FLAGS if f != "-O3"], "-O1", "-g",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc (sanitized api.cpp) failed:\n{r.stdout}\n{r.stderr}")
+    # the sanitizer runtime is preloaded at run time, so the link needs no flag
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", api_obj, *objs, "-o", SAN_LIB],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (sanitized) failed:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

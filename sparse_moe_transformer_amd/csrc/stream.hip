@@ -892,9 +892,7 @@ hipError_t launch_stream_down(const StreamArgs& a, const Workspace& ws, hipStrea
   const int kd = ud ? (sh.D / 64 + ksd - 1) / ksd * 64 : 0;
   const size_t lds = std::max(size_t(std::max(sh.I, kd)) * kRowsChunk * 2, size_t(5) * kRowsChunk * kDownColsMax * 4);
   const dim3 grid(ud + max_active * nblk);
-  if (a.fp8 && fused)
-    hipLaunchKernelGGL((k_stream_down<true, true>), grid, dim3(kThreads), lds, s, a, ws, ud);
-  else if (a.fp8)
+  if (a.fp8)  // FP8 down units read the rows k_stream_geglu wrote (stream_fused_geglu)
     hipLaunchKernelGGL((k_stream_down<true, false>), grid, dim3(kThreads), lds, s, a, ws, ud);
   else if (fused)
     hipLaunchKernelGGL((k_stream_down<false, true>), grid, dim3(kThreads), lds, s, a, ws, ud);
