@@ -43,8 +43,8 @@ def parse():
     p.add_argument("--no-skew", action="store_true")
     p.add_argument("--skew-steps", type=int, default=10)
     p.add_argument("--no-nvfp4", action="store_true")
-    p.add_argument("--nvfp4-steps", type=int, default=10, help="chains of --nvfp4-layers layers")
-    p.add_argument("--nvfp4-layers", type=int, default=4)
+    p.add_argument("--nvfp4-steps", type=int, default=3, help="timed chains of --nvfp4-layers layers")
+    p.add_argument("--nvfp4-layers", type=int, default=30)
     p.add_argument("--no-block", action="store_true", help="skip the sandwich-norm sub-block leg")
     p.add_argument("--block-steps", type=int, default=100)
     p.add_argument("--no-dense", action="store_true", help="skip the E4B dense FFN leg")
@@ -52,7 +52,7 @@ def parse():
     p.add_argument("--no-w4a4", action="store_true", help="skip the NVFP4 W4A4 leg")
     p.add_argument("--dense-steps", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--cpu-decode-only", action="store_true", help="time the oracle at decode only")
     return p.parse_args()
 
 
@@ -318,25 +318,119 @@ def traffic_of(kernel):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(shape, x, w, bias, seconds):
-    """The oracle (as it stands) on the host cores over a bounded sample."""
-    import oracle
+def host_info():
+    """CPU model (from /proc/cpuinfo), the BLAS library and its thread count
+    (from threadpoolctl) that the oracle's numpy uses."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     from threadpoolctl import threadpool_info
-    cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-                or [1])
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.moe_ffn(x, w["router"], w["gate"], w["up"], w["down"], w["dgate"], w["dup"],
-                       w["ddown"], top_k=shape.top_k, bias=bias, intermediates=False)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or n >= 50:
-            break
-    return {"value": n * shape.tokens / el, "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{n} full fp64 oracle forwards of the T={shape.tokens} workload "
-                      f"({el:.1f} s, numpy/OpenBLAS)"}
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    vendor = blas[0].get("internal_api", "?") if blas else "none"
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    return {"cpu_model": model, "blas": vendor, "blas_threads": int(threads),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def time_oracle(fn, runs):
+    """Median (and every) wall time of `runs` calls of fn."""
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)), ts
+
+
+def cpu_baseline(dec, x, w, bias, legs=True):
+    """The oracle (as it stands, fp64 numpy) on the host cores: decode (the
+    headline's workload, median of 3 forwards) and, with legs, the tiny
+    workload and prefill (median of 3), skew and one NVFP4 stack layer (one
+    run each), each as tokens/s of the workload it times."""
+    import oracle
+    import synth
+    info = host_info()
+
+    def ffn(xx, ww, k, b=None):
+        return oracle.moe_ffn(xx, ww["router"], ww["gate"], ww["up"], ww["down"], ww["dgate"], ww["dup"],
+                              ww["ddown"], top_k=k, bias=b, intermediates=False)
+
+    med, ts = time_oracle(lambda: ffn(x, w, dec.top_k, bias), 3)
+    out = {"value": dec.tokens / med, "unit": "tokens/s", "cores": info["blas_threads"], "kind": "oracle",
+           "sample": f"median of 3 full fp64 oracle forwards of the decode workload (T={dec.tokens}, "
+                     f"{med:.2f} s each); numpy on {info['blas']} with {info['blas_threads']} threads",
+           "host": info}
+    if not legs:
+        return out
+    out["legs"] = {}
+
+    def leg(name, shape, runs, ww=None, b=None):
+        xx = synth.make_x(shape)
+        ww = ww if ww is not None else synth.make_weights(shape)
+        m, tt = time_oracle(lambda: ffn(xx, ww, shape.top_k, b), runs)
+        out["legs"][name] = {"tokens": shape.tokens, "value": shape.tokens / m, "unit": "tokens/s",
+                             "seconds": [round(t, 3) for t in tt], "runs": runs}
+
+    leg("tiny", synth.TINY, 3)
+    leg("prefill", synth.PREFILL, 3, ww=w)
+    leg("skew", synth.SKEW, 1, ww=w, b=synth.zipf_bias(synth.SKEW.experts))
+    leg("nvfp4_stack_layer", synth.NVFP4_STACK, 1, ww=synth.make_nvfp4_weights(synth.NVFP4_STACK))
+    return out
+
+
+def run_nvfp4_stack(torch, shape, n_layers, chains):
+    """The NVFP4 residual stack x <- x + FFN_l(x) over n_layers distinct
+    layers, in place.  Two layers are generated and quantised on the host
+    from their seeds; layer l takes base layer l % 2's packed experts in a
+    seeded permutation of the expert axis (copied into memory of its own),
+    its own seeded bf16 router and a copy of the base's dense matrices, so
+    each layer streams its own 439 MB.  Returns the time per chain."""
+    import synth
+    from sparse_moe_transformer_amd import MoeFFN, binding
+    H, E = shape.hidden, shape.experts
+    bases = [upload_nvfp4(torch, synth.make_nvfp4_weights(shape, layer=l)) for l in range(2)]
+    layers = []
+    for l in range(n_layers):
+        b = bases[l % 2]
+        perm = torch.from_numpy(np.random.default_rng([0, l, 99]).permutation(E)).cuda()
+        lw = {"router": to_dev_bf16(torch, synth.normal_bf16(0, l, synth.TID_ROUTER, (H, E), H ** -0.5))}
+        for n in ("gate", "up", "down"):
+            lw[n] = {k: v.index_select(0, perm).contiguous() for k, v in b[n].items()}
+        for n in ("dgate", "dup", "ddown"):
+            lw[n] = {k: v.clone() for k, v in b[n].items()}
+        layers.append(lw)
+    del bases
+    x0 = to_dev_bf16(torch, synth.make_x(shape))
+    xd = x0.clone()
+    ffn = MoeFFN.for_shape(shape, accumulate=True)
+
+    def chain():
+        xd.copy_(x0)
+        for lw in layers:
+            ffn.forward_nvfp4(xd, lw, xd)
+
+    chain()  # warm up
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(chains):
+        chain()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_chain = ev0.elapsed_time(ev1) / chains
+    stage_mask = (1 << binding.MOE_FFN_NUM_STAGES) - 1
+    binding.check(binding.moe_ffn_profile_begin(ffn.h, stage_mask, n_layers))
+    chain()
+    rc, stage_ms, stage_n = binding.moe_ffn_profile_end(ffn.h)
+    binding.check(rc)
+    ffn.close()
+    return ms_chain, [1000.0 * m / n if n else 0.0 for m, n in zip(stage_ms, stage_n)]
 
 
 def main():
@@ -376,8 +470,8 @@ def main():
                    "top_k": dec.top_k, "expert_dim": dec.expert_dim, "dense_dim": dec.dense_dim,
                    "weight_copies": args.copies, "graph": bool(args.graph),
                    "active_experts": r["n_act"]},
-        "roofline": {"bound": "hbm", "kernel": "k_stream_gateup (routed gate/up + 3/8 of the dense units, "
-                                               "weight streaming)",
+        "roofline": {"bound": "hbm", "scope": "dominant kernel (the whole step is step_hbm)",
+                     "kernel": "k_stream_gateup (routed gate/up + 3/8 of the dense units, weight streaming)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes": gu_bytes, "avg_us": gu_us},
@@ -433,17 +527,18 @@ def main():
     if not args.no_nvfp4:
         st = synth.NVFP4_STACK
         L = args.nvfp4_layers
-        rn = run_workload(torch, st, args.nvfp4_steps * L, 2 * L, 2, False, layers=L)
-        us = rn["ms_per_step"] * 1e3
+        ms_chain, stage_us = run_nvfp4_stack(torch, st, L, args.nvfp4_steps)
+        us = ms_chain * 1e3 / L
         wbytes = nvfp4_layer_weight_bytes(st)
         line["nvfp4_stack"] = {
-            "workload": f"NVFP4 weight-only layer of the 30-layer residual stack, T=1024 "
-                        f"(chains of {L} layers over 2 distinct seeded layers)",
-            "tokens": st.tokens, "value": st.tokens / (us * 1e-6), "unit": "tokens/s per layer",
-            "us_per_layer": us, "stack_ms_30_layers": 30 * us * 1e-3,
+            "workload": f"residual stack of {L} distinct NVFP4 weight-only layers, T=1024 (x <- x + FFN_l(x) in "
+                        f"place; layers built from 2 seeded quantised layers by seeded expert permutations, each "
+                        f"with its own seeded router and its own copy of every matrix)",
+            "tokens": st.tokens, "layers": L, "stack_ms": ms_chain, "chains_timed": args.nvfp4_steps,
+            "value": st.tokens / (us * 1e-6), "unit": "tokens/s per layer", "us_per_layer": us,
             "layer_weight_bytes": wbytes, "hbm_frac": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "mfma_frac": step_flops(st) / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
-            "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rn["stage_avg_us"]])),
+            "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in stage_us])),
         }
     if not args.no_nvfp4:
         # one NVFP4 layer at decode (T = 8): weights streamed into registers
@@ -513,17 +608,17 @@ def main():
     if not args.no_w4a4:
         from dataclasses import replace
         st = replace(synth.NVFP4_STACK, layers=1)
-        rw = run_workload(torch, st, args.nvfp4_steps * 4, 8, 2, False, w4a4=True)
+        rw = run_workload(torch, st, 40, 8, 2, False, w4a4=True)
         us = rw["ms_per_step"] * 1e3
         line["w4a4"] = {
             "workload": "one NVFP4 layer with NVFP4 activations (W4A4), T=1024, 2 distinct seeded layers rotated",
             "tokens": st.tokens, "value": st.tokens / (us * 1e-6), "unit": "tokens/s per layer",
-            "us_per_layer": us, "steps": args.nvfp4_steps * 4,
+            "us_per_layer": us, "steps": 40,
             "mfma_frac": step_flops(st) / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
             "stage_avg_us": dict(zip(STAGES, [round(v, 2) for v in rw["stage_avg_us"]])),
         }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(dec, r["x"], r["w"], r["bias"], args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(dec, r["x"], r["w"], r["bias"], legs=not args.cpu_decode_only)
     print(json.dumps(line), flush=True)
 
 
