@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_ffn.so")
 
-SOURCES = ["route.hip", "gemm.hip", "fp4mm.hip", "stream.hip", "combine.hip", "quant.hip", "api.cpp"]
+SOURCES = ["route.hip", "gemm.hip", "fp4mm.hip", "fp4stream.hip", "stream.hip", "combine.hip", "quant.hip", "api.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32 (the host

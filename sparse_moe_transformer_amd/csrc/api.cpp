@@ -254,8 +254,9 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   const auto* wr = static_cast<const moe::bf16_t*>(router_w);
   bool stream = (h->variant == MOE_FFN_VARIANT_STREAM) ||
                 (h->variant == MOE_FFN_VARIANT_AUTO && T <= kStreamMaxTokens);
-  if (args.nvfp4) stream = false;             // the streaming kernels read bf16 [K, N] weights only
   if (T > moe::kRouteSmallT) stream = false;  // their scratch holds at most 64 tokens' rows
+  // NVFP4 weights stream through their own kernels where the shape fits them
+  if (args.nvfp4 && !moe::fp4_stream_fits(sh)) stream = false;
   const int mt = int((size_t(T) * sh.k + moe::kGemmBM - 1) / moe::kGemmBM + sh.E);
   const int mt128 = int((size_t(T) * sh.k + moe::kFp4BM - 1) / moe::kFp4BM + sh.E);
   const bool experts = sh.E > 0;  // else a dense FFN: no routing stages
@@ -264,6 +265,7 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   // and run the MFMA tiles, whose routing it feeds, at any T
   const bool small_route = experts && T <= moe::kRouteSmallT && moe::route_small_fits(sh);
   if (experts && !small_route) stream = false;
+  const bool fs4 = stream && args.nvfp4;  // the NVFP4 streaming kernels
   // a dense FFN on the MFMA path writes its output rows from the down GEMM
   const bool direct = !experts && !stream && !nm && !(h->cfg.flags & MOE_FFN_ACCUMULATE);
   {
@@ -276,7 +278,7 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
       xb = ws.xn;
       args.x = ws.xn;
     }
-    e = stream ? moe::launch_route_dense(args, wr, bias, ws, s)
+    e = stream && !fs4 ? moe::launch_route_dense(args, wr, bias, ws, s)
         : !experts                 ? hipSuccess
         : small_route               ? moe::launch_route_small(sh, xb, wr, bias, ws, s)
                                    : moe::launch_route_large(sh, xb, wr, bias, ws, s);
@@ -300,13 +302,14 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
       if (e != hipSuccess) return hip_fail(e, "activation quantiser");
       args.x = ws.xn;
     }
-    e = stream        ? moe::launch_stream_gateup(args, ws, s)
+    e = fs4           ? moe::launch_fs4_gateup(args, ws, s)
+        : stream      ? moe::launch_stream_gateup(args, ws, s)
         : args.nvfp4 ? moe::launch_fp4_gateup(args, ws, mt128, s)
                      : moe::launch_gemm_gateup(args, ws, mt, s);
     tm.stop();
     if (e != hipSuccess) return hip_fail(e, "gate/up");
   }
-  if (stream && !moe::stream_fused_geglu(sh, args.fp8)) {
+  if (stream && !fs4 && !moe::stream_fused_geglu(sh, args.fp8)) {
     // a GeGLU pass over the summed partials (otherwise the down units form
     // their rows themselves)
     StageTimer tm(h, MOE_FFN_STAGE_GEGLU, s, timing);
@@ -323,7 +326,8 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
       if (e != hipSuccess) return hip_fail(e, "activation quantiser");
     }
     moe::bf16_t* yd_direct = direct ? static_cast<moe::bf16_t*>(out) : nullptr;
-    e = stream        ? moe::launch_stream_down(args, ws, s)
+    e = fs4           ? moe::launch_fs4_down(args, ws, s)
+        : stream      ? moe::launch_stream_down(args, ws, s)
         : args.nvfp4 ? moe::launch_fp4_down(args, ws, mt128, s, yd_direct)
                      : moe::launch_gemm_down(args, ws, mt, s, yd_direct);
     tm.stop();
@@ -331,7 +335,7 @@ int run_forward(moe_ffn_handle* h, int T, const void* x, const void* router_w, c
   }
   if (!direct) {
     StageTimer tm(h, MOE_FFN_STAGE_COMBINE, s, timing);
-    const int yd_slices = stream && sh.D > 0 ? moe::dense_down_slices(sh) : 0;
+    const int yd_slices = stream && !fs4 && sh.D > 0 ? moe::dense_down_slices(sh) : 0;
     e = nm ? moe::launch_combine_norm(sh, ws, xres, nm->post, nm->eps, static_cast<moe::bf16_t*>(out), yd_slices,
                                       stream, s)
            : moe::launch_combine(sh, ws, static_cast<moe::bf16_t*>(out), (h->cfg.flags & MOE_FFN_ACCUMULATE) != 0,

@@ -210,6 +210,15 @@ hipError_t launch_fp4_gateup(const StreamArgs& a, const Workspace& ws, int max_t
 hipError_t launch_fp4_down(const StreamArgs& a, const Workspace& ws, int max_tiles128, hipStream_t s,
                            bf16_t* yd_out = nullptr);
 
+// NVFP4 weights streamed for few tokens (fp4stream.hip): the router runs
+// first (launch_route_small), then gate/up writes h / h_d (bf16, slot rows)
+// with the GeGLU, and down writes y (slot rows) and y_d in bf16, for the
+// combine with slot_rows and no dense slices.  fp4_stream_fits: the shape
+// and T these kernels take (T <= 64; H, I, D multiples of 64 up to 3072).
+bool fp4_stream_fits(const Shape& sh);
+hipError_t launch_fs4_gateup(const StreamArgs& a, const Workspace& ws, hipStream_t s);
+hipError_t launch_fs4_down(const StreamArgs& a, const Workspace& ws, hipStream_t s);
+
 // yd_slices: 0 = dense output in ws.y_d (bf16); n > 0 = n fp32 slices in
 // ws.ydp, summed in order (and stored to ws.y_d as bf16).  slot_rows: the
 // expert rows of token t are ws.y rows t*k .. t*k+k-1 (streaming path);

@@ -428,55 +428,6 @@ __device__ const float* unit8_x_rows(int nr, const uint8_t* w, int ldw, int kbeg
 // routing, derived in the block
 // ---------------------------------------------------------------------------
 
-// The rows of the ai-th expert that has tokens (experts in ascending id),
-// derived from topk_idx of the T <= 64 tokens by the block itself, so no
-// grouping tables (and no kernel to build them) are needed.  Row r is the
-// slot s = t * k + j of its r-th token t (ascending), j being the expert's
-// place in the token's list; slot[r] receives s.  Returns the expert id
-// (-1 when fewer than ai + 1 experts have tokens) and its row count.  Every
-// thread of the block must call it.
-struct ExpertRows {
-  int e, rows;
-};
-__device__ ExpertRows expert_rows(const Shape& sh, const int32_t* __restrict__ topk, int ai, int* slot) {
-  __shared__ unsigned long long mask[256];  // bit t: token t picked the expert
-  __shared__ unsigned long long pres[4];    // bit e: expert e has tokens
-  __shared__ int tk[kStreamRows];           // topk_idx, read from global memory once
-  const int tid = threadIdx.x, E = sh.E, k = sh.k, n = sh.T * sh.k;
-  for (int i = tid; i < E; i += kThreads) mask[i] = 0;
-  if (tid < 4) pres[tid] = 0;
-  __syncthreads();
-  for (int s = tid; s < n; s += kThreads) {
-    const int e = topk[s];
-    tk[s] = e;
-    atomicOr(&mask[e], 1ull << (s / k));
-    atomicOr(&pres[e >> 6], 1ull << (e & 63));
-  }
-  __syncthreads();
-  int e = -1, left = ai;  // block-uniform
-#pragma unroll
-  for (int wd = 0; wd < 4; ++wd) {
-    unsigned long long m = pres[wd];
-    const int c = __popcll(m);
-    if (e < 0 && left < c) {
-      for (int i = 0; i < left; ++i) m &= m - 1;
-      e = wd * 64 + __builtin_ctzll(m);
-    }
-    if (e < 0) left -= c;
-  }
-  e = __builtin_amdgcn_readfirstlane(e);
-  if (e < 0) return {-1, 0};
-  const unsigned long long m = mask[e];
-  if (tid < sh.T && ((m >> tid) & 1ull)) {
-    int j = 0;
-    for (int jj = 0; jj < k; ++jj)
-      if (tk[tid * k + jj] == e) j = jj;
-    slot[__popcll(m & ((1ull << tid) - 1ull))] = tid * k + j;
-  }
-  __syncthreads();
-  return {e, __builtin_amdgcn_readfirstlane(int(__popcll(m)))};
-}
-
 // ---------------------------------------------------------------------------
 // gate/up
 // ---------------------------------------------------------------------------

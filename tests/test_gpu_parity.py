@@ -352,14 +352,17 @@ def test_nvfp4_block(torch, T):
     full_check(s, x, w, None, out, r, inter, nvfp4_w=pk)
 
 
-def test_nvfp4_every_token_count(torch):
-    """NVFP4 weights streamed into registers at every T from 1 to 64 on one
-    handle, each forward checked in full: T <= 32 runs one 32-row tile per
-    expert with 2-wave column blocks, larger T the 128-row tiles."""
+@pytest.mark.parametrize("variant", [AUTO, MFMA, STREAM])
+def test_nvfp4_every_token_count(torch, variant):
+    """NVFP4 weights at every T from 1 to 64 on one handle, each forward
+    checked in full.  AUTO streams the packed weights (k_fs4_*) up to T = 32
+    and runs the register-fed MFMA tiles (k_fp4mm) above; MFMA runs the tiles
+    at every T (one 32-row tile per expert up to T = 32, 128-row tiles above);
+    STREAM streams at every T."""
     s64 = synth.FFNShape("mid_fp4", 64, 512, 32, 4, 128, 192, nvfp4=True)
     _, w, pk = nvfp4_inputs(s64, seed=9)
     from sparse_moe_transformer_amd import MoeFFN
-    ffn = MoeFFN.for_shape(s64, max_tokens=64)
+    ffn = MoeFFN.for_shape(s64, max_tokens=64, variant=variant)
     wd = G.up_nvfp4_weights(pk)
     for T in range(1, 65):
         s = s64.with_tokens(T)
@@ -372,11 +375,23 @@ def test_nvfp4_every_token_count(torch):
         full_check(s, x, w, None, G.to_f64(out), r, ffn.intermediates(T), nvfp4_w=pk)
 
 
-def test_nvfp4_decode_26b(torch):
+@pytest.mark.parametrize("T", [1, 16])
+def test_nvfp4_stream_wide_expert(torch, T):
+    """Streamed NVFP4 with an expert width of 1024: the down units' chunk
+    loads take several batches per column (the 26B shape needs one)."""
+    s = synth.FFNShape("wide_fp4", T, 512, 16, 2, 1024, 256, nvfp4=True)
+    x, w, pk = nvfp4_inputs(s, seed=40 + T)
+    out, r, inter, _ = run_gpu(torch, s, x, pk, None, STREAM, nvfp4=True)
+    full_check(s, x, w, None, out, r, inter, nvfp4_w=pk)
+
+
+@pytest.mark.parametrize("variant", [AUTO, MFMA])
+def test_nvfp4_decode_26b(torch, variant):
+    """The 26B NVFP4 layer at T = 8: streamed (AUTO) and on the MFMA tiles."""
     s = synth.NVFP4_STACK.with_tokens(8)
     x = synth.make_x(s)
     pk = synth.make_nvfp4_weights(s)
-    out, r, inter, _ = run_gpu(torch, s, x, pk, None, AUTO, nvfp4=True)
+    out, r, inter, _ = run_gpu(torch, s, x, pk, None, variant, nvfp4=True)
     full_check(s, x, pk, None, out, r, inter, nvfp4_w=pk)
 
 
