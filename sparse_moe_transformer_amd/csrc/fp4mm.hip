@@ -31,7 +31,8 @@
 //
 // Pipeline per 64-k step: the A rows of the step go global -> LDS by DMA
 // (buffer loads with the lds flag) D steps ahead; the weight codes and
-// scales of a step are loaded into registers PF steps ahead.  Every load is
+// scales of a step are loaded into registers PF steps ahead (decode-sized
+// tiles), or in bursts of 4 steps one burst ahead (128-row tiles).  Every load is
 // issued in every step (rows past a tile's end and columns past N get an
 // out-of-range offset: no memory access, zeros), so the wait counts are
 // constants.
@@ -45,6 +46,7 @@ namespace moe {
 namespace {
 
 constexpr int kStepK = 64;  // k per pipeline step
+constexpr int kBurst = 4;  // weight steps per load burst of the 128-row tiles
 constexpr int kXcd = 8;
 enum { FM_GATEUP = 0, FM_DOWN = 1 };
 
@@ -129,7 +131,29 @@ __device__ __forceinline__ void unroll(F&& f) {
   }
 }
 
-template <int MODE, int W, int NR, int PF, int D>
+// Weight loads in bursts (BS > 1): at each step s with s % BS == 0 a wave
+// loads the weights of steps s + BS .. s + 2 BS - 1, so the 2 BS 16-byte
+// pieces of one column's 128-byte code line that a burst covers are
+// requested together, and the 4 scale dwords of a column's BS = 4 steps are
+// one 16-byte load.  Per step the order is: wait, barrier, A copies of step
+// s + D - 1 (CA), then the burst if any (BS steps' code loads, then the
+// scale loads).  burst_wait(p): loads issued after
+// the last one that step s = q BS + p needs, in that steady order; the
+// prologue replays it exactly when D - 1 == BS.
+constexpr int burst_wait(int BS, int D, int CA, int NQ, int NS, int p) {
+  // a burst: BS steps of NQ code loads, then NS scale loads (one per group)
+  const int s = 8 * BS + p;  // any step past the prologue
+  const int burst = BS * NQ + NS;
+  auto issued = [&](int u) { return CA + (u % BS == 0 ? burst : 0); };  // loads issued in step u
+  int after_a = (((s - D + 1) % BS) == 0) ? burst : 0;                 // A(s) issued in step s - D + 1
+  for (int u = s - D + 2; u < s; ++u) after_a += issued(u);
+  const int b = (s / BS - 1) * BS;                                      // the burst holding step s
+  int after_b = (BS - 1 - p) * NQ;  // its code loads after step s's; its scales come last
+  for (int u = b + 1; u < s; ++u) after_b += issued(u);
+  return after_a < after_b ? after_a : after_b;
+}
+
+template <int MODE, int W, int NR, int PF, int D, int BS>
 __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0, int units_total) {
   constexpr int kRowsT = 32 * NR;         // rows of a tile
   constexpr int kAStage = kRowsT * 128;   // bytes of one A stage (64 k bf16 per row)
@@ -140,6 +164,8 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
   // later when PF <= D - 1, else A(s))
   constexpr int kWaitVm = (PF <= D - 1) ? (PF - 1) * (CA + NB) : NB + (D - 2) * (CA + NB);
   static_assert(kWaitVm < 64, "vmcnt range");
+  static_assert(BS == 1 || D - 1 == BS, "the burst prologue replays the steady order only for D - 1 == BS");
+  constexpr int kSlots = BS > 1 ? 2 * BS : PF + 1;  // weight register slots (slot = step % kSlots)
 
   // ---- logical unit of this block (XCD-aware remap over the real units)
   const int n1 = s1.tiles ? (*s1.n_tiles) * s1.nblk : units_total - units0;
@@ -242,10 +268,25 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // weight registers of PF + 1 steps (slot = step % (PF + 1))
-    u32x4_t bq[PF + 1][2];
-    uint32_t bs[PF + 1][2];
+    u32x4_t bq[kSlots][2];
+    uint32_t bs[kSlots][2];  // per step (BS == 1)
+    // BS > 1: the scale dwords of a burst's BS steps are one 16-byte load
+    // per column group, from step sbase[b] of the two bursts in flight (the
+    // first step, or nsteps - 4 near the end, so the load stays in the row)
+    u32x4_t bs4[2][2];
+    int sbase[2] = {0, 0};
 
+    auto load_q = [&](int st, u32x4_t (&q)[2]) {
+      const int s = min(st, nsteps - 1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) q[j] = bload<u32x4_t, 0>(qrs[j], uint32_t(qoff[j]), uint32_t(s * 32));
+    };
+    auto load_s4 = [&](int st, int bslot) {
+      const int b = max(0, min(st, nsteps - 4));
+      sbase[bslot] = b;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bs4[bslot][j] = bload<u32x4_t, 0>(srs[j], uint32_t(soff[j]), uint32_t(b * 4));
+    };
     auto load_b = [&](int st, u32x4_t (&q)[2], uint32_t (&sc)[2]) {
       const int s = min(st, nsteps - 1);
 #pragma unroll
@@ -257,26 +298,61 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
 
     // prologue: A of steps 0 .. D - 2, weights of steps 0 .. PF - 1, in the
     // per-iteration order (A first), so the constant waits hold from step 0
+    if constexpr (BS == 1) {
 #pragma unroll
-    for (int st = 0; st < (D - 1 > PF ? D - 1 : PF); ++st) {
-      if (st < D - 1) issue_a(st);
-      if (st < PF) load_b(st, bq[st], bs[st]);
+      for (int st = 0; st < (D - 1 > PF ? D - 1 : PF); ++st) {
+        if (st < D - 1) issue_a(st);
+        if (st < PF) load_b(st, bq[st], bs[st]);
+      }
+    } else {
+      // virtual steps -BS .. -1: A of steps 0 .. D - 2, the burst of steps
+      // 0 .. BS - 1 after the first
+#pragma unroll
+      for (int st = 0; st < D - 1; ++st) {
+        issue_a(st);
+        if (st == 0) {
+          unroll<BS>([&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            load_q(I, bq[I]);
+          });
+          load_s4(0, 0);
+        }
+      }
     }
 
     auto step = [&](int s, auto slot_c) {
-      constexpr int SL = decltype(slot_c)::value;                 // s % (PF + 1)
-      constexpr int SLN = (SL + PF) % (PF + 1);                    // slot of step s + PF
-      wait_vm<kWaitVm>();  // A and weights of step s landed (this wave's loads)
-      block_barrier();     // every wave's A copies of step s landed; step s - 1's slot is free
+      constexpr int SL = decltype(slot_c)::value;  // s % kSlots
+      constexpr int P = SL % BS;                   // position in the burst (BS > 1)
+      wait_vm<BS == 1 ? kWaitVm : burst_wait(BS, D, CA, 2, 2, P)>();  // A and weights of step s landed
+      block_barrier();  // every wave's A copies of step s landed; step s - 1's slot is free
       issue_a(s + D - 1);
-      load_b(s + PF, bq[SLN], bs[SLN]);
+      if constexpr (BS == 1) {
+        constexpr int SLN = (SL + PF) % (PF + 1);  // slot of step s + PF
+        load_b(s + PF, bq[SLN], bs[SLN]);
+      } else if constexpr (P == 0) {
+        // the slots of steps s + BS .. s + 2 BS - 1 held steps s - BS .. s - 1
+        unroll<BS>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          load_q(s + BS + I, bq[(SL + BS + I) % kSlots]);
+        });
+        load_s4(s + BS, ((SL + BS) / BS) % 2);
+      }
       if (NI == 0) return;
       // the group scales of k = 32 hf .. + 15 and + 16 .. + 31 are bytes
       // 2 hf and 2 hf + 1 of the scale dword
       float sa[2], sb[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t sw = bs[SL][j] >> (16 * hf);
+        uint32_t sd;
+        if constexpr (BS == 1) {
+          sd = bs[SL][j];
+        } else {
+          constexpr int B = (SL / BS) % 2;
+          const int e = s - sbase[B];  // 0 .. 3
+          const u32x4_t v = bs4[B][j];
+          sd = e == 0 ? v[0] : e == 1 ? v[1] : e == 2 ? v[2] : v[3];
+        }
+        const uint32_t sw = sd >> (16 * hf);
         sa[j] = e4m3_f32(sw & 0xFFu);
         sb[j] = e4m3_f32((sw >> 8) & 0xFFu);
       }
@@ -301,11 +377,11 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
       }
     };
 
-    for (int s0 = 0; s0 < nsteps; s0 += PF + 1) {
+    for (int t0 = 0; t0 < nsteps; t0 += kSlots) {
       // the register slot of each step is a compile-time index
-      unroll<PF + 1>([&](auto ic) {
+      unroll<kSlots>([&](auto ic) {
         constexpr int I = decltype(ic)::value;
-        if (s0 + I < nsteps) step(s0 + I, ic);
+        if (t0 + I < nsteps) step(t0 + I, ic);
       });
     }
     wait_vm<0>();  // no copy may still be landing when the block exits
@@ -346,7 +422,7 @@ F4Seg empty_seg() {
 // the two launch shapes: decode-sized row tiles (every expert's rows fit
 // one 32-row tile, 2-wave column blocks, weights 8 steps ahead) and 128-row
 // tiles with 8-wave column blocks
-template <int MODE, int W, int NR, int PF, int D>
+template <int MODE, int W, int NR, int PF, int D, int BS>
 hipError_t launch_shape(const F4Seg& d, const F4Seg& e, hipStream_t st) {
   constexpr int kRowsT = 32 * NR;
   const int ud = d.A ? ((d.host_rows + kRowsT - 1) / kRowsT) * d.nblk : 0;
@@ -354,7 +430,7 @@ hipError_t launch_shape(const F4Seg& d, const F4Seg& e, hipStream_t st) {
   const int total = ud + ue;
   if (total <= 0) return hipSuccess;
   const int per = (ud + kXcd - 1) / kXcd + (ue + kXcd - 1) / kXcd;
-  hipLaunchKernelGGL((k_fp4mm<MODE, W, NR, PF, D>), dim3(per * kXcd), dim3(W * 64), 0, st, d, e, ud, total);
+  hipLaunchKernelGGL((k_fp4mm<MODE, W, NR, PF, D, BS>), dim3(per * kXcd), dim3(W * 64), 0, st, d, e, ud, total);
   return hipGetLastError();
 }
 
@@ -404,7 +480,7 @@ hipError_t launch_fp4_gateup(const StreamArgs& a, const Workspace& ws, int max_t
     e.max_tiles = small ? std::min(sh.E, sh.T * sh.k) : max_tiles128;
     e.in_scale = a.in_scale;
   }
-  return small ? launch_shape<FM_GATEUP, 2, 1, 8, 6>(d, e, s) : launch_shape<FM_GATEUP, 8, 4, 6, 5>(d, e, s);
+  return small ? launch_shape<FM_GATEUP, 2, 1, 8, 6, 1>(d, e, s) : launch_shape<FM_GATEUP, 8, 4, 6, 5, kBurst>(d, e, s);
 }
 
 hipError_t launch_fp4_down(const StreamArgs& a, const Workspace& ws, int max_tiles128, hipStream_t s,
@@ -439,7 +515,7 @@ hipError_t launch_fp4_down(const StreamArgs& a, const Workspace& ws, int max_til
     e.max_tiles = small ? std::min(sh.E, sh.T * sh.k) : max_tiles128;
     e.in_scale = a.in_scale ? a.in_scale + 1 : nullptr;
   }
-  return small ? launch_shape<FM_DOWN, 2, 1, 8, 6>(d, e, s) : launch_shape<FM_DOWN, 8, 4, 6, 5>(d, e, s);
+  return small ? launch_shape<FM_DOWN, 2, 1, 8, 6, 1>(d, e, s) : launch_shape<FM_DOWN, 8, 4, 6, 5, kBurst>(d, e, s);
 }
 
 }  // namespace moe
