@@ -65,6 +65,7 @@ constexpr int kFsRows = 4;  // activation rows per pass
 constexpr int kGuJB = 2;
 constexpr int kGuGroups = 1;
 constexpr int kGuUnitCols = 16 * kGuGroups;
+constexpr int kGuDepth = 2;  // steps in the register ring
 // down: a step is kDnJB chunks of each of the lane's kDnNC columns; a group
 // is 8 kDnNC columns per wave (32 kDnNC per block); routed units are
 // kDnGroups groups, dense units (K = D, three times longer here) kDdGroups
@@ -73,6 +74,7 @@ constexpr int kDnNC = 1;
 constexpr int kDnGroups = 2;
 constexpr int kDdGroups = 1;
 constexpr int kDnGroupCols = 32 * kDnNC;
+constexpr int kDnDepth = 2;
 
 // Stage rows [c0, c0 + nr) of the activation matrix into xs[r][0..K) (bf16):
 // row r is src + idx(r) * ld.  16 bytes per thread per step.
@@ -190,10 +192,22 @@ __device__ __forceinline__ void compute_step(float (&acc)[NC][NR], const StepBuf
   }
 }
 
-// Runs the steps of one row pass: stage() stages the pass's rows into xs
-// (after the first step's loads are issued) and emit(g, acc) receives each
-// group's sums (per lane, not yet folded over the chunk lanes).
-template <int NC, int JB, int NR, class Col, class Stage, class Emit>
+// f(integral_constant<0>) .. f(integral_constant<N - 1>), in order
+template <int N, class F>
+__device__ __forceinline__ void static_for(const F& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+// Runs the steps of one row pass, DEPTH - 1 steps' loads in flight ahead of
+// the one computed (a ring of DEPTH register buffers): stage() stages the
+// pass's rows into xs after the first loads are issued, and emit(g, acc)
+// receives each group's sums (per lane, not yet folded over the chunk
+// lanes).  The loop runs whole rounds of DEPTH steps and issues a step's
+// loads in every slot (past the last step, the last one again, unused).
+template <int NC, int JB, int NR, int DEPTH, class Col, class Stage, class Emit>
 __device__ __forceinline__ void run_steps(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs, int K, int G,
                                           const bf16_t* xs, const Col& col, const Stage& stage, const Emit& emit) {
   const int l = threadIdx.x & 7;
@@ -204,28 +218,29 @@ __device__ __forceinline__ void run_steps(__amdgpu_buffer_rsrc_t rq, __amdgpu_bu
   for (int m = 0; m < NC; ++m)
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[m][r] = 0.f;
-  StepBuf<NC, JB> A, B;
-  issue_step(A, rq, rs, K, nq, nb, 0, l, col);
+  StepBuf<NC, JB> buf[DEPTH];
+  static_for<DEPTH - 1>([&](auto ic) {
+    constexpr int I = decltype(ic)::value;
+    issue_step(buf[I], rq, rs, K, nq, nb, min(I, S - 1), l, col);
+  });
   stage();
   __syncthreads();
-  auto finish = [&](int step) {
-    if (step % nb == nb - 1) {
-      emit(step / nb, acc);
+  for (int s0 = 0; s0 < S; s0 += DEPTH) {
+    static_for<DEPTH>([&](auto ic) {
+      constexpr int I = decltype(ic)::value;
+      const int s = s0 + I;
+      issue_step(buf[(I + DEPTH - 1) % DEPTH], rq, rs, K, nq, nb, min(s + DEPTH - 1, S - 1), l, col);
+      if (s < S) {
+        compute_step<NC, JB, NR>(acc, buf[I], nq, nb, s, l, xs, K);
+        if (s % nb == nb - 1) {
+          emit(s / nb, acc);
 #pragma unroll
-      for (int m = 0; m < NC; ++m)
+          for (int m = 0; m < NC; ++m)
 #pragma unroll
-        for (int r = 0; r < NR; ++r) acc[m][r] = 0.f;
-    }
-  };
-  for (int s = 0; s < S; s += 2) {
-    issue_step(B, rq, rs, K, nq, nb, min(s + 1, S - 1), l, col);
-    compute_step<NC, JB, NR>(acc, A, nq, nb, s, l, xs, K);
-    finish(s);
-    if (s + 1 < S) {
-      issue_step(A, rq, rs, K, nq, nb, min(s + 2, S - 1), l, col);
-      compute_step<NC, JB, NR>(acc, B, nq, nb, s + 1, l, xs, K);
-      finish(s + 1);
-    }
+            for (int r = 0; r < NR; ++r) acc[m][r] = 0.f;
+        }
+      }
+    });
   }
 }
 
@@ -312,7 +327,7 @@ __global__ __launch_bounds__(kFsThreads) __attribute__((amdgpu_waves_per_eu(5, 8
         if (l == r && r < nr) gs[mi][r][16 * g + 8 * wm + c] = v;
       }
     };
-    with_rows(nr, [&](auto nrc) { run_steps<1, kGuJB, decltype(nrc)::value>(rq, rs, K, kGuGroups, xs, col, stage, emit); });
+    with_rows(nr, [&](auto nrc) { run_steps<1, kGuJB, decltype(nrc)::value, kGuDepth>(rq, rs, K, kGuGroups, xs, col, stage, emit); });
     __syncthreads();  // gs complete; xs free
     for (int i = threadIdx.x; i < nr * ncols; i += kFsThreads) {
       const int r = i / ncols, cc = i - r * ncols;
@@ -356,7 +371,7 @@ __device__ __forceinline__ void down_unit(const Fp4Mat& M, long long mat, int K,
           if (l == r && r < nr) ys[r][kDnGroupCols * g + 8 * kDnNC * wave + 8 * m + c] = bf16_t(f32_to_bf16_bits(v));
         }
     };
-    with_rows(nr, [&](auto nrc) { run_steps<kDnNC, kDnJB, decltype(nrc)::value>(rq, rs, K, G, xs, col, stage, emit); });
+    with_rows(nr, [&](auto nrc) { run_steps<kDnNC, kDnJB, decltype(nrc)::value, kDnDepth>(rq, rs, K, G, xs, col, stage, emit); });
     __syncthreads();
     for (int i = threadIdx.x; i < nr * ncols; i += kFsThreads) {
       const int r = i / ncols, cc = i - r * ncols;

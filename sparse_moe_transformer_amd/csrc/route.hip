@@ -205,8 +205,8 @@ __global__ __launch_bounds__(kThreads) void k_topk(Shape sh, int nslices, const 
   wave_route_token(zs[wid], E, sh.k, ws.topk_idx + size_t(t) * sh.k, ws.topk_w + size_t(t) * sh.k);
 }
 
-// Large-T router with E = 128 or 256: one block of 4 waves per 32 tokens
-// computes their logits over all of K with v_mfma_f32_32x32x16_bf16 and
+// Large-T router with E = 128 or 256: one block of 4 waves per 16 or 32
+// tokens computes their logits over all of K with v_mfma_f32_32x32x16_bf16 and
 // routes them, so no partial logits go through memory.  Per 64-k step the
 // x rows ([32][64] bf16, 128 B rows) and the W_r rows ([64][E], split in
 // 128-column halves of 256 B rows) go global -> LDS by DMA (buffer loads
@@ -215,10 +215,16 @@ __global__ __launch_bounds__(kThreads) void k_topk(Shape sh, int nslices, const 
 // c of k row at c ^ 4 (k % 4)).  The MFMA B operand (8 consecutive k of one
 // expert per lane) is read with the gfx950 transposing LDS read.  Wave w
 // owns experts 32 w .. + 31 of each half.  Then the logits (+ bias) go to
-// LDS and each wave routes 8 tokens (wave_route_token).
+// LDS and each wave routes a quarter of the block's tokens (wave_route_token).
 constexpr int kRmStep = 64;  // k per step
-constexpr int kRouteFusedMinT = 8192;
-constexpr int kRmDepth = 4;  // LDS stages
+constexpr int kRmDepth = 4;  // LDS stages (6 measured slower: fewer blocks per CU)
+// T from which the one-launch router replaces the split-K logits and the
+// per-token top-k, and from which its blocks take 32 tokens instead of 16
+// (the rows past 16 are zeros in the 32-row MFMA; at T = 4096 the 16-token
+// blocks fill all CUs: 38 us against 56 us with 32-token blocks and 47 us
+// split; at T = 16384 the 32-token blocks: 73 us against 89 us)
+constexpr int kRouteFusedMinT = 4096;
+constexpr int kRouteFused32T = 8192;
 
 typedef int i32x4v_t __attribute__((ext_vector_type(4)));
 typedef short s16x4v_t __attribute__((ext_vector_type(4)));
@@ -243,7 +249,7 @@ __device__ __forceinline__ void rm_wait() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int NH>  // 128-column halves of E
+template <int NH, int TOK>  // 128-column halves of E; tokens per block (16 or 32)
 __global__ __launch_bounds__(256) void k_route_mfma(Shape sh, const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr,
                                                     const float* __restrict__ bias, Workspace ws) {
   constexpr int E = 128 * NH;
@@ -260,7 +266,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(Shape sh, const bf16_t* __re
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, lc = lane & 31;
-  const int t0 = blockIdx.x * 32;
+  const int t0 = blockIdx.x * TOK;
   const int H = sh.H, nsteps = H / kRmStep;
 
   // x copy of wave w: rows 8 w .. + 7; lane: row 8 w + lane / 8, slot lane % 8
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(Shape sh, const bf16_t* __re
   int xoff;
   {
     const int r = 8 * wave + (lane >> 3);
-    xoff = t0 + r < sh.T ? int((uint32_t(t0 + r) * uint32_t(H) + uint32_t(((lane & 7) ^ (r & 7)) * 8)) * 2u)
+    xoff = r < TOK && t0 + r < sh.T ? int((uint32_t(t0 + r) * uint32_t(H) + uint32_t(((lane & 7) ^ (r & 7)) * 8)) * 2u)
                          : int(0x80000000u);  // past T: out of range, zeros
   }
   // W_r copy q of wave w: k rows 4 (CB w + q) .. + 3 of the step, across the
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(Shape sh, const bf16_t* __re
     for (int r = 0; r < 16; ++r) zs[(8 * (r >> 2) + 4 * hf + (r & 3)) * E + e] = acc[j][r] + b;
   }
   __syncthreads();
-  for (int t = wave; t < 32 && t0 + t < sh.T; t += 4)
+  for (int t = wave; t < TOK && t0 + t < sh.T; t += 4)
     wave_route_token(zs + t * E, E, sh.k, ws.topk_idx + size_t(t0 + t) * sh.k, ws.topk_w + size_t(t0 + t) * sh.k);
 }
 
@@ -429,14 +435,18 @@ hipError_t launch_gemm_router(const Shape& sh, const bf16_t* x, const bf16_t* wr
 hipError_t launch_route_large(const Shape& sh, const bf16_t* x, const bf16_t* wr, const float* bias,
                               const Workspace& ws, hipStream_t s) {
   if ((sh.E == 128 || sh.E == 256) && sh.H % kRmStep == 0 && sh.T >= kRouteFusedMinT) {
-    // logits and routing in one launch, 32 tokens per block (measured:
-    // faster than the split-K logits and the per-token top-k from about
-    // T = 8192 on; below that its few blocks leave most CUs idle)
-    const dim3 grid((sh.T + 31) / 32);
-    if (sh.E == 128)
-      hipLaunchKernelGGL(k_route_mfma<1>, grid, dim3(256), 0, s, sh, x, wr, bias, ws);
+    // logits and routing in one launch (below kRouteFusedMinT its blocks
+    // leave CUs idle and the split-K path is faster)
+    const bool t32 = sh.T >= kRouteFused32T;
+    const dim3 grid((sh.T + (t32 ? 31 : 15)) / (t32 ? 32 : 16));
+    if (sh.E == 128 && t32)
+      hipLaunchKernelGGL((k_route_mfma<1, 32>), grid, dim3(256), 0, s, sh, x, wr, bias, ws);
+    else if (sh.E == 128)
+      hipLaunchKernelGGL((k_route_mfma<1, 16>), grid, dim3(256), 0, s, sh, x, wr, bias, ws);
+    else if (t32)
+      hipLaunchKernelGGL((k_route_mfma<2, 32>), grid, dim3(256), 0, s, sh, x, wr, bias, ws);
     else
-      hipLaunchKernelGGL(k_route_mfma<2>, grid, dim3(256), 0, s, sh, x, wr, bias, ws);
+      hipLaunchKernelGGL((k_route_mfma<2, 16>), grid, dim3(256), 0, s, sh, x, wr, bias, ws);
     return hipGetLastError();
   }
   int nslices = 1;

@@ -150,14 +150,15 @@ def test_mfma_router_and_bias(torch, T):
 
 @pytest.mark.parametrize("H,E,k,T", [(512, 4, 2, 5), (2816, 256, 8, 8), (512, 24, 3, 7), (512, 16, 4, 8),
                                      (256, 8, 8, 8), (2816, 172, 8, 8), (2304, 212, 8, 5), (512, 256, 8, 200),
-                                     (512, 128, 8, 97), (512, 256, 8, 8200), (256, 128, 4, 8195)])
+                                     (512, 128, 8, 97), (512, 256, 8, 8200), (256, 128, 4, 8195),
+                                     (512, 256, 8, 4099), (256, 128, 4, 4100)])
 def test_router_shapes(torch, H, E, k, T):
     """Small-T router variants: 8-expert chunks (E/8 a power of two, several
     row batches at E = 256), and the per-expert path for other E.  Two
     shapes (wide H, E not a multiple of 8) do not fit the small-T router's
-    launch shape: they route with the large-T kernels.  T >= 8192 with
-    E = 128 or 256 takes the one-launch MFMA router (32 tokens per block,
-    ragged last block)."""
+    launch shape: they route with the large-T kernels.  T >= 4096 with
+    E = 128 or 256 takes the one-launch MFMA router (16 tokens per block
+    below T = 8192, 32 from there; ragged last blocks)."""
     s = synth.FFNShape("rt", T, H, E, k, 64, 64)
     x, w, _ = G.make_inputs(s, seed=E)
     out, r, inter, _ = run_gpu(torch, s, x, w, None, AUTO)
