@@ -32,7 +32,9 @@
 // Pipeline per 64-k step: the A rows of the step go global -> LDS by DMA
 // (buffer loads with the lds flag) D steps ahead; the weight codes and
 // scales of a step are loaded into registers PF steps ahead (decode-sized
-// tiles), or in bursts of 4 steps one burst ahead (128-row tiles).  Every load is
+// tiles), or in bursts of 2 steps one burst ahead (128-row tiles; 3 A stages:
+// the shallower ring leaves registers to the scheduler, 190 us per gate/up
+// launch at T = 1024 against 196 with bursts of 4 and 5 stages).  Every load is
 // issued in every step (rows past a tile's end and columns past N get an
 // out-of-range offset: no memory access, zeros), so the wait counts are
 // constants.
@@ -46,7 +48,7 @@ namespace moe {
 namespace {
 
 constexpr int kStepK = 64;  // k per pipeline step
-constexpr int kBurst = 4;  // weight steps per load burst of the 128-row tiles
+constexpr int kBurst = 2;  // weight steps per load burst of the 128-row tiles (A: kBurst + 1 LDS stages)
 constexpr int kXcd = 8;
 enum { FM_GATEUP = 0, FM_DOWN = 1 };
 
@@ -134,21 +136,22 @@ __device__ __forceinline__ void unroll(F&& f) {
 // Weight loads in bursts (BS > 1): at each step s with s % BS == 0 a wave
 // loads the weights of steps s + BS .. s + 2 BS - 1, so the 2 BS 16-byte
 // pieces of one column's 128-byte code line that a burst covers are
-// requested together, and the 4 scale dwords of a column's BS = 4 steps are
+// requested together, and the scale dwords of a column's BS <= 4 steps are
 // one 16-byte load.  Per step the order is: wait, barrier, A copies of step
-// s + D - 1 (CA), then the burst if any (BS steps' code loads, then the
-// scale loads).  burst_wait(p): loads issued after
+// s + D - 1 (CA), then the burst if any (the scale loads, then BS steps'
+// code loads).  burst_wait(p): loads issued after
 // the last one that step s = q BS + p needs, in that steady order; the
 // prologue replays it exactly when D - 1 == BS.
 constexpr int burst_wait(int BS, int D, int CA, int NQ, int NS, int p) {
-  // a burst: BS steps of NQ code loads, then NS scale loads (one per group)
+  // a burst: NS scale loads (one per group, all its steps), then BS steps of
+  // NQ code loads; step p of it needs the scales and its own codes
   const int s = 8 * BS + p;  // any step past the prologue
   const int burst = BS * NQ + NS;
   auto issued = [&](int u) { return CA + (u % BS == 0 ? burst : 0); };  // loads issued in step u
   int after_a = (((s - D + 1) % BS) == 0) ? burst : 0;                 // A(s) issued in step s - D + 1
   for (int u = s - D + 2; u < s; ++u) after_a += issued(u);
   const int b = (s / BS - 1) * BS;                                      // the burst holding step s
-  int after_b = (BS - 1 - p) * NQ;  // its code loads after step s's; its scales come last
+  int after_b = (BS - 1 - p) * NQ;  // the burst's code loads after step s's (its scales came first)
   for (int u = b + 1; u < s; ++u) after_b += issued(u);
   return after_a < after_b ? after_a : after_b;
 }
@@ -165,6 +168,7 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
   constexpr int kWaitVm = (PF <= D - 1) ? (PF - 1) * (CA + NB) : NB + (D - 2) * (CA + NB);
   static_assert(kWaitVm < 64, "vmcnt range");
   static_assert(BS == 1 || D - 1 == BS, "the burst prologue replays the steady order only for D - 1 == BS");
+  static_assert(BS <= 4, "a burst's scale dwords are one 16-byte load");
   constexpr int kSlots = BS > 1 ? 2 * BS : PF + 1;  // weight register slots (slot = step % kSlots)
 
   // ---- logical unit of this block (XCD-aware remap over the real units)
@@ -311,11 +315,11 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
       for (int st = 0; st < D - 1; ++st) {
         issue_a(st);
         if (st == 0) {
+          load_s4(0, 0);
           unroll<BS>([&](auto ic) {
             constexpr int I = decltype(ic)::value;
             load_q(I, bq[I]);
           });
-          load_s4(0, 0);
         }
       }
     }
@@ -331,11 +335,11 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
         load_b(s + PF, bq[SLN], bs[SLN]);
       } else if constexpr (P == 0) {
         // the slots of steps s + BS .. s + 2 BS - 1 held steps s - BS .. s - 1
+        load_s4(s + BS, ((SL + BS) / BS) % 2);
         unroll<BS>([&](auto ic) {
           constexpr int I = decltype(ic)::value;
           load_q(s + BS + I, bq[(SL + BS + I) % kSlots]);
         });
-        load_s4(s + BS, ((SL + BS) / BS) % 2);
       }
       if (NI == 0) return;
       // the group scales of k = 32 hf .. + 15 and + 16 .. + 31 are bytes
@@ -480,7 +484,7 @@ hipError_t launch_fp4_gateup(const StreamArgs& a, const Workspace& ws, int max_t
     e.max_tiles = small ? std::min(sh.E, sh.T * sh.k) : max_tiles128;
     e.in_scale = a.in_scale;
   }
-  return small ? launch_shape<FM_GATEUP, 2, 1, 8, 6, 1>(d, e, s) : launch_shape<FM_GATEUP, 8, 4, 6, 5, kBurst>(d, e, s);
+  return small ? launch_shape<FM_GATEUP, 2, 1, 8, 6, 1>(d, e, s) : launch_shape<FM_GATEUP, 8, 4, 6, kBurst + 1, kBurst>(d, e, s);
 }
 
 hipError_t launch_fp4_down(const StreamArgs& a, const Workspace& ws, int max_tiles128, hipStream_t s,
@@ -515,7 +519,7 @@ hipError_t launch_fp4_down(const StreamArgs& a, const Workspace& ws, int max_til
     e.max_tiles = small ? std::min(sh.E, sh.T * sh.k) : max_tiles128;
     e.in_scale = a.in_scale ? a.in_scale + 1 : nullptr;
   }
-  return small ? launch_shape<FM_DOWN, 2, 1, 8, 6, 1>(d, e, s) : launch_shape<FM_DOWN, 8, 4, 6, 5, kBurst>(d, e, s);
+  return small ? launch_shape<FM_DOWN, 2, 1, 8, 6, 1>(d, e, s) : launch_shape<FM_DOWN, 8, 4, 6, kBurst + 1, kBurst>(d, e, s);
 }
 
 }  // namespace moe
