@@ -156,6 +156,57 @@ constexpr int burst_wait(int BS, int D, int CA, int NQ, int NS, int p) {
   return after_a < after_b ? after_a : after_b;
 }
 
+// Proof at compile time that the constant waits are enough: replay the
+// issue sequence of the first 8 rounds (prologue included) and check at
+// every step that the wait leaves no load outstanding that the step reads.
+// Loads are tagged by kind (A copy, weight codes, weight scales) and step.
+// BS == 1: the per-step order (A copies, then per group codes and scales of
+// step s + PF) with the wait w1; BS > 1: the burst order above.
+constexpr bool waits_cover(int BS, int D, int PF, int CA, int NQ, int NS, int w1) {
+  constexpr int kMax = 4096;
+  int kind[kMax] = {}, step[kMax] = {};  // kind: 0 A, 1 codes, 2 scales
+  int n = 0;
+  auto push = [&](int k, int st, int count) {
+    for (int i = 0; i < count; ++i) {
+      kind[n] = k;
+      step[n] = st;
+      ++n;
+    }
+  };
+  auto burst = [&](int b) {
+    push(2, b, NS);
+    for (int i = 0; i < BS; ++i) push(1, b + i, NQ);
+  };
+  const int rounds = 8 * (BS > 1 ? 2 * BS : PF + 1);
+  if (BS == 1) {
+    for (int st = 0; st < (D - 1 > PF ? D - 1 : PF); ++st) {
+      if (st < D - 1) push(0, st, CA);
+      if (st < PF) push(1, st, NQ + NS);
+    }
+  } else {
+    for (int st = 0; st < D - 1; ++st) {
+      push(0, st, CA);
+      if (st == 0) burst(0);
+    }
+  }
+  for (int s = 0; s < rounds; ++s) {
+    const int w = BS == 1 ? w1 : burst_wait(BS, D, CA, NQ, NS, s % BS);
+    int last = -1;
+    for (int i = 0; i < n; ++i) {
+      const bool needed = (kind[i] == 0 && step[i] == s) || (kind[i] == 1 && step[i] == s) ||
+                          (kind[i] == 2 && (BS == 1 ? step[i] == s : step[i] == s - s % BS));
+      if (needed) last = i;
+    }
+    if (last < 0 || n - 1 - last < w) return false;  // a needed load could still be in flight
+    push(0, s + D - 1, CA);
+    if (BS == 1)
+      push(1, s + PF, NQ + NS);
+    else if (s % BS == 0)
+      burst(s + BS);
+  }
+  return true;
+}
+
 template <int MODE, int W, int NR, int PF, int D, int BS>
 __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0, int units_total) {
   constexpr int kRowsT = 32 * NR;         // rows of a tile
@@ -169,6 +220,7 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
   static_assert(kWaitVm < 64, "vmcnt range");
   static_assert(BS == 1 || D - 1 == BS, "the burst prologue replays the steady order only for D - 1 == BS");
   static_assert(BS <= 4, "a burst's scale dwords are one 16-byte load");
+  static_assert(waits_cover(BS, D, PF, (32 * NR * 128) / 1024 / W, 2, 2, kWaitVm), "a step's wait leaves a needed load in flight");
   constexpr int kSlots = BS > 1 ? 2 * BS : PF + 1;  // weight register slots (slot = step % kSlots)
 
   // ---- logical unit of this block (XCD-aware remap over the real units)
