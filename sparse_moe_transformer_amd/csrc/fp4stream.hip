@@ -60,8 +60,9 @@ namespace {
 constexpr int kFsThreads = 256;
 constexpr int kPolicyNT = 2;  // nontemporal: the weights are read once
 constexpr int kFsRows = 4;  // activation rows per pass
-// gate/up: a step is kGuJB chunks of the lane's column; a group is 4 columns
-// per wave (16 per block); a unit is kGuGroups groups
+// gate/up: a step is kGuJB chunks of the lane's column; a group is 8
+// columns per wave, 16 per block (waves 0-1 gate, 2-3 up, same columns); a
+// unit is kGuGroups groups
 constexpr int kGuJB = 2;
 constexpr int kGuGroups = 1;
 constexpr int kGuUnitCols = 16 * kGuGroups;
@@ -343,8 +344,8 @@ __global__ __launch_bounds__(kFsThreads) __attribute__((amdgpu_waves_per_eu(5, 8
 // ---------------------------------------------------------------------------
 
 // Unit of G groups from column n0 (a group: kDnGroupCols columns, wave w's
-// part 16 w .. 16 w + 15, lane column 8 m + c); rows src[idx(r)] of length K;
-// output rows out[idx(r)] of length N (bf16).
+// part 8 kDnNC w .. + 8 kDnNC - 1, lane column 8 m + c of it); rows
+// src[idx(r)] of length K; output rows out[idx(r)] of length N (bf16).
 template <class Idx>
 __device__ __forceinline__ void down_unit(const Fp4Mat& M, long long mat, int K, int N, int n0, int G, float ts,
                                           const bf16_t* __restrict__ src, int rows, const Idx& idx,
