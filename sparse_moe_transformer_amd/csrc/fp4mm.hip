@@ -218,6 +218,10 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
   // later when PF <= D - 1, else A(s))
   constexpr int kWaitVm = (PF <= D - 1) ? (PF - 1) * (CA + NB) : NB + (D - 2) * (CA + NB);
   static_assert(kWaitVm < 64, "vmcnt range");
+  // a wave that copies A only: at step s's wait its copies of steps s + 1 ..
+  // s + D - 2 may stay in flight
+  constexpr int kWaitA = CA * (D - 2);
+  static_assert(D >= 2 && kWaitA < 64, "A ring depth");
   static_assert(BS == 1 || D - 1 == BS, "the burst prologue replays the steady order only for D - 1 == BS");
   static_assert(BS <= 4, "a burst's scale dwords are one 16-byte load");
   static_assert(waits_cover(BS, D, PF, (32 * NR * 128) / 1024 / W, 2, 2, kWaitVm), "a step's wait leaves a needed load in flight");
@@ -261,7 +265,9 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
 
   // ---- A copies: copy q of wave w fills tile rows 8 (CA w + q) .. + 7 of a
   // stage; lane: row + lane / 8, LDS chunk lane % 8 <- global chunk
-  // (lane % 8) ^ (row % 8) (the XOR spreads the fragment reads over the banks)
+  // (lane % 8) ^ ((row / 2) % 8): the XOR spreads the fragment reads over the
+  // banks (the two 128-byte rows of a 256-byte span share it; with
+  // row % 8 the reads measured half the full LDS rate on gfx950)
   const i32x4_t arsrc = rsrc4(S.A);
   int aoff[CA];
 #pragma unroll
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
     const int r = 8 * (CA * wave + q) + (lane >> 3);
     const int rr = r < rows ? r : 0;
     const uint32_t gr = S.gather ? uint32_t(S.gather[row0 + rr]) : uint32_t(row0 + rr);
-    aoff[q] = r < rows ? int((gr * uint32_t(S.lda) + uint32_t(((lane & 7) ^ (r & 7)) * 8)) * 2u) : kOutOfRange;
+    aoff[q] = r < rows ? int((gr * uint32_t(S.lda) + uint32_t(((lane & 7) ^ ((r >> 1) & 7)) * 8)) * 2u) : kOutOfRange;
   }
 
   // ---- B: column group j of this wave: gate/up: gate (j = 0) and up (j = 1)
@@ -353,8 +359,17 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
     };
 
     // prologue: A of steps 0 .. D - 2, weights of steps 0 .. PF - 1, in the
-    // per-iteration order (A first), so the constant waits hold from step 0
-    if constexpr (BS == 1) {
+    // per-iteration order (A first), so the constant waits hold from step 0.
+    // A wave with no valid column group (NI == 0) still copies its share of
+    // every A stage for the others but loads no weights: the compiler would
+    // delete loads whose results are never used, and the waits that count
+    // them would then let the wave reach the barrier with its A copies still
+    // in flight.  Such a wave issues A copies only and waits with its own
+    // count (kWaitA).
+    if constexpr (NI == 0) {
+#pragma unroll
+      for (int st = 0; st < D - 1; ++st) issue_a(st);
+    } else if constexpr (BS == 1) {
 #pragma unroll
       for (int st = 0; st < (D - 1 > PF ? D - 1 : PF); ++st) {
         if (st < D - 1) issue_a(st);
@@ -379,10 +394,12 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
     auto step = [&](int s, auto slot_c) {
       constexpr int SL = decltype(slot_c)::value;  // s % kSlots
       constexpr int P = SL % BS;                   // position in the burst (BS > 1)
-      wait_vm<BS == 1 ? kWaitVm : burst_wait(BS, D, CA, 2, 2, P)>();  // A and weights of step s landed
+      wait_vm<NI == 0 ? kWaitA : BS == 1 ? kWaitVm : burst_wait(BS, D, CA, 2, 2, P)>();  // A and weights of step s landed
       block_barrier();  // every wave's A copies of step s landed; step s - 1's slot is free
       issue_a(s + D - 1);
-      if constexpr (BS == 1) {
+      if constexpr (NI == 0) {
+        return;
+      } else if constexpr (BS == 1) {
         constexpr int SLN = (SL + PF) % (PF + 1);  // slot of step s + PF
         load_b(s + PF, bq[SLN], bs[SLN]);
       } else if constexpr (P == 0) {
@@ -393,7 +410,6 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
           load_q(s + BS + I, bq[(SL + BS + I) % kSlots]);
         });
       }
-      if (NI == 0) return;
       // the group scales of k = 32 hf .. + 15 and + 16 .. + 31 are bytes
       // 2 hf and 2 hf + 1 of the scale dword
       float sa[2], sb[2];
@@ -425,7 +441,7 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
         for (int rb = 0; rb < NI; ++rb) {
           const int r = 32 * rb + lc;
           const bf16x8_t a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-              abase + r * 128 + (((4 * hf + i) ^ (r & 7)) << 4));
+              abase + r * 128 + (((4 * hf + i) ^ ((r >> 1) & 7)) << 4));
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[rb][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[j], acc[rb][j], 0, 0, 0);

@@ -30,7 +30,12 @@
 //
 // LDS layouts (16-byte chunks XOR-swizzled so that every fragment read and
 // every copy touches the bank groups evenly):
-//   A  [320 rows][32 k]: 64 B per row, chunk c of row r at c ^ fa(r).
+//   A  [320 rows][32 k]: 64 B per row, chunk c of row r at c ^ fa(r), with
+//      fa(r) = (r / 4) % 4: the four rows that share a 256-byte span take
+//      the same XOR, and the next four another (measured on gfx950 at the
+//      full 128-bit LDS read rate, ~244 B per clock per CU, for every
+//      fragment row base the tile uses; an XOR that also varies inside a
+//      4-row span, such as (r / 2) % 4, measured half of it)
 //   B  bf16 weights are [K, N] (N contiguous) and stay so in LDS: two halves
 //      (gate / up, or columns 0-127 / 128-255) of [32 k][128 n], 256 B per k
 //      row, chunk c of row k at c ^ fb(k).  The MFMA B operand (8
@@ -175,7 +180,7 @@ __device__ __forceinline__ void wait_counts() {
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // swizzled chunk positions (see the header)
-__device__ __forceinline__ int fa(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int fa(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int fb(int k) { return 4 * (k & 3); }
 
 template <int MODE, int WF>

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(Shape sh, int nslices, const 
 // x rows ([32][64] bf16, 128 B rows) and the W_r rows ([64][E], split in
 // 128-column halves of 256 B rows) go global -> LDS by DMA (buffer loads
 // with the lds flag) three steps ahead; 16-byte chunks are XOR-swizzled as
-// in the grouped GEMM tiles (x: chunk c of row r at c ^ (r % 8); W_r: chunk
+// in the grouped GEMM tiles (x: chunk c of row r at c ^ ((r / 2) % 8); W_r: chunk
 // c of k row at c ^ 4 (k % 4)).  The MFMA B operand (8 consecutive k of one
 // expert per lane) is read with the gfx950 transposing LDS read.  Wave w
 // owns experts 32 w .. + 31 of each half.  Then the logits (+ bias) go to
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(Shape sh, const bf16_t* __re
   int xoff;
   {
     const int r = 8 * wave + (lane >> 3);
-    xoff = r < TOK && t0 + r < sh.T ? int((uint32_t(t0 + r) * uint32_t(H) + uint32_t(((lane & 7) ^ (r & 7)) * 8)) * 2u)
+    xoff = r < TOK && t0 + r < sh.T ? int((uint32_t(t0 + r) * uint32_t(H) + uint32_t(((lane & 7) ^ ((r >> 1) & 7)) * 8)) * 2u)
                          : int(0x80000000u);  // past T: out of range, zeros
   }
   // W_r copy q of wave w: k rows 4 (CB w + q) .. + 3 of the step, across the
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(Shape sh, const bf16_t* __re
       rm_copy(wrs, sb + kA + (c >> 4) * (kRmStep * 256) + (c & 15) * 1024, woff[q], kk * E * 2);
     }
   };
-  // fragment addresses: A row lc, k-step i: chunk (2 i + hf) ^ (lc % 8);
+  // fragment addresses: A row lc, k-step i: chunk (2 i + hf) ^ ((lc / 2) % 8);
   // B (half j, columns 32 wave ..): as in the grouped GEMM's transposing reads
   int bfr;
   {
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(Shape sh, const bf16_t* __re
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bf16x8_t a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-          sa + lc * 128 + (((2 * i + hf) ^ (lc & 7)) << 4));
+          sa + lc * 128 + (((2 * i + hf) ^ ((lc >> 1) & 7)) << 4));
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
         const lds_u8* p = sbp + j * (kRmStep * 256) + bfr + i * 16 * 256;

@@ -415,6 +415,44 @@ def test_nvfp4_26b(torch):
     print(f"nvfp4 26B layer near-ties: {near}")
 
 
+@pytest.mark.parametrize("case", ["26b_t1024", "ragged"])
+def test_nvfp4_repeatable(torch, case):
+    """NVFP4 tiles give bit-identical, finite results on repeated calls.
+
+    A block whose last column group lies partly past the matrix has waves
+    without columns: they copy their share of every A stage for the other
+    waves and compute nothing.  Such a wave must not reach a step's barrier
+    before its own A copies of that step have landed, or the other waves read
+    stale LDS.  At the 26B shape (T = 1024, 128-row tiles of 8 column waves)
+    the last dense gate/up block has 2 of its 8 waves inside the 2112
+    columns, the last routed gate/up block 6 of 8 and the last down blocks 4
+    of 8; in the ragged case (T = 100, the same tiles) the last blocks keep
+    2 of 8 waves (dense gate/up, D = 320), 6 of 8 (routed gate/up, I = 192)
+    and 4 of 8 (down, H = 768)."""
+    if case == "26b_t1024":
+        s = synth.NVFP4_STACK
+        x = synth.make_x(s)
+        pk = synth.make_nvfp4_weights(s)
+        w = pk
+    else:
+        s = synth.FFNShape("ragged_fp4", 100, 768, 16, 2, 192, 320, nvfp4=True)
+        x, w, pk = nvfp4_inputs(s, seed=51)
+    ffn = None
+    first = None
+    for rep in range(4):
+        out, r, inter, ffn = run_gpu(torch, s, x, pk, None, MFMA, nvfp4=True, ffn=ffn)
+        vals = [out] + [G.to_f64(inter[n]) for n in ("h", "y", "h_d", "y_d")]
+        for v in vals:
+            assert np.isfinite(v).all(), f"{case}: non-finite values on call {rep}"
+        if first is None:
+            first = vals
+            if case != "26b_t1024":  # the 26B layer's oracle check is test_nvfp4_26b
+                full_check(s, x, w, None, out, r, inter, nvfp4_w=pk)
+        else:
+            for name, a, b in zip(("out", "h", "y", "h_d", "y_d"), first, vals):
+                assert np.array_equal(a, b), f"{case}: {name} differs between call 0 and call {rep}"
+
+
 # Layers of the NVFP4 residual stack in this test (the stack has 30; set
 # MOE_STACK_LAYERS=30 to run all of them, ~15 s of host work per layer).
 STACK_LAYERS = int(os.environ.get("MOE_STACK_LAYERS", "4"))
