@@ -207,6 +207,26 @@ constexpr bool waits_cover(int BS, int D, int PF, int CA, int NQ, int NS, int w1
   return true;
 }
 
+// The same check for a wave that copies A only (no column inside the
+// matrix): CA copies per step, D - 1 steps ahead, and the wait w.
+constexpr bool a_waits_cover(int D, int CA, int w) {
+  constexpr int kMax = 1024;
+  int step[kMax] = {};
+  int n = 0;
+  auto push = [&](int st) {
+    for (int i = 0; i < CA; ++i) step[n++] = st;
+  };
+  for (int st = 0; st < D - 1; ++st) push(st);
+  for (int s = 0; s < 32; ++s) {
+    int last = -1;
+    for (int i = 0; i < n; ++i)
+      if (step[i] == s) last = i;
+    if (last < 0 || n - 1 - last < w) return false;
+    push(s + D - 1);
+  }
+  return true;
+}
+
 template <int MODE, int W, int NR, int PF, int D, int BS>
 __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0, int units_total) {
   constexpr int kRowsT = 32 * NR;         // rows of a tile
@@ -222,6 +242,7 @@ __global__ __launch_bounds__(W * 64) void k_fp4mm(F4Seg s0, F4Seg s1, int units0
   // s + D - 2 may stay in flight
   constexpr int kWaitA = CA * (D - 2);
   static_assert(D >= 2 && kWaitA < 64, "A ring depth");
+  static_assert(a_waits_cover(D, CA, kWaitA), "an A-only wave's wait leaves its copies of the step in flight");
   static_assert(BS == 1 || D - 1 == BS, "the burst prologue replays the steady order only for D - 1 == BS");
   static_assert(BS <= 4, "a burst's scale dwords are one 16-byte load");
   static_assert(waits_cover(BS, D, PF, (32 * NR * 128) / 1024 / W, 2, 2, kWaitVm), "a step's wait leaves a needed load in flight");
