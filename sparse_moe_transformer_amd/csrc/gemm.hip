@@ -19,12 +19,15 @@
 // 128 up columns at the same output positions (a wave owns 32 of each), so
 // the GeGLU epilogue pairs them in registers.
 //
-// Pipeline: K advances in stages of 32; kStages LDS stages (32 KB each) are
+// Pipeline: K advances in stages of 32; kStages LDS stages (36 KB each) are
 // in flight.  Operand tiles go from global memory straight to LDS (buffer
 // loads with the lds flag, 16 bytes per lane, no registers), issued
 // kStages - 1 stages ahead, without spending VGPRs on them; each wave waits
 // for its own copies of the stage about to be used, then the block meets at
-// a barrier.  Registers hold one 16-k sub-step of fragments ahead: a wave
+// a barrier.  A wave's copies of the next stage go out one after every
+// second MFMA rather than as a burst after the barrier (a burst of the 8
+// waves' copies queues at the CU's address unit and stalls their MFMA
+// issue).  Registers hold one 16-k sub-step of fragments ahead: a wave
 // reads the next sub-step's fragments from LDS while the MFMAs of the
 // current one run.
 //
@@ -316,21 +319,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   const int kt0 = ks * nk_all / S.ksplit;
   const int nk = (ks + 1) * nk_all / S.ksplit - kt0;
 
-  auto issue = [&](int st) {  // copies of stage st into its LDS ring slot
+  // copy n of stage st into its LDS ring slot: n < kACopies an A copy, then
+  // (bf16) the two B copies
+  auto issue_one = [&](int st, int n) {
     const int kk = (kt0 + min(st, nk - 1)) * BK;
     const uint32_t sbase_addr = lds_base + uint32_t((st % kDepth) * kStageStride);
-#pragma unroll
-    for (int q = 0; q < kACopies; ++q) {
-      const int c = kACopies * wave + q;  // wave-uniform
+    if (n < kACopies) {
+      const int c = kACopies * wave + n;  // wave-uniform
       const uint32_t dst = c < BM / 16 ? sbase_addr + c * 1024 : lds_base + uint32_t(kDummy + (c - BM / 16) * 1024);
-      copy_b128_to_lds(arsrc, dst, aoff[q], kk * 2);
+      copy_b128_to_lds(arsrc, dst, aoff[n], kk * 2);
+    } else if (WF == W_BF16) {
+      const int q = n - kACopies;
+      copy_b128_to_lds(brsrc, sbase_addr + kAOpBytes + bh * (kBOpBytes / 2) + (8 * (wave & 3) + 4 * q) * 256,
+                       boff[q], int(uint32_t(kk) * brow));
     }
-    if (WF == W_BF16) {
+  };
+  auto issue = [&](int st) {  // every copy of stage st
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-        copy_b128_to_lds(brsrc, sbase_addr + kAOpBytes + bh * (kBOpBytes / 2) + (8 * (wave & 3) + 4 * q) * 256,
-                         boff[q], int(uint32_t(kk) * brow));
-    }
+    for (int n = 0; n < kACopies + (WF == W_BF16 ? 2 : 0); ++n) issue_one(st, n);
   };
   // raw codes of stage st into its raw area (one copy per lane)
   auto issue_raw = [&](int st) {
@@ -471,6 +477,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
     };
+    // the same with copies n0 .. n1 - 1 of stage st spread between the MFMAs
+    // (one after every second MFMA, the rest after the last): issued as a
+    // burst right after the barrier, the 8 waves' 40 copies queue at the
+    // CU's address unit together and hold the waves' MFMA issue behind them
+    auto mma_copies = [&](const Frags& f, int st, int n0, int n1) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+          if (j == 1 && n0 + i < n1) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(st, n0 + i);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#pragma unroll
+      for (int n = n0 + NI; n < n1; ++n) issue_one(st, n);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
     Frags f0, f1;  // sub-step 0 and sub-step 1 of a stage
 #pragma unroll
     for (int st = 0; st < kDepth; ++st) stage_in(st);
@@ -481,12 +510,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     // Registers hold one sub-step ahead, not a stage.
     auto step = [&](int kt) {
       read_sub(abase_of(kt), bbase_of(kt), 1, f1);
-      mma(f0);
-      if (WF == W_BF16) {
-        // bf16: copies run kDepth stages ahead
+      if (WF == W_BF16 && MODE == MODE_GATEUP) {
+        // gate/up: this wave has read all of stage kt once its second
+        // sub-step's fragments are in registers, so the block meets before
+        // the first sub-step's MFMAs and the copies of stage kt + kDepth are
+        // spread over both sub-steps (measured at T = 4096: 26B gate/up
+        // ~2.5% and E4B gate/up ~4% faster than meeting between them; the
+        // down GEMMs keep the later meeting, E4B down being 6% slower with
+        // the earlier one)
         wait_counts<(kDepth - 2) * kPerStage, 0>();  // stage kt + 1 landed; stage kt's fragments read
         block_barrier();
-        stage_in(kt + kDepth);
+        mma_copies(f0, kt + kDepth, 0, 3);
+        read_sub(abase_of(kt + 1), bbase_of(kt + 1), 0, f0);
+        mma_copies(f1, kt + kDepth, 3, kPerStage);
+        return;
+      }
+      mma(f0);
+      if (WF == W_BF16) {
+        // bf16: copies run kDepth stages ahead, issued between the MFMAs of
+        // the second sub-step
+        wait_counts<(kDepth - 2) * kPerStage, 0>();  // stage kt + 1 landed; stage kt's fragments read
+        block_barrier();
+        read_sub(abase_of(kt + 1), bbase_of(kt + 1), 0, f0);
+        mma_copies(f1, kt + kDepth, 0, kPerStage);
+        return;
       } else {
         // FP8 / NVFP4: stage kt + 2's raw codes are decoded in this step;
         // stages kt + 3 .. kt + kDepth - 1 stay in flight across the barrier
