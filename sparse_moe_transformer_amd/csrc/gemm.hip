@@ -319,8 +319,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
   const int kt0 = ks * nk_all / S.ksplit;
   const int nk = (ks + 1) * nk_all / S.ksplit - kt0;
 
+  // raw codes of stage st into its raw area (one copy per lane)
+  auto issue_raw = [&](int st) {
+    const int kidx = kt0 + min(st, nk - 1);
+    const uint32_t rb = lds_base + uint32_t((st % kDepth) * kStageStride + kAOpBytes);
+    if (WF == W_FP8) {
+      copy_b128_to_lds(rrsrc, rb + wave * 1024, roff, int(uint32_t(kidx * BK) * uint32_t(S.ldb)));
+    }
+  };
   // copy n of stage st into its LDS ring slot: n < kACopies an A copy, then
-  // (bf16) the two B copies
+  // the two B copies (bf16) or the raw codes (FP8)
   auto issue_one = [&](int st, int n) {
     const int kk = (kt0 + min(st, nk - 1)) * BK;
     const uint32_t sbase_addr = lds_base + uint32_t((st % kDepth) * kStageStride);
@@ -332,19 +340,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
       const int q = n - kACopies;
       copy_b128_to_lds(brsrc, sbase_addr + kAOpBytes + bh * (kBOpBytes / 2) + (8 * (wave & 3) + 4 * q) * 256,
                        boff[q], int(uint32_t(kk) * brow));
+    } else {
+      issue_raw(st);
     }
   };
   auto issue = [&](int st) {  // every copy of stage st
 #pragma unroll
     for (int n = 0; n < kACopies + (WF == W_BF16 ? 2 : 0); ++n) issue_one(st, n);
-  };
-  // raw codes of stage st into its raw area (one copy per lane)
-  auto issue_raw = [&](int st) {
-    const int kidx = kt0 + min(st, nk - 1);
-    const uint32_t rb = lds_base + uint32_t((st % kDepth) * kStageStride + kAOpBytes);
-    if (WF == W_FP8) {
-      copy_b128_to_lds(rrsrc, rb + wave * 1024, roff, int(uint32_t(kidx * BK) * uint32_t(S.ldb)));
-    }
   };
   // raw codes of stage st (landed) -> the stage's bf16 B tile
   auto decode = [&](int st) {
@@ -540,10 +542,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
         wait_counts<(kDepth - 3) * kPerStage, 0>();  // stage kt + 2 landed; this wave's decode of kt + 1 written
         block_barrier();
         decode(kt + 2);
-        stage_in(kt + kDepth);
       }
       read_sub(abase_of(kt + 1), bbase_of(kt + 1), 0, f0);
-      mma(f1);
+      mma_copies(f1, kt + kDepth, 0, kPerStage);
     };
     if (WF == W_BF16) {
       wait_counts<(kDepth - 1) * kPerStage, 0>();  // stage 0 landed (this wave's copies)
