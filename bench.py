@@ -505,7 +505,7 @@ def main():
             "value": pre.tokens / (rp["ms_per_step"] * 1e-3), "unit": "tokens/s",
             "ms_per_step": rp["ms_per_step"], "steps": args.prefill_steps,
             "step_tflops": step_tf, "step_mfma_frac": step_tf / BF16_PEAK_TFLOPS,
-            "roofline": {"bound": "mfma", "kernel": "k_gemm<2,0> (gate/up MFMA GEMM: routed + dense, GeGLU)",
+            "roofline": {"bound": "mfma", "kernel": "k_gemm<2,0,true> (gate/up MFMA GEMM: routed + dense, GeGLU)",
                          "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf / BF16_PEAK_TFLOPS, "traffic": traffic_of("k_gemm<2, 0>"),
                          "algorithmic_flops": gateup_flops(pre), "avg_us": gu_us},

@@ -83,6 +83,7 @@ constexpr int kBOpBytes = BN * BK * 2;          // the B tile of a stage: 16 KB
 constexpr int kStageBytes = kAOpBytes + kBOpBytes;  // A, then B
 constexpr int kACopies = 3;                     // A copies per wave per stage (1 KB each; 20 of the 24 land in A)
 constexpr int kDummyBytes = 4096;               // where the 4 surplus A copies land (never read)
+constexpr int kEarlyMaxK = 4096;                // plain (down) launches up to this K meet before a stage's first sub-step
 
 enum { MODE_PLAIN_BF16 = 0, MODE_PLAIN_F32 = 1, MODE_GATEUP = 2 };
 enum { W_BF16 = 0, W_FP8 = 2 };
@@ -186,7 +187,9 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 __device__ __forceinline__ int fa(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int fb(int k) { return 4 * (k & 3); }
 
-template <int MODE, int WF>
+// EARLY (bf16 tiles): the block meets before a stage's first sub-step
+// instead of between its two (see the K loop)
+template <int MODE, int WF, bool EARLY>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0, int units_total) {
   // ---- logical tile of this block (XCD-aware remap over the real tiles) ----
   // Each segment is spread evenly over the XCDs on its own (its tiles can
@@ -512,14 +515,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Seg s0, Seg s1, int units0
     // Registers hold one sub-step ahead, not a stage.
     auto step = [&](int kt) {
       read_sub(abase_of(kt), bbase_of(kt), 1, f1);
-      if (WF == W_BF16 && MODE == MODE_GATEUP) {
-        // gate/up: this wave has read all of stage kt once its second
-        // sub-step's fragments are in registers, so the block meets before
-        // the first sub-step's MFMAs and the copies of stage kt + kDepth are
-        // spread over both sub-steps (measured at T = 4096: 26B gate/up
-        // ~2.5% and E4B gate/up ~4% faster than meeting between them; the
-        // down GEMMs keep the later meeting, E4B down being 6% slower with
-        // the earlier one)
+      if (WF == W_BF16 && EARLY) {
+        // this wave has read all of stage kt once its second sub-step's
+        // fragments are in registers, so the block meets before the first
+        // sub-step's MFMAs and the copies of stage kt + kDepth are spread
+        // over both sub-steps (measured at T = 4096 against meeting between
+        // them: 26B gate/up ~2.5%, E4B gate/up ~4% and 26B down ~2% faster;
+        // the E4B down GEMM, K = 10240 on 160 tiles, 6% slower, so launches
+        // of plain tiles with K past kEarlyMaxK keep the later meeting)
         wait_counts<(kDepth - 2) * kPerStage, 0>();  // stage kt + 1 landed; stage kt's fragments read
         block_barrier();
         mma_copies(f0, kt + kDepth, 0, 3);
@@ -645,13 +648,13 @@ Seg empty_seg() {
   return s;
 }
 
-template <int MODE, int WF>
+template <int MODE, int WF, bool EARLY = MODE == MODE_GATEUP>
 hipError_t launch(const Seg& a, const Seg& b, int units_a, int units_b, hipStream_t st) {
   const int total = units_a + units_b;
   if (total <= 0) return hipSuccess;
   // slots per XCD: both segments' shares (the kernel's remap)
   const int per = (units_a + kXcd - 1) / kXcd + (units_b + kXcd - 1) / kXcd;
-  hipLaunchKernelGGL((k_gemm<MODE, WF>), dim3(per * kXcd), dim3(kThreads), 0, st, a, b, units_a, total);
+  hipLaunchKernelGGL((k_gemm<MODE, WF, EARLY>), dim3(per * kXcd), dim3(kThreads), 0, st, a, b, units_a, total);
   return hipGetLastError();
 }
 
@@ -762,7 +765,9 @@ hipError_t launch_gemm_down(const StreamArgs& a, const Workspace& ws, int max_mt
   e.max_mtiles = sh.E > 0 ? max_mtiles : 0;
   const int ud = sh.D > 0 ? host_units(d) : 0;
   if (a.fp8) return launch<MODE_PLAIN_BF16, W_FP8>(d, e, ud, grouped_units(e), s);
-  return launch<MODE_PLAIN_BF16, W_BF16>(d, e, ud, grouped_units(e), s);
+  const int kmax = std::max(d.A ? d.K : 0, e.mtiles ? e.K : 0);
+  if (kmax <= kEarlyMaxK) return launch<MODE_PLAIN_BF16, W_BF16, true>(d, e, ud, grouped_units(e), s);
+  return launch<MODE_PLAIN_BF16, W_BF16, false>(d, e, ud, grouped_units(e), s);
 }
 
 }  // namespace moe
