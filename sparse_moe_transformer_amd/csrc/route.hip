@@ -412,6 +412,48 @@ __global__ __launch_bounds__(kThreads) void k_align_scatter(Shape sh, Workspace 
   }
 }
 
+// Up to kAlignScanBlocks token blocks: the scatter with the column scan
+// folded in.  Each block sums the per-block counts of k_align_count itself
+// (every expert's total, and its own first row per expert from the blocks
+// before it: at most 64 x 256 counts, from the L2), so the scan launch is
+// saved; past that many blocks the re-reads would cost more than the launch.
+constexpr int kAlignScanBlocks = 64;
+__global__ __launch_bounds__(kThreads) void k_align_scatter_scan(Shape sh, int nblk, Workspace ws) {
+  const int T = sh.T, E = sh.E, k = sh.k;
+  const int b = blockIdx.x;
+  __shared__ int offs[257];
+  __shared__ int base[256];
+  __shared__ int scratch[kThreads / kWave + 1];
+  const int e = threadIdx.x;  // E <= kThreads
+  int tot = 0, pre = 0;
+  if (e < E) {
+#pragma unroll 16
+    for (int b2 = 0; b2 < nblk; ++b2) {
+      const int cnt = ws.blk_base[size_t(b2) * E + e];
+      tot += cnt;
+      pre += b2 < b ? cnt : 0;
+    }
+  }
+  int total;
+  const int off = block_exclusive_scan<kThreads>(e < E ? tot : 0, scratch, total);
+  if (e < E) {
+    offs[e] = off;
+    base[e] = pre;
+  }
+  __syncthreads();
+  if (b == 0) (void)build_offsets_and_tiles<kThreads>(tot, E, ws, scratch);
+  for (int i = threadIdx.x; i < 64 * k; i += kThreads) {
+    const int tl = i / k, j = i % k;
+    const int t = b * 64 + tl;
+    if (t >= T) continue;
+    const int ee = ws.topk_idx[size_t(t) * k + j];
+    const uint64_t m = ws.blk_mask[size_t(b) * E + ee];
+    const int p = offs[ee] + base[ee] + __popcll(m & ((1ull << tl) - 1ull));
+    ws.perm[p] = t;
+    ws.pos[size_t(t) * k + j] = p;
+  }
+}
+
 }  // namespace
 
 bool route_small_fits(const Shape& sh) { return sh.E > 0 && route_small_config(sh).ok; }
@@ -468,8 +510,12 @@ hipError_t launch_route_large(const Shape& sh, const bf16_t* x, const bf16_t* wr
 hipError_t launch_align(const Shape& sh, const Workspace& ws, hipStream_t s) {
   const int nblk = (sh.T + 63) / 64;
   hipLaunchKernelGGL(k_align_count, dim3(nblk), dim3(kThreads), 0, s, sh, ws);
-  hipLaunchKernelGGL(k_align_colscan, dim3(sh.E), dim3(kThreads), 0, s, sh, nblk, ws);
-  hipLaunchKernelGGL(k_align_scatter, dim3(nblk), dim3(kThreads), 0, s, sh, ws);
+  if (nblk <= kAlignScanBlocks) {
+    hipLaunchKernelGGL(k_align_scatter_scan, dim3(nblk), dim3(kThreads), 0, s, sh, nblk, ws);
+  } else {
+    hipLaunchKernelGGL(k_align_colscan, dim3(sh.E), dim3(kThreads), 0, s, sh, nblk, ws);
+    hipLaunchKernelGGL(k_align_scatter, dim3(nblk), dim3(kThreads), 0, s, sh, ws);
+  }
   return hipGetLastError();
 }
 
