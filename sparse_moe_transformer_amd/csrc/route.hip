@@ -192,12 +192,14 @@ __global__ __launch_bounds__(kThreads) void k_topk(Shape sh, int nslices, const 
   const size_t slice = size_t(sh.T) * E;
   for (int e = lane; e < E; e += kWave) {
     const float* p = ws.logits + size_t(t) * E + e;
-    float v[16];
+    // every slice's load in flight before the ordered sum (nslices <=
+    // kRouterSlices: launch_route_large caps it)
+    float v[kRouterSlices];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = j < nslices ? p[j * slice] : 0.f;
+    for (int j = 0; j < kRouterSlices; ++j) v[j] = j < nslices ? p[j * slice] : 0.f;
     float z = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) z += v[j];
+    for (int j = 0; j < kRouterSlices; ++j) z += v[j];
     if (bias) z += bias[e];
     zs[wid][e] = z;
   }
