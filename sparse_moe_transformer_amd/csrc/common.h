@@ -77,7 +77,8 @@ struct Workspace {
 };
 
 constexpr int kRouterSlices = 16;  // most K-slices of the large-T router logits
-constexpr int kRouteSlices = 32;   // K-slices of the small-T router logits
+constexpr int kRouteSlices = 32;   // most K-slices of the small-T router logits
+constexpr int kRouteSlicesFirst = 16;  // ... tried first
 constexpr int kRouteSmallT = 64;   // largest T of the one-block-per-token router and the streaming path
 constexpr int kGemmBM = 320;       // MFMA tile rows (tokens): ~256 +- 16 rows per expert at T = 4096 fit one tile
 constexpr int kFp4BM = 128;        // row tiles of the NVFP4 weight-streaming GEMMs
