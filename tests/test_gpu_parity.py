@@ -158,7 +158,8 @@ def test_router_shapes(torch, H, E, k, T):
     shapes (wide H, E not a multiple of 8) do not fit the small-T router's
     launch shape: they route with the large-T kernels.  T >= 4096 with
     E = 128 or 256 takes the one-launch MFMA router (16 tokens per block
-    below T = 8192, 32 from there; ragged last blocks)."""
+    below T = 8192, 32 from there; ragged last blocks).  E = 256 at H = 2816
+    does not fit the router's 16 K-slices and takes 32."""
     s = synth.FFNShape("rt", T, H, E, k, 64, 64)
     x, w, _ = G.make_inputs(s, seed=E)
     out, r, inter, _ = run_gpu(torch, s, x, w, None, AUTO)
