@@ -13,7 +13,8 @@
 // is a deterministic function of topk_idx (no atomics decide positions).
 //
 // Two routes:
-//   T <= 64: partial logits of kRouteSlices K-slices (many small blocks,
+//   T <= 64: partial logits of 16 K-slices, or 32 where 16 do not fit the
+//     launch shape (route_small_config; many small blocks,
 //     so W_r streams at full bandwidth); the last slice block of a token
 //     group sums the slices in fixed order and routes the group
 //     (route_dev.h).
