@@ -148,7 +148,7 @@ def test_mfma_router_and_bias(torch, T):
         full_check(s, x, w, bias, out, r, inter)
 
 
-@pytest.mark.parametrize("H,E,k,T", [(512, 4, 2, 5), (2816, 256, 8, 8), (512, 24, 3, 7), (512, 16, 4, 8),
+@pytest.mark.parametrize("H,E,k,T", [(512, 4, 2, 5), (2816, 256, 8, 8), (2816, 132, 8, 8), (512, 24, 3, 7), (512, 16, 4, 8),
                                      (256, 8, 8, 8), (2816, 172, 8, 8), (2304, 212, 8, 5), (512, 256, 8, 200),
                                      (512, 128, 8, 97), (512, 256, 8, 8200), (256, 128, 4, 8195),
                                      (512, 256, 8, 4099), (256, 128, 4, 4100)])
@@ -158,8 +158,9 @@ def test_router_shapes(torch, H, E, k, T):
     shapes (wide H, E not a multiple of 8) do not fit the small-T router's
     launch shape: they route with the large-T kernels.  T >= 4096 with
     E = 128 or 256 takes the one-launch MFMA router (16 tokens per block
-    below T = 8192, 32 from there; ragged last blocks).  E = 256 at H = 2816
-    does not fit the router's 16 K-slices and takes 32."""
+    below T = 8192, 32 from there; ragged last blocks).  E = 256 and E = 132
+    (4-expert chunks) at H = 2816 do not fit the router's 16 K-slices and
+    take 32."""
     s = synth.FFNShape("rt", T, H, E, k, 64, 64)
     x, w, _ = G.make_inputs(s, seed=E)
     out, r, inter, _ = run_gpu(torch, s, x, w, None, AUTO)
