@@ -220,7 +220,9 @@ __global__ __launch_bounds__(kThreads) void k_topk(Shape sh, int nslices, const 
 // owns experts 32 w .. + 31 of each half.  Then the logits (+ bias) go to
 // LDS and each wave routes a quarter of the block's tokens (wave_route_token).
 constexpr int kRmStep = 64;  // k per step
-constexpr int kRmDepth = 4;  // LDS stages (6 measured slower: fewer blocks per CU)
+// LDS stages (6 measured slower at T = 16384, fewer blocks per CU; 6 and 7
+// at T = 4096, one block per CU either way, 36.2 and 37.4 against 34.6 us)
+constexpr int kRmDepth = 4;
 // T from which the one-launch router replaces the split-K logits and the
 // per-token top-k, and from which its blocks take 32 tokens instead of 16
 // (the rows past 16 are zeros in the 32-row MFMA; at T = 4096 the 16-token
